@@ -1,0 +1,181 @@
+"""Benchmark: the streaming 5 s video decode at 704x1248 on one MI355X.
+
+One step = one whole decode of the synthetic Wan2.2-style decoder (48 -> 384 channels, 2 mid
+residual blocks, 4 up stages of 384/384/192/96 channels, 2 of them temporal): latents
+[1, 48, 31, 44, 78] in passes of 4 latent frames with the causal caches carried between passes,
+121 bf16 frames of 704x1248 out. Inputs (latents, packed weights, cache, workspace) are resident
+in HBM before the timed region starts; the timed region holds exactly `--steps` decodes.
+
+Prints one JSON line: frames/s (value), ms per decode, the matrix-core conv kernels' achieved
+TFLOP/s against the bf16 dense peak (measured with HIP events around every conv launch in the
+timed region), peak HBM, and the CPU oracle timed on a bounded sample of the same decode.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import causal_convolution_causalconv3d_amd as wvd  # noqa: E402
+import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_conv_flops(spec: wl.DecoderSpec, latent_frames: int, fpp: int, hw=(wl.LATENT_H, wl.LATENT_W)) -> float:
+    """2*M*N*K of every conv of the decode, with the spatial x2 conv in its four-phase form
+    (4 taps of C per phase at the low resolution), real (unpadded) channel counts."""
+    total = 0.0
+    start = 0
+    while start < latent_frames:
+        n = min(fpp, latent_frames - start)
+        first = start == 0
+        T = n
+        H, W = hw
+        c = spec.base_channels
+        P = T * H * W
+        total += 2.0 * P * c * 27 * spec.z_channels
+        for _ in range(spec.mid_resblocks):
+            total += 2.0 * P * c * 27 * c * 2
+        for s, cs in enumerate(spec.stage_channels):
+            P = T * H * W
+            for j in range(spec.stage_resblocks):
+                cin = c if j == 0 else cs
+                total += 2.0 * P * cs * 27 * cin + 2.0 * P * cs * 27 * cs
+                if cin != cs:
+                    total += 2.0 * P * cs * cin
+            c = cs
+            if spec.temporal[s]:
+                Tc = T - 1 if first else T
+                total += 2.0 * Tc * H * W * (2 * c) * 3 * c
+                T = 2 * T - 1 if first else 2 * T
+            total += 2.0 * (4 * T * H * W) * c * (4 * c)
+            H, W = 2 * H, 2 * W
+        total += 2.0 * T * H * W * spec.out_channels * 27 * c
+        start += n
+    return total
+
+
+def cpu_baseline(seconds_hint: float = 15.0):
+    """The oracle (as it stands) on a bounded sample of the same decode: a 12x16 latent crop,
+    one pass of 2 latent frames (8 video frames of 192x256), scaled to full-frame frames/s by the
+    crop's share of the 44x78 latent frame."""
+    import oracle  # CPU baseline leg only
+
+    crop = (12, 16)
+    z, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=2, latent_hw=crop)
+    p = oracle.as_numpy_params(params)
+    zz = oracle._f32(z[0])
+    t0 = time.perf_counter()
+    video = oracle.decode(zz, p, wl.FULL_DECODER, frames_per_pass=2, first_frame_rule=False)
+    dt = time.perf_counter() - t0
+    share = (crop[0] * crop[1]) / float(wl.LATENT_H * wl.LATENT_W)
+    frames_equiv = video.shape[1] * share
+    return {"value": frames_equiv / dt, "unit": "frames/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"oracle decode of a {crop[0]}x{crop[1]} latent crop, 2 latent frames (one pass, {video.shape[1]} "
+                      f"frames of {crop[0] * 16}x{crop[1] * 16}) in {dt:.1f} s, scaled by the crop's share "
+                      f"{share:.4f} of the 44x78 latent frame"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--frames-per-pass", type=int, default=4)
+    ap.add_argument("--latent-frames", type=int, default=31)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode is not sharded here.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    spec = wl.FULL_DECODER
+    _, params = wl.decoder_weights(spec, seed=4, latent_frames=4)
+    z = wl.streaming_latents(seed=5, latent_frames=args.latent_frames).to(torch.bfloat16).cuda()
+    dec = wvd.Decoder(wvd.make_desc(), params)
+    del params
+    fpp = args.frames_per_pass
+    F = dec.video_frames(args.latent_frames, fpp)
+    video = torch.empty((1, 3, F, wl.VIDEO_H, wl.VIDEO_W), dtype=torch.bfloat16, device="cuda")
+    dec.workspace(fpp)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        dec.decode(z, frames_per_pass=fpp, out=video)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+
+    wvd.timing_reset()
+    wvd.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dec.decode(z, frames_per_pass=fpp, out=video)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wvd.timing_enable(False)
+    per_cfg = wvd.timing_read()
+    peak_alloc = torch.cuda.max_memory_allocated() / 2 ** 30
+    peak_reserved = torch.cuda.max_memory_reserved() / 2 ** 30
+
+    elapsed = t1 - t0
+    ms_per_step = 1000.0 * elapsed / args.steps
+    fps = F * args.steps / elapsed
+    conv_ms = sum(v[1] for v in per_cfg.values())
+    conv_flops = sum(v[2] for v in per_cfg.values())
+    # the dominant kernel: the conv configuration with the most time
+    dom_name, (dom_n, dom_ms, dom_flops) = max(per_cfg.items(), key=lambda kv: kv[1][1])
+    dom_tflops = (dom_flops / dom_n) / (dom_ms / dom_n * 1e-3) / 1e12
+    algo = algorithmic_conv_flops(spec, args.latent_frames, fpp)
+
+    line = {
+        "metric": "decoded frames/s at 704x1248 + conv TFLOP/s vs bf16 MFMA peak; peak HBM GiB",
+        "value": round(fps, 3),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "streaming 5 s decode: latents [1,48,31,44,78] -> video [1,3,121,704,1248], "
+                               f"{fpp} latent frames per pass, decoder 48->384, 2 mid resblocks, stages "
+                               "384/384/192/96 (2 resblocks each, time x2 on the first two), random Kaiming weights",
+                   "latent_frames": args.latent_frames, "video_frames": F, "frames_per_pass": fpp,
+                   "global_batch": 1, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "launches_per_step": dom_n // args.steps,
+                     "avg_launch_us": round(1000.0 * dom_ms / dom_n, 2),
+                     "flops_per_launch": dom_flops / dom_n},
+        "conv": {"tflops": round(conv_flops / (conv_ms * 1e-3) / 1e12, 2),
+                 "frac_of_peak": round(conv_flops / (conv_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 "conv_ms_per_step": round(conv_ms / args.steps, 3),
+                 "algorithmic_tflop_per_step": round(algo / 1e12, 3),
+                 "timed_tflop_per_step": round(conv_flops / args.steps / 1e12, 3),
+                 "per_config": {k: {"launches": v[0], "ms": round(v[1], 3), "tflops": round(v[2] / (v[1] * 1e-3) / 1e12, 2)}
+                                for k, v in per_cfg.items()}},
+        "peak_hbm_gib": round(peak_alloc, 3),
+        "peak_hbm_reserved_gib": round(peak_reserved, 3),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,1170 @@
+// C ABI of libwvd: validation, dispatch, the layer drivers (residual block, upsampling), the
+// decoder's weight packing, cache handle and chunk driver, and kernel timing.
+//
+// The decode follows the reference decoder printed on the FastVideo compare page "[perf] PAN2
+// sampling: Wan2.2 VAE decode kernel, split decode, fused DiT kernels" (its decode_chunk,
+// up_block, residual_block, cached_conv and causal_conv functions, and the docstring's "Causal
+// caches" and "The first latent frame yields one frame" parts), in the synthetic topology of
+// wvd_decoder_desc. All device memory comes from the caller.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/wvd.h"
+#include "common.h"
+
+using namespace wvd;
+
+namespace {
+
+thread_local std::string g_err;
+
+wvd_status fail(wvd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+wvd_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return WVD_OK;
+  return fail(WVD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define WVD_TRY(expr)                  \
+  do {                                 \
+    const wvd_status _st = (expr);     \
+    if (_st != WVD_OK) return _st;     \
+  } while (0)
+
+#define WVD_HIP(expr, what)                                   \
+  do {                                                        \
+    const hipError_t _e = (expr);                             \
+    if (_e != hipSuccess) return hip_status(_e, what);        \
+  } while (0)
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t numel(const wvd_tensor* t) { return t->n * t->c * t->t * t->h * t->w; }
+size_t elem_size(int dtype) { return dtype == WVD_BF16 ? 2 : 4; }
+
+// Checks a tensor descriptor; `dtype`/`layout` -1 accept any.
+wvd_status check_tensor(const wvd_tensor* t, const char* name, int dtype, int layout, bool allow_empty_t) {
+  if (!t) return fail(WVD_ERR_ARG, "%s is null", name);
+  if (t->n != 1) return fail(WVD_ERR_SHAPE, "%s: batch must be 1 (got %lld)", name, (long long)t->n);
+  if (t->c <= 0 || t->h <= 0 || t->w <= 0 || t->t < 0 || (!allow_empty_t && t->t == 0))
+    return fail(WVD_ERR_SHAPE, "%s: invalid sizes [%lld,%lld,%lld,%lld,%lld]", name, (long long)t->n,
+                (long long)t->c, (long long)t->t, (long long)t->h, (long long)t->w);
+  if (t->dtype != WVD_F32 && t->dtype != WVD_BF16) return fail(WVD_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+  if (t->layout != WVD_NCTHW && t->layout != WVD_NTHWC)
+    return fail(WVD_ERR_LAYOUT, "%s: unknown layout %d", name, t->layout);
+  if (dtype >= 0 && t->dtype != dtype)
+    return fail(WVD_ERR_DTYPE, "%s: expected %s", name, dtype == WVD_BF16 ? "bf16" : "fp32");
+  if (layout >= 0 && t->layout != layout)
+    return fail(WVD_ERR_LAYOUT, "%s: expected %s", name, layout == WVD_NTHWC ? "NTHWC" : "NCTHW");
+  if (numel(t) > 0 && !t->data) return fail(WVD_ERR_ARG, "%s: null data", name);
+  if (t->data && !aligned16(t->data)) return fail(WVD_ERR_ALIGN, "%s: data not 16-byte aligned", name);
+  if (numel(t) * (int64_t)t->c > ((int64_t)1 << 62)) return fail(WVD_ERR_SHAPE, "%s: too large", name);
+  return WVD_OK;
+}
+
+bool same_grid(const wvd_tensor* a, const wvd_tensor* b) { return a->h == b->h && a->w == b->w; }
+
+// ------------------------------------------------------------------------------------------
+// Timing of the matrix-core conv launches.
+// ------------------------------------------------------------------------------------------
+struct TimingRecord {
+  int config;
+  hipEvent_t start, stop;
+  double flops;
+};
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TimingRecord> pending;
+  std::vector<hipEvent_t> pool;
+  std::vector<int64_t> launches;
+  std::vector<double> ms, flops;
+} g_timing;
+
+hipEvent_t pooled_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t e = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+wvd_status run_conv(const ConvProblem& p, hipStream_t s, double flops) {
+  const bool timed = g_timing.on;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timed) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    e0 = pooled_event();
+    e1 = pooled_event();
+    if (!e0 || !e1) return fail(WVD_ERR_HIP, "hipEventCreate failed");
+    WVD_HIP(hipEventRecord(e0, s), "hipEventRecord");
+  }
+  int cfg = -1;
+  WVD_HIP(launch_conv_mfma(p, s, &cfg), "conv_mfma launch");
+  if (timed) {
+    WVD_HIP(hipEventRecord(e1, s), "hipEventRecord");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.pending.push_back({cfg, e0, e1, flops});
+  }
+  return WVD_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// Convolution problems
+// ------------------------------------------------------------------------------------------
+int64_t packed_elems(int co, int ci, int taps, int phases) {
+  return (int64_t)phases * round_up(co, 32) * taps * round_up(ci, 32);
+}
+
+// A plain causal conv on NTHWC bf16: y [T][H][W][Co] (+ residual).
+ConvProblem plain_problem(const bf16_t* x, const bf16_t* hist, int T, int H, int W, int Ci, int Th,
+                          const void* wpk, int co, int kt, int kh, int kw, const float* bias, bf16_t* y,
+                          const bf16_t* res) {
+  ConvProblem p;
+  memset(&p, 0, sizeof(p));
+  p.x = x;
+  p.hist = hist;
+  p.T = T;
+  p.H = H;
+  p.W = W;
+  p.Ci = Ci;
+  p.Th = hist ? Th : 0;
+  p.wpk = (const bf16_t*)wpk;
+  p.ntaps = kt * kh * kw;
+  p.Cip = (int)round_up(Ci, 32);
+  p.Npad = (int)round_up(co, 32);
+  p.phases = 1;
+  p.kt = kt;
+  p.kh = kh;
+  p.kw = kw;
+  p.N = co;
+  p.bias = bias;
+  p.y = y;
+  p.res = res;
+  p.To = T;
+  p.Ho = H;
+  p.Wo = W;
+  p.nsplit = co;
+  p.fbase = 0;
+  p.fmul = 1;
+  p.hmul = 1;
+  p.wmul = 1;
+  return p;
+}
+
+double conv_flops(int64_t M, int N, int64_t K) { return 2.0 * (double)M * (double)N * (double)K; }
+
+// Causal time conv C -> 2C whose output channel c goes to frame fbase + 2t and C + c to
+// fbase + 2t + 1 of y [To][H][W][C].
+wvd_status run_time_conv(const bf16_t* x, const bf16_t* hist, int T, int H, int W, int C, int Th, const void* wpk,
+                         const float* bias, bf16_t* y, int To, int fbase, hipStream_t s) {
+  ConvProblem p = plain_problem(x, hist, T, H, W, C, Th, wpk, 2 * C, 3, 1, 1, bias, y, nullptr);
+  p.To = To;
+  p.nsplit = C;
+  p.fmul = 2;
+  p.fbase = fbase;
+  return run_conv(p, s, conv_flops((int64_t)T * H * W, 2 * C, 3LL * C));
+}
+
+// Nearest x2 + 3x3 conv as four phase convs: x [T][H][W][C] -> y [T][2H][2W][C].
+wvd_status run_phase_conv(const bf16_t* x, int T, int H, int W, int C, const void* wpk, const float* bias, bf16_t* y,
+                          hipStream_t s) {
+  ConvProblem p = plain_problem(x, nullptr, T, H, W, C, 0, wpk, C, 1, 1, 1, bias, y, nullptr);
+  p.ntaps = 4;
+  p.phases = 4;
+  p.kt = 1;
+  p.kh = 2;
+  p.kw = 2;
+  p.Ho = 2 * H;
+  p.Wo = 2 * W;
+  p.hmul = 2;
+  p.wmul = 2;
+  return run_conv(p, s, conv_flops((int64_t)T * H * W * 4, C, 4LL * C));
+}
+
+// History a conv leaves (the page's cached_conv rule), copied into a separate tensor.
+// frame_bytes: bytes of one frame (NTHWC) of the conv input.
+wvd_status copy_history_out(const void* x, int T, const void* hist, int Th, void* out, size_t frame_bytes,
+                            hipStream_t s) {
+  if (T >= 2) {
+    WVD_HIP(hipMemcpyAsync(out, (const char*)x + (size_t)(T - 2) * frame_bytes, 2 * frame_bytes,
+                           hipMemcpyDeviceToDevice, s),
+            "history copy");
+  } else if (T == 1) {
+    if (Th >= 1) {
+      WVD_HIP(hipMemcpyAsync(out, (const char*)hist + (size_t)(Th - 1) * frame_bytes, frame_bytes,
+                             hipMemcpyDeviceToDevice, s),
+              "history copy");
+      WVD_HIP(hipMemcpyAsync((char*)out + frame_bytes, x, frame_bytes, hipMemcpyDeviceToDevice, s), "history copy");
+    } else {
+      WVD_HIP(hipMemcpyAsync(out, x, frame_bytes, hipMemcpyDeviceToDevice, s), "history copy");
+    }
+  } else if (Th > 0) {
+    WVD_HIP(hipMemcpyAsync(out, hist, (size_t)Th * frame_bytes, hipMemcpyDeviceToDevice, s), "history copy");
+  }
+  return WVD_OK;
+}
+
+int history_frames_after(int T, int Th) {
+  if (T >= 2) return 2;
+  if (T == 1) return Th >= 1 ? 2 : 1;
+  return Th;
+}
+
+// In-place update of a cache slot holding `valid` frames right-aligned in [2][frame].
+wvd_status update_slot(char* slot, int& valid, const void* x, int T, size_t frame_bytes, hipStream_t s) {
+  if (T >= 2) {
+    WVD_HIP(hipMemcpyAsync(slot, (const char*)x + (size_t)(T - 2) * frame_bytes, 2 * frame_bytes,
+                           hipMemcpyDeviceToDevice, s),
+            "cache update");
+    valid = 2;
+  } else if (T == 1) {
+    if (valid >= 1) WVD_HIP(hipMemcpyAsync(slot, slot + frame_bytes, frame_bytes, hipMemcpyDeviceToDevice, s), "cache update");
+    WVD_HIP(hipMemcpyAsync(slot + frame_bytes, x, frame_bytes, hipMemcpyDeviceToDevice, s), "cache update");
+    valid = valid >= 1 ? 2 : 1;
+  }
+  return WVD_OK;
+}
+
+}  // namespace
+
+// ==============================================================================================
+// Basic entry points
+// ==============================================================================================
+extern "C" const char* wvd_last_error(void) { return g_err.c_str(); }
+extern "C" int wvd_abi_version(void) { return WVD_ABI_VERSION; }
+
+extern "C" wvd_status wvd_convert(const wvd_tensor* x, wvd_tensor* y, wvd_stream stream) {
+  WVD_TRY(check_tensor(x, "x", -1, -1, true));
+  WVD_TRY(check_tensor(y, "y", -1, -1, true));
+  if (x->c != y->c || x->t != y->t || x->h != y->h || x->w != y->w)
+    return fail(WVD_ERR_SHAPE, "convert: x and y sizes differ");
+  if (x->data == y->data && numel(x) > 0) return fail(WVD_ERR_ARG, "convert: x and y must not overlap");
+  return hip_status(launch_convert(x->data, x->dtype == WVD_BF16, x->layout == WVD_NCTHW, y->data, y->dtype == WVD_BF16,
+                                   y->layout == WVD_NCTHW, (int)x->c, (int)x->t, (int)x->h, (int)x->w,
+                                   (hipStream_t)stream),
+                    "convert launch");
+}
+
+extern "C" size_t wvd_conv_packed_bytes(int co, int ci, int kt, int kh, int kw, int mode) {
+  if (co <= 0 || ci <= 0) return 0;
+  if (mode == WVD_PACK_PHASE2X) return (size_t)packed_elems(co, ci, 4, 4) * 2;
+  if (mode != WVD_PACK_CONV || kt <= 0 || kh <= 0 || kw <= 0 || kt % 2 == 0 || kh % 2 == 0 || kw % 2 == 0 ||
+      kt * kh * kw > 27)
+    return 0;
+  return (size_t)packed_elems(co, ci, kt * kh * kw, 1) * 2;
+}
+
+extern "C" wvd_status wvd_conv_pack(const void* w_raw, int w_dtype, int co, int ci, int kt, int kh, int kw, int mode,
+                                    void* packed, wvd_stream stream) {
+  if (!w_raw || !packed) return fail(WVD_ERR_ARG, "conv_pack: null pointer");
+  if (w_dtype != WVD_F32 && w_dtype != WVD_BF16) return fail(WVD_ERR_DTYPE, "conv_pack: weight dtype");
+  if (co <= 0 || ci <= 0) return fail(WVD_ERR_SHAPE, "conv_pack: channels must be positive");
+  if (!aligned16(packed)) return fail(WVD_ERR_ALIGN, "conv_pack: packed buffer not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int npad = (int)round_up(co, 32), cip = (int)round_up(ci, 32);
+  if (mode == WVD_PACK_PHASE2X) {
+    if (kt != 1 || kh != 3 || kw != 3) return fail(WVD_ERR_SHAPE, "conv_pack: phase packing needs a 1x3x3 kernel");
+    return hip_status(launch_pack_phase2x(w_raw, w_dtype == WVD_BF16, co, ci, npad, cip, (bf16_t*)packed, s),
+                      "pack launch");
+  }
+  if (mode != WVD_PACK_CONV) return fail(WVD_ERR_ARG, "conv_pack: unknown mode %d", mode);
+  if (kt <= 0 || kh <= 0 || kw <= 0 || kt % 2 == 0 || kh % 2 == 0 || kw % 2 == 0 || kt * kh * kw > 27)
+    return fail(WVD_ERR_UNSUPPORTED, "conv_pack: kernel sizes must be odd with at most 27 taps");
+  return hip_status(launch_pack_conv(w_raw, w_dtype == WVD_BF16, co, ci, kt * kh * kw, npad, cip, (bf16_t*)packed, s),
+                    "pack launch");
+}
+
+extern "C" wvd_status wvd_causal_conv3d(const wvd_tensor* x, const void* w, int co, int kt, int kh, int kw,
+                                        const float* bias, const wvd_tensor* hist, const wvd_tensor* residual,
+                                        wvd_tensor* y, wvd_tensor* hist_out, wvd_stream stream) {
+  WVD_TRY(check_tensor(x, "x", -1, -1, true));
+  WVD_TRY(check_tensor(y, "y", x->dtype, x->layout, true));
+  if (!w) return fail(WVD_ERR_ARG, "weights are null");
+  if (co <= 0 || kt <= 0 || kh <= 0 || kw <= 0 || kt % 2 == 0 || kh % 2 == 0 || kw % 2 == 0 || kt * kh * kw > 27)
+    return fail(WVD_ERR_UNSUPPORTED, "kernel sizes must be odd with at most 27 taps, co > 0");
+  if (y->c != co || y->t != x->t || !same_grid(x, y)) return fail(WVD_ERR_SHAPE, "y must be [1, co, T, H, W] of x");
+  const int P = 2 * (kt / 2);
+  int Th = 0;
+  if (hist) {
+    WVD_TRY(check_tensor(hist, "hist", x->dtype, x->layout, true));
+    if (hist->c != x->c || !same_grid(hist, x)) return fail(WVD_ERR_SHAPE, "hist must match x in c, h, w");
+    if (hist->t > P) return fail(WVD_ERR_SHAPE, "hist has %lld frames, the conv takes at most %d", (long long)hist->t, P);
+    Th = (int)hist->t;
+  }
+  if (hist_out) {
+    WVD_TRY(check_tensor(hist_out, "hist_out", x->dtype, x->layout, true));
+    if (hist_out->c != x->c || !same_grid(hist_out, x)) return fail(WVD_ERR_SHAPE, "hist_out must match x in c, h, w");
+    const int want = history_frames_after((int)x->t, Th);
+    if (hist_out->t != want) return fail(WVD_ERR_SHAPE, "hist_out must have %d frames", want);
+    if (hist && hist_out->data == hist->data && want > 0) return fail(WVD_ERR_ARG, "hist_out may not alias hist");
+    if (x->layout != WVD_NTHWC) return fail(WVD_ERR_LAYOUT, "hist_out needs NTHWC tensors");
+  }
+  if (!aligned16(w)) return fail(WVD_ERR_ALIGN, "weights not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int T = (int)x->t, H = (int)x->h, W = (int)x->w, Ci = (int)x->c;
+  if (x->dtype == WVD_F32) {
+    if (residual) return fail(WVD_ERR_UNSUPPORTED, "the fp32 path takes no residual");
+    if (T > 0)
+      WVD_HIP(launch_conv_fp32((const float*)x->data, hist ? (const float*)hist->data : nullptr, (const float*)w, bias,
+                               (float*)y->data, Ci, T, H, W, Th, co, kt, kh, kw, x->layout == WVD_NCTHW, s),
+              "conv_fp32 launch");
+  } else {
+    if (x->layout != WVD_NTHWC) return fail(WVD_ERR_LAYOUT, "the bf16 path needs NTHWC tensors");
+    if (Ci % 8 != 0) return fail(WVD_ERR_UNSUPPORTED, "bf16 path: input channels must be a multiple of 8");
+    if (co % 4 != 0) return fail(WVD_ERR_UNSUPPORTED, "bf16 path: output channels must be a multiple of 4");
+    if (residual) {
+      WVD_TRY(check_tensor(residual, "residual", WVD_BF16, WVD_NTHWC, true));
+      if (residual->c != co || residual->t != x->t || !same_grid(residual, x))
+        return fail(WVD_ERR_SHAPE, "residual must have y's shape");
+    }
+    if ((int64_t)T * H * W >= ((int64_t)1 << 31)) return fail(WVD_ERR_UNSUPPORTED, "too many positions");
+    if (T > 0) {
+      ConvProblem p = plain_problem((const bf16_t*)x->data, hist ? (const bf16_t*)hist->data : nullptr, T, H, W, Ci,
+                                    Th, w, co, kt, kh, kw, bias, (bf16_t*)y->data,
+                                    residual ? (const bf16_t*)residual->data : nullptr);
+      WVD_TRY(run_conv(p, s, conv_flops((int64_t)T * H * W, co, (int64_t)kt * kh * kw * Ci)));
+    }
+  }
+  if (hist_out)
+    WVD_TRY(copy_history_out(x->data, T, hist ? hist->data : nullptr, Th, hist_out->data,
+                             (size_t)H * W * Ci * elem_size(x->dtype), s));
+  return WVD_OK;
+}
+
+extern "C" wvd_status wvd_rmsnorm_silu(const wvd_tensor* x, const float* gamma, float eps, int apply_silu, wvd_tensor* y,
+                                       wvd_stream stream) {
+  WVD_TRY(check_tensor(x, "x", WVD_BF16, WVD_NTHWC, true));
+  WVD_TRY(check_tensor(y, "y", WVD_BF16, WVD_NTHWC, true));
+  if (!gamma) return fail(WVD_ERR_ARG, "gamma is null");
+  if (x->c != y->c || x->t != y->t || !same_grid(x, y)) return fail(WVD_ERR_SHAPE, "y must have x's shape");
+  if (x->c % 8 != 0 || x->c > 512) return fail(WVD_ERR_UNSUPPORTED, "channels must be a multiple of 8, at most 512");
+  if (!(eps >= 0.0f)) return fail(WVD_ERR_ARG, "eps must be >= 0");
+  return hip_status(launch_norm_silu((const bf16_t*)x->data, gamma, eps, apply_silu, (bf16_t*)y->data,
+                                     x->t * x->h * x->w, (int)x->c, (hipStream_t)stream),
+                    "norm launch");
+}
+
+// ==============================================================================================
+// Residual block
+// ==============================================================================================
+namespace {
+
+struct ResblockArgs {
+  const bf16_t* x;
+  bf16_t* y;
+  int T, H, W;
+  const wvd_resblock_weights* w;
+  float eps;
+  const bf16_t* hist1;
+  int th1;
+  const bf16_t* hist2;
+  int th2;
+  // workspace
+  bf16_t* a;   // activated input, max(cin, cout) channels
+  bf16_t* h;   // conv1 output
+  bf16_t* sc;  // shortcut output (cin != cout)
+};
+
+// y = conv2(a2) + (x or shortcut(x)); a1 = SiLU(norm1(x)), h = conv1(a1), a2 = SiLU(norm2(h)).
+// `after_conv1` / `after_conv2` run right after each conv (the cache updates read a1 / a2).
+template <class F1, class F2>
+wvd_status resblock_core(const ResblockArgs& r, hipStream_t s, F1 after_conv1, F2 after_conv2) {
+  const wvd_resblock_weights* w = r.w;
+  const int64_t P = (int64_t)r.T * r.H * r.W;
+  const bf16_t* residual = r.x;
+  if (w->cin != w->cout) {
+    ConvProblem sc = plain_problem(r.x, nullptr, r.T, r.H, r.W, w->cin, 0, w->shortcut, w->cout, 1, 1, 1,
+                                   w->shortcut_bias, r.sc, nullptr);
+    WVD_TRY(run_conv(sc, s, conv_flops(P, w->cout, w->cin)));
+    residual = r.sc;
+  }
+  WVD_HIP(launch_norm_silu(r.x, w->gamma1, r.eps, 1, r.a, P, w->cin, s), "norm launch");
+  ConvProblem c1 = plain_problem(r.a, r.hist1, r.T, r.H, r.W, w->cin, r.th1, w->conv1, w->cout, 3, 3, 3, w->bias1, r.h,
+                                 nullptr);
+  WVD_TRY(run_conv(c1, s, conv_flops(P, w->cout, 27LL * w->cin)));
+  WVD_TRY(after_conv1(r.a));
+  WVD_HIP(launch_norm_silu(r.h, w->gamma2, r.eps, 1, r.a, P, w->cout, s), "norm launch");
+  ConvProblem c2 = plain_problem(r.a, r.hist2, r.T, r.H, r.W, w->cout, r.th2, w->conv2, w->cout, 3, 3, 3, w->bias2,
+                                 r.y, residual);
+  WVD_TRY(run_conv(c2, s, conv_flops(P, w->cout, 27LL * w->cout)));
+  WVD_TRY(after_conv2(r.a));
+  return WVD_OK;
+}
+
+size_t resblock_ws(int cin, int cout, int64_t positions) {
+  const int64_t cmax = std::max(cin, cout);
+  size_t b = (size_t)round_up(positions * cmax * 2, 256) + (size_t)round_up(positions * cout * 2, 256);
+  if (cin != cout) b += (size_t)round_up(positions * cout * 2, 256);
+  return b;
+}
+
+wvd_status check_resblock_weights(const wvd_resblock_weights* w) {
+  if (!w) return fail(WVD_ERR_ARG, "resblock weights are null");
+  if (w->cin <= 0 || w->cout <= 0 || w->cin % 8 || w->cout % 8 || w->cin > 512 || w->cout > 512)
+    return fail(WVD_ERR_UNSUPPORTED, "resblock channels must be multiples of 8 up to 512");
+  if (!w->gamma1 || !w->conv1 || !w->gamma2 || !w->conv2) return fail(WVD_ERR_ARG, "resblock weight pointer is null");
+  if (w->cin != w->cout && !w->shortcut) return fail(WVD_ERR_ARG, "cin != cout needs the shortcut weight");
+  if (!aligned16(w->conv1) || !aligned16(w->conv2) || (w->shortcut && !aligned16(w->shortcut)))
+    return fail(WVD_ERR_ALIGN, "packed weights must be 16-byte aligned");
+  return WVD_OK;
+}
+
+}  // namespace
+
+extern "C" size_t wvd_resblock_workspace_bytes(int cin, int cout, int t, int h, int w) {
+  if (cin <= 0 || cout <= 0 || t < 0 || h <= 0 || w <= 0) return 0;
+  return resblock_ws(cin, cout, (int64_t)t * h * w);
+}
+
+extern "C" wvd_status wvd_resblock(const wvd_tensor* x, const wvd_resblock_weights* wts, float eps,
+                                   const wvd_tensor* hist1, const wvd_tensor* hist2, wvd_tensor* y,
+                                   wvd_tensor* hist1_out, wvd_tensor* hist2_out, void* ws, size_t ws_bytes,
+                                   wvd_stream stream) {
+  WVD_TRY(check_resblock_weights(wts));
+  WVD_TRY(check_tensor(x, "x", WVD_BF16, WVD_NTHWC, true));
+  WVD_TRY(check_tensor(y, "y", WVD_BF16, WVD_NTHWC, true));
+  if (x->c != wts->cin || y->c != wts->cout || y->t != x->t || !same_grid(x, y))
+    return fail(WVD_ERR_SHAPE, "x must be [1, cin, T, H, W] and y [1, cout, T, H, W]");
+  if (x->data == y->data && numel(x) > 0) return fail(WVD_ERR_ARG, "y may not alias x");
+  const wvd_tensor* hs[2] = {hist1, hist2};
+  const wvd_tensor* ho[2] = {hist1_out, hist2_out};
+  const int hc[2] = {wts->cin, wts->cout};
+  int th[2] = {0, 0};
+  for (int i = 0; i < 2; ++i) {
+    if (hs[i]) {
+      WVD_TRY(check_tensor(hs[i], i ? "hist2" : "hist1", WVD_BF16, WVD_NTHWC, true));
+      if (hs[i]->c != hc[i] || !same_grid(hs[i], x) || hs[i]->t > 2)
+        return fail(WVD_ERR_SHAPE, "hist%d must be [1, %d, <=2, H, W]", i + 1, hc[i]);
+      th[i] = (int)hs[i]->t;
+    }
+  }
+  for (int i = 0; i < 2; ++i) {
+    if (ho[i]) {
+      WVD_TRY(check_tensor(ho[i], i ? "hist2_out" : "hist1_out", WVD_BF16, WVD_NTHWC, true));
+      const int want = history_frames_after((int)x->t, th[i]);
+      if (ho[i]->c != hc[i] || !same_grid(ho[i], x) || ho[i]->t != want)
+        return fail(WVD_ERR_SHAPE, "hist%d_out must be [1, %d, %d, H, W]", i + 1, hc[i], want);
+      if (hs[i] && hs[i]->data == ho[i]->data && want > 0) return fail(WVD_ERR_ARG, "hist_out may not alias hist");
+    }
+  }
+  if (!(eps >= 0.0f)) return fail(WVD_ERR_ARG, "eps must be >= 0");
+  const int64_t P = x->t * x->h * x->w;
+  const size_t need = resblock_ws(wts->cin, wts->cout, P);
+  if (ws_bytes < need) return fail(WVD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+  if (P > 0 && (!ws || !aligned16(ws))) return fail(WVD_ERR_ALIGN, "workspace null or not 16-byte aligned");
+  if (x->t == 0) {
+    hipStream_t s = (hipStream_t)stream;
+    for (int i = 0; i < 2; ++i)
+      if (ho[i] && hs[i] && th[i] > 0)
+        WVD_HIP(hipMemcpyAsync(ho[i]->data, hs[i]->data, (size_t)numel(hs[i]) * 2, hipMemcpyDeviceToDevice, s),
+                "history copy");
+    return WVD_OK;
+  }
+  ResblockArgs r;
+  r.x = (const bf16_t*)x->data;
+  r.y = (bf16_t*)y->data;
+  r.T = (int)x->t;
+  r.H = (int)x->h;
+  r.W = (int)x->w;
+  r.w = wts;
+  r.eps = eps;
+  r.hist1 = hist1 ? (const bf16_t*)hist1->data : nullptr;
+  r.th1 = th[0];
+  r.hist2 = hist2 ? (const bf16_t*)hist2->data : nullptr;
+  r.th2 = th[1];
+  char* base = (char*)ws;
+  r.a = (bf16_t*)base;
+  base += round_up(P * std::max(wts->cin, wts->cout) * 2, 256);
+  r.h = (bf16_t*)base;
+  base += round_up(P * wts->cout * 2, 256);
+  r.sc = (bf16_t*)base;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t fb1 = (size_t)x->h * x->w * wts->cin * 2, fb2 = (size_t)x->h * x->w * wts->cout * 2;
+  return resblock_core(
+      r, s,
+      [&](const bf16_t* a1) {
+        return hist1_out ? copy_history_out(a1, r.T, r.hist1, th[0], hist1_out->data, fb1, s) : WVD_OK;
+      },
+      [&](const bf16_t* a2) {
+        return hist2_out ? copy_history_out(a2, r.T, r.hist2, th[1], hist2_out->data, fb2, s) : WVD_OK;
+      });
+}
+
+// ==============================================================================================
+// Upsampling
+// ==============================================================================================
+extern "C" size_t wvd_upsample_workspace_bytes(int c, int t, int h, int w, int spatial, int temporal, int order) {
+  if (c <= 0 || t < 0 || h <= 0 || w <= 0) return 0;
+  if (spatial && temporal) {
+    // the intermediate of the first step
+    const int64_t inter = (order == WVD_SPATIAL_FIRST) ? (int64_t)t * 4 * h * w * c : (int64_t)2 * t * h * w * c;
+    return (size_t)round_up(inter * 2, 256);
+  }
+  return 0;
+}
+
+extern "C" wvd_status wvd_upsample(const wvd_tensor* x, const void* spatial, const float* spatial_bias,
+                                   const void* temporal, const float* temporal_bias, int order, int first,
+                                   const wvd_tensor* time_hist, wvd_tensor* y, wvd_tensor* time_hist_out, void* ws,
+                                   size_t ws_bytes, wvd_stream stream) {
+  WVD_TRY(check_tensor(x, "x", WVD_BF16, WVD_NTHWC, true));
+  WVD_TRY(check_tensor(y, "y", WVD_BF16, WVD_NTHWC, true));
+  if (!spatial && !temporal) return fail(WVD_ERR_ARG, "neither step is on");
+  if (order != WVD_TIME_FIRST && order != WVD_SPATIAL_FIRST) return fail(WVD_ERR_ARG, "unknown order");
+  if ((spatial && !aligned16(spatial)) || (temporal && !aligned16(temporal)))
+    return fail(WVD_ERR_ALIGN, "packed weights must be 16-byte aligned");
+  const int C = (int)x->c, T = (int)x->t;
+  if (C % 8 != 0) return fail(WVD_ERR_UNSUPPORTED, "channels must be a multiple of 8");
+  const int tf = (temporal && first) ? 1 : 0;  // frames that pass through the time step
+  const int64_t To = temporal ? (first ? (T > 0 ? 2LL * T - 1 : 0) : 2LL * T) : T;
+  const int64_t Ho = spatial ? 2 * x->h : x->h, Wo = spatial ? 2 * x->w : x->w;
+  if (y->c != C || y->t != To || y->h != Ho || y->w != Wo)
+    return fail(WVD_ERR_SHAPE, "y must be [1, %d, %lld, %lld, %lld]", C, (long long)To, (long long)Ho, (long long)Wo);
+  if (x->data == y->data && numel(x) > 0) return fail(WVD_ERR_ARG, "y may not alias x");
+  // geometry of the time conv's input grid
+  const int th_h = (int)((temporal && order == WVD_SPATIAL_FIRST && spatial) ? Ho : x->h);
+  const int th_w = (int)((temporal && order == WVD_SPATIAL_FIRST && spatial) ? Wo : x->w);
+  const int Tc = T - tf;  // frames the time conv sees
+  int Th = 0;
+  if (time_hist) {
+    if (!temporal) return fail(WVD_ERR_ARG, "time_hist without a time step");
+    WVD_TRY(check_tensor(time_hist, "time_hist", WVD_BF16, WVD_NTHWC, true));
+    if (time_hist->c != C || time_hist->h != th_h || time_hist->w != th_w || time_hist->t > 2)
+      return fail(WVD_ERR_SHAPE, "time_hist must be [1, C, <=2, h, w] of the time conv's input");
+    if (first && time_hist->t > 0) return fail(WVD_ERR_STATE, "the first chunk has no time history");
+    Th = (int)time_hist->t;
+  }
+  if (time_hist_out) {
+    if (!temporal) return fail(WVD_ERR_ARG, "time_hist_out without a time step");
+    WVD_TRY(check_tensor(time_hist_out, "time_hist_out", WVD_BF16, WVD_NTHWC, true));
+    const int want = history_frames_after(Tc < 0 ? 0 : Tc, Th);
+    if (time_hist_out->c != C || time_hist_out->h != th_h || time_hist_out->w != th_w || time_hist_out->t != want)
+      return fail(WVD_ERR_SHAPE, "time_hist_out must be [1, C, %d, h, w]", want);
+    if (time_hist && time_hist->data == time_hist_out->data && want > 0)
+      return fail(WVD_ERR_ARG, "time_hist_out may not alias time_hist");
+  }
+  const size_t need = wvd_upsample_workspace_bytes(C, T, (int)x->h, (int)x->w, spatial != nullptr, temporal != nullptr, order);
+  if (ws_bytes < need) return fail(WVD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+  if (need > 0 && (!ws || !aligned16(ws))) return fail(WVD_ERR_ALIGN, "workspace null or not 16-byte aligned");
+  if (T == 0) return WVD_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int H = (int)x->h, W = (int)x->w;
+  const bf16_t* hist = time_hist ? (const bf16_t*)time_hist->data : nullptr;
+
+  // time step: src [T][h][w][C] -> dst [To_t][h][w][C]
+  auto time_step = [&](const bf16_t* src, int h, int w, bf16_t* dst) -> wvd_status {
+    const size_t fb = (size_t)h * w * C * 2;
+    const int To_t = first ? 2 * T - 1 : 2 * T;
+    if (tf) WVD_HIP(hipMemcpyAsync(dst, src, fb, hipMemcpyDeviceToDevice, s), "first frame copy");
+    if (Tc > 0) WVD_TRY(run_time_conv(src + (size_t)tf * h * w * C, hist, Tc, h, w, C, Th, temporal, temporal_bias, dst, To_t, tf, s));
+    if (time_hist_out) WVD_TRY(copy_history_out(src + (size_t)tf * h * w * C, Tc, hist, Th, time_hist_out->data, fb, s));
+    return WVD_OK;
+  };
+  if (spatial && temporal) {
+    bf16_t* inter = (bf16_t*)ws;
+    if (order == WVD_TIME_FIRST) {
+      WVD_TRY(time_step((const bf16_t*)x->data, H, W, inter));
+      WVD_TRY(run_phase_conv(inter, (int)To, H, W, C, spatial, spatial_bias, (bf16_t*)y->data, s));
+    } else {
+      WVD_TRY(run_phase_conv((const bf16_t*)x->data, T, H, W, C, spatial, spatial_bias, inter, s));
+      WVD_TRY(time_step(inter, 2 * H, 2 * W, (bf16_t*)y->data));
+    }
+  } else if (spatial) {
+    WVD_TRY(run_phase_conv((const bf16_t*)x->data, T, H, W, C, spatial, spatial_bias, (bf16_t*)y->data, s));
+  } else {
+    WVD_TRY(time_step((const bf16_t*)x->data, H, W, (bf16_t*)y->data));
+  }
+  return WVD_OK;
+}
+
+// ==============================================================================================
+// Decoder: parameters, packing, cache, chunk driver
+// ==============================================================================================
+namespace {
+
+enum ParamKind { K_CONV3 = 0, K_CONV1 = 1, K_TIME = 2, K_SPATIAL = 3, K_GAMMA = 4, K_BIAS = 5 };
+
+struct Param {
+  std::string name;
+  int kind;
+  int co, ci;          // convs; gamma/bias: co = length
+  size_t offset;       // in the packed blob
+  size_t bytes;
+};
+
+struct ResPlan {
+  int cin, cout;
+  int gamma1, w1, b1, gamma2, w2, b2, ws, bs;  // param indices (ws/bs -1 without shortcut)
+  int slot1, slot2;
+};
+
+struct StagePlan {
+  std::vector<ResPlan> res;
+  int c;
+  int temporal;
+  int tw, tb, time_slot;  // time conv params and cache slot (-1 if none)
+  int sw, sb;
+};
+
+struct Slot {
+  int level, c;
+  size_t offset, frame_bytes;
+};
+
+struct Plan {
+  std::vector<Param> params;
+  int conv_in_w, conv_in_b, conv_in_slot;
+  std::vector<ResPlan> mid;
+  std::vector<StagePlan> stages;
+  int norm_out, out_w, out_b, out_slot;
+  std::vector<Slot> slots;
+  size_t packed_bytes, cache_bytes;
+};
+
+wvd_status check_desc(const wvd_decoder_desc* d) {
+  if (!d) return fail(WVD_ERR_ARG, "decoder desc is null");
+  if (d->n_stages < 0 || d->n_stages > WVD_MAX_STAGES) return fail(WVD_ERR_ARG, "n_stages out of range");
+  auto okc = [](int c) { return c > 0 && c % 8 == 0 && c <= 512; };
+  if (!okc(d->z_channels) || !okc(d->base_channels))
+    return fail(WVD_ERR_UNSUPPORTED, "z and base channels must be multiples of 8 up to 512");
+  for (int s = 0; s < d->n_stages; ++s)
+    if (!okc(d->stage_channels[s])) return fail(WVD_ERR_UNSUPPORTED, "stage channels must be multiples of 8 up to 512");
+  if (d->mid_resblocks < 0 || d->stage_resblocks < 0 || d->mid_resblocks > 16 || d->stage_resblocks > 16)
+    return fail(WVD_ERR_ARG, "resblock counts out of range");
+  if (d->out_channels <= 0 || d->out_channels > 32) return fail(WVD_ERR_UNSUPPORTED, "out_channels must be 1..32");
+  if (d->latent_h <= 0 || d->latent_w <= 0 || d->latent_h > 4096 || d->latent_w > 4096)
+    return fail(WVD_ERR_ARG, "latent size out of range");
+  if (!(d->eps >= 0.0f)) return fail(WVD_ERR_ARG, "eps must be >= 0");
+  return WVD_OK;
+}
+
+int add_param(Plan& p, const std::string& name, int kind, int co, int ci) {
+  Param q;
+  q.name = name;
+  q.kind = kind;
+  q.co = co;
+  q.ci = ci;
+  switch (kind) {
+    case K_CONV3: q.bytes = (size_t)packed_elems(co, ci, 27, 1) * 2; break;
+    case K_CONV1: q.bytes = (size_t)packed_elems(co, ci, 1, 1) * 2; break;
+    case K_TIME: q.bytes = (size_t)packed_elems(co, ci, 3, 1) * 2; break;
+    case K_SPATIAL: q.bytes = (size_t)packed_elems(co, ci, 4, 4) * 2; break;
+    default: q.bytes = (size_t)co * 4; break;
+  }
+  q.offset = 0;
+  p.params.push_back(q);
+  return (int)p.params.size() - 1;
+}
+
+int add_slot(Plan& p, const wvd_decoder_desc* d, int level, int c) {
+  Slot s;
+  s.level = level;
+  s.c = c;
+  s.frame_bytes = (size_t)(d->latent_h << level) * (size_t)(d->latent_w << level) * c * 2;
+  s.offset = 0;
+  p.slots.push_back(s);
+  return (int)p.slots.size() - 1;
+}
+
+ResPlan add_res(Plan& p, const wvd_decoder_desc* d, const std::string& pre, int cin, int cout, int level) {
+  ResPlan r;
+  r.cin = cin;
+  r.cout = cout;
+  r.gamma1 = add_param(p, pre + ".norm1.gamma", K_GAMMA, cin, 0);
+  r.w1 = add_param(p, pre + ".conv1.weight", K_CONV3, cout, cin);
+  r.b1 = add_param(p, pre + ".conv1.bias", K_BIAS, cout, 0);
+  r.gamma2 = add_param(p, pre + ".norm2.gamma", K_GAMMA, cout, 0);
+  r.w2 = add_param(p, pre + ".conv2.weight", K_CONV3, cout, cout);
+  r.b2 = add_param(p, pre + ".conv2.bias", K_BIAS, cout, 0);
+  r.ws = r.bs = -1;
+  if (cin != cout) {
+    r.ws = add_param(p, pre + ".shortcut.weight", K_CONV1, cout, cin);
+    r.bs = add_param(p, pre + ".shortcut.bias", K_BIAS, cout, 0);
+  }
+  r.slot1 = add_slot(p, d, level, cin);
+  r.slot2 = add_slot(p, d, level, cout);
+  return r;
+}
+
+Plan make_plan(const wvd_decoder_desc* d) {
+  Plan p;
+  int c = d->base_channels;
+  p.conv_in_w = add_param(p, "conv_in.weight", K_CONV3, c, d->z_channels);
+  p.conv_in_b = add_param(p, "conv_in.bias", K_BIAS, c, 0);
+  p.conv_in_slot = add_slot(p, d, 0, d->z_channels);
+  for (int i = 0; i < d->mid_resblocks; ++i) p.mid.push_back(add_res(p, d, "mid." + std::to_string(i), c, c, 0));
+  for (int s = 0; s < d->n_stages; ++s) {
+    StagePlan st;
+    const int cs = d->stage_channels[s];
+    for (int j = 0; j < d->stage_resblocks; ++j)
+      st.res.push_back(add_res(p, d, "up." + std::to_string(s) + ".res." + std::to_string(j), j == 0 ? c : cs, cs, s));
+    c = cs;
+    st.c = c;
+    st.temporal = d->stage_temporal[s] != 0;
+    st.tw = st.tb = st.time_slot = -1;
+    if (st.temporal) {
+      st.tw = add_param(p, "up." + std::to_string(s) + ".time.weight", K_TIME, 2 * c, c);
+      st.tb = add_param(p, "up." + std::to_string(s) + ".time.bias", K_BIAS, 2 * c, 0);
+      st.time_slot = add_slot(p, d, s, c);
+    }
+    st.sw = add_param(p, "up." + std::to_string(s) + ".spatial.weight", K_SPATIAL, c, c);
+    st.sb = add_param(p, "up." + std::to_string(s) + ".spatial.bias", K_BIAS, c, 0);
+    p.stages.push_back(st);
+  }
+  p.norm_out = add_param(p, "norm_out.gamma", K_GAMMA, c, 0);
+  p.out_w = add_param(p, "conv_out.weight", K_CONV3, d->out_channels, c);
+  p.out_b = add_param(p, "conv_out.bias", K_BIAS, d->out_channels, 0);
+  p.out_slot = add_slot(p, d, d->n_stages, c);
+  size_t off = 0;
+  for (auto& q : p.params) {
+    q.offset = off;
+    off += (size_t)round_up((int64_t)q.bytes, 256);
+  }
+  p.packed_bytes = off;
+  off = 0;
+  for (auto& s : p.slots) {
+    s.offset = off;
+    off += (size_t)round_up((int64_t)(2 * s.frame_bytes), 256);
+  }
+  p.cache_bytes = off;
+  return p;
+}
+
+void param_shape(const wvd_decoder_desc* d, const Param& q, int* ndim, int64_t shape[5]) {
+  (void)d;
+  for (int i = 0; i < 5; ++i) shape[i] = 0;
+  switch (q.kind) {
+    case K_CONV3: *ndim = 5; shape[0] = q.co; shape[1] = q.ci; shape[2] = shape[3] = shape[4] = 3; break;
+    case K_CONV1: *ndim = 5; shape[0] = q.co; shape[1] = q.ci; shape[2] = shape[3] = shape[4] = 1; break;
+    case K_TIME: *ndim = 5; shape[0] = q.co; shape[1] = q.ci; shape[2] = 3; shape[3] = shape[4] = 1; break;
+    case K_SPATIAL: *ndim = 4; shape[0] = q.co; shape[1] = q.ci; shape[2] = shape[3] = 3; break;
+    default: *ndim = 1; shape[0] = q.co; break;
+  }
+}
+
+uint64_t desc_hash(const wvd_decoder_desc* d) {
+  // FNV-1a over the descriptor's fields
+  uint64_t h = 1469598103934665603ULL;
+  const int v[] = {d->z_channels, d->base_channels, d->n_stages, d->mid_resblocks, d->stage_resblocks,
+                   d->out_channels, d->latent_h, d->latent_w};
+  auto mix = [&](uint32_t x) {
+    for (int i = 0; i < 4; ++i) {
+      h ^= (x >> (8 * i)) & 0xffu;
+      h *= 1099511628211ULL;
+    }
+  };
+  for (int x : v) mix((uint32_t)x);
+  for (int s = 0; s < d->n_stages; ++s) {
+    mix((uint32_t)d->stage_channels[s]);
+    mix((uint32_t)d->stage_temporal[s]);
+  }
+  uint32_t e;
+  memcpy(&e, &d->eps, 4);
+  mix(e);
+  return h;
+}
+
+// Frames at each point of one chunk of n latent frames.
+struct ChunkFrames {
+  int64_t stage_in[WVD_MAX_STAGES];  // frames of the stage's resblocks
+  int64_t stage_out[WVD_MAX_STAGES]; // after the stage's time conv
+  int64_t video;
+};
+
+ChunkFrames chunk_frames(const wvd_decoder_desc* d, int64_t n, bool first_rule) {
+  ChunkFrames f;
+  int64_t t = n;
+  for (int s = 0; s < d->n_stages; ++s) {
+    f.stage_in[s] = t;
+    if (d->stage_temporal[s]) t = (first_rule && t > 0) ? 2 * t - 1 : 2 * t;
+    f.stage_out[s] = t;
+  }
+  f.video = t;
+  return f;
+}
+
+// Workspace buffers of the chunk driver (elements of bf16).
+struct WsLayout {
+  size_t zc, x0, x1, a, h, sc;  // byte offsets
+  size_t total;
+};
+
+WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n) {
+  const ChunkFrames f = chunk_frames(d, n, false);  // the largest frame counts
+  int64_t stream = 0, act = 0, hbuf = 0, scbuf = 0;
+  const int64_t hw0 = (int64_t)d->latent_h * d->latent_w;
+  auto hw = [&](int level) { return hw0 << (2 * level); };
+  int c = d->base_channels;
+  stream = std::max(stream, n * hw(0) * c);
+  act = std::max(act, n * hw(0) * std::max(c, d->z_channels));
+  hbuf = std::max(hbuf, n * hw(0) * c);
+  for (int s = 0; s < d->n_stages; ++s) {
+    const int cs = d->stage_channels[s];
+    const int64_t P = f.stage_in[s] * hw(s);
+    stream = std::max(stream, P * std::max(c, cs));
+    act = std::max(act, P * std::max(c, cs));
+    hbuf = std::max(hbuf, P * cs);
+    if (c != cs) scbuf = std::max(scbuf, P * cs);
+    c = cs;
+    // time conv output, then the spatial upsample output at the next level
+    act = std::max(act, f.stage_out[s] * hw(s) * c);
+    stream = std::max(stream, f.stage_out[s] * hw(s) * c);
+    stream = std::max(stream, f.stage_out[s] * hw(s + 1) * c);
+    act = std::max(act, f.stage_out[s] * hw(s + 1) * c);
+  }
+  act = std::max(act, f.video * hw(d->n_stages) * c);
+  WsLayout w;
+  size_t off = 0;
+  auto take = [&](int64_t elems) {
+    const size_t o = off;
+    off += (size_t)round_up(elems * 2, 256);
+    return o;
+  };
+  w.zc = take(n * hw0 * d->z_channels);
+  w.x0 = take(stream);
+  w.x1 = take(stream);
+  w.a = take(act);
+  w.h = take(hbuf);
+  w.sc = take(scbuf);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+struct wvd_cache_s {
+  uint64_t hash;
+  char* storage;
+  std::vector<int> valid;  // frames held per slot (right-aligned)
+  int64_t next_latent;
+  int64_t next_frame;
+  int rule;  // first_frame_rule of the decode in progress (-1 before the first chunk)
+};
+
+extern "C" int wvd_decoder_param_count(const wvd_decoder_desc* d) {
+  if (check_desc(d) != WVD_OK) return -1;
+  return (int)make_plan(d).params.size();
+}
+
+extern "C" wvd_status wvd_decoder_param_info(const wvd_decoder_desc* d, int index, const char** name, int* ndim,
+                                             int64_t shape[5]) {
+  WVD_TRY(check_desc(d));
+  // names live in a per-thread table so the returned pointers stay valid after the call
+  thread_local std::vector<std::string> names;
+  const Plan p = make_plan(d);
+  if (index < 0 || index >= (int)p.params.size()) return fail(WVD_ERR_ARG, "parameter index out of range");
+  names.resize(p.params.size());
+  names[index] = p.params[index].name;
+  if (name) *name = names[index].c_str();
+  int nd = 0;
+  int64_t sh[5];
+  param_shape(d, p.params[index], &nd, sh);
+  if (ndim) *ndim = nd;
+  if (shape)
+    for (int i = 0; i < 5; ++i) shape[i] = sh[i];
+  return WVD_OK;
+}
+
+extern "C" size_t wvd_decoder_packed_bytes(const wvd_decoder_desc* d) {
+  if (check_desc(d) != WVD_OK) return 0;
+  return make_plan(d).packed_bytes;
+}
+
+extern "C" wvd_status wvd_decoder_pack(const wvd_decoder_desc* d, const float* const* params, void* packed,
+                                       wvd_stream stream) {
+  WVD_TRY(check_desc(d));
+  if (!params || !packed) return fail(WVD_ERR_ARG, "null params or packed buffer");
+  if (!aligned16(packed)) return fail(WVD_ERR_ALIGN, "packed buffer not 16-byte aligned");
+  const Plan p = make_plan(d);
+  for (size_t i = 0; i < p.params.size(); ++i)
+    if (!params[i]) return fail(WVD_ERR_ARG, "parameter %zu (%s) is null", i, p.params[i].name.c_str());
+  hipStream_t s = (hipStream_t)stream;
+  for (size_t i = 0; i < p.params.size(); ++i) {
+    const Param& q = p.params[i];
+    char* dst = (char*)packed + q.offset;
+    const int npad = (int)round_up(q.co, 32), cip = (int)round_up(q.ci, 32);
+    switch (q.kind) {
+      case K_CONV3:
+        WVD_HIP(launch_pack_conv(params[i], 0, q.co, q.ci, 27, npad, cip, (bf16_t*)dst, s), "pack launch");
+        break;
+      case K_CONV1:
+        WVD_HIP(launch_pack_conv(params[i], 0, q.co, q.ci, 1, npad, cip, (bf16_t*)dst, s), "pack launch");
+        break;
+      case K_TIME:
+        WVD_HIP(launch_pack_conv(params[i], 0, q.co, q.ci, 3, npad, cip, (bf16_t*)dst, s), "pack launch");
+        break;
+      case K_SPATIAL:
+        WVD_HIP(launch_pack_phase2x(params[i], 0, q.co, q.ci, npad, cip, (bf16_t*)dst, s), "pack launch");
+        break;
+      default:
+        WVD_HIP(launch_copy_f32(params[i], (float*)dst, q.co, s), "copy launch");
+        break;
+    }
+  }
+  return WVD_OK;
+}
+
+extern "C" size_t wvd_cache_bytes(const wvd_decoder_desc* d) {
+  if (check_desc(d) != WVD_OK) return 0;
+  return make_plan(d).cache_bytes;
+}
+
+extern "C" wvd_status wvd_cache_init(const wvd_decoder_desc* d, void* storage, wvd_cache* out) {
+  WVD_TRY(check_desc(d));
+  if (!out) return fail(WVD_ERR_ARG, "out is null");
+  if (!storage || !aligned16(storage)) return fail(WVD_ERR_ALIGN, "cache storage null or not 16-byte aligned");
+  const Plan p = make_plan(d);
+  wvd_cache c = new (std::nothrow) wvd_cache_s;
+  if (!c) return fail(WVD_ERR_ARG, "out of host memory");
+  c->hash = desc_hash(d);
+  c->storage = (char*)storage;
+  c->valid.assign(p.slots.size(), 0);
+  c->next_latent = 0;
+  c->next_frame = 0;
+  c->rule = -1;
+  *out = c;
+  return WVD_OK;
+}
+
+extern "C" wvd_status wvd_cache_reset(wvd_cache c) {
+  if (!c) return fail(WVD_ERR_ARG, "cache is null");
+  std::fill(c->valid.begin(), c->valid.end(), 0);
+  c->next_latent = 0;
+  c->next_frame = 0;
+  c->rule = -1;
+  return WVD_OK;
+}
+
+extern "C" void wvd_cache_destroy(wvd_cache c) { delete c; }
+extern "C" int64_t wvd_cache_next_latent(wvd_cache c) { return c ? c->next_latent : -1; }
+
+extern "C" size_t wvd_decode_workspace_bytes(const wvd_decoder_desc* d, int max_latent_frames) {
+  if (check_desc(d) != WVD_OK || max_latent_frames <= 0) return 0;
+  return ws_layout(d, max_latent_frames).total;
+}
+
+extern "C" int64_t wvd_chunk_video_frames(const wvd_decoder_desc* d, int64_t n, int first, int first_frame_rule) {
+  if (check_desc(d) != WVD_OK || n < 0) return -1;
+  return chunk_frames(d, n, first && first_frame_rule).video;
+}
+
+extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* packed, wvd_cache cache,
+                                       const wvd_tensor* z, int first, int first_frame_rule, wvd_tensor* video,
+                                       int64_t frame_offset, void* ws, size_t ws_bytes, wvd_stream stream) {
+  WVD_TRY(check_desc(d));
+  if (!packed || !aligned16(packed)) return fail(WVD_ERR_ALIGN, "packed weights null or not 16-byte aligned");
+  if (!cache) return fail(WVD_ERR_ARG, "cache is null");
+  if (cache->hash != desc_hash(d)) return fail(WVD_ERR_STATE, "the cache belongs to another decoder");
+  WVD_TRY(check_tensor(z, "z", WVD_BF16, -1, false));
+  WVD_TRY(check_tensor(video, "video", WVD_BF16, WVD_NCTHW, true));
+  if (z->c != d->z_channels || z->h != d->latent_h || z->w != d->latent_w)
+    return fail(WVD_ERR_SHAPE, "z must be [1, %d, n, %d, %d]", d->z_channels, d->latent_h, d->latent_w);
+  if ((first != 0) != (cache->next_latent == 0))
+    return fail(WVD_ERR_STATE, first ? "first chunk on a cache that has history (reset it)"
+                                     : "not the first chunk, but the cache is empty");
+  if (!first && cache->rule != (first_frame_rule != 0))
+    return fail(WVD_ERR_STATE, "first_frame_rule changed within a decode");
+  if (frame_offset != cache->next_frame)
+    return fail(WVD_ERR_STATE, "frame_offset %lld, the previous chunk ended at %lld", (long long)frame_offset,
+                (long long)cache->next_frame);
+  const int64_t n = z->t;
+  const bool rule = first && first_frame_rule;
+  const ChunkFrames fr = chunk_frames(d, n, rule);
+  const int L = d->n_stages;
+  const int64_t vh = (int64_t)d->latent_h << L, vw = (int64_t)d->latent_w << L;
+  if (video->c != d->out_channels || video->h != vh || video->w != vw)
+    return fail(WVD_ERR_SHAPE, "video must be [1, %d, F, %lld, %lld]", d->out_channels, (long long)vh, (long long)vw);
+  if (frame_offset < 0 || frame_offset + fr.video > video->t)
+    return fail(WVD_ERR_SHAPE, "chunk frames %lld..%lld do not fit a video of %lld frames", (long long)frame_offset,
+                (long long)(frame_offset + fr.video), (long long)video->t);
+  if (n > 4096) return fail(WVD_ERR_UNSUPPORTED, "chunk too long");
+  const WsLayout wl = ws_layout(d, n);
+  if (ws_bytes < wl.total) return fail(WVD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, wl.total);
+  if (!ws || !aligned16(ws)) return fail(WVD_ERR_ALIGN, "workspace null or not 16-byte aligned");
+
+  hipStream_t s = (hipStream_t)stream;
+  const Plan p = make_plan(d);
+  const char* pk = (const char*)packed;
+  auto W_ = [&](int idx) -> const void* { return pk + p.params[idx].offset; };
+  auto F_ = [&](int idx) -> const float* { return (const float*)(pk + p.params[idx].offset); };
+  char* wsb = (char*)ws;
+  bf16_t* zc = (bf16_t*)(wsb + wl.zc);
+  bf16_t* bx[2] = {(bf16_t*)(wsb + wl.x0), (bf16_t*)(wsb + wl.x1)};
+  bf16_t* ba = (bf16_t*)(wsb + wl.a);
+  bf16_t* bh = (bf16_t*)(wsb + wl.h);
+  bf16_t* bsc = (bf16_t*)(wsb + wl.sc);
+  auto slot_ptr = [&](int slot) { return (bf16_t*)(cache->storage + p.slots[slot].offset); };
+  auto slot_hist = [&](int slot) -> const bf16_t* {
+    const int v = cache->valid[slot];
+    return v ? (const bf16_t*)((char*)slot_ptr(slot) + (2 - v) * p.slots[slot].frame_bytes) : nullptr;
+  };
+  // conv with the slot's history, then the slot update from the conv's input
+  auto cached_conv = [&](ConvProblem cp, int slot, const bf16_t* input, int T, double flops) -> wvd_status {
+    cp.hist = slot_hist(slot);
+    cp.Th = cache->valid[slot];
+    WVD_TRY(run_conv(cp, s, flops));
+    int v = cache->valid[slot];
+    WVD_TRY(update_slot((char*)slot_ptr(slot), v, input, T, p.slots[slot].frame_bytes, s));
+    cache->valid[slot] = v;
+    return WVD_OK;
+  };
+
+  // latents in NTHWC
+  const bf16_t* zin = (const bf16_t*)z->data;
+  if (z->layout == WVD_NCTHW) {
+    WVD_HIP(launch_convert(z->data, 1, 1, zc, 1, 0, d->z_channels, (int)n, d->latent_h, d->latent_w, s), "convert launch");
+    zin = zc;
+  }
+  int cur = 0;  // index of the stream buffer holding the activation
+  int H = d->latent_h, Wd = d->latent_w;
+  int64_t T = n;
+  int c = d->base_channels;
+  {
+    const int64_t P = T * H * Wd;
+    ConvProblem cp = plain_problem(zin, nullptr, (int)T, H, Wd, d->z_channels, 0, W_(p.conv_in_w), c, 3, 3, 3,
+                                   F_(p.conv_in_b), bx[cur], nullptr);
+    WVD_TRY(cached_conv(cp, p.conv_in_slot, zin, (int)T, conv_flops(P, c, 27LL * d->z_channels)));
+  }
+  auto resblock = [&](const ResPlan& r) -> wvd_status {
+    const int64_t P = T * H * Wd;
+    const bf16_t* x = bx[cur];
+    bf16_t* y = bx[cur];  // in place when the residual is x itself
+    const bf16_t* residual = x;
+    if (r.cin != r.cout) {
+      ConvProblem sc = plain_problem(x, nullptr, (int)T, H, Wd, r.cin, 0, W_(r.ws), r.cout, 1, 1, 1, F_(r.bs), bsc, nullptr);
+      WVD_TRY(run_conv(sc, s, conv_flops(P, r.cout, r.cin)));
+      residual = bsc;
+    }
+    WVD_HIP(launch_norm_silu(x, F_(r.gamma1), d->eps, 1, ba, P, r.cin, s), "norm launch");
+    ConvProblem c1 = plain_problem(ba, nullptr, (int)T, H, Wd, r.cin, 0, W_(r.w1), r.cout, 3, 3, 3, F_(r.b1), bh, nullptr);
+    WVD_TRY(cached_conv(c1, r.slot1, ba, (int)T, conv_flops(P, r.cout, 27LL * r.cin)));
+    WVD_HIP(launch_norm_silu(bh, F_(r.gamma2), d->eps, 1, ba, P, r.cout, s), "norm launch");
+    ConvProblem c2 = plain_problem(ba, nullptr, (int)T, H, Wd, r.cout, 0, W_(r.w2), r.cout, 3, 3, 3, F_(r.b2), y, residual);
+    WVD_TRY(cached_conv(c2, r.slot2, ba, (int)T, conv_flops(P, r.cout, 27LL * r.cout)));
+    return WVD_OK;
+  };
+  for (const ResPlan& r : p.mid) WVD_TRY(resblock(r));
+  for (int si = 0; si < L; ++si) {
+    const StagePlan& st = p.stages[si];
+    for (const ResPlan& r : st.res) {
+      WVD_TRY(resblock(r));
+      c = r.cout;
+    }
+    const bf16_t* x = bx[cur];
+    if (st.temporal) {
+      const size_t fb = (size_t)H * Wd * c * 2;
+      const int tf = rule ? 1 : 0;
+      const int64_t To = fr.stage_out[si];
+      const int Tc = (int)(T - tf);
+      bf16_t* dst = ba;  // the activated buffer is free here
+      if (tf && T > 0) WVD_HIP(hipMemcpyAsync(dst, x, fb, hipMemcpyDeviceToDevice, s), "first frame copy");
+      if (Tc > 0) {
+        const bf16_t* src = x + (size_t)tf * H * Wd * c;
+        ConvProblem cp = plain_problem(src, nullptr, Tc, H, Wd, c, 0, W_(st.tw), 2 * c, 3, 1, 1, F_(st.tb), dst, nullptr);
+        cp.To = (int)To;
+        cp.nsplit = c;
+        cp.fmul = 2;
+        cp.fbase = tf;
+        WVD_TRY(cached_conv(cp, st.time_slot, src, Tc, conv_flops((int64_t)Tc * H * Wd, 2 * c, 3LL * c)));
+      }
+      T = To;
+      // spatial upsample from the time conv's output into the stream buffer
+      WVD_TRY(run_phase_conv(dst, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur], s));
+    } else {
+      WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur ^ 1], s));
+      cur ^= 1;
+    }
+    H *= 2;
+    Wd *= 2;
+  }
+  // norm_out + SiLU, then conv_out straight into the video (NCTHW) at frame_offset
+  {
+    const int64_t P = T * H * Wd;
+    WVD_HIP(launch_norm_silu(bx[cur], F_(p.norm_out), d->eps, 1, ba, P, c, s), "norm launch");
+    const int co = d->out_channels;
+    ConvProblem cp = plain_problem(ba, nullptr, (int)T, H, Wd, c, 0, W_(p.out_w), co, 3, 3, 3, F_(p.out_b),
+                                   (bf16_t*)video->data, nullptr);
+    cp.y_ncthw = 1;
+    cp.y_cstride = video->t * vh * vw;
+    cp.fbase = (int)frame_offset;
+    cp.To = (int)video->t;
+    WVD_TRY(cached_conv(cp, p.out_slot, ba, (int)T, conv_flops(P, co, 27LL * c)));
+  }
+  cache->next_latent += n;
+  cache->next_frame += fr.video;
+  if (first) cache->rule = first_frame_rule != 0;
+  return WVD_OK;
+}
+
+// ==============================================================================================
+// Timing
+// ==============================================================================================
+extern "C" wvd_status wvd_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = on != 0;
+  return WVD_OK;
+}
+
+extern "C" wvd_status wvd_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& r : g_timing.pending) {
+    hipEventSynchronize(r.stop);
+    g_timing.pool.push_back(r.start);
+    g_timing.pool.push_back(r.stop);
+  }
+  g_timing.pending.clear();
+  g_timing.launches.assign(conv_config_count(), 0);
+  g_timing.ms.assign(conv_config_count(), 0.0);
+  g_timing.flops.assign(conv_config_count(), 0.0);
+  return WVD_OK;
+}
+
+extern "C" int wvd_timing_read(int i, const char** name, int64_t* launches, double* ms, double* flops) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  const int n = conv_config_count();
+  if ((int)g_timing.launches.size() != n) {
+    g_timing.launches.assign(n, 0);
+    g_timing.ms.assign(n, 0.0);
+    g_timing.flops.assign(n, 0.0);
+  }
+  for (auto& r : g_timing.pending) {
+    float t = 0.0f;
+    if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&t, r.start, r.stop) == hipSuccess &&
+        r.config >= 0 && r.config < n) {
+      g_timing.launches[r.config] += 1;
+      g_timing.ms[r.config] += t;
+      g_timing.flops[r.config] += r.flops;
+    }
+    g_timing.pool.push_back(r.start);
+    g_timing.pool.push_back(r.stop);
+  }
+  g_timing.pending.clear();
+  if (!name) return n;
+  if (i < 0 || i >= n) return -1;
+  *name = conv_config_name(i);
+  if (launches) *launches = g_timing.launches[i];
+  if (ms) *ms = g_timing.ms[i];
+  if (flops) *flops = g_timing.flops[i];
+  return n;
+}

@@ -1,0 +1,91 @@
+// Shared device/host helpers of libwvd (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wvd {
+
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+
+// bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// SiLU(v) = v * sigmoid(v) = v / (1 + e^-v), with the hardware exp2 and reciprocal.
+__device__ __forceinline__ float silu_f32(float v) {
+  const float e = __builtin_amdgcn_exp2f(-v * 1.4426950408889634f);
+  return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+}  // namespace wvd
+
+// Host-side launch helpers (defined in the .hip files, called by api.cpp).
+namespace wvd {
+
+// One convolution "problem" for the matrix-core implicit-GEMM kernel. The GEMM is
+//   D[n][m] = sum_k Wpk[phase][n][k] * A[k][m]
+// with m an output position of the input grid (t, h, w), n an output channel and k a (tap,
+// input channel) pair. A[k][m] is the input element at the tap's offset from m, read from `x`
+// (frames >= 0), `hist` (frames -Th..-1) or zero (outside the grid or before the history).
+struct ConvProblem {
+  const bf16_t* x;     // [T][H][W][Ci]
+  const bf16_t* hist;  // [Th][H][W][Ci] or null
+  int T, H, W, Ci, Th;
+  const bf16_t* wpk;   // packed weights [phases][Npad][ntaps][Cip]
+  int ntaps, Cip, Npad, phases;
+  // Taps: with phases == 1, tap = (i*kh + j)*kw + k has offsets (i - 2*(kt/2), j - kh/2, k - kw/2);
+  // with phases == 4 (x2 spatial upsampling), phase (a, b) tap u*2 + v has offsets
+  // (0, u + a - 1, v + b - 1).
+  int kt, kh, kw;
+  int N;               // real output channels (columns stored)
+  const float* bias;   // [N] or null
+  // Output mapping: output element (n, t, h, w, phase p=(a,b)) goes to
+  //   frame f = fbase + fmul*t + n / nsplit, channel n % nsplit,
+  //   row = hmul*h + a, col = wmul*w + b   (a = p / 2, b = p % 2 when phases == 4)
+  // in y [To][Ho][Wo][nsplit] (NTHWC) or, with y_ncthw, y[n][f][row][col] with plane stride.
+  bf16_t* y;
+  const bf16_t* res;   // residual with y's layout and shape (NTHWC only), or null
+  int To, Ho, Wo, nsplit, fbase, fmul, hmul, wmul;
+  int y_ncthw;
+  int64_t y_cstride;   // channel stride of the NCTHW output (elements)
+};
+
+hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id);
+const char* conv_config_name(int config_id);
+int conv_config_count();
+
+hipError_t launch_conv_fp32(const float* x, const float* hist, const float* w, const float* bias, float* y, int Ci,
+                            int T, int H, int W, int Th, int Co, int kt, int kh, int kw, int layout_ncthw,
+                            hipStream_t s);
+
+hipError_t launch_norm_silu(const bf16_t* x, const float* gamma, float eps, int silu, bf16_t* y, int64_t positions,
+                            int C, hipStream_t s);
+
+hipError_t launch_convert(const void* x, int x_bf16, int x_ncthw, void* y, int y_bf16, int y_ncthw, int C, int T,
+                          int H, int W, hipStream_t s);
+
+// Pack raw weights [Co][Ci][kt][kh][kw] (fp32 or bf16) into [phases][Npad][ntaps][Cip] bf16.
+hipError_t launch_pack_conv(const void* w, int w_bf16, int Co, int Ci, int ntaps_raw, int Npad, int Cip,
+                            bf16_t* out, hipStream_t s);
+hipError_t launch_pack_phase2x(const void* w, int w_bf16, int Co, int Ci, int Npad, int Cip, bf16_t* out,
+                               hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
+
+}  // namespace wvd

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU): every declared symbol is exported, the decoder's
+parameter table, sizes, frame counts and the validation paths that return before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_convolution_causalconv3d_amd as wvd
+import workloads as wl
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "wvd.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wvd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = wvd.lib()
+    declared = _declared()
+    assert len(declared) >= 20
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(wvd.exported_symbols()) == set(declared)
+    assert lib.wvd_abi_version() == 1
+
+
+def test_param_table_matches_the_workload_names_and_shapes():
+    spec = wl.FULL_DECODER
+    desc = wvd.make_desc()
+    names = wvd.param_names(desc)
+    ref = [(n, s) for n, s, _ in wl.decoder_param_list(spec)]
+    assert [n for n, _ in names] == [n for n, _ in ref]
+    assert [tuple(s) for _, s in names] == [tuple(s) for _, s in ref]
+    convs = [n for n, s in names if len(s) >= 4]
+    gammas = [n for n, _ in names if n.endswith("gamma")]
+    assert len(convs) == 30 and len(gammas) == 21  # the one-pass decoder workload's counts
+
+
+def test_sizes():
+    L = wvd.lib()
+    desc = wvd.make_desc()
+    assert L.wvd_conv_packed_bytes(384, 384, 3, 3, 3, 0) == 384 * 27 * 384 * 2
+    assert L.wvd_conv_packed_bytes(3, 96, 3, 3, 3, 0) == 32 * 27 * 96 * 2
+    assert L.wvd_conv_packed_bytes(96, 96, 1, 3, 3, 1) == 4 * 96 * 4 * 96 * 2
+    assert L.wvd_conv_packed_bytes(48, 48, 2, 3, 3, 0) == 0
+    # cache: two frames per causal conv input; 1.1 GB for the full decoder
+    cache = L.wvd_cache_bytes(ctypes.byref(desc))
+    assert 1.0e9 < cache < 1.3e9
+    ws4 = L.wvd_decode_workspace_bytes(ctypes.byref(desc), 4)
+    ws8 = L.wvd_decode_workspace_bytes(ctypes.byref(desc), 8)
+    assert 0 < ws4 < ws8
+
+
+def test_chunk_frame_counts():
+    L = wvd.lib()
+    desc = wvd.make_desc()
+    f = lambda n, first, rule: L.wvd_chunk_video_frames(ctypes.byref(desc), n, first, rule)
+    assert f(4, 0, 1) == 16 and f(4, 1, 0) == 16 and f(4, 1, 1) == 13 and f(1, 1, 1) == 1 and f(3, 0, 1) == 12
+    dec_total = sum(f(n, int(i == 0), 1) for i, n in enumerate([4] * 7 + [3]))
+    assert dec_total == 121
+
+
+def _fake_tensor(c, t, h, w, dtype=wvd.WVD_BF16, layout=wvd.WVD_NTHWC, ptr=0x1000):
+    return wvd.Tensor(ptr, dtype, layout, 1, c, t, h, w)
+
+
+def test_validation_errors_before_any_launch():
+    L = wvd.lib()
+    x = _fake_tensor(16, 4, 8, 8)
+    y = _fake_tensor(16, 4, 8, 8)
+    # odd kernel sizes only
+    st = L.wvd_causal_conv3d(ctypes.byref(x), ctypes.c_void_p(0x2000), 16, 2, 3, 3, None, None, None, ctypes.byref(y),
+                             None, None)
+    assert st == 8 and b"odd" in L.wvd_last_error()
+    # shape mismatch
+    y_bad = _fake_tensor(16, 3, 8, 8)
+    st = L.wvd_causal_conv3d(ctypes.byref(x), ctypes.c_void_p(0x2000), 16, 3, 3, 3, None, None, None,
+                             ctypes.byref(y_bad), None, None)
+    assert st == 2
+    # misaligned data
+    x_mis = _fake_tensor(16, 4, 8, 8, ptr=0x1008)
+    st = L.wvd_causal_conv3d(ctypes.byref(x_mis), ctypes.c_void_p(0x2000), 16, 3, 3, 3, None, None, None,
+                             ctypes.byref(y), None, None)
+    assert st == 5
+    # too much history
+    h3 = _fake_tensor(16, 3, 8, 8)
+    st = L.wvd_causal_conv3d(ctypes.byref(x), ctypes.c_void_p(0x2000), 16, 3, 3, 3, None, ctypes.byref(h3), None,
+                             ctypes.byref(y), None, None)
+    assert st == 2
+    # bf16 path needs NTHWC
+    xn = _fake_tensor(16, 4, 8, 8, layout=wvd.WVD_NCTHW)
+    yn = _fake_tensor(16, 4, 8, 8, layout=wvd.WVD_NCTHW)
+    st = L.wvd_causal_conv3d(ctypes.byref(xn), ctypes.c_void_p(0x2000), 16, 3, 3, 3, None, None, None,
+                             ctypes.byref(yn), None, None)
+    assert st == 4
+    # norm: channels beyond the supported width
+    xb = _fake_tensor(1024, 1, 2, 2)
+    st = L.wvd_rmsnorm_silu(ctypes.byref(xb), ctypes.c_void_p(0x3000), 1e-6, 1, ctypes.byref(xb), None)
+    assert st == 8
+
+
+def test_cache_state_machine_rejects_out_of_order_chunks():
+    L = wvd.lib()
+    desc = wvd.make_desc()
+    h = ctypes.c_void_p()
+    assert L.wvd_cache_init(ctypes.byref(desc), ctypes.c_void_p(0x10000), ctypes.byref(h)) == 0
+    z = _fake_tensor(48, 4, 44, 78)
+    video = _fake_tensor(3, 121, 704, 1248, layout=wvd.WVD_NCTHW)
+    ws = L.wvd_decode_workspace_bytes(ctypes.byref(desc), 4)
+    packed = ctypes.c_void_p(0x20000)
+    # not first, but the cache is empty
+    st = L.wvd_decode_chunk(ctypes.byref(desc), packed, h, ctypes.byref(z), 0, 1, ctypes.byref(video), 0,
+                            ctypes.c_void_p(0x30000), ws, None)
+    assert st == 6
+    # wrong frame offset
+    st = L.wvd_decode_chunk(ctypes.byref(desc), packed, h, ctypes.byref(z), 1, 1, ctypes.byref(video), 5,
+                            ctypes.c_void_p(0x30000), ws, None)
+    assert st == 6
+    # workspace too small
+    st = L.wvd_decode_chunk(ctypes.byref(desc), packed, h, ctypes.byref(z), 1, 1, ctypes.byref(video), 0,
+                            ctypes.c_void_p(0x30000), ws - 1, None)
+    assert st == 7
+    # a cache from another decoder
+    other = wvd.make_desc(latent_h=8, latent_w=8)
+    st = L.wvd_decode_chunk(ctypes.byref(other), packed, h, ctypes.byref(_fake_tensor(48, 4, 8, 8)), 1, 1,
+                            ctypes.byref(_fake_tensor(3, 13, 128, 128, layout=wvd.WVD_NCTHW)), 0,
+                            ctypes.c_void_p(0x30000), ws, None)
+    assert st == 6
+    # video too short for the chunk
+    short = _fake_tensor(3, 12, 704, 1248, layout=wvd.WVD_NCTHW)
+    st = L.wvd_decode_chunk(ctypes.byref(desc), packed, h, ctypes.byref(z), 1, 1, ctypes.byref(short), 0,
+                            ctypes.c_void_p(0x30000), ws, None)
+    assert st == 2
+    assert L.wvd_cache_next_latent(h) == 0
+    L.wvd_cache_destroy(h)
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(wvd, "_lib", None)
+    monkeypatch.setattr(wvd, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        wvd.lib()

@@ -1,0 +1,303 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle, element by element, on the
+same seeded inputs. Sizes span several tiles and ragged tails; the BASELINE-size cases follow in
+test_gpu_fullsize.py.
+
+Tolerances. fp32 path: max abs error <= 1e-4 (fp32 accumulation of <= 27*Ci products against the
+oracle's double sums). bf16 single ops (one conv, one norm): elementwise
+|d| <= 2 * 2^-9 * |ref| + 1e-4 * max|ref| (one bf16 rounding of the result, a flipped rounding,
+and fp32 summation error), on identical bf16 inputs. Composite layers (residual block, upsample
+stage), whose bf16 path rounds its intermediates: normwise max relative error <= 2e-2. Whole
+decodes: PSNR >= 55 dB against the fp32 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import causal_convolution_causalconv3d_amd as wvd
+import oracle
+import workloads as wl
+from gpu_util import bf16_elementwise_ok, from_dev_nthwc, log, psnr, rel_max, to_dev_nthwc
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g) * scale
+
+
+# ---------------------------------------------------------------------------------------------
+# fp32 path (the single-conv fp32 workload)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", ["NCTHW", "NTHWC"])
+@pytest.mark.parametrize("Th", [0, 1, 2])
+def test_fp32_single_conv(layout, Th):
+    log(f"fp32 conv layout={layout} Th={Th}")
+    cfg = wl.single_conv_fp32()
+    x, w, b = cfg["x"], cfg["weight"], cfg["bias"]
+    hist = _rand((1, 16, Th, 16, 16), 11) if Th else None
+    ref = oracle.causal_conv3d(x[0], w, b, None if hist is None else hist[0])
+    dev = lambda t: (t.contiguous() if layout == "NCTHW" else t.permute(0, 2, 3, 4, 1).contiguous()).cuda()
+    xd, wd, bd = dev(x), w.contiguous().cuda(), b.cuda()
+    hd = dev(hist) if hist is not None else None
+    hout = None
+    if layout == "NTHWC":
+        hout = torch.empty((1, 2, 16, 16, 16), device="cuda")
+    y = wvd.causal_conv3d(xd, wd, 16, bias=bd, hist=hd, hist_out=hout, layout=layout)
+    torch.cuda.synchronize()
+    got = y[0].cpu().numpy() if layout == "NCTHW" else y[0].cpu().permute(3, 0, 1, 2).numpy()
+    assert got.shape == ref.shape
+    err = float(np.abs(got - ref).max())
+    log(f"  max abs err {err:.3e}")
+    assert err <= 1e-4
+    if hout is not None:
+        assert torch.equal(hout.cpu(), xd[:, -2:].cpu())
+
+
+# ---------------------------------------------------------------------------------------------
+# bf16 matrix-core conv
+# ---------------------------------------------------------------------------------------------
+CONV_CASES = [
+    # Ci, Co, T, H, W, kernel, Th
+    (96, 96, 3, 13, 17, (3, 3, 3), 2),
+    (384, 384, 2, 9, 11, (3, 3, 3), 1),
+    (48, 384, 3, 7, 9, (3, 3, 3), 0),     # conv_in: a partial 32-channel chunk
+    (192, 96, 2, 11, 21, (3, 3, 3), 2),
+    (384, 192, 2, 10, 13, (3, 3, 3), 0),
+    (96, 32, 3, 12, 37, (3, 3, 3), 1),    # a narrow output (one 32-channel block)
+    (64, 64, 2, 5, 7, (3, 3, 3), 2),
+    (384, 192, 3, 9, 10, (1, 1, 1), 0),   # residual-block shortcut
+    (192, 384, 4, 6, 9, (3, 1, 1), 2),    # time conv, plain layout
+    (96, 96, 1, 3, 3, (1, 3, 3), 0),      # a per-frame 2-D conv, tiny
+]
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "x".join(map(str, c[:5])) + f"_k{''.join(map(str, c[5]))}_h{c[6]}")
+def test_bf16_conv_matches_oracle(case):
+    Ci, Co, T, H, W, k, Th = case
+    log(f"bf16 conv {case}")
+    seed = Ci * 7 + Co * 3 + T * 11 + H * 13 + W * 17 + Th
+    x = wl.bf16_values(_rand((1, Ci, T, H, W), seed))
+    w = wl.bf16_values(wl.kaiming(torch.Generator().manual_seed(seed + 1), (Co, Ci) + k))
+    b = 0.1 * _rand((Co,), seed + 2)
+    hist = wl.bf16_values(_rand((1, Ci, Th, H, W), seed + 3)) if Th else None
+    ref = oracle.causal_conv3d(x[0], w, b, None if hist is None else hist[0])
+    y = wvd.causal_conv3d(to_dev_nthwc(x), wvd.conv_pack(w.cuda()), Co, kernel=k, bias=b.cuda(),
+                          hist=None if hist is None else to_dev_nthwc(hist))
+    torch.cuda.synchronize()
+    got = from_dev_nthwc(y)
+    ok, worst = bf16_elementwise_ok(got, ref)
+    log(f"  rel {rel_max(got, ref):.3e} worst/bound {worst:.3f}")
+    assert ok, worst
+
+
+def test_bf16_conv_residual_and_hist_out():
+    Ci, Co, T, H, W = 96, 96, 3, 10, 12
+    x = wl.bf16_values(_rand((1, Ci, T, H, W), 21))
+    res = wl.bf16_values(_rand((1, Co, T, H, W), 22))
+    w = wl.bf16_values(wl.kaiming(torch.Generator().manual_seed(23), (Co, Ci, 3, 3, 3)))
+    hist = wl.bf16_values(_rand((1, Ci, 1, H, W), 24))
+    ref = oracle.add(oracle.causal_conv3d(x[0], w, None, hist[0]), res[0])
+    xd, hd = to_dev_nthwc(x), to_dev_nthwc(hist)
+    hout = torch.empty((1, 2, H, W, Ci), dtype=torch.bfloat16, device="cuda")
+    y = wvd.causal_conv3d(xd, wvd.conv_pack(w.cuda()), Co, hist=hd, residual=to_dev_nthwc(res), hist_out=hout)
+    torch.cuda.synchronize()
+    ok, worst = bf16_elementwise_ok(from_dev_nthwc(y), ref)
+    assert ok, worst
+    assert torch.equal(hout[:, :], xd[:, -2:])
+    # a one-frame input keeps the old last history frame in front of it
+    hout1 = torch.empty((1, 2, H, W, Ci), dtype=torch.bfloat16, device="cuda")
+    wvd.causal_conv3d(xd[:, :1].contiguous(), wvd.conv_pack(w.cuda()), Co, hist=hd, hist_out=hout1)
+    torch.cuda.synchronize()
+    assert torch.equal(hout1[:, 0], hd[:, 0]) and torch.equal(hout1[:, 1], xd[:, 0])
+
+
+def test_bf16_conv_chunked_equals_one_shot_bitwise():
+    """Carrying the history between chunks gives the very same bits as one conv over all frames."""
+    Ci, Co, T, H, W = 96, 96, 5, 9, 14
+    x = to_dev_nthwc(_rand((1, Ci, T, H, W), 31))
+    wp = wvd.conv_pack(wl.kaiming(torch.Generator().manual_seed(32), (Co, Ci, 3, 3, 3)).cuda())
+    whole = wvd.causal_conv3d(x, wp, Co)
+    for splits in ([1, 4], [2, 3], [1, 1, 1, 1, 1], [4, 1]):
+        parts, start, hist = [], 0, None
+        for n in splits:
+            xc = x[:, start:start + n].contiguous()
+            th = 0 if hist is None else hist.shape[1]
+            hout = torch.empty((1, wvd.history_frames_after(n, th), H, W, Ci), dtype=torch.bfloat16, device="cuda")
+            parts.append(wvd.causal_conv3d(xc, wp, Co, hist=hist, hist_out=hout))
+            hist = hout
+            start += n
+        assert torch.equal(torch.cat(parts, dim=1), whole), splits
+
+
+# ---------------------------------------------------------------------------------------------
+# RMS norm + SiLU
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("C", [48, 96, 192, 384])
+def test_norm_silu_matches_oracle(C):
+    log(f"norm C={C}")
+    x = wl.bf16_values(_rand((1, C, 3, 7, 11), C) * 3.0)
+    gamma = 1.0 + 0.1 * _rand((C,), C + 1)
+    ref = oracle.silu(oracle.rms_norm(x[0], gamma, 1e-6))
+    y = wvd.rmsnorm_silu(to_dev_nthwc(x), gamma.cuda(), 1e-6)
+    torch.cuda.synchronize()
+    ok, worst = bf16_elementwise_ok(from_dev_nthwc(y), ref, floor=1e-6)
+    assert ok, worst
+    # the norm alone (no SiLU)
+    ref2 = oracle.rms_norm(x[0], gamma, 1e-6)
+    y2 = wvd.rmsnorm_silu(to_dev_nthwc(x), gamma.cuda(), 1e-6, silu=False)
+    torch.cuda.synchronize()
+    ok, worst = bf16_elementwise_ok(from_dev_nthwc(y2), ref2, floor=1e-6)
+    assert ok, worst
+
+
+# ---------------------------------------------------------------------------------------------
+# Residual block
+# ---------------------------------------------------------------------------------------------
+def test_resblock_given_history_matches_oracle():
+    cfg = wl.resblock_bf16(seed=2, C=384, T=4, H=6, W=10)
+    p = oracle.as_numpy_params(cfg["params"])
+    ref = oracle.resblock(cfg["x"][0], p, "res", {}, 1e-6, given_hist=oracle._f32(cfg["hist"][0]))
+    wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+    hd = to_dev_nthwc(cfg["hist"])
+    y = wvd.resblock(to_dev_nthwc(cfg["x"]), wts, 1e-6, hist1=hd, hist2=hd)
+    torch.cuda.synchronize()
+    r = rel_max(from_dev_nthwc(y), ref)
+    log(f"resblock rel {r:.3e}")
+    assert r <= 2e-2
+
+
+def test_resblock_shortcut_and_histories_match_oracle():
+    cfg = wl.resblock_bf16(seed=12, C=384, T=3, H=7, W=9, Cout=192, hist_frames=0)
+    p = oracle.as_numpy_params(cfg["params"])
+    h1 = wl.bf16_values(_rand((1, 384, 2, 7, 9), 13))
+    h2 = wl.bf16_values(_rand((1, 192, 1, 7, 9), 14))
+    x = oracle._f32(cfg["x"][0])
+    a1 = oracle.norm_silu(x, p["res.norm1.gamma"], 1e-6)
+    h = oracle.causal_conv3d(a1, p["res.conv1.weight"], p["res.conv1.bias"], h1[0].numpy())
+    a2 = oracle.norm_silu(h, p["res.norm2.gamma"], 1e-6)
+    h2o = oracle.causal_conv3d(a2, p["res.conv2.weight"], p["res.conv2.bias"], h2[0].numpy())
+    ref = oracle.add(h2o, oracle.causal_conv3d(x, p["res.shortcut.weight"], p["res.shortcut.bias"]))
+    wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+    o1 = torch.empty((1, 2, 7, 9, 384), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty((1, 2, 7, 9, 192), dtype=torch.bfloat16, device="cuda")
+    y = wvd.resblock(to_dev_nthwc(cfg["x"]), wts, 1e-6, hist1=to_dev_nthwc(h1), hist2=to_dev_nthwc(h2), hist1_out=o1,
+                     hist2_out=o2)
+    torch.cuda.synchronize()
+    r = rel_max(from_dev_nthwc(y), ref)
+    log(f"resblock 384->192 rel {r:.3e}")
+    assert r <= 2e-2
+    # the saved histories are the activated conv inputs' last two frames
+    a1_last = from_dev_nthwc(o1)
+    assert rel_max(a1_last, a1[:, -2:]) <= 2e-2
+
+
+# ---------------------------------------------------------------------------------------------
+# Upsampling
+# ---------------------------------------------------------------------------------------------
+def test_upsample_stage_spatial_first_matches_oracle():
+    cfg = wl.upsample_stage_bf16(seed=3, C=192, T=3, H=10, W=14)
+    p = {k: oracle._f32(v) for k, v in cfg.items() if k != "x"}
+    ref = oracle.upsample_stage(cfg["x"][0], p)
+    y = wvd.upsample(to_dev_nthwc(cfg["x"]), spatial=wvd.conv_pack(cfg["spatial.weight"].cuda(), wvd.WVD_PACK_PHASE2X),
+                     spatial_bias=cfg["spatial.bias"].cuda(), temporal=wvd.conv_pack(cfg["time.weight"].cuda()),
+                     temporal_bias=cfg["time.bias"].cuda(), order=wvd.WVD_SPATIAL_FIRST)
+    torch.cuda.synchronize()
+    got = from_dev_nthwc(y)
+    assert got.shape == ref.shape == (192, 6, 20, 28)
+    r = rel_max(got, ref)
+    log(f"upsample stage rel {r:.3e}")
+    assert r <= 2e-2
+
+
+@pytest.mark.parametrize("first", [False, True])
+def test_upsample_time_first_with_history(first):
+    C, T, H, W = 96, 3, 9, 11
+    x = wl.bf16_values(_rand((1, C, T, H, W), 41))
+    ws = wl.bf16_values(wl.kaiming(torch.Generator().manual_seed(42), (C, C, 3, 3)))
+    wt = wl.bf16_values(wl.kaiming(torch.Generator().manual_seed(43), (2 * C, C, 3, 1, 1)))
+    bs, bt = 0.1 * _rand((C,), 44), 0.1 * _rand((2 * C,), 45)
+    hist = None if first else wl.bf16_values(_rand((1, C, 2, H, W), 46))
+    cache = {} if first else {"t": oracle._f32(hist[0])}
+    xt = oracle.time_upsample_first(x[0], wt, bt, cache, "t") if first else oracle.time_upsample(x[0], wt, bt, cache, "t")
+    ref = oracle.spatial_upsample(xt, ws, bs)
+    hout = torch.empty((1, 2, H, W, C), dtype=torch.bfloat16, device="cuda")
+    y = wvd.upsample(to_dev_nthwc(x), spatial=wvd.conv_pack(ws.cuda(), wvd.WVD_PACK_PHASE2X), spatial_bias=bs.cuda(),
+                     temporal=wvd.conv_pack(wt.cuda()), temporal_bias=bt.cuda(), order=wvd.WVD_TIME_FIRST, first=first,
+                     time_hist=None if hist is None else to_dev_nthwc(hist), time_hist_out=hout)
+    torch.cuda.synchronize()
+    got = from_dev_nthwc(y)
+    assert got.shape == ref.shape
+    r = rel_max(got, ref)
+    log(f"upsample time-first first={first} rel {r:.3e}")
+    assert r <= 2e-2
+    assert np.array_equal(from_dev_nthwc(hout), cache["t"])
+    if first:  # frame 0 passes through, spatially upsampled only
+        ref0 = oracle.spatial_upsample(x[0][:, :1], ws, bs)
+        assert rel_max(got[:, :1], ref0) <= 2e-2
+
+
+# ---------------------------------------------------------------------------------------------
+# Whole decodes at reduced size
+# ---------------------------------------------------------------------------------------------
+SMALL_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 32, 32))
+
+
+def _gpu_decoder(spec, params, latent_hw):
+    desc = wvd.make_desc(z_channels=spec.z_channels, base_channels=spec.base_channels,
+                         stage_channels=spec.stage_channels, stage_temporal=spec.temporal,
+                         mid_resblocks=spec.mid_resblocks, stage_resblocks=spec.stage_resblocks,
+                         out_channels=spec.out_channels, eps=spec.eps, latent_h=latent_hw[0], latent_w=latent_hw[1])
+    return wvd.Decoder(desc, params)
+
+
+@pytest.mark.parametrize("rule", [True, False])
+def test_small_decoder_matches_oracle_and_is_pass_size_invariant(rule):
+    hw = (5, 7)
+    z, params = wl.decoder_weights(SMALL_GPU, seed=50, latent_frames=3, latent_hw=hw)
+    ref = oracle.decode(z[0], oracle.as_numpy_params(params), SMALL_GPU, frames_per_pass=3, first_frame_rule=rule)
+    dec = _gpu_decoder(SMALL_GPU, params, hw)
+    zd = z.to(torch.bfloat16).cuda()
+    videos = [dec.decode(zd, frames_per_pass=f, first_frame_rule=rule) for f in (3, 1, 2)]
+    torch.cuda.synchronize()
+    for v in videos[1:]:
+        assert torch.equal(v, videos[0])
+    got = videos[0][0].float().cpu().numpy()
+    assert got.shape == ref.shape
+    q = psnr(got, ref)
+    log(f"small decoder rule={rule} psnr {q:.2f} dB rel {rel_max(got, ref):.3e}")
+    assert q >= 55.0
+
+
+def test_full_channel_decoder_small_latent_matches_oracle():
+    spec = wl.FULL_DECODER
+    hw = (3, 5)
+    z, params = wl.decoder_weights(spec, seed=51, latent_frames=2, latent_hw=hw)
+    ref = oracle.decode(z[0], oracle.as_numpy_params(params), spec, frames_per_pass=2)
+    dec = _gpu_decoder(spec, params, hw)
+    v = dec.decode(z.to(torch.bfloat16).cuda(), frames_per_pass=1)
+    torch.cuda.synchronize()
+    got = v[0].float().cpu().numpy()
+    assert got.shape == ref.shape == (3, 5, 48, 80)
+    q = psnr(got, ref)
+    log(f"full-channel decoder psnr {q:.2f} dB")
+    assert q >= 55.0
+
+
+def test_decoder_causality_and_independence_on_gpu():
+    hw = (4, 6)
+    z, params = wl.decoder_weights(SMALL_GPU, seed=52, latent_frames=4, latent_hw=hw)
+    dec = _gpu_decoder(SMALL_GPU, params, hw)
+    zd = z.to(torch.bfloat16).cuda()
+    base = dec.decode(zd, frames_per_pass=2).clone()
+    other = wl.streaming_latents(seed=53, latent_frames=3, spec=SMALL_GPU, latent_hw=hw).to(torch.bfloat16).cuda()
+    dec.decode(other, frames_per_pass=3)
+    again = dec.decode(zd, frames_per_pass=2)
+    assert torch.equal(again, base)
+    for k in (1, 3):
+        z2 = zd.clone()
+        z2[:, :, k] += 1.0
+        v2 = dec.decode(z2, frames_per_pass=2)
+        keep = 4 * k - 3
+        assert torch.equal(v2[:, :, :keep], base[:, :, :keep])
+        assert not torch.equal(v2[:, :, keep], base[:, :, keep])
