@@ -63,12 +63,12 @@ def algorithmic_conv_flops(spec: wl.DecoderSpec, latent_frames: int, fpp: int, h
 
 
 def cpu_baseline(seconds_hint: float = 15.0):
-    """The oracle (as it stands) on a bounded sample of the same decode: a 12x16 latent crop,
-    one pass of 2 latent frames (8 video frames of 192x256), scaled to full-frame frames/s by the
-    crop's share of the 44x78 latent frame."""
+    """The oracle (as it stands) on a bounded sample of the same decode: a 20x28 latent crop,
+    one pass of 2 latent frames (8 video frames of 320x448), scaled to full-frame frames/s by the
+    crop's share of the 44x78 latent frame (about 10 s on 16 host cores)."""
     import oracle  # CPU baseline leg only
 
-    crop = (12, 16)
+    crop = (20, 28)
     z, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=2, latent_hw=crop)
     p = oracle.as_numpy_params(params)
     zz = oracle._f32(z[0])

@@ -1,0 +1,108 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the bench times.
+
+  * residual block [1,384,4,44,78] with its 2-frame cache: every output against the oracle;
+  * upsample stage [1,192,4,176,312] -> [1,192,8,352,624]: windows (corners, edges, centre)
+    against the oracle run on the matching input crop plus a one-pixel halo (a conv is
+    translation-equivariant, so the crop's interior equals the full-size result);
+  * one-pass decode [1,48,4,44,78] -> [1,3,16,704,1248]: against the oracle's values at 32768
+    seeded positions (tests/golden/decoder_onepass_samples.npz, written by make_decoder_golden.py
+    from the oracle alone), and bitwise pass-size invariance;
+  * streaming 5 s decode [1,48,31,44,78] -> 121 frames: bitwise equal for 4 frames per pass, 3,
+    and all 31 in one pass (the one-shot form).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import causal_convolution_causalconv3d_amd as wvd
+import oracle
+import workloads as wl
+from gpu_util import from_dev_nthwc, log, psnr, rel_max, to_dev_nthwc
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "decoder_onepass_samples.npz")
+
+
+def test_resblock_full_size():
+    cfg = wl.resblock_bf16()  # [1,384,4,44,78] + [1,384,2,44,78] cache, seed 2
+    p = oracle.as_numpy_params(cfg["params"])
+    ref = oracle.resblock(cfg["x"][0], p, "res", {}, 1e-6, given_hist=oracle._f32(cfg["hist"][0]))
+    wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+    hd = to_dev_nthwc(cfg["hist"])
+    y = wvd.resblock(to_dev_nthwc(cfg["x"]), wts, 1e-6, hist1=hd, hist2=hd)
+    torch.cuda.synchronize()
+    got = from_dev_nthwc(y)
+    r = rel_max(got, ref)
+    log(f"resblock full size: rel {r:.3e}, psnr {psnr(got, ref):.2f} dB")
+    assert r <= 2e-2
+
+
+def test_upsample_stage_full_size_windows():
+    cfg = wl.upsample_stage_bf16()  # [1,192,4,176,312], seed 3
+    x = cfg["x"]
+    _, C, T, H, W = x.shape
+    p = {k: oracle._f32(v) for k, v in cfg.items() if k != "x"}
+    y = wvd.upsample(to_dev_nthwc(x), spatial=wvd.conv_pack(cfg["spatial.weight"].cuda(), wvd.WVD_PACK_PHASE2X),
+                     spatial_bias=cfg["spatial.bias"].cuda(), temporal=wvd.conv_pack(cfg["time.weight"].cuda()),
+                     temporal_bias=cfg["time.bias"].cuda(), order=wvd.WVD_SPATIAL_FIRST)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (1, 2 * T, 2 * H, 2 * W, C)
+    S = 12
+    windows = [(0, 0), (H - S, W - S), (H // 2, W // 2), (0, W // 3), (H // 3, 0), (H - S, 0)]
+    for r0, c0 in windows:
+        r1, c1 = r0 + S, c0 + S
+        a0, a1 = max(r0 - 1, 0), min(r1 + 1, H)
+        b0, b1 = max(c0 - 1, 0), min(c1 + 1, W)
+        ref = oracle.upsample_stage(x[0, :, :, a0:a1, b0:b1], p)
+        ref = ref[:, :, 2 * (r0 - a0):2 * (r0 - a0) + 2 * S, 2 * (c0 - b0):2 * (c0 - b0) + 2 * S]
+        got = y[0, :, 2 * r0:2 * r1, 2 * c0:2 * c1].float().cpu().permute(3, 0, 1, 2).numpy()
+        r = rel_max(got, ref)
+        log(f"upsample window ({r0},{c0}): rel {r:.3e}")
+        assert r <= 2e-2
+
+
+def _full_decoder(params):
+    return wvd.Decoder(wvd.make_desc(), params)
+
+
+def test_one_pass_decode_full_size_against_oracle_samples():
+    z, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
+    dec = _full_decoder(params)
+    zd = z.to(torch.bfloat16).cuda()
+    v4 = dec.decode(zd, frames_per_pass=4, first_frame_rule=False)
+    torch.cuda.synchronize()
+    assert tuple(v4.shape) == (1, 3, 16, 704, 1248)
+    assert bool(torch.isfinite(v4.float()).all())
+    for fpp in (1, 3):
+        assert torch.equal(dec.decode(zd, frames_per_pass=fpp, first_frame_rule=False), v4), fpp
+    if not os.path.exists(GOLDEN):
+        pytest.skip("golden samples not generated (tests/golden/make_decoder_golden.py)")
+    g = np.load(GOLDEN)
+    flat = v4[0].float().cpu().reshape(-1).numpy()
+    got, ref = flat[g["index"]], g["value"]
+    mse = float(((got.astype(np.float64) - ref) ** 2).mean())
+    rng = float(g["vmax"] - g["vmin"])
+    q = math.inf if mse == 0 else 10 * math.log10(rng * rng / mse)
+    log(f"one-pass decode vs oracle samples: psnr {q:.2f} dB, max abs {np.abs(got - ref).max():.3e}, range {rng:.3f}")
+    assert q >= 55.0
+
+
+def test_streaming_decode_full_size_pass_size_invariant():
+    _, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
+    z = wl.streaming_latents(seed=5, latent_frames=31).to(torch.bfloat16).cuda()
+    dec = _full_decoder(params)
+    v4 = dec.decode(z, frames_per_pass=4).clone()
+    torch.cuda.synchronize()
+    assert tuple(v4.shape) == (1, 3, 121, 704, 1248)
+    assert bool(torch.isfinite(v4.float()).all())
+    for fpp in (3, 31):
+        log(f"streaming decode fpp={fpp}")
+        v = dec.decode(z, frames_per_pass=fpp)
+        torch.cuda.synchronize()
+        assert torch.equal(v, v4), fpp
+        del v
+        dec._ws = None
+        torch.cuda.empty_cache()
