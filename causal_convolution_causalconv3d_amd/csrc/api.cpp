@@ -603,7 +603,7 @@ extern "C" wvd_status wvd_upsample(const wvd_tensor* x, const void* spatial, con
 // ==============================================================================================
 namespace {
 
-enum ParamKind { K_CONV3 = 0, K_CONV1 = 1, K_TIME = 2, K_SPATIAL = 3, K_GAMMA = 4, K_BIAS = 5 };
+enum ParamKind { K_CONV3 = 0, K_CONV1 = 1, K_TIME = 2, K_SPATIAL = 3, K_GAMMA = 4, K_BIAS = 5, K_HEAD = 6 };
 
 struct Param {
   std::string name;
@@ -670,6 +670,7 @@ int add_param(Plan& p, const std::string& name, int kind, int co, int ci) {
     case K_CONV1: q.bytes = (size_t)packed_elems(co, ci, 1, 1) * 2; break;
     case K_TIME: q.bytes = (size_t)packed_elems(co, ci, 3, 1) * 2; break;
     case K_SPATIAL: q.bytes = (size_t)packed_elems(co, ci, 4, 4) * 2; break;
+    case K_HEAD: q.bytes = (size_t)packed_elems(9 * co, ci, 3, 1) * 2; break;
     default: q.bytes = (size_t)co * 4; break;
   }
   q.offset = 0;
@@ -733,7 +734,7 @@ Plan make_plan(const wvd_decoder_desc* d) {
     p.stages.push_back(st);
   }
   p.norm_out = add_param(p, "norm_out.gamma", K_GAMMA, c, 0);
-  p.out_w = add_param(p, "conv_out.weight", K_CONV3, d->out_channels, c);
+  p.out_w = add_param(p, "conv_out.weight", K_HEAD, d->out_channels, c);
   p.out_b = add_param(p, "conv_out.bias", K_BIAS, d->out_channels, 0);
   p.out_slot = add_slot(p, d, d->n_stages, c);
   size_t off = 0;
@@ -755,7 +756,8 @@ void param_shape(const wvd_decoder_desc* d, const Param& q, int* ndim, int64_t s
   (void)d;
   for (int i = 0; i < 5; ++i) shape[i] = 0;
   switch (q.kind) {
-    case K_CONV3: *ndim = 5; shape[0] = q.co; shape[1] = q.ci; shape[2] = shape[3] = shape[4] = 3; break;
+    case K_CONV3:
+    case K_HEAD: *ndim = 5; shape[0] = q.co; shape[1] = q.ci; shape[2] = shape[3] = shape[4] = 3; break;
     case K_CONV1: *ndim = 5; shape[0] = q.co; shape[1] = q.ci; shape[2] = shape[3] = shape[4] = 1; break;
     case K_TIME: *ndim = 5; shape[0] = q.co; shape[1] = q.ci; shape[2] = 3; shape[3] = shape[4] = 1; break;
     case K_SPATIAL: *ndim = 4; shape[0] = q.co; shape[1] = q.ci; shape[2] = shape[3] = 3; break;
@@ -804,6 +806,9 @@ ChunkFrames chunk_frames(const wvd_decoder_desc* d, int64_t n, bool first_rule) 
   return f;
 }
 
+// Channels of the head's tap planes: 9 per output channel, padded to a multiple of 4.
+int head_zc(int co) { return (int)round_up(9 * co, 4); }
+
 // Workspace buffers of the chunk driver (elements of bf16).
 struct WsLayout {
   size_t zc, x0, x1, a, h, sc;  // byte offsets
@@ -834,6 +839,8 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n) {
     act = std::max(act, f.stage_out[s] * hw(s + 1) * c);
   }
   act = std::max(act, f.video * hw(d->n_stages) * c);
+  // the head's fp32 tap planes Z (zc floats = 2*zc bf16 per position) live in a stream buffer
+  stream = std::max(stream, f.video * hw(d->n_stages) * 2 * head_zc(d->out_channels));
   WsLayout w;
   size_t off = 0;
   auto take = [&](int64_t elems) {
@@ -916,6 +923,10 @@ extern "C" wvd_status wvd_decoder_pack(const wvd_decoder_desc* d, const float* c
         break;
       case K_SPATIAL:
         WVD_HIP(launch_pack_phase2x(params[i], 0, q.co, q.ci, npad, cip, (bf16_t*)dst, s), "pack launch");
+        break;
+      case K_HEAD:
+        WVD_HIP(launch_pack_head(params[i], 0, q.co, q.ci, (int)round_up(9 * q.co, 32), cip, (bf16_t*)dst, s),
+                "pack launch");
         break;
       default:
         WVD_HIP(launch_copy_f32(params[i], (float*)dst, q.co, s), "copy launch");
@@ -1098,18 +1109,23 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     H *= 2;
     Wd *= 2;
   }
-  // norm_out + SiLU, then conv_out straight into the video (NCTHW) at frame_offset
+  // norm_out + SiLU, then conv_out as temporal tap planes Z (fp32, in the free stream buffer)
+  // and the 9-tap stencil into the video (NCTHW) at frame_offset
   {
     const int64_t P = T * H * Wd;
     WVD_HIP(launch_norm_silu(bx[cur], F_(p.norm_out), d->eps, 1, ba, P, c, s), "norm launch");
     const int co = d->out_channels;
-    ConvProblem cp = plain_problem(ba, nullptr, (int)T, H, Wd, c, 0, W_(p.out_w), co, 3, 3, 3, F_(p.out_b),
-                                   (bf16_t*)video->data, nullptr);
-    cp.y_ncthw = 1;
-    cp.y_cstride = video->t * vh * vw;
-    cp.fbase = (int)frame_offset;
-    cp.To = (int)video->t;
+    const int zc = head_zc(co);
+    float* Z = (float*)bx[cur ^ 1];
+    ConvProblem cp = plain_problem(ba, nullptr, (int)T, H, Wd, c, 0, W_(p.out_w), 9 * co, 3, 1, 1, nullptr, nullptr,
+                                   nullptr);
+    cp.y = Z;
+    cp.y_f32 = 1;
+    cp.nsplit = zc;
     WVD_TRY(cached_conv(cp, p.out_slot, ba, (int)T, conv_flops(P, co, 27LL * c)));
+    WVD_HIP(launch_head_stencil(Z, zc, co, F_(p.out_b), (bf16_t*)video->data, video->t, (int)frame_offset, (int)T, H,
+                                Wd, s),
+            "head launch");
   }
   cache->next_latent += n;
   cache->next_frame += fr.video;

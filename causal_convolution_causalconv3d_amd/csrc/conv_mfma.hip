@@ -21,6 +21,7 @@
 // video) is applied in the epilogue together with the bias and an optional residual add, and
 // the result is rounded to bf16 once.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -30,10 +31,6 @@ namespace {
 
 constexpr int LDS_ROW = 40;  // bf16 per LDS row: 32 channels + 8 pad (80 bytes: no bank conflicts)
 
-struct LoadCursor {
-  int tap, chunk;
-};
-
 template <int NB, int MB, int WAVES>
 __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProblem p) {
   constexpr int BN = NB * 32;
@@ -41,7 +38,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   constexpr int NT = WAVES * 64;
   constexpr int WPIECES = BN * 4;  // 16-byte pieces of one weight K step
   constexpr int WLOADS = (WPIECES + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2][BN * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) bf16_t lds[3][BN * LDS_ROW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -51,8 +48,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   const int phase = blockIdx.z;
 
   const int HW = p.H * p.W;
-  const int M = p.T * HW;
-  const int numM = (M + BM - 1) / BM;
+  // M tiles never straddle a frame, so the source frame of every tap is uniform per workgroup.
+  const int tpf = (HW + BM - 1) / BM;  // tiles per frame
+  const int numM = p.T * tpf;
   const int numN = (p.Npad + BN - 1) / BN;
   const int total = numM * numN;
 
@@ -65,94 +63,111 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
   const int mt = lin / numN, nt = lin - (lin / numN) * numN;
   const int n0 = nt * BN;
-  const int mbase = mt * BM + wave * (MB * 32);
+  const int tf = mt / tpf;                                        // the tile's frame
+  const int mbase = (mt - tf * tpf) * BM + wave * (MB * 32);      // position within the frame
 
-  int pt[MB], ph[MB], pw[MB];
+  const int pa = (p.phases == 4) ? (phase >> 1) : 0;
+  const int pb = (p.phases == 4) ? (phase & 1) : 0;
+  // tap offsets: (i - 2*(kt/2), j - kh/2, k - kw/2), or for a phase (0, j + a - 1, k + b - 1)
+  const int dt0 = (p.phases == 4) ? 0 : -2 * (p.kt >> 1);
+  const int dh0 = (p.phases == 4) ? pa - 1 : -(p.kh >> 1);
+  const int dw0 = (p.phases == 4) ? pb - 1 : -(p.kw >> 1);
+
+  // Per lane and row block: the position (h, w), its byte offset in a frame, and a mask of the
+  // spatial taps (j, k) whose neighbour lies inside the frame (bit j*kw + k).
+  int ph[MB], pw[MB];
   bool pv[MB];
+  uint32_t loff[MB], smask[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int m = mbase + mb * 32 + l32;
-    pv[mb] = m < M;
+    pv[mb] = m < HW;
     const int mm = pv[mb] ? m : 0;
-    const int t = mm / HW;
-    const int r = mm - t * HW;
-    const int h = r / p.W;
-    pt[mb] = t;
+    const int h = mm / p.W;
+    const int w = mm - h * p.W;
     ph[mb] = h;
-    pw[mb] = r - h * p.W;
+    pw[mb] = w;
+    loff[mb] = (uint32_t)((mm * p.Ci + half * 16) * 2);
+    uint32_t msk = 0;
+    for (int j = 0; j < p.kh; ++j)
+      for (int k = 0; k < p.kw; ++k) {
+        const int hh = h + dh0 + j, ww = w + dw0 + k;
+        if (pv[mb] && hh >= 0 && hh < p.H && ww >= 0 && ww < p.W) msk |= 1u << (j * p.kw + k);
+      }
+    smask[mb] = msk;
   }
 
   const int nchunks = p.Cip >> 5;
   const int nk = p.ntaps * nchunks;
   const int64_t frame_elems = (int64_t)HW * p.Ci;
+  const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
   const int64_t wrow = (int64_t)p.ntaps * p.Cip;
   const bf16_t* wbase = p.wpk + ((int64_t)phase * p.Npad + n0) * wrow;
-  const int pa = (p.phases == 4) ? (phase >> 1) : 0;
-  const int pb = (p.phases == 4) ? (phase & 1) : 0;
-
-  // Per-tap row pointers of this lane (recomputed when the load cursor enters a new tap).
-  const bf16_t* rowp[MB];
-  auto set_tap = [&](int tap) {
-    int dt, dh, dw;
-    if (p.phases == 4) {
-      dt = 0;
-      dh = (tap >> 1) + pa - 1;
-      dw = (tap & 1) + pb - 1;
-    } else {
-      const int khw = p.kh * p.kw;
-      const int i = tap / khw;
-      const int j = (tap - i * khw) / p.kw;
-      dt = i - 2 * (p.kt >> 1);
-      dh = j - (p.kh >> 1);
-      dw = tap - i * khw - j * p.kw - (p.kw >> 1);
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int s = pt[mb] + dt;
-      const int hh = ph[mb] + dh;
-      const int ww = pw[mb] + dw;
-      const bool ok = pv[mb] && hh >= 0 && hh < p.H && ww >= 0 && ww < p.W && s >= -p.Th;
-      const bf16_t* base = (s >= 0) ? p.x + (int64_t)s * frame_elems : p.hist + (int64_t)(s + p.Th) * frame_elems;
-      rowp[mb] = ok ? base + (int64_t)(hh * p.W + ww) * p.Ci + half * 16 : nullptr;
-    }
-  };
 
   typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-  u32x4 areg[2][MB][2];
+  constexpr int STAGES = 3;
+  u32x4 areg[STAGES][MB][2];
   u32x4 wreg[WLOADS];
 
-  auto load_act = [&](u32x4 (&dst)[MB][2], int chunk) {
-    const int c = chunk * 32 + half * 16;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (rowp[mb] && c + s * 8 < p.Ci) v = *(const u32x4*)(rowp[mb] + chunk * 32 + s * 8);
-        dst[mb][s] = v;
+  // K order: the 32-channel chunk outermost, the taps inside it (k fastest), so consecutive K steps
+  // read the same channels one position apart and mostly hit the L1 cache.
+  struct Cursor {
+    int chunk, tap, ti, tj, tk;
+  };
+  auto advance = [&](Cursor& c) {
+    ++c.tap;
+    if (++c.tk == p.kw) {
+      c.tk = 0;
+      if (++c.tj == p.kh) {
+        c.tj = 0;
+        if (++c.ti == p.kt) {
+          c.ti = 0;
+          c.tap = 0;
+          ++c.chunk;
+        }
       }
     }
   };
-  auto load_w = [&](int tap, int chunk) {
+  // Activation operands come from range-checked buffer loads over one frame: the frame (current
+  // input or history) is uniform, a lane whose tap falls outside the frame, before the history
+  // or past the channels gets the out-of-range offset `frame_bytes` and the hardware returns 0.
+  auto load_act = [&](u32x4 (&dst)[MB][2], const Cursor& c) {
+    const int s = tf + dt0 + c.ti;  // source frame (negative: history)
+    const bool fok = s >= -p.Th;
+    const bf16_t* fbase = (s >= 0) ? p.x + (int64_t)s * frame_elems
+                                   : (fok ? p.hist + (int64_t)(s + p.Th) * frame_elems : p.x);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)fbase, (short)0, (int)frame_bytes, 0x00020000);
+    const int uoff = (((dh0 + c.tj) * p.W + (dw0 + c.tk)) * p.Ci + c.chunk * 32) * 2;
+    const int bit = c.tj * p.kw + c.tk;
+    const int ch = c.chunk * 32 + half * 16;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const bool ok = fok & (((smask[mb] >> bit) & 1u) != 0u);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const bool use = ok & (ch + q * 8 < p.Ci);
+        const int vo = use ? (int)loff[mb] + uoff + q * 16 : (int)frame_bytes;
+        dst[mb][q] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0);
+      }
+    }
+  };
+  // Weight rows past Npad (only in a partial last N tile) read row Npad-1: those columns are
+  // never stored. Threads past the tile's pieces repeat the last piece (same data, same address).
+  auto load_w = [&](const Cursor& c) {
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
-      const int q = tid + i * NT;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (q < WPIECES) {
-        const int row = q >> 2, piece = q & 3;
-        if (n0 + row < p.Npad) v = *(const u32x4*)(wbase + row * wrow + tap * p.Cip + chunk * 32 + piece * 8);
-      }
-      wreg[i] = v;
+      const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
+      const int row = min(q >> 2, p.Npad - 1 - n0), piece = q & 3;
+      wreg[i] = *(const u32x4*)(wbase + row * wrow + c.tap * p.Cip + c.chunk * 32 + piece * 8);
     }
   };
   auto store_w = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
-      const int q = tid + i * NT;
-      if (q < WPIECES) {
-        const int row = q >> 2, piece = q & 3;
-        *(u32x4*)(&lds[buf][row * LDS_ROW + piece * 8]) = wreg[i];
-      }
+      const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
+      const int row = q >> 2, piece = q & 3;
+      *(u32x4*)(&lds[buf][row * LDS_ROW + piece * 8]) = wreg[i];
     }
   };
 
@@ -166,16 +181,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
 
   auto compute = [&](const u32x4 (&a)[MB][2], int buf) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int q = 0; q < 2; ++q) {
       bf16x8 wf[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 v = *(const u32x4*)(&lds[buf][(nb * 32 + l32) * LDS_ROW + half * 16 + s * 8]);
+        const u32x4 v = *(const u32x4*)(&lds[buf][(nb * 32 + l32) * LDS_ROW + half * 16 + q * 8]);
         wf[nb] = __builtin_bit_cast(bf16x8, v);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 af = __builtin_bit_cast(bf16x8, a[mb][s]);
+        const bf16x8 af = __builtin_bit_cast(bf16x8, a[mb][q]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], af, acc[nb][mb], 0, 0, 0);
@@ -183,44 +198,41 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
     }
   };
 
-  // Prologue: K step 0.
-  LoadCursor cur = {0, 0};
-  set_tap(0);
-  load_act(areg[0], 0);
-  load_w(0, 0);
+  // Three-stage pipeline: step k computes from activation registers and LDS weights of stage
+  // k % 3 while the loads of step k + 2 are in flight.
+  Cursor cur = {0, 0, 0, 0, 0};  // the next step to load
+  load_w(cur);
+  load_act(areg[0], cur);
   store_w(0);
+  if (nk > 1) {
+    advance(cur);
+    load_w(cur);
+    load_act(areg[1], cur);
+    store_w(1);
+  }
   __syncthreads();
 
-  auto advance = [&](LoadCursor& c) {
-    if (++c.chunk == nchunks) {
-      c.chunk = 0;
-      ++c.tap;
-      set_tap(c.tap);
-    }
-  };
-
-  // Main loop, unrolled by two so the register double buffer is indexed statically; an odd
-  // last K step runs after the loop (no exit from the middle of the body, which would split
-  // the accumulators' live ranges).
-  int k = 0;
-  for (; k + 2 <= nk; k += 2) {
-    advance(cur);
-    load_act(areg[1], cur.chunk);
-    load_w(cur.tap, cur.chunk);
-    compute(areg[0], 0);
-    store_w(1);
-    __syncthreads();
+  auto step = [&](auto S, int k) {
+    constexpr int s0 = decltype(S)::value;
+    constexpr int s2 = (s0 + 2) % STAGES;
     const bool more = k + 2 < nk;
     if (more) {
       advance(cur);
-      load_act(areg[0], cur.chunk);
-      load_w(cur.tap, cur.chunk);
+      load_w(cur);  // before the activations: the LDS store below then waits for these alone
+      load_act(areg[s2], cur);
     }
-    compute(areg[1], 1);
-    if (more) store_w(0);
+    compute(areg[s0], s0);
+    if (more) store_w(s2);
     __syncthreads();
+  };
+  int k = 0;
+  for (; k + STAGES <= nk; k += STAGES) {
+    step(std::integral_constant<int, 0>{}, k);
+    step(std::integral_constant<int, 1>{}, k + 1);
+    step(std::integral_constant<int, 2>{}, k + 2);
   }
-  if (k < nk) compute(areg[0], 0);
+  if (k < nk) step(std::integral_constant<int, 0>{}, k);
+  if (k + 1 < nk) step(std::integral_constant<int, 1>{}, k + 1);
 
   // Epilogue: lane holds, per (nb, mb, g), channels n0 + nb*32 + g*8 + half*4 + {0..3} of
   // position mbase + mb*32 + l32. Scheduling barriers keep one (mb, nb) block in flight at a
@@ -240,11 +252,18 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][g * 4 + e] + ((p.bias && n + e < p.N) ? p.bias[n + e] : 0.0f);
-        if (!p.y_ncthw) {
-          // the 4 channels share a frame and are contiguous (nsplit is a multiple of 4 here)
-          const int f = p.fbase + p.fmul * pt[mb] + n / p.nsplit;
-          const int nc = n % p.nsplit;
-          const int64_t idx = (((int64_t)f * p.Ho + orow) * p.Wo + ocol) * p.nsplit + nc;
+        // the 4 channels share a frame and are contiguous (nsplit is a multiple of 4)
+        const int f = p.fbase + p.fmul * tf + n / p.nsplit;
+        const int nc = n % p.nsplit;
+        const int64_t idx = (((int64_t)f * p.Ho + orow) * p.Wo + ocol) * p.nsplit + nc;
+        if (p.y_f32) {
+          float4 o;
+          o.x = n + 0 < p.N ? v[0] : 0.0f;
+          o.y = n + 1 < p.N ? v[1] : 0.0f;
+          o.z = n + 2 < p.N ? v[2] : 0.0f;
+          o.w = n + 3 < p.N ? v[3] : 0.0f;
+          *(float4*)((float*)p.y + idx) = o;
+        } else {
           if (p.res) {
             const uint2 r = *(const uint2*)(p.res + idx);
             v[0] += bf16_lo(r.x);
@@ -255,13 +274,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
           uint2 o;
           o.x = pack_bf16x2(v[0], v[1]);
           o.y = pack_bf16x2(v[2], v[3]);
-          *(uint2*)(p.y + idx) = o;
-        } else {
-          const int f = p.fbase + pt[mb];
-          const int64_t pix = ((int64_t)f * p.Ho + orow) * p.Wo + ocol;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) p.y[(int64_t)(n + e) * p.y_cstride + pix] = (bf16_t)f32_to_bf16(v[e]);
+          *(uint2*)((bf16_t*)p.y + idx) = o;
         }
       }
     }
@@ -286,22 +299,23 @@ const ConfigEntry kConfigs[] = {
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-int64_t blocks_for(const ConfigEntry& c, int64_t M, int Npad) {
+// Workgroups of a problem: per frame ceil(H*W / BM) position tiles, times the channel tiles.
+int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t HW, int Npad) {
   const int64_t bm = (int64_t)c.waves * c.mb * 32, bn = (int64_t)c.nb * 32;
-  return ((M + bm - 1) / bm) * ((Npad + bn - 1) / bn);
+  return T * ((HW + bm - 1) / bm) * ((Npad + bn - 1) / bn);
 }
 
 // Largest tile whose grid still gives every CU at least one workgroup per phase.
-int choose_config(int64_t M, int Npad, int phases) {
+int choose_config(int64_t T, int64_t HW, int Npad, int phases) {
   const int64_t cus = 256;
   if (Npad <= 32) return 3;
   if (Npad % 192 == 0) {
-    if (blocks_for(kConfigs[0], M, Npad) * phases >= cus) return 0;
-    if (blocks_for(kConfigs[4], M, Npad) * phases >= cus) return 4;
+    if (blocks_for(kConfigs[0], T, HW, Npad) * phases >= cus) return 0;
+    if (blocks_for(kConfigs[4], T, HW, Npad) * phases >= cus) return 4;
     return 2;
   }
   if (Npad % 96 == 0) {
-    if (blocks_for(kConfigs[1], M, Npad) * phases >= cus) return 1;
+    if (blocks_for(kConfigs[1], T, HW, Npad) * phases >= cus) return 1;
     return 2;
   }
   return 2;
@@ -313,11 +327,13 @@ const char* conv_config_name(int id) { return (id >= 0 && id < kNumConfigs) ? kC
 int conv_config_count() { return kNumConfigs; }
 
 hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id) {
-  const int64_t M = (int64_t)p.T * p.H * p.W;
-  if (M == 0) return hipSuccess;
-  const int id = choose_config(M, p.Npad, p.phases);
+  const int64_t HW = (int64_t)p.H * p.W;
+  if (p.T == 0 || HW == 0) return hipSuccess;
+  // one frame is addressed with 32-bit byte offsets
+  if (HW * p.Ci * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int id = choose_config(p.T, HW, p.Npad, p.phases);
   const ConfigEntry& c = kConfigs[id];
-  const int64_t blocks = blocks_for(c, M, p.Npad);
+  const int64_t blocks = blocks_for(c, p.T, HW, p.Npad);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (config_id) *config_id = id;
   hipLaunchKernelGGL(c.kernel, dim3((unsigned)blocks, 1, p.phases), dim3(c.waves * 64), 0, s, p);
