@@ -38,7 +38,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   constexpr int NT = WAVES * 64;
   constexpr int WPIECES = BN * 4;  // 16-byte pieces of one weight K step
   constexpr int WLOADS = (WPIECES + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[3][BN * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) bf16_t lds[4][BN * LDS_ROW];  // weight stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -105,37 +105,43 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   const bf16_t* wbase = p.wpk + ((int64_t)phase * p.Npad + n0) * wrow;
 
   typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-  constexpr int STAGES = 3;
-  u32x4 areg[STAGES][MB][2];
-  u32x4 wreg[WLOADS];
+  u32x4 areg[3][MB][2];     // activations of steps k (in use), k + 1 and k + 2 (in flight)
+  u32x4 wreg[2][WLOADS];    // weights of steps k + 2 and k + 3 on their way to LDS
+  u32x4 wf[2][2][NB];       // weight fragments of steps k (in use) and k + 1 (read from LDS)
 
   // K order: the 32-channel chunk outermost, the taps inside it (k fastest), so consecutive K steps
-  // read the same channels one position apart and mostly hit the L1 cache.
+  // read the same channels one position apart and mostly hit the L1 cache. The step count is
+  // rounded up to a multiple of 6 (the register rotation period); cursors move without branches,
+  // stop at the last real step, and activation loads of the padding steps return zeros, so those
+  // steps add nothing.
+  const int nk6 = (nk + 5) / 6 * 6;
   struct Cursor {
-    int chunk, tap, ti, tj, tk;
+    int step, chunk, tap, ti, tj, tk;
   };
   auto advance = [&](Cursor& c) {
-    ++c.tap;
-    if (++c.tk == p.kw) {
-      c.tk = 0;
-      if (++c.tj == p.kh) {
-        c.tj = 0;
-        if (++c.ti == p.kt) {
-          c.ti = 0;
-          c.tap = 0;
-          ++c.chunk;
-        }
-      }
-    }
+    const bool go = c.step + 1 < nk;
+    const int tk1 = c.tk + 1;
+    const bool wk = tk1 == p.kw;
+    const int tj1 = c.tj + (wk ? 1 : 0);
+    const bool wj = tj1 == p.kh;
+    const int ti1 = c.ti + (wj ? 1 : 0);
+    const bool wi = ti1 == p.kt;
+    c.tk = go ? (wk ? 0 : tk1) : c.tk;
+    c.tj = go ? (wj ? 0 : tj1) : c.tj;
+    c.ti = go ? (wi ? 0 : ti1) : c.ti;
+    c.chunk = go ? c.chunk + (wi ? 1 : 0) : c.chunk;
+    c.tap = go ? (wi ? 0 : c.tap + 1) : c.tap;
+    c.step = c.step + 1;  // keeps counting: steps >= nk are padding
   };
   // Activation operands come from range-checked buffer loads over one frame: the frame (current
-  // input or history) is uniform, a lane whose tap falls outside the frame, before the history
-  // or past the channels gets the out-of-range offset `frame_bytes` and the hardware returns 0.
+  // input or history) is uniform, a lane whose tap falls outside the frame, before the history,
+  // past the channels or in a padding step gets the out-of-range offset `frame_bytes` and the
+  // hardware returns 0.
   auto load_act = [&](u32x4 (&dst)[MB][2], const Cursor& c) {
     const int s = tf + dt0 + c.ti;  // source frame (negative: history)
-    const bool fok = s >= -p.Th;
+    const bool fok = (s >= -p.Th) & (c.step < nk);
     const bf16_t* fbase = (s >= 0) ? p.x + (int64_t)s * frame_elems
-                                   : (fok ? p.hist + (int64_t)(s + p.Th) * frame_elems : p.x);
+                                   : ((s >= -p.Th) ? p.hist + (int64_t)(s + p.Th) * frame_elems : p.x);
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)fbase, (short)0, (int)frame_bytes, 0x00020000);
     const int uoff = (((dh0 + c.tj) * p.W + (dw0 + c.tk)) * p.Ci + c.chunk * 32) * 2;
@@ -154,21 +160,28 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   };
   // Weight rows past Npad (only in a partial last N tile) read row Npad-1: those columns are
   // never stored. Threads past the tile's pieces repeat the last piece (same data, same address).
-  auto load_w = [&](const Cursor& c) {
+  auto load_w = [&](u32x4 (&dst)[WLOADS], const Cursor& c) {
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
       const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
       const int row = min(q >> 2, p.Npad - 1 - n0), piece = q & 3;
-      wreg[i] = *(const u32x4*)(wbase + row * wrow + c.tap * p.Cip + c.chunk * 32 + piece * 8);
+      dst[i] = *(const u32x4*)(wbase + row * wrow + c.tap * p.Cip + c.chunk * 32 + piece * 8);
     }
   };
-  auto store_w = [&](int buf) {
+  auto store_w = [&](const u32x4 (&src)[WLOADS], int buf) {
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
       const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
       const int row = q >> 2, piece = q & 3;
-      *(u32x4*)(&lds[buf][row * LDS_ROW + piece * 8]) = wreg[i];
+      *(u32x4*)(&lds[buf][row * LDS_ROW + piece * 8]) = src[i];
     }
+  };
+  auto read_w = [&](u32x4 (&dst)[2][NB], int buf) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        dst[q][nb] = *(const u32x4*)(&lds[buf][(nb * 32 + l32) * LDS_ROW + half * 16 + q * 8]);
   };
 
   floatx16 acc[NB][MB];
@@ -179,60 +192,73 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
 
-  auto compute = [&](const u32x4 (&a)[MB][2], int buf) {
+  auto compute = [&](const u32x4 (&a)[MB][2], const u32x4 (&w)[2][NB]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      bf16x8 wf[NB];
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 v = *(const u32x4*)(&lds[buf][(nb * 32 + l32) * LDS_ROW + half * 16 + q * 8]);
-        wf[nb] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 af = __builtin_bit_cast(bf16x8, a[mb][q]);
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], af, acc[nb][mb], 0, 0, 0);
-      }
-    }
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[q][nb]),
+                                                                __builtin_bit_cast(bf16x8, a[mb][q]), acc[nb][mb],
+                                                                0, 0, 0);
   };
 
-  // Three-stage pipeline: step k computes from activation registers and LDS weights of stage
-  // k % 3 while the loads of step k + 2 are in flight.
-  Cursor cur = {0, 0, 0, 0, 0};  // the next step to load
-  load_w(cur);
-  load_act(areg[0], cur);
-  store_w(0);
-  if (nk > 1) {
-    advance(cur);
-    load_w(cur);
-    load_act(areg[1], cur);
-    store_w(1);
-  }
+  // Pipeline (LDS weight stages: step j in stage j % 4). Step k multiplies the activations loaded
+  // during step k - 2 with the weight fragments read from LDS during step k - 1. Meanwhile it
+  // loads the activations of step k + 2 and the weights of step k + 3 (into registers), reads the
+  // fragments of step k + 1, and at its end stores the weights of step k + 2 (loaded during step
+  // k - 1) into their LDS stage, which every wave finished reading three barriers earlier. Every
+  // load has about two steps of matrix work to arrive.
+  Cursor ca = {0, 0, 0, 0, 0, 0};  // activations: the next step to load
+  Cursor cw = {0, 0, 0, 0, 0, 0};  // weights: the next step to load
+  load_w(wreg[0], cw);
+  advance(cw);
+  store_w(wreg[0], 0);
+  load_w(wreg[0], cw);
+  advance(cw);
+  store_w(wreg[0], 1);
+  load_w(wreg[1], cw);  // step 2, stored at the end of step 0
+  advance(cw);
+  load_act(areg[0], ca);
+  advance(ca);
+  load_act(areg[1], ca);
+  advance(ca);
   __syncthreads();
+  read_w(wf[0], 0);
 
+  constexpr int NMFMA = 2 * MB * NB;
   auto step = [&](auto S, int k) {
-    constexpr int s0 = decltype(S)::value;
-    constexpr int s2 = (s0 + 2) % STAGES;
-    const bool more = k + 2 < nk;
-    if (more) {
-      advance(cur);
-      load_w(cur);  // before the activations: the LDS store below then waits for these alone
-      load_act(areg[s2], cur);
+    constexpr int s6 = decltype(S)::value;
+    constexpr int a_cur = s6 % 3, a_new = (s6 + 2) % 3;
+    constexpr int w_new = s6 & 1, w_old = (s6 + 1) & 1;
+    constexpr int f_cur = s6 & 1, f_new = (s6 + 1) & 1;
+    load_w(wreg[w_new], cw);  // step k + 3
+    advance(cw);
+    load_act(areg[a_new], ca);  // step k + 2
+    advance(ca);
+    read_w(wf[f_new], (k + 1) & 3);
+    compute(areg[a_cur], wf[f_cur]);
+    // one matrix instruction, then a few others: VMEM loads first, LDS reads next
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < WLOADS + 2 * MB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      else if (i < WLOADS + 2 * MB + 2 * NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
     }
-    compute(areg[s0], s0);
-    if (more) store_w(s2);
+    __builtin_amdgcn_sched_barrier(0);
+    store_w(wreg[w_old], (k + 2) & 3);  // step k + 2
     __syncthreads();
   };
-  int k = 0;
-  for (; k + STAGES <= nk; k += STAGES) {
+  for (int k = 0; k < nk6; k += 6) {
     step(std::integral_constant<int, 0>{}, k);
     step(std::integral_constant<int, 1>{}, k + 1);
     step(std::integral_constant<int, 2>{}, k + 2);
+    step(std::integral_constant<int, 3>{}, k + 3);
+    step(std::integral_constant<int, 4>{}, k + 4);
+    step(std::integral_constant<int, 5>{}, k + 5);
   }
-  if (k < nk) step(std::integral_constant<int, 0>{}, k);
-  if (k + 1 < nk) step(std::integral_constant<int, 1>{}, k + 1);
 
   // Epilogue: lane holds, per (nb, mb, g), channels n0 + nb*32 + g*8 + half*4 + {0..3} of
   // position mbase + mb*32 + l32. Scheduling barriers keep one (mb, nb) block in flight at a
@@ -290,12 +316,15 @@ struct ConfigEntry {
 #define WVD_CONV_CONFIG(NB, MB, W) \
   { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, conv_mfma_kernel<NB, MB, W> }
 
+// Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
+// bigger per-wave tiles at one wave per SIMD: the second wave issues matrix work while the first
+// waits on memory.
 const ConfigEntry kConfigs[] = {
-    WVD_CONV_CONFIG(6, 2, 4),  // 192 x 256 tiles
-    WVD_CONV_CONFIG(3, 4, 4),  // 96 x 512
+    WVD_CONV_CONFIG(6, 1, 8),  // 192 x 256, 2 waves/SIMD
+    WVD_CONV_CONFIG(6, 1, 4),  // 192 x 128, 2 workgroups/CU
+    WVD_CONV_CONFIG(3, 1, 8),  // 96 x 256
     WVD_CONV_CONFIG(3, 1, 4),  // 96 x 128: small grids
     WVD_CONV_CONFIG(1, 4, 4),  // 32 x 512: a few output channels
-    WVD_CONV_CONFIG(6, 1, 4),  // 192 x 128
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -305,20 +334,17 @@ int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t HW, int Npad) {
   return T * ((HW + bm - 1) / bm) * ((Npad + bn - 1) / bn);
 }
 
-// Largest tile whose grid still gives every CU at least one workgroup per phase.
+// The largest tile whose grid still gives every CU a workgroup per phase.
 int choose_config(int64_t T, int64_t HW, int Npad, int phases) {
   const int64_t cus = 256;
-  if (Npad <= 32) return 3;
+  if (Npad <= 32) return 4;
   if (Npad % 192 == 0) {
     if (blocks_for(kConfigs[0], T, HW, Npad) * phases >= cus) return 0;
-    if (blocks_for(kConfigs[4], T, HW, Npad) * phases >= cus) return 4;
-    return 2;
-  }
-  if (Npad % 96 == 0) {
     if (blocks_for(kConfigs[1], T, HW, Npad) * phases >= cus) return 1;
-    return 2;
+    return 3;
   }
-  return 2;
+  if (Npad % 96 == 0 && blocks_for(kConfigs[2], T, HW, Npad) * phases >= cus) return 2;
+  return 3;
 }
 
 }  // namespace
