@@ -167,6 +167,7 @@ ConvProblem plain_problem(const bf16_t* x, const bf16_t* hist, int T, int H, int
   p.nsplit = co;
   p.fbase = 0;
   p.fmul = 1;
+  p.fstride = 1;
   p.hmul = 1;
   p.wmul = 1;
   return p;
@@ -652,7 +653,7 @@ wvd_status check_desc(const wvd_decoder_desc* d) {
     if (!okc(d->stage_channels[s])) return fail(WVD_ERR_UNSUPPORTED, "stage channels must be multiples of 8 up to 512");
   if (d->mid_resblocks < 0 || d->stage_resblocks < 0 || d->mid_resblocks > 16 || d->stage_resblocks > 16)
     return fail(WVD_ERR_ARG, "resblock counts out of range");
-  if (d->out_channels <= 0 || d->out_channels > 32) return fail(WVD_ERR_UNSUPPORTED, "out_channels must be 1..32");
+  if (d->out_channels <= 0 || d->out_channels > 4) return fail(WVD_ERR_UNSUPPORTED, "out_channels must be 1..4");
   if (d->latent_h <= 0 || d->latent_w <= 0 || d->latent_h > 4096 || d->latent_w > 4096)
     return fail(WVD_ERR_ARG, "latent size out of range");
   if (!(d->eps >= 0.0f)) return fail(WVD_ERR_ARG, "eps must be >= 0");
@@ -670,7 +671,7 @@ int add_param(Plan& p, const std::string& name, int kind, int co, int ci) {
     case K_CONV1: q.bytes = (size_t)packed_elems(co, ci, 1, 1) * 2; break;
     case K_TIME: q.bytes = (size_t)packed_elems(co, ci, 3, 1) * 2; break;
     case K_SPATIAL: q.bytes = (size_t)packed_elems(co, ci, 4, 4) * 2; break;
-    case K_HEAD: q.bytes = (size_t)packed_elems(9 * co, ci, 3, 1) * 2; break;
+    case K_HEAD: q.bytes = (size_t)packed_elems(36, ci, 3, 1) * 2; break;
     default: q.bytes = (size_t)co * 4; break;
   }
   q.offset = 0;
@@ -806,8 +807,9 @@ ChunkFrames chunk_frames(const wvd_decoder_desc* d, int64_t n, bool first_rule) 
   return f;
 }
 
-// Channels of the head's tap planes: 9 per output channel, padded to a multiple of 4.
-int head_zc(int co) { return (int)round_up(9 * co, 4); }
+// The head's tap planes: 9 planes of 4 fp32 channels per position (float4 = 16 bytes per
+// position and plane), 8 bf16 elements' worth of bytes per plane and position.
+constexpr int kHeadPlanes = 9;
 
 // Workspace buffers of the chunk driver (elements of bf16).
 struct WsLayout {
@@ -839,8 +841,8 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n) {
     act = std::max(act, f.stage_out[s] * hw(s + 1) * c);
   }
   act = std::max(act, f.video * hw(d->n_stages) * c);
-  // the head's fp32 tap planes Z (zc floats = 2*zc bf16 per position) live in a stream buffer
-  stream = std::max(stream, f.video * hw(d->n_stages) * 2 * head_zc(d->out_channels));
+  // the head's fp32 tap planes Z (9 planes x 4 floats = 72 bf16 per position) live in a stream buffer
+  stream = std::max(stream, f.video * hw(d->n_stages) * kHeadPlanes * 8);
   WsLayout w;
   size_t off = 0;
   auto take = [&](int64_t elems) {
@@ -925,7 +927,7 @@ extern "C" wvd_status wvd_decoder_pack(const wvd_decoder_desc* d, const float* c
         WVD_HIP(launch_pack_phase2x(params[i], 0, q.co, q.ci, npad, cip, (bf16_t*)dst, s), "pack launch");
         break;
       case K_HEAD:
-        WVD_HIP(launch_pack_head(params[i], 0, q.co, q.ci, (int)round_up(9 * q.co, 32), cip, (bf16_t*)dst, s),
+        WVD_HIP(launch_pack_head(params[i], 0, q.co, q.ci, (int)round_up(36, 32), cip, (bf16_t*)dst, s),
                 "pack launch");
         break;
       default:
@@ -1115,16 +1117,18 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     const int64_t P = T * H * Wd;
     WVD_HIP(launch_norm_silu(bx[cur], F_(p.norm_out), d->eps, 1, ba, P, c, s), "norm launch");
     const int co = d->out_channels;
-    const int zc = head_zc(co);
     float* Z = (float*)bx[cur ^ 1];
-    ConvProblem cp = plain_problem(ba, nullptr, (int)T, H, Wd, c, 0, W_(p.out_w), 9 * co, 3, 1, 1, nullptr, nullptr,
+    // n = tap*4 + o: each lane's 4 accumulator channels are one tap's 4 colour slots, stored as
+    // one float4 into plane `tap`: frame f = t + T*tap of a [9T][H][W][4] tensor
+    ConvProblem cp = plain_problem(ba, nullptr, (int)T, H, Wd, c, 0, W_(p.out_w), 36, 3, 1, 1, nullptr, nullptr,
                                    nullptr);
     cp.y = Z;
     cp.y_f32 = 1;
-    cp.nsplit = zc;
+    cp.nsplit = 4;
+    cp.fstride = (int)T;
+    cp.To = (int)T * kHeadPlanes;
     WVD_TRY(cached_conv(cp, p.out_slot, ba, (int)T, conv_flops(P, co, 27LL * c)));
-    WVD_HIP(launch_head_stencil(Z, zc, co, F_(p.out_b), (bf16_t*)video->data, video->t, (int)frame_offset, (int)T, H,
-                                Wd, s),
+    WVD_HIP(launch_head_stencil(Z, co, F_(p.out_b), (bf16_t*)video->data, video->t, (int)frame_offset, (int)T, H, Wd, s),
             "head launch");
   }
   cache->next_latent += n;

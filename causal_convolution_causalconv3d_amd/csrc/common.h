@@ -57,13 +57,13 @@ struct ConvProblem {
   int N;               // real output channels (columns stored)
   const float* bias;   // [N] or null
   // Output mapping: output element (n, t, h, w, phase p=(a,b)) goes to
-  //   frame f = fbase + fmul*t + n / nsplit, channel n % nsplit,
+  //   frame f = fbase + fmul*t + fstride*(n / nsplit), channel n % nsplit,
   //   row = hmul*h + a, col = wmul*w + b   (a = p / 2, b = p % 2 when phases == 4)
   // in y [To][Ho][Wo][nsplit] (NTHWC), bf16, or fp32 when y_f32 is set (channels n >= N of a
   // 4-channel group are then stored as zeros).
   void* y;
   const bf16_t* res;   // bf16 residual with y's layout and shape, or null (bf16 output only)
-  int To, Ho, Wo, nsplit, fbase, fmul, hmul, wmul;
+  int To, Ho, Wo, nsplit, fbase, fmul, fstride, hmul, wmul;
   int y_f32;
 };
 
@@ -88,12 +88,13 @@ hipError_t launch_pack_phase2x(const void* w, int w_bf16, int Co, int Ci, int Np
                                hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t s);
 
-// Output head. Raw conv_out weight [Co][Ci][3][3][3] -> a temporal (3,1,1) conv with 9*Co outputs,
-// output n = (j*3 + k)*Co + o taking W[o][:, :, j, k], packed [Npad][3][Cip] bf16.
+// Output head (Co <= 4 output channels). Raw conv_out weight [Co][Ci][3][3][3] -> a temporal
+// (3,1,1) conv with 36 outputs, output n = (j*3 + k)*4 + o taking W[o][:, :, j, k] (zero for o >= Co),
+// packed [Npad][3][Cip] bf16.
 hipError_t launch_pack_head(const void* w, int w_bf16, int Co, int Ci, int Npad, int Cip, bf16_t* out, hipStream_t s);
-// video[o][fbase + t][h][w] = bias[o] + sum_{j,k} Z[t][h+j-1][w+k-1][(j*3+k)*Co + o] (zero outside the
-// frame), Z fp32 [T][H][W][zc]; video bf16 NCTHW with `frames` frames per channel plane.
-hipError_t launch_head_stencil(const float* Z, int zc, int Co, const float* bias, bf16_t* video, int64_t frames,
-                               int fbase, int T, int H, int W, hipStream_t s);
+// video[o][fbase + t][h][w] = bias[o] + sum_{j,k} Z[j*3+k][t][h+j-1][w+k-1][o] (zero outside the frame),
+// Z fp32 [9][T][H][W][4] tap planes; video bf16 NCTHW with `frames` frames per channel plane.
+hipError_t launch_head_stencil(const float* Z, int Co, const float* bias, bf16_t* video, int64_t frames, int fbase,
+                               int T, int H, int W, hipStream_t s);
 
 }  // namespace wvd

@@ -63,8 +63,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
   const int mt = lin / numN, nt = lin - (lin / numN) * numN;
   const int n0 = nt * BN;
-  const int tf = mt / tpf;                                        // the tile's frame
-  const int mbase = (mt - tf * tpf) * BM + wave * (MB * 32);      // position within the frame
+  // frames fastest: the same positions of consecutive frames run next to each other on one XCD,
+  // so the three temporal taps of a tile hit in L2
+  const int tf = mt % p.T;                                        // the tile's frame
+  const int mbase = (mt / p.T) * BM + wave * (MB * 32);           // position within the frame
 
   const int pa = (p.phases == 4) ? (phase >> 1) : 0;
   const int pb = (p.phases == 4) ? (phase & 1) : 0;
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][g * 4 + e] + ((p.bias && n + e < p.N) ? p.bias[n + e] : 0.0f);
         // the 4 channels share a frame and are contiguous (nsplit is a multiple of 4)
-        const int f = p.fbase + p.fmul * tf + n / p.nsplit;
+        const int f = p.fbase + p.fmul * tf + p.fstride * (n / p.nsplit);
         const int nc = n % p.nsplit;
         const int64_t idx = (((int64_t)f * p.Ho + orow) * p.Wo + ocol) * p.nsplit + nc;
         if (p.y_f32) {
