@@ -63,10 +63,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
   const int mt = lin / numN, nt = lin - (lin / numN) * numN;
   const int n0 = nt * BN;
-  // frames fastest: the same positions of consecutive frames run next to each other on one XCD,
-  // so the three temporal taps of a tile hit in L2
-  const int tf = mt % p.T;                                        // the tile's frame
-  const int mbase = (mt / p.T) * BM + wave * (MB * 32);           // position within the frame
+  // Tile order: a conv with spatial taps runs a frame's tiles next to each other (neighbouring
+  // rows meet in L2); a temporal-only conv (the time upsample, the head) runs the same positions
+  // of consecutive frames next to each other, so its three temporal taps hit in L2.
+  const bool time_fast = (p.kh == 1) & (p.kw == 1) & (p.phases == 1);
+  const int tf = time_fast ? mt % p.T : mt / tpf;                  // the tile's frame
+  const int tile = time_fast ? mt / p.T : mt - tf * tpf;
+  const int mbase = tile * BM + wave * (MB * 32);                  // position within the frame
 
   const int pa = (p.phases == 4) ? (phase >> 1) : 0;
   const int pb = (p.phases == 4) ? (phase & 1) : 0;
