@@ -103,6 +103,8 @@ def lib():
             "wvd_timing_reset": ([], ctypes.c_int),
             "wvd_timing_read": ([ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+            "wvd_timing_launch": ([ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -120,7 +122,8 @@ def exported_symbols() -> Sequence[str]:
             "wvd_upsample_workspace_bytes", "wvd_upsample", "wvd_decoder_param_count", "wvd_decoder_param_info",
             "wvd_decoder_packed_bytes", "wvd_decoder_pack", "wvd_cache_bytes", "wvd_cache_init", "wvd_cache_reset",
             "wvd_cache_destroy", "wvd_cache_next_latent", "wvd_decode_workspace_bytes", "wvd_decode_chunk",
-            "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read"]
+            "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read",
+            "wvd_timing_launch"]
 
 
 def _check(status: int):
@@ -388,4 +391,25 @@ def timing_read():
         L.wvd_timing_read(i, ctypes.byref(name), ctypes.byref(launches), ctypes.byref(ms), ctypes.byref(flops))
         if launches.value:
             out[name.value.decode()] = (launches.value, ms.value, flops.value)
+    return out
+
+
+def timing_launches():
+    """Every timed conv launch since the last reset: (config name, ms, flops, shape dict)."""
+    L = lib()
+    n = L.wvd_timing_launch(-1, None, None, None, None)
+    names = {}
+    for i in range(L.wvd_timing_read(-1, None, None, None, None)):
+        nm = ctypes.c_char_p()
+        L.wvd_timing_read(i, ctypes.byref(nm), None, None, None)
+        names[i] = nm.value.decode()
+    out = []
+    for i in range(n):
+        cfg = ctypes.c_int()
+        ms = ctypes.c_double()
+        fl = ctypes.c_double()
+        sh = (ctypes.c_int * 8)()
+        L.wvd_timing_launch(i, ctypes.byref(cfg), ctypes.byref(ms), ctypes.byref(fl), sh)
+        out.append((names.get(cfg.value, "?"), ms.value, fl.value,
+                    dict(zip(("T", "H", "W", "Ci", "N", "taps", "phases", "Th"), list(sh)))))
     return out

@@ -88,6 +88,13 @@ struct TimingRecord {
   int config;
   hipEvent_t start, stop;
   double flops;
+  int shape[8];  // T, H, W, Ci, N, taps, phases, Th
+};
+struct LaunchRecord {
+  int config;
+  float ms;
+  double flops;
+  int shape[8];
 };
 struct TimingState {
   std::mutex mu;
@@ -96,6 +103,7 @@ struct TimingState {
   std::vector<hipEvent_t> pool;
   std::vector<int64_t> launches;
   std::vector<double> ms, flops;
+  std::vector<LaunchRecord> log;  // every timed launch since the last reset
 } g_timing;
 
 hipEvent_t pooled_event() {
@@ -124,7 +132,8 @@ wvd_status run_conv(const ConvProblem& p, hipStream_t s, double flops) {
   if (timed) {
     WVD_HIP(hipEventRecord(e1, s), "hipEventRecord");
     std::lock_guard<std::mutex> lk(g_timing.mu);
-    g_timing.pending.push_back({cfg, e0, e1, flops});
+    TimingRecord r{cfg, e0, e1, flops, {p.T, p.H, p.W, p.Ci, p.N, p.ntaps, p.phases, p.Th}};
+    g_timing.pending.push_back(r);
   }
   return WVD_OK;
 }
@@ -1157,7 +1166,23 @@ extern "C" wvd_status wvd_timing_reset(void) {
   g_timing.launches.assign(conv_config_count(), 0);
   g_timing.ms.assign(conv_config_count(), 0.0);
   g_timing.flops.assign(conv_config_count(), 0.0);
+  g_timing.log.clear();
   return WVD_OK;
+}
+
+extern "C" int wvd_timing_launch(int i, int* config, double* ms, double* flops, int shape[8]) {
+  const char* nm = nullptr;
+  wvd_timing_read(0, &nm, nullptr, nullptr, nullptr);  // drains the pending events
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  const int n = (int)g_timing.log.size();
+  if (i < 0 || i >= n) return n;
+  const LaunchRecord& r = g_timing.log[i];
+  if (config) *config = r.config;
+  if (ms) *ms = r.ms;
+  if (flops) *flops = r.flops;
+  if (shape)
+    for (int k = 0; k < 8; ++k) shape[k] = r.shape[k];
+  return n;
 }
 
 extern "C" int wvd_timing_read(int i, const char** name, int64_t* launches, double* ms, double* flops) {
@@ -1175,6 +1200,9 @@ extern "C" int wvd_timing_read(int i, const char** name, int64_t* launches, doub
       g_timing.launches[r.config] += 1;
       g_timing.ms[r.config] += t;
       g_timing.flops[r.config] += r.flops;
+      LaunchRecord l{r.config, t, r.flops, {}};
+      for (int k = 0; k < 8; ++k) l.shape[k] = r.shape[k];
+      g_timing.log.push_back(l);
     }
     g_timing.pool.push_back(r.start);
     g_timing.pool.push_back(r.stop);

@@ -231,6 +231,10 @@ wvd_status wvd_timing_reset(void);
  * the summed algorithmic FLOPs (2*M*N*K with the real, unpadded sizes). Returns the count of
  * configurations when name is null. */
 int wvd_timing_read(int i, const char** name, int64_t* launches, double* ms, double* flops);
+/* Launch i (0-based, in launch order) since the last reset: its configuration index, milliseconds,
+ * algorithmic FLOPs and problem shape {T, H, W, Ci, N, taps, phases, history frames}. Returns the
+ * number of recorded launches (call with i = -1 to count). */
+int wvd_timing_launch(int i, int* config, double* ms, double* flops, int shape[8]);
 
 #ifdef __cplusplus
 }
