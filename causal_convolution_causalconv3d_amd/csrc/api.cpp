@@ -196,10 +196,14 @@ wvd_status run_time_conv(const bf16_t* x, const bf16_t* hist, int T, int H, int 
   return run_conv(p, s, conv_flops((int64_t)T * H * W, 2 * C, 3LL * C));
 }
 
-// Nearest x2 + 3x3 conv as four phase convs: x [T][H][W][C] -> y [T][2H][2W][C].
+// Nearest x2 + 3x3 conv as four phase convs: x [T][H][W][C] -> y [T][2H][2W][C]; with norm_gamma,
+// y is SiLU(RMS norm) of the upsampled tensor (fused in the epilogue).
 wvd_status run_phase_conv(const bf16_t* x, int T, int H, int W, int C, const void* wpk, const float* bias, bf16_t* y,
-                          hipStream_t s) {
+                          hipStream_t s, const float* norm_gamma = nullptr, float norm_eps = 0.0f) {
   ConvProblem p = plain_problem(x, nullptr, T, H, W, C, 0, wpk, C, 1, 1, 1, bias, y, nullptr);
+  p.norm_gamma = norm_gamma;
+  p.norm_eps = norm_eps;
+  p.norm_silu = 1;
   p.ntaps = 4;
   p.phases = 4;
   p.kt = 1;
@@ -412,13 +416,25 @@ wvd_status resblock_core(const ResblockArgs& r, hipStream_t s, F1 after_conv1, F
   WVD_HIP(launch_norm_silu(r.x, w->gamma1, r.eps, 1, r.a, P, w->cin, s), "norm launch");
   ConvProblem c1 = plain_problem(r.a, r.hist1, r.T, r.H, r.W, w->cin, r.th1, w->conv1, w->cout, 3, 3, 3, w->bias1, r.h,
                                  nullptr);
+  // conv2's input a2 = SiLU(norm2(h)): fused into conv1's epilogue when one workgroup holds every
+  // output channel of a position (then h is never stored), else a separate pass
+  const bool fuse = conv_can_fuse_norm((int)round_up(w->cout, 32));
+  if (fuse) {
+    c1.norm_gamma = w->gamma2;
+    c1.norm_eps = r.eps;
+    c1.norm_silu = 1;
+  }
   WVD_TRY(run_conv(c1, s, conv_flops(P, w->cout, 27LL * w->cin)));
   WVD_TRY(after_conv1(r.a));
-  WVD_HIP(launch_norm_silu(r.h, w->gamma2, r.eps, 1, r.a, P, w->cout, s), "norm launch");
-  ConvProblem c2 = plain_problem(r.a, r.hist2, r.T, r.H, r.W, w->cout, r.th2, w->conv2, w->cout, 3, 3, 3, w->bias2,
+  const bf16_t* a2 = r.h;
+  if (!fuse) {
+    WVD_HIP(launch_norm_silu(r.h, w->gamma2, r.eps, 1, r.a, P, w->cout, s), "norm launch");
+    a2 = r.a;
+  }
+  ConvProblem c2 = plain_problem(a2, r.hist2, r.T, r.H, r.W, w->cout, r.th2, w->conv2, w->cout, 3, 3, 3, w->bias2,
                                  r.y, residual);
   WVD_TRY(run_conv(c2, s, conv_flops(P, w->cout, 27LL * w->cout)));
-  WVD_TRY(after_conv2(r.a));
+  WVD_TRY(after_conv2(a2));
   return WVD_OK;
 }
 
@@ -434,6 +450,7 @@ wvd_status check_resblock_weights(const wvd_resblock_weights* w) {
   if (w->cin <= 0 || w->cout <= 0 || w->cin % 8 || w->cout % 8 || w->cin > 512 || w->cout > 512)
     return fail(WVD_ERR_UNSUPPORTED, "resblock channels must be multiples of 8 up to 512");
   if (!w->gamma1 || !w->conv1 || !w->gamma2 || !w->conv2) return fail(WVD_ERR_ARG, "resblock weight pointer is null");
+  if (!aligned16(w->gamma1) || !aligned16(w->gamma2)) return fail(WVD_ERR_ALIGN, "gammas must be 16-byte aligned");
   if (w->cin != w->cout && !w->shortcut) return fail(WVD_ERR_ARG, "cin != cout needs the shortcut weight");
   if (!aligned16(w->conv1) || !aligned16(w->conv2) || (w->shortcut && !aligned16(w->shortcut)))
     return fail(WVD_ERR_ALIGN, "packed weights must be 16-byte aligned");
@@ -1080,19 +1097,36 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     }
     WVD_HIP(launch_norm_silu(x, F_(r.gamma1), d->eps, 1, ba, P, r.cin, s), "norm launch");
     ConvProblem c1 = plain_problem(ba, nullptr, (int)T, H, Wd, r.cin, 0, W_(r.w1), r.cout, 3, 3, 3, F_(r.b1), bh, nullptr);
+    // norm2 + SiLU fused into conv1's epilogue when one workgroup holds all output channels
+    const bool fuse = conv_can_fuse_norm((int)round_up(r.cout, 32));
+    if (fuse) {
+      c1.norm_gamma = F_(r.gamma2);
+      c1.norm_eps = d->eps;
+      c1.norm_silu = 1;
+    }
     WVD_TRY(cached_conv(c1, r.slot1, ba, (int)T, conv_flops(P, r.cout, 27LL * r.cin)));
-    WVD_HIP(launch_norm_silu(bh, F_(r.gamma2), d->eps, 1, ba, P, r.cout, s), "norm launch");
-    ConvProblem c2 = plain_problem(ba, nullptr, (int)T, H, Wd, r.cout, 0, W_(r.w2), r.cout, 3, 3, 3, F_(r.b2), y, residual);
-    WVD_TRY(cached_conv(c2, r.slot2, ba, (int)T, conv_flops(P, r.cout, 27LL * r.cout)));
+    const bf16_t* a2 = bh;
+    if (!fuse) {
+      WVD_HIP(launch_norm_silu(bh, F_(r.gamma2), d->eps, 1, ba, P, r.cout, s), "norm launch");
+      a2 = ba;
+    }
+    ConvProblem c2 = plain_problem(a2, nullptr, (int)T, H, Wd, r.cout, 0, W_(r.w2), r.cout, 3, 3, 3, F_(r.b2), y, residual);
+    WVD_TRY(cached_conv(c2, r.slot2, a2, (int)T, conv_flops(P, r.cout, 27LL * r.cout)));
     return WVD_OK;
   };
   for (const ResPlan& r : p.mid) WVD_TRY(resblock(r));
+  // The last stage's spatial upsample also applies norm_out + SiLU in its epilogue when one
+  // workgroup holds every channel (the L4 tensor is then written once, already activated).
+  const bf16_t* act = nullptr;  // conv_out's input once norm_out has been applied
+  bf16_t* zbuf = nullptr;       // a free buffer for the head's tap planes
   for (int si = 0; si < L; ++si) {
     const StagePlan& st = p.stages[si];
     for (const ResPlan& r : st.res) {
       WVD_TRY(resblock(r));
       c = r.cout;
     }
+    const bool fuse_out = si == L - 1 && conv_can_fuse_norm((int)round_up(c, 32));
+    const float* ng = fuse_out ? F_(p.norm_out) : nullptr;
     const bf16_t* x = bx[cur];
     if (st.temporal) {
       const size_t fb = (size_t)H * Wd * c * 2;
@@ -1112,7 +1146,15 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
       }
       T = To;
       // spatial upsample from the time conv's output into the stream buffer
-      WVD_TRY(run_phase_conv(dst, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur], s));
+      WVD_TRY(run_phase_conv(dst, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur], s, ng, d->eps));
+      if (fuse_out) {
+        act = bx[cur];
+        zbuf = bx[cur ^ 1];
+      }
+    } else if (fuse_out) {
+      WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), ba, s, ng, d->eps));
+      act = ba;
+      zbuf = bx[cur ^ 1];
     } else {
       WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur ^ 1], s));
       cur ^= 1;
@@ -1120,23 +1162,27 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     H *= 2;
     Wd *= 2;
   }
-  // norm_out + SiLU, then conv_out as temporal tap planes Z (fp32, in the free stream buffer)
-  // and the 9-tap stencil into the video (NCTHW) at frame_offset
+  // norm_out + SiLU (unless fused above), then conv_out as temporal tap planes Z (fp32, in a free
+  // stream buffer) and the 9-tap stencil into the video (NCTHW) at frame_offset
   {
     const int64_t P = T * H * Wd;
-    WVD_HIP(launch_norm_silu(bx[cur], F_(p.norm_out), d->eps, 1, ba, P, c, s), "norm launch");
+    if (!act) {
+      WVD_HIP(launch_norm_silu(bx[cur], F_(p.norm_out), d->eps, 1, ba, P, c, s), "norm launch");
+      act = ba;
+      zbuf = bx[cur ^ 1];
+    }
     const int co = d->out_channels;
-    float* Z = (float*)bx[cur ^ 1];
+    float* Z = (float*)zbuf;
     // n = tap*4 + o: each lane's 4 accumulator channels are one tap's 4 colour slots, stored as
     // one float4 into plane `tap`: frame f = t + T*tap of a [9T][H][W][4] tensor
-    ConvProblem cp = plain_problem(ba, nullptr, (int)T, H, Wd, c, 0, W_(p.out_w), 36, 3, 1, 1, nullptr, nullptr,
+    ConvProblem cp = plain_problem(act, nullptr, (int)T, H, Wd, c, 0, W_(p.out_w), 36, 3, 1, 1, nullptr, nullptr,
                                    nullptr);
     cp.y = Z;
     cp.y_f32 = 1;
     cp.nsplit = 4;
     cp.fstride = (int)T;
     cp.To = (int)T * kHeadPlanes;
-    WVD_TRY(cached_conv(cp, p.out_slot, ba, (int)T, conv_flops(P, co, 27LL * c)));
+    WVD_TRY(cached_conv(cp, p.out_slot, act, (int)T, conv_flops(P, co, 27LL * c)));
     WVD_HIP(launch_head_stencil(Z, co, F_(p.out_b), (bf16_t*)video->data, video->t, (int)frame_offset, (int)T, H, Wd, s),
             "head launch");
   }

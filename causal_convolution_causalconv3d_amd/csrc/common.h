@@ -65,9 +65,15 @@ struct ConvProblem {
   const bf16_t* res;   // bf16 residual with y's layout and shape, or null (bf16 output only)
   int To, Ho, Wo, nsplit, fbase, fmul, fstride, hmul, wmul;
   int y_f32;
+  // Optional fused channel RMS norm (+ SiLU) of the output (bf16 output, no residual, one
+  // channel tile: Npad <= conv_can_fuse_norm's limit): y = SiLU(gamma * v / sqrt(mean_c v^2 + eps)).
+  const float* norm_gamma;  // [N] or null
+  float norm_eps;
+  int norm_silu;
 };
 
 hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id);
+bool conv_can_fuse_norm(int Npad);
 const char* conv_config_name(int config_id);
 int conv_config_count();
 

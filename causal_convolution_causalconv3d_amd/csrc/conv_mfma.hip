@@ -268,6 +268,57 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   // Epilogue: lane holds, per (nb, mb, g), channels n0 + nb*32 + g*8 + half*4 + {0..3} of
   // position mbase + mb*32 + l32. Scheduling barriers keep one (mb, nb) block in flight at a
   // time so the accumulators are not all copied out of the AGPRs at once.
+  if (p.norm_gamma) {
+    // Fused channel RMS norm (+ SiLU) of the conv output: the workgroup holds every channel of
+    // its positions (one N tile), split between lanes l and l ^ 32, so the per-position sum of
+    // squares is this lane's part plus one cross-lane exchange. fp32 statistics on the unrounded
+    // sums, one bf16 rounding of the activated value.
+    const float inv_n = 1.0f / (float)p.N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int n = nb * 32 + g * 8 + half * 4 + e;
+            const float v = n < p.N ? acc[nb][mb][g * 4 + e] + (p.bias ? p.bias[n] : 0.0f) : 0.0f;
+            ss = fmaf(v, v, ss);
+          }
+      ss += __shfl_xor(ss, 32, 64);
+      const float r = rsqrtf(ss * inv_n + p.norm_eps);
+      const bool valid = pv[mb];
+      const int orow = p.hmul * ph[mb] + pa;
+      const int ocol = p.wmul * pw[mb] + pb;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = nb * 32 + g * 8 + half * 4;
+          if (!valid || n >= p.N) continue;
+          const float4 gm = *(const float4*)(p.norm_gamma + n);
+          const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = (acc[nb][mb][g * 4 + e] + (p.bias ? p.bias[n + e] : 0.0f)) * r * gv[e];
+            if (p.norm_silu) v[e] = silu_f32(v[e]);
+          }
+          const int f = p.fbase + p.fmul * tf + p.fstride * (n / p.nsplit);
+          const int nc = n % p.nsplit;
+          const int64_t idx = (((int64_t)f * p.Ho + orow) * p.Wo + ocol) * p.nsplit + nc;
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *(uint2*)((bf16_t*)p.y + idx) = o;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const bool valid = pv[mb];
@@ -332,6 +383,7 @@ const ConfigEntry kConfigs[] = {
     WVD_CONV_CONFIG(1, 4, 4),  // 32 x 512: a few output channels
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+constexpr int kMaxFusedNormN = 192;  // the widest channel tile
 
 // Workgroups of a problem: per frame ceil(H*W / BM) position tiles, times the channel tiles.
 int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t HW, int Npad) {
@@ -340,9 +392,13 @@ int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t HW, int Npad) {
 }
 
 // The largest tile whose grid still gives every CU a workgroup per phase.
-int choose_config(int64_t T, int64_t HW, int Npad, int phases) {
+int choose_config(int64_t T, int64_t HW, int Npad, int phases, bool one_n_tile) {
   const int64_t cus = 256;
   if (Npad <= 32) return 4;
+  if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup
+    if (Npad <= 96) return blocks_for(kConfigs[2], T, HW, Npad) * phases >= cus ? 2 : 3;
+    return blocks_for(kConfigs[0], T, HW, Npad) * phases >= cus ? 0 : 1;
+  }
   if (Npad % 192 == 0) {
     if (blocks_for(kConfigs[0], T, HW, Npad) * phases >= cus) return 0;
     if (blocks_for(kConfigs[1], T, HW, Npad) * phases >= cus) return 1;
@@ -354,6 +410,8 @@ int choose_config(int64_t T, int64_t HW, int Npad, int phases) {
 
 }  // namespace
 
+bool conv_can_fuse_norm(int Npad) { return Npad <= kMaxFusedNormN; }
+
 const char* conv_config_name(int id) { return (id >= 0 && id < kNumConfigs) ? kConfigs[id].name : "?"; }
 int conv_config_count() { return kNumConfigs; }
 
@@ -362,7 +420,8 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id)
   if (p.T == 0 || HW == 0) return hipSuccess;
   // one frame is addressed with 32-bit byte offsets
   if (HW * p.Ci * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const int id = choose_config(p.T, HW, p.Npad, p.phases);
+  if (p.norm_gamma && (p.Npad > kMaxFusedNormN || p.res || p.y_f32 || p.nsplit != p.N)) return hipErrorInvalidValue;
+  const int id = choose_config(p.T, HW, p.Npad, p.phases, p.norm_gamma != nullptr);
   const ConfigEntry& c = kConfigs[id];
   const int64_t blocks = blocks_for(c, p.T, HW, p.Npad);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;

@@ -167,6 +167,21 @@ def test_resblock_given_history_matches_oracle():
     assert r <= 2e-2
 
 
+@pytest.mark.parametrize("C", [96, 192])
+def test_resblock_widths_match_oracle(C):
+    """Widths whose conv1 carries the second norm in its epilogue (one channel tile)."""
+    cfg = wl.resblock_bf16(seed=20 + C, C=C, T=3, H=9, W=13)
+    p = oracle.as_numpy_params(cfg["params"])
+    ref = oracle.resblock(cfg["x"][0], p, "res", {}, 1e-6, given_hist=oracle._f32(cfg["hist"][0]))
+    wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+    hd = to_dev_nthwc(cfg["hist"])
+    y = wvd.resblock(to_dev_nthwc(cfg["x"]), wts, 1e-6, hist1=hd, hist2=hd)
+    torch.cuda.synchronize()
+    r = rel_max(from_dev_nthwc(y), ref)
+    log(f"resblock C={C} rel {r:.3e}")
+    assert r <= 2e-2
+
+
 def test_resblock_shortcut_and_histories_match_oracle():
     cfg = wl.resblock_bf16(seed=12, C=384, T=3, H=7, W=9, Cout=192, hist_frames=0)
     p = oracle.as_numpy_params(cfg["params"])
