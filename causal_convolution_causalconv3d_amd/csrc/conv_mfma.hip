@@ -378,9 +378,10 @@ struct ConfigEntry {
 const ConfigEntry kConfigs[] = {
     WVD_CONV_CONFIG(6, 1, 8),  // 192 x 256, 2 waves/SIMD
     WVD_CONV_CONFIG(6, 1, 4),  // 192 x 128, 2 workgroups/CU
-    WVD_CONV_CONFIG(3, 1, 8),  // 96 x 256
+    WVD_CONV_CONFIG(3, 1, 8),  // 96 x 256, 2 waves/SIMD
     WVD_CONV_CONFIG(3, 1, 4),  // 96 x 128: small grids
     WVD_CONV_CONFIG(1, 4, 4),  // 32 x 512: a few output channels
+    WVD_CONV_CONFIG(3, 2, 8),  // 96 x 512, 2 waves/SIMD: long reductions (3x3x3 taps)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kMaxFusedNormN = 192;  // the widest channel tile
@@ -392,11 +393,14 @@ int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t HW, int Npad) {
 }
 
 // The largest tile whose grid still gives every CU a workgroup per phase.
-int choose_config(int64_t T, int64_t HW, int Npad, int phases, bool one_n_tile) {
+// A 96-wide channel tile takes two position blocks per wave on 3x3x3 convs (half the weight
+// fragment reads per matrix op; measured faster there), one on short reductions.
+int choose_config(int64_t T, int64_t HW, int Npad, int phases, int ntaps, bool one_n_tile) {
   const int64_t cus = 256;
   if (Npad <= 32) return 4;
+  const int n96 = (ntaps >= 9 && blocks_for(kConfigs[5], T, HW, Npad) * phases >= cus) ? 5 : 2;
   if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup
-    if (Npad <= 96) return blocks_for(kConfigs[2], T, HW, Npad) * phases >= cus ? 2 : 3;
+    if (Npad <= 96) return blocks_for(kConfigs[2], T, HW, Npad) * phases >= cus ? n96 : 3;
     return blocks_for(kConfigs[0], T, HW, Npad) * phases >= cus ? 0 : 1;
   }
   if (Npad % 192 == 0) {
@@ -404,7 +408,7 @@ int choose_config(int64_t T, int64_t HW, int Npad, int phases, bool one_n_tile) 
     if (blocks_for(kConfigs[1], T, HW, Npad) * phases >= cus) return 1;
     return 3;
   }
-  if (Npad % 96 == 0 && blocks_for(kConfigs[2], T, HW, Npad) * phases >= cus) return 2;
+  if (Npad % 96 == 0 && blocks_for(kConfigs[2], T, HW, Npad) * phases >= cus) return n96;
   return 3;
 }
 
@@ -421,7 +425,7 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id)
   // one frame is addressed with 32-bit byte offsets
   if (HW * p.Ci * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if (p.norm_gamma && (p.Npad > kMaxFusedNormN || p.res || p.y_f32 || p.nsplit != p.N)) return hipErrorInvalidValue;
-  const int id = choose_config(p.T, HW, p.Npad, p.phases, p.norm_gamma != nullptr);
+  const int id = choose_config(p.T, HW, p.Npad, p.phases, p.ntaps, p.norm_gamma != nullptr);
   const ConfigEntry& c = kConfigs[id];
   const int64_t blocks = blocks_for(c, p.T, HW, p.Npad);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
