@@ -105,6 +105,7 @@ def lib():
                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
             "wvd_timing_launch": ([ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
+            "wvd_conv_force_config": ([ctypes.c_int], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -123,7 +124,7 @@ def exported_symbols() -> Sequence[str]:
             "wvd_decoder_packed_bytes", "wvd_decoder_pack", "wvd_cache_bytes", "wvd_cache_init", "wvd_cache_reset",
             "wvd_cache_destroy", "wvd_cache_next_latent", "wvd_decode_workspace_bytes", "wvd_decode_chunk",
             "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read",
-            "wvd_timing_launch"]
+            "wvd_timing_launch", "wvd_conv_force_config"]
 
 
 def _check(status: int):
@@ -392,6 +393,27 @@ def timing_read():
         if launches.value:
             out[name.value.decode()] = (launches.value, ms.value, flops.value)
     return out
+
+
+def conv_config_names():
+    """Names of the matrix-core conv configurations, by index."""
+    L = lib()
+    out = []
+    for i in range(L.wvd_timing_read(-1, None, None, None, None)):
+        nm = ctypes.c_char_p()
+        L.wvd_timing_read(i, ctypes.byref(nm), None, None, None)
+        out.append(nm.value.decode())
+    return out
+
+
+def conv_force_config(config):
+    """Run every following conv launch with configuration `config` (index or name), or with the
+    automatic choice when config is None or -1 (testing and tuning)."""
+    if config is None:
+        config = -1
+    elif isinstance(config, str):
+        config = conv_config_names().index(config)
+    _check(lib().wvd_conv_force_config(int(config)))
 
 
 def timing_launches():

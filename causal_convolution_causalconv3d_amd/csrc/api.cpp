@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cstring>
 #include <new>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -117,6 +118,9 @@ hipEvent_t pooled_event() {
   return e;
 }
 
+// Configuration forced by wvd_conv_force_config (-1: automatic choice).
+std::atomic<int> g_force_config{-1};
+
 wvd_status run_conv(const ConvProblem& p, hipStream_t s, double flops) {
   const bool timed = g_timing.on;
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -128,7 +132,9 @@ wvd_status run_conv(const ConvProblem& p, hipStream_t s, double flops) {
     WVD_HIP(hipEventRecord(e0, s), "hipEventRecord");
   }
   int cfg = -1;
-  WVD_HIP(launch_conv_mfma(p, s, &cfg), "conv_mfma launch");
+  const hipError_t le = launch_conv_mfma(p, s, &cfg, g_force_config.load());
+  if (le == hipErrorNotSupported) return fail(WVD_ERR_UNSUPPORTED, "forced conv configuration cannot run this problem");
+  WVD_HIP(le, "conv_mfma launch");
   if (timed) {
     WVD_HIP(hipEventRecord(e1, s), "hipEventRecord");
     std::lock_guard<std::mutex> lk(g_timing.mu);
@@ -1195,6 +1201,12 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
 // ==============================================================================================
 // Timing
 // ==============================================================================================
+extern "C" wvd_status wvd_conv_force_config(int config) {
+  if (config < -1 || config >= conv_config_count()) return fail(WVD_ERR_ARG, "conv config index out of range");
+  g_force_config.store(config);
+  return WVD_OK;
+}
+
 extern "C" wvd_status wvd_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
   g_timing.on = on != 0;

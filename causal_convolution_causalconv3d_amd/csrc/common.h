@@ -72,7 +72,8 @@ struct ConvProblem {
   int norm_silu;
 };
 
-hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id);
+// force_config >= 0 runs that configuration (hipErrorNotSupported when it cannot run p).
+hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id, int force_config = -1);
 bool conv_can_fuse_norm(int Npad);
 const char* conv_config_name(int config_id);
 int conv_config_count();

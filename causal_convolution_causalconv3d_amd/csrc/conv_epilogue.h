@@ -1,0 +1,112 @@
+// Epilogue of the matrix-core convolution kernels: bias, optional residual add or fused channel
+// RMS norm (+ SiLU), the output mapping of ConvProblem, and one bf16 (or fp32) rounding.
+#pragma once
+
+#include "common.h"
+
+namespace wvd {
+
+// The lane holds, per (nb, mb, g), channels n0 + nb*32 + g*8 + half*4 + {0..3} of position
+// (ph[mb], pw[mb]) of frame tf (valid when pv[mb]); (pa, pb) is the output phase. Scheduling
+// barriers keep one (mb, nb) block in flight at a time so the accumulators are not all copied
+// out of the AGPRs at once.
+template <int NB, int MB>
+__device__ __forceinline__ void conv_epilogue(const ConvProblem& p, floatx16 (&acc)[NB][MB], const int (&ph)[MB],
+                                              const int (&pw)[MB], const bool (&pv)[MB], int tf, int n0, int pa,
+                                              int pb, int half) {
+  if (p.norm_gamma) {
+    // Fused channel RMS norm (+ SiLU) of the conv output: the workgroup holds every channel of
+    // its positions (one N tile), split between lanes l and l ^ 32, so the per-position sum of
+    // squares is this lane's part plus one cross-lane exchange. fp32 statistics on the unrounded
+    // sums, one bf16 rounding of the activated value.
+    const float inv_n = 1.0f / (float)p.N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int n = nb * 32 + g * 8 + half * 4 + e;
+            const float v = n < p.N ? acc[nb][mb][g * 4 + e] + (p.bias ? p.bias[n] : 0.0f) : 0.0f;
+            ss = fmaf(v, v, ss);
+          }
+      ss += __shfl_xor(ss, 32, 64);
+      const float r = rsqrtf(ss * inv_n + p.norm_eps);
+      const bool valid = pv[mb];
+      const int orow = p.hmul * ph[mb] + pa;
+      const int ocol = p.wmul * pw[mb] + pb;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = nb * 32 + g * 8 + half * 4;
+          if (!valid || n >= p.N) continue;
+          const float4 gm = *(const float4*)(p.norm_gamma + n);
+          const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = (acc[nb][mb][g * 4 + e] + (p.bias ? p.bias[n + e] : 0.0f)) * r * gv[e];
+            if (p.norm_silu) v[e] = silu_f32(v[e]);
+          }
+          const int f = p.fbase + p.fmul * tf + p.fstride * (n / p.nsplit);
+          const int nc = n % p.nsplit;
+          const int64_t idx = (((int64_t)f * p.Ho + orow) * p.Wo + ocol) * p.nsplit + nc;
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *(uint2*)((bf16_t*)p.y + idx) = o;
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const bool valid = pv[mb];
+    const int orow = p.hmul * ph[mb] + pa;
+    const int ocol = p.wmul * pw[mb] + pb;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + nb * 32 + g * 8 + half * 4;
+        if (!valid || n >= p.N) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][g * 4 + e] + ((p.bias && n + e < p.N) ? p.bias[n + e] : 0.0f);
+        // the 4 channels share a frame and are contiguous (nsplit is a multiple of 4)
+        const int f = p.fbase + p.fmul * tf + p.fstride * (n / p.nsplit);
+        const int nc = n % p.nsplit;
+        const int64_t idx = (((int64_t)f * p.Ho + orow) * p.Wo + ocol) * p.nsplit + nc;
+        if (p.y_f32) {
+          float4 o;
+          o.x = n + 0 < p.N ? v[0] : 0.0f;
+          o.y = n + 1 < p.N ? v[1] : 0.0f;
+          o.z = n + 2 < p.N ? v[2] : 0.0f;
+          o.w = n + 3 < p.N ? v[3] : 0.0f;
+          *(float4*)((float*)p.y + idx) = o;
+        } else {
+          if (p.res) {
+            const uint2 r = *(const uint2*)(p.res + idx);
+            v[0] += bf16_lo(r.x);
+            v[1] += bf16_hi(r.x);
+            v[2] += bf16_lo(r.y);
+            v[3] += bf16_hi(r.y);
+          }
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *(uint2*)((bf16_t*)p.y + idx) = o;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace wvd

@@ -23,7 +23,7 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "common.h"
+#include "conv_epilogue.h"
 
 namespace wvd {
 
@@ -265,112 +265,276 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
     step(std::integral_constant<int, 5>{}, k + 5);
   }
 
-  // Epilogue: lane holds, per (nb, mb, g), channels n0 + nb*32 + g*8 + half*4 + {0..3} of
-  // position mbase + mb*32 + l32. Scheduling barriers keep one (mb, nb) block in flight at a
-  // time so the accumulators are not all copied out of the AGPRs at once.
-  if (p.norm_gamma) {
-    // Fused channel RMS norm (+ SiLU) of the conv output: the workgroup holds every channel of
-    // its positions (one N tile), split between lanes l and l ^ 32, so the per-position sum of
-    // squares is this lane's part plus one cross-lane exchange. fp32 statistics on the unrounded
-    // sums, one bf16 rounding of the activated value.
-    const float inv_n = 1.0f / (float)p.N;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float ss = 0.0f;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int n = nb * 32 + g * 8 + half * 4 + e;
-            const float v = n < p.N ? acc[nb][mb][g * 4 + e] + (p.bias ? p.bias[n] : 0.0f) : 0.0f;
-            ss = fmaf(v, v, ss);
-          }
-      ss += __shfl_xor(ss, 32, 64);
-      const float r = rsqrtf(ss * inv_n + p.norm_eps);
-      const bool valid = pv[mb];
-      const int orow = p.hmul * ph[mb] + pa;
-      const int ocol = p.wmul * pw[mb] + pb;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = nb * 32 + g * 8 + half * 4;
-          if (!valid || n >= p.N) continue;
-          const float4 gm = *(const float4*)(p.norm_gamma + n);
-          const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] = (acc[nb][mb][g * 4 + e] + (p.bias ? p.bias[n + e] : 0.0f)) * r * gv[e];
-            if (p.norm_silu) v[e] = silu_f32(v[e]);
-          }
-          const int f = p.fbase + p.fmul * tf + p.fstride * (n / p.nsplit);
-          const int nc = n % p.nsplit;
-          const int64_t idx = (((int64_t)f * p.Ho + orow) * p.Wo + ocol) * p.nsplit + nc;
-          uint2 o;
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          *(uint2*)((bf16_t*)p.y + idx) = o;
-        }
-      }
-    }
-    return;
-  }
+  conv_epilogue<NB, MB>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
+}
+
+// Halo-tile variant for KS x KS spatial taps: KS = 3 (phases == 1, kh == kw == 3, any kt) or
+// KS = 2 (the four 2x2 phase convs of the x2 upsampling, phases == 4, one workgroup per phase).
+// A workgroup owns TR = WAVES*MB rows x 32 columns of one frame and BN = 32*NB output channels;
+// wave w owns rows w*MB .. w*MB + MB - 1 (one 32-position block per row). The K loop runs over
+// stages (32-channel chunk outermost, temporal tap inside), KS*KS steps (the spatial taps) per
+// stage. A stage's input patch, (TR + 2) x 34 positions x 32 channels of the tap's source frame
+// (the tile with a 1-pixel halo), is read from memory once, staged in LDS (double-buffered,
+// 80-byte position stride: conflict-free 16-byte reads of 32 consecutive positions), and every
+// spatial tap reads its activation operand from it. Out-of-frame, out-of-channel and
+// pre-history reads are hardware zeros as above. The weights go through LDS one K step at a time
+// as in conv_mfma_kernel.
+constexpr int PROW = 40;  // bf16 per patch position: 32 channels + 8 pad
+
+template <int NB, int MB, int WAVES, int KS>
+__global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProblem p) {
+  static_assert(KS == 2 || KS == 3, "3x3 taps, or 2x2 phase taps");
+  constexpr int SPS = KS * KS;              // steps per stage
+  constexpr int STORE_S = SPS == 9 ? 4 : 2;  // the step that stores the next stage's patch
+  constexpr int BN = NB * 32;
+  constexpr int TR = WAVES * MB;
+  constexpr int PR = TR + 2, PC = 34;
+  constexpr int PATCH = PR * PC * PROW + 8;  // + one 16-byte slot for the surplus pieces
+  constexpr int NT = WAVES * 64;
+  constexpr int WPIECES = BN * 4;
+  constexpr int WLOADS = (WPIECES + NT - 1) / NT;
+  constexpr int PPIECES = PR * PC * 4;  // 16-byte pieces of one patch
+  constexpr int PLOADS = (PPIECES + NT - 1) / NT;
+  static_assert(NT % 4 == 0, "a thread's pieces share one channel group");
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w[4][BN * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_p[2][PATCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int phase = blockIdx.z;
+  const int pa = (KS == 2) ? (phase >> 1) : 0;
+  const int pb = (KS == 2) ? (phase & 1) : 0;
+
+  const int numR = (p.H + TR - 1) / TR, numC = (p.W + 31) / 32;
+  const int tpf = numR * numC;
+  const int numN = (p.Npad + BN - 1) / BN;
+  const int total = p.T * tpf * numN;
+  // XCD-aware order as in conv_mfma_kernel; the channel tiles of a position tile are adjacent
+  // (they read the same patches).
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int q8 = total >> 3, r8 = total & 7;
+  const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
+  const int mt = lin / numN, nt = lin - (lin / numN) * numN;
+  const int n0 = nt * BN;
+  const int tf = mt / tpf;
+  const int rem = mt - tf * tpf;
+  const int rt = rem / numC;
+  const int h0 = rt * TR, w0 = (rem - rt * numC) * 32;
+  const int dt0 = -2 * (p.kt >> 1);
+
+  int ph[MB], pw[MB];
+  bool pv[MB];
+  // Byte offset of this lane's operand for tap (0, 0) in a patch buffer: patch position
+  // (r + 1 + dh0, l32 + 1 + dw0) with the first tap's offset (dh0, dw0) = (-1, -1), or for phase
+  // (a, b) of the x2 upsampling (a - 1, b - 1).
+  uint32_t boff[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const bool valid = pv[mb];
-    const int orow = p.hmul * ph[mb] + pa;
-    const int ocol = p.wmul * pw[mb] + pb;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + nb * 32 + g * 8 + half * 4;
-        if (!valid || n >= p.N) continue;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][g * 4 + e] + ((p.bias && n + e < p.N) ? p.bias[n + e] : 0.0f);
-        // the 4 channels share a frame and are contiguous (nsplit is a multiple of 4)
-        const int f = p.fbase + p.fmul * tf + p.fstride * (n / p.nsplit);
-        const int nc = n % p.nsplit;
-        const int64_t idx = (((int64_t)f * p.Ho + orow) * p.Wo + ocol) * p.nsplit + nc;
-        if (p.y_f32) {
-          float4 o;
-          o.x = n + 0 < p.N ? v[0] : 0.0f;
-          o.y = n + 1 < p.N ? v[1] : 0.0f;
-          o.z = n + 2 < p.N ? v[2] : 0.0f;
-          o.w = n + 3 < p.N ? v[3] : 0.0f;
-          *(float4*)((float*)p.y + idx) = o;
-        } else {
-          if (p.res) {
-            const uint2 r = *(const uint2*)(p.res + idx);
-            v[0] += bf16_lo(r.x);
-            v[1] += bf16_hi(r.x);
-            v[2] += bf16_lo(r.y);
-            v[3] += bf16_hi(r.y);
-          }
-          uint2 o;
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          *(uint2*)((bf16_t*)p.y + idx) = o;
-        }
-      }
-    }
+    const int r = wave * MB + mb;
+    ph[mb] = h0 + r;
+    pw[mb] = w0 + l32;
+    pv[mb] = (ph[mb] < p.H) & (pw[mb] < p.W);
+    boff[mb] = (uint32_t)((((r + pa) * PC + l32 + pb) * PROW + half * 16) * 2);
   }
+
+  // This thread's patch pieces: position (pr, pc) of the patch, channel group tid & 3.
+  const int ch8 = (tid & 3) * 8;
+  int goff[PLOADS];       // byte offset in a frame (chunk 0), or -1 outside the frame
+  uint32_t poff[PLOADS];  // byte offset in a patch buffer
+#pragma unroll
+  for (int i = 0; i < PLOADS; ++i) {
+    const int piece = tid + i * NT;
+    const int pos = piece >> 2;
+    const int pr = pos / PC, pc = pos - (pos / PC) * PC;
+    const int hh = h0 - 1 + pr, ww = w0 - 1 + pc;
+    const bool inb = (piece < PPIECES) & (hh >= 0) & (hh < p.H) & (ww >= 0) & (ww < p.W);
+    goff[i] = inb ? ((hh * p.W + ww) * p.Ci + ch8) * 2 : -1;
+    poff[i] = piece < PPIECES ? (uint32_t)((pos * PROW + ch8) * 2) : (uint32_t)((PATCH - 8) * 2);
+  }
+
+  const int nchunks = p.Cip >> 5;
+  const int ng = nchunks * p.kt;
+  const int64_t frame_elems = (int64_t)p.H * p.W * p.Ci;
+  const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
+  const int64_t wrow = (int64_t)p.ntaps * p.Cip;
+  const bf16_t* wbase = p.wpk + ((int64_t)phase * p.Npad + n0) * wrow;
+
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+  u32x4 wreg[2][WLOADS];  // weights of steps k + 2 and k + 3 on their way to LDS
+  u32x4 preg[PLOADS];     // the next stage's patch on its way to LDS
+  u32x4 wf[2][NB];        // weight fragments of the current and the next half step
+  u32x4 bf[2][MB];        // activation fragments of the current and the next half step
+
+  // Stage cursor: (chunk, temporal tap) of a stage and its weight column base.
+  struct Stage {
+    int chunk, i, col;
+  };
+  auto stage_at = [&](int chunk, int i) -> Stage { return {chunk, i, i * SPS * p.Cip + chunk * 32}; };
+  auto next_stage = [&](const Stage& c) -> Stage {
+    // past the last stage the cursor stays put (its loads are never used)
+    if (c.chunk * p.kt + c.i + 1 >= ng) return c;
+    return (c.i + 1 == p.kt) ? stage_at(c.chunk + 1, 0) : stage_at(c.chunk, c.i + 1);
+  };
+
+  auto load_patch = [&](u32x4 (&dst)[PLOADS], const Stage& c, bool live) {
+    const int sf = tf + dt0 + c.i;  // source frame (negative: history)
+    const bool fok = live & (sf >= -p.Th) & (c.chunk * 32 + ch8 < p.Ci);
+    const bf16_t* fbase = (sf >= 0) ? p.x + (int64_t)sf * frame_elems
+                                    : ((sf >= -p.Th) ? p.hist + (int64_t)(sf + p.Th) * frame_elems : p.x);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)fbase, (short)0, (int)frame_bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < PLOADS; ++i) {
+      const int vo = (fok & (goff[i] >= 0)) ? goff[i] + c.chunk * 64 : (int)frame_bytes;
+      dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0);
+    }
+  };
+  auto store_patch = [&](const u32x4 (&src)[PLOADS], int buf) {
+#pragma unroll
+    for (int i = 0; i < PLOADS; ++i) *(u32x4*)((char*)lds_p[buf] + poff[i]) = src[i];
+  };
+  auto load_w = [&](u32x4 (&dst)[WLOADS], int col) {
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i) {
+      const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
+      const int row = min(q >> 2, p.Npad - 1 - n0), piece = q & 3;
+      dst[i] = *(const u32x4*)(wbase + row * wrow + col + piece * 8);
+    }
+  };
+  auto store_w = [&](const u32x4 (&src)[WLOADS], int buf) {
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i) {
+      const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
+      const int row = q >> 2, piece = q & 3;
+      *(u32x4*)(&lds_w[buf][row * LDS_ROW + piece * 8]) = src[i];
+    }
+  };
+  // fragments of K half q (channels half*16 + q*8 .. + 7 of the chunk) of spatial tap `tap`
+  auto read_a = [&](u32x4 (&dst)[NB], int buf, int q) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) dst[nb] = *(const u32x4*)(&lds_w[buf][(nb * 32 + l32) * LDS_ROW + half * 16 + q * 8]);
+  };
+  auto read_b = [&](u32x4 (&dst)[MB], int buf, int tap, int q) {
+    const int j = tap / KS, k = tap - (tap / KS) * KS;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      dst[mb] = *(const u32x4*)((const char*)lds_p[buf] + boff[mb] + ((j * PC + k) * PROW + q * 8) * 2);
+  };
+
+  floatx16 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
+
+  auto compute = [&](const u32x4 (&w)[NB], const u32x4 (&a)[MB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[nb]),
+                                                              __builtin_bit_cast(bf16x8, a[mb]), acc[nb][mb], 0, 0, 0);
+  };
+
+  // Pipeline. Weights: step j's slice sits in LDS stage j % 4; during step k the weights of step
+  // k + 3 are loaded into registers and those of step k + 2 (loaded during step k - 1) are
+  // stored at the step's end. Patches: stage g's patch sits in buffer g % 2; the next stage's
+  // patch is loaded at step 0 of a stage and stored at step 4 (its buffer was last read in
+  // step 7 of the previous stage). Fragments are read one half step (K = 16) ahead; one barrier
+  // per step. (With KS = 2 the patch is stored at step 2 and first read in step 3.)
+  Stage cur = stage_at(0, 0);
+  Stage nxt = next_stage(cur);
+  load_w(wreg[0], cur.col);
+  store_w(wreg[0], 0);
+  load_w(wreg[0], cur.col + p.Cip);
+  store_w(wreg[0], 1);
+  load_w(wreg[0], cur.col + 2 * p.Cip);  // step 2, stored at the end of step 0
+  load_patch(preg, cur, true);
+  store_patch(preg, 0);
+  __syncthreads();
+  read_a(wf[0], 0, 0);
+  read_b(bf[0], 0, 0, 0);
+
+  constexpr int NM = MB * NB;  // matrix ops per half step
+  auto step = [&](auto PP, auto SS, int k, int g) {
+    constexpr int P = decltype(PP)::value;  // stage parity: patch buffer
+    constexpr int S = decltype(SS)::value;  // spatial tap
+    constexpr int KP = (P * SPS + S) & 1;   // parity of k
+    // half step 0 (step k + 3 lies in this stage or the next: SPS >= 4)
+    load_w(wreg[KP ^ 1], S + 3 < SPS ? cur.col + (S + 3) * p.Cip : nxt.col + (S + 3 - SPS) * p.Cip);
+    if constexpr (S == 0) load_patch(preg, nxt, g + 1 < ng);
+    read_a(wf[1], k & 3, 1);
+    read_b(bf[1], P, S, 1);
+    compute(wf[0], bf[0]);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // half step 1
+    read_a(wf[0], (k + 1) & 3, 0);
+    if constexpr (S < SPS - 1) read_b(bf[0], P, S + 1, 0);
+    else read_b(bf[0], P ^ 1, 0, 0);
+    compute(wf[1], bf[1]);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    store_w(wreg[KP], (k + 2) & 3);
+    if constexpr (S == STORE_S) store_patch(preg, P ^ 1);
+    __syncthreads();
+  };
+  auto stage = [&](auto PP, int g) {
+    const int k = g * SPS;
+    step(PP, std::integral_constant<int, 0>{}, k + 0, g);
+    step(PP, std::integral_constant<int, 1>{}, k + 1, g);
+    step(PP, std::integral_constant<int, 2>{}, k + 2, g);
+    step(PP, std::integral_constant<int, 3>{}, k + 3, g);
+    if constexpr (SPS == 9) {
+      step(PP, std::integral_constant<int, 4>{}, k + 4, g);
+      step(PP, std::integral_constant<int, 5>{}, k + 5, g);
+      step(PP, std::integral_constant<int, 6>{}, k + 6, g);
+      step(PP, std::integral_constant<int, 7>{}, k + 7, g);
+      step(PP, std::integral_constant<int, 8>{}, k + 8, g);
+    }
+    cur = nxt;
+    nxt = next_stage(nxt);
+  };
+  int g = 0;
+  for (; g + 1 < ng; g += 2) {
+    stage(std::integral_constant<int, 0>{}, g);
+    stage(std::integral_constant<int, 1>{}, g + 1);
+  }
+  if (g < ng) stage(std::integral_constant<int, 0>{}, g);
+
+  conv_epilogue<NB, MB>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
 }
 
 struct ConfigEntry {
   const char* name;
   int nb, mb, waves;
+  int halo;  // conv_halo_kernel's KS (WAVES*MB rows x 32 columns per tile), or 0
   void (*kernel)(const ConvProblem);
 };
 
 #define WVD_CONV_CONFIG(NB, MB, W) \
-  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, conv_mfma_kernel<NB, MB, W> }
+  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, conv_mfma_kernel<NB, MB, W> }
+#define WVD_HALO_CONFIG(NB, MB, W) \
+  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, conv_halo_kernel<NB, MB, W, 3> }
+#define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
+  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, conv_halo_kernel<NB, MB, W, 2> }
 
 // Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
 // bigger per-wave tiles at one wave per SIMD: the second wave issues matrix work while the first
@@ -382,33 +546,54 @@ const ConfigEntry kConfigs[] = {
     WVD_CONV_CONFIG(3, 1, 4),  // 96 x 128: small grids
     WVD_CONV_CONFIG(1, 4, 4),  // 32 x 512: a few output channels
     WVD_CONV_CONFIG(3, 2, 8),  // 96 x 512, 2 waves/SIMD: long reductions (3x3x3 taps)
+    WVD_HALO_CONFIG(6, 1, 8),  // 192 x (8 rows x 32 columns)
+    WVD_HALO_CONFIG(3, 2, 8),  // 96 x (16 rows x 32 columns)
+    WVD_PHASE_HALO_CONFIG(6, 1, 8),  // x2 upsampling phases: 192 x (8 rows x 32 columns)
+    WVD_PHASE_HALO_CONFIG(3, 2, 8),  // x2 upsampling phases: 96 x (16 rows x 32 columns)
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kMaxFusedNormN = 192;  // the widest channel tile
 
-// Workgroups of a problem: per frame ceil(H*W / BM) position tiles, times the channel tiles.
-int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t HW, int Npad) {
-  const int64_t bm = (int64_t)c.waves * c.mb * 32, bn = (int64_t)c.nb * 32;
-  return T * ((HW + bm - 1) / bm) * ((Npad + bn - 1) / bn);
+// Workgroups of a problem: per frame ceil(H*W / BM) position tiles (halo kernels: ceil(H / rows)
+// x ceil(W / 32)), times the channel tiles.
+int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t H, int64_t W, int Npad) {
+  const int64_t bn = (int64_t)c.nb * 32;
+  const int64_t nt = (Npad + bn - 1) / bn;
+  if (c.halo) {
+    const int64_t tr = (int64_t)c.waves * c.mb;
+    return T * ((H + tr - 1) / tr) * ((W + 31) / 32) * nt;
+  }
+  const int64_t bm = (int64_t)c.waves * c.mb * 32;
+  return T * ((H * W + bm - 1) / bm) * nt;
 }
 
-// The largest tile whose grid still gives every CU a workgroup per phase.
-// A 96-wide channel tile takes two position blocks per wave on 3x3x3 convs (half the weight
-// fragment reads per matrix op; measured faster there), one on short reductions.
-int choose_config(int64_t T, int64_t HW, int Npad, int phases, int ntaps, bool one_n_tile) {
+// Convolutions with 3x3 spatial taps take the halo kernel with 96 x (16 x 32) tiles (measured the
+// fastest on every 3x3x3 layer of the decoder, 384-channel ones included: two position blocks per
+// wave halve the weight fragment reads per matrix op), or its 192-wide variant when a fused norm
+// needs more channels in one tile. Otherwise: the largest linear tile whose grid still gives every
+// CU a workgroup per phase; a 96-wide channel tile takes two position blocks per wave on long
+// reductions, one on short ones.
+int choose_config(const ConvProblem& p, bool one_n_tile) {
   const int64_t cus = 256;
+  const int64_t T = p.T, H = p.H, W = p.W;
+  const int Npad = p.Npad, phases = p.phases;
   if (Npad <= 32) return 4;
-  const int n96 = (ntaps >= 9 && blocks_for(kConfigs[5], T, HW, Npad) * phases >= cus) ? 5 : 2;
+  if (phases == 1 && p.kh == 3 && p.kw == 3) return (one_n_tile && Npad > 96) ? 6 : 7;
+  // The phase convs (K = 4 taps x C) have short reductions: the halo kernel wins from 192
+  // channels up; at 96 (with the fused norm) the linear kernel's smaller LDS footprint and
+  // overlapping workgroups do better.
+  if (phases == 4 && p.kh == 2 && p.kw == 2 && Npad >= 192 && !one_n_tile) return 9;
+  const int n96 = (p.ntaps >= 9 && blocks_for(kConfigs[5], T, H, W, Npad) * phases >= cus) ? 5 : 2;
   if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup
-    if (Npad <= 96) return blocks_for(kConfigs[2], T, HW, Npad) * phases >= cus ? n96 : 3;
-    return blocks_for(kConfigs[0], T, HW, Npad) * phases >= cus ? 0 : 1;
+    if (Npad <= 96) return blocks_for(kConfigs[2], T, H, W, Npad) * phases >= cus ? n96 : 3;
+    return blocks_for(kConfigs[0], T, H, W, Npad) * phases >= cus ? 0 : 1;
   }
   if (Npad % 192 == 0) {
-    if (blocks_for(kConfigs[0], T, HW, Npad) * phases >= cus) return 0;
-    if (blocks_for(kConfigs[1], T, HW, Npad) * phases >= cus) return 1;
+    if (blocks_for(kConfigs[0], T, H, W, Npad) * phases >= cus) return 0;
+    if (blocks_for(kConfigs[1], T, H, W, Npad) * phases >= cus) return 1;
     return 3;
   }
-  if (Npad % 96 == 0 && blocks_for(kConfigs[2], T, HW, Npad) * phases >= cus) return n96;
+  if (Npad % 96 == 0 && blocks_for(kConfigs[2], T, H, W, Npad) * phases >= cus) return n96;
   return 3;
 }
 
@@ -419,15 +604,30 @@ bool conv_can_fuse_norm(int Npad) { return Npad <= kMaxFusedNormN; }
 const char* conv_config_name(int id) { return (id >= 0 && id < kNumConfigs) ? kConfigs[id].name : "?"; }
 int conv_config_count() { return kNumConfigs; }
 
-hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id) {
+// Whether configuration id can run p: halo tiles need 3x3 spatial taps without phases, a fused
+// norm needs one channel tile.
+bool conv_config_fits(const ConvProblem& p, int id) {
+  if (id < 0 || id >= kNumConfigs) return false;
+  const ConfigEntry& c = kConfigs[id];
+  if (c.halo == 3 && !(p.phases == 1 && p.kh == 3 && p.kw == 3)) return false;
+  if (c.halo == 2 && !(p.phases == 4 && p.kh == 2 && p.kw == 2)) return false;
+  if (p.norm_gamma && c.nb * 32 < p.Npad) return false;
+  return true;
+}
+
+hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id, int force_config) {
   const int64_t HW = (int64_t)p.H * p.W;
   if (p.T == 0 || HW == 0) return hipSuccess;
   // one frame is addressed with 32-bit byte offsets
   if (HW * p.Ci * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if (p.norm_gamma && (p.Npad > kMaxFusedNormN || p.res || p.y_f32 || p.nsplit != p.N)) return hipErrorInvalidValue;
-  const int id = choose_config(p.T, HW, p.Npad, p.phases, p.ntaps, p.norm_gamma != nullptr);
+  int id = choose_config(p, p.norm_gamma != nullptr);
+  if (force_config >= 0) {
+    if (!conv_config_fits(p, force_config)) return hipErrorNotSupported;
+    id = force_config;
+  }
   const ConfigEntry& c = kConfigs[id];
-  const int64_t blocks = blocks_for(c, p.T, HW, p.Npad);
+  const int64_t blocks = blocks_for(c, p.T, p.H, p.W, p.Npad);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (config_id) *config_id = id;
   hipLaunchKernelGGL(c.kernel, dim3((unsigned)blocks, 1, p.phases), dim3(c.waves * 64), 0, s, p);

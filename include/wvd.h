@@ -235,6 +235,13 @@ int wvd_timing_read(int i, const char** name, int64_t* launches, double* ms, dou
  * algorithmic FLOPs and problem shape {T, H, W, Ci, N, taps, phases, history frames}. Returns the
  * number of recorded launches (call with i = -1 to count). */
 int wvd_timing_launch(int i, int* config, double* ms, double* flops, int shape[8]);
+/* Testing and tuning support: run every following matrix-core convolution launch with
+ * configuration `config` (an index of wvd_timing_read), or with the automatic choice again
+ * when config is -1. A launch the forced configuration cannot run (a halo-tile configuration on
+ * a convolution without 3x3 spatial taps, or a channel tile narrower than a fused norm needs)
+ * fails with WVD_ERR_UNSUPPORTED. WVD_ERR_ARG for an index out of range. Process-wide; not for
+ * use while another thread launches. */
+wvd_status wvd_conv_force_config(int config);
 
 #ifdef __cplusplus
 }

@@ -91,6 +91,86 @@ def test_bf16_conv_matches_oracle(case):
     assert ok, worst
 
 
+SPATIAL3_CASES = [c for c in CONV_CASES if c[5][1:] == (3, 3)]
+
+
+@pytest.mark.parametrize("case", SPATIAL3_CASES, ids=lambda c: "x".join(map(str, c[:5])) + f"_k{''.join(map(str, c[5]))}_h{c[6]}")
+def test_bf16_conv_every_config_matches_oracle(case):
+    """Every kernel configuration (linear tiles and halo tiles), forced, on ragged 3x3-tap convs."""
+    Ci, Co, T, H, W, k, Th = case
+    seed = Ci * 5 + Co * 7 + T * 3 + H * 19 + W * 23 + Th
+    x = wl.bf16_values(_rand((1, Ci, T, H, W), seed))
+    w = wl.bf16_values(wl.kaiming(torch.Generator().manual_seed(seed + 1), (Co, Ci) + k))
+    b = 0.1 * _rand((Co,), seed + 2)
+    hist = wl.bf16_values(_rand((1, Ci, Th, H, W), seed + 3)) if Th else None
+    ref = oracle.causal_conv3d(x[0], w, b, None if hist is None else hist[0])
+    xd, wp, bd = to_dev_nthwc(x), wvd.conv_pack(w.cuda()), b.cuda()
+    hd = None if hist is None else to_dev_nthwc(hist)
+    names = wvd.conv_config_names()
+    assert any(n.startswith("conv_halo") for n in names)
+    ran = 0
+    try:
+        for i, name in enumerate(names):
+            log(f"bf16 conv {case} forced {name}")
+            wvd.conv_force_config(i)
+            try:
+                y = wvd.causal_conv3d(xd, wp, Co, kernel=k, bias=bd, hist=hd)
+            except wvd.WvdError as e:
+                assert e.status == 8 and name.startswith("conv_phase_halo"), (name, str(e))
+                continue
+            torch.cuda.synchronize()
+            ok, worst = bf16_elementwise_ok(from_dev_nthwc(y), ref)
+            assert ok, (name, worst)
+            ran += 1
+    finally:
+        wvd.conv_force_config(None)
+    assert ran >= len(names) - 2
+
+
+@pytest.mark.parametrize("C,T,H,W", [(96, 2, 19, 37), (192, 1, 9, 40), (384, 2, 5, 7)])
+def test_spatial_upsample_every_config_matches_oracle(C, T, H, W):
+    """Nearest x2 + 3x3 conv as four phase convs, under every configuration that runs them.
+    The phase weights are bf16 sums of up to four bf16 taps (a second rounding), so the bar is
+    the per-layer normwise one; all configurations share the K order and agree bit for bit."""
+    g = torch.Generator().manual_seed(C + 7 * H + W)
+    x = wl.bf16_values(torch.randn((1, C, T, H, W), generator=g))
+    w = wl.bf16_values(wl.kaiming(g, (C, C, 3, 3)))
+    b = 0.1 * torch.randn((C,), generator=g)
+    ref = oracle.spatial_upsample(x[0], w, b)
+    xd, wp, bd = to_dev_nthwc(x), wvd.conv_pack(w.cuda(), wvd.WVD_PACK_PHASE2X), b.cuda()
+    auto = wvd.upsample(xd, spatial=wp, spatial_bias=bd)
+    torch.cuda.synchronize()
+    r = rel_max(from_dev_nthwc(auto), ref)
+    log(f"spatial upsample C={C} rel {r:.3e}")
+    assert r <= 2e-2
+    ran = []
+    try:
+        for i, name in enumerate(wvd.conv_config_names()):
+            wvd.conv_force_config(i)
+            try:
+                y = wvd.upsample(xd, spatial=wp, spatial_bias=bd)
+            except wvd.WvdError as e:
+                assert e.status == 8 and name.startswith("conv_halo"), (name, str(e))
+                continue
+            torch.cuda.synchronize()
+            assert torch.equal(y, auto), name
+            ran.append(name)
+    finally:
+        wvd.conv_force_config(None)
+    assert any(n.startswith("conv_phase_halo") for n in ran)
+
+
+def test_forced_halo_config_rejects_other_taps():
+    x = to_dev_nthwc(wl.bf16_values(_rand((1, 96, 2, 5, 6), 41)))
+    wp = wvd.conv_pack(wl.kaiming(torch.Generator().manual_seed(42), (96, 96, 3, 1, 1)).cuda())
+    try:
+        wvd.conv_force_config("conv_halo_n3_m2_w8")
+        with pytest.raises(wvd.WvdError):
+            wvd.causal_conv3d(x, wp, 96, kernel=(3, 1, 1))
+    finally:
+        wvd.conv_force_config(None)
+
+
 def test_bf16_conv_residual_and_hist_out():
     Ci, Co, T, H, W = 96, 96, 3, 10, 12
     x = wl.bf16_values(_rand((1, Ci, T, H, W), 21))
@@ -180,6 +260,29 @@ def test_resblock_widths_match_oracle(C):
     r = rel_max(from_dev_nthwc(y), ref)
     log(f"resblock C={C} rel {r:.3e}")
     assert r <= 2e-2
+
+
+@pytest.mark.parametrize("C", [96, 192])
+def test_resblock_halo_configs_match_oracle(C):
+    """The halo-tile kernels with the fused norm (conv1) and the residual add (conv2)."""
+    cfg = wl.resblock_bf16(seed=30 + C, C=C, T=3, H=19, W=45)
+    p = oracle.as_numpy_params(cfg["params"])
+    ref = oracle.resblock(cfg["x"][0], p, "res", {}, 1e-6, given_hist=oracle._f32(cfg["hist"][0]))
+    wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+    hd = to_dev_nthwc(cfg["hist"])
+    xd = to_dev_nthwc(cfg["x"])
+    try:
+        for name in ("conv_halo_n6_m1_w8", "conv_halo_n3_m2_w8"):
+            if C > 96 and name == "conv_halo_n3_m2_w8":
+                continue  # a 96-wide tile cannot hold a 192-channel norm
+            wvd.conv_force_config(name)
+            y = wvd.resblock(xd, wts, 1e-6, hist1=hd, hist2=hd)
+            torch.cuda.synchronize()
+            r = rel_max(from_dev_nthwc(y), ref)
+            log(f"resblock C={C} {name} rel {r:.3e}")
+            assert r <= 2e-2
+    finally:
+        wvd.conv_force_config(None)
 
 
 def test_resblock_shortcut_and_histories_match_oracle():
