@@ -27,6 +27,8 @@ import workloads as wl  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 
+from causal_convolution_causalconv3d_amd import profiling  # noqa: E402
+
 
 def algorithmic_conv_flops(spec: wl.DecoderSpec, latent_frames: int, fpp: int, hw=(wl.LATENT_H, wl.LATENT_W)) -> float:
     """2*M*N*K of every conv of the decode, with the spatial x2 conv in its four-phase form
@@ -83,6 +85,16 @@ def cpu_baseline(seconds_hint: float = 15.0):
                       f"{share:.4f} of the 44x78 latent frame"}
 
 
+def conv_launch_bytes(sh) -> float:
+    """Algorithmic HBM bytes of one conv launch: the input frames it reads (with up to kt - 1 history
+    frames) once, the packed weights once, the bf16 output once (a residual read is not counted)."""
+    kt = 3 if sh["taps"] in (27, 3) else 1
+    frames_in = sh["T"] + min(sh["Th"], kt - 1)
+    hw = sh["H"] * sh["W"]
+    return 2.0 * (frames_in * hw * sh["Ci"] + sh["phases"] * sh["N"] * sh["taps"] * sh["Ci"]
+                  + sh["T"] * hw * sh["phases"] * sh["N"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +103,8 @@ def main():
     ap.add_argument("--frames-per-pass", type=int, default=4)
     ap.add_argument("--latent-frames", type=int, default=31)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy kernel over MIB MiB (calibrates the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode is not sharded here.",
@@ -99,6 +113,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        profiling.copy_calibration_run(args.copy_calibration)
+        return
 
     spec = wl.FULL_DECODER
     _, params = wl.decoder_weights(spec, seed=4, latent_frames=4)
@@ -126,6 +144,8 @@ def main():
     t1 = time.perf_counter()
     wvd.timing_enable(False)
     per_cfg = wvd.timing_read()
+    per_mem = wvd.timing_read_mem()
+    launches = wvd.timing_launches()
     peak_alloc = torch.cuda.max_memory_allocated() / 2 ** 30
     peak_reserved = torch.cuda.max_memory_reserved() / 2 ** 30
 
@@ -138,6 +158,7 @@ def main():
     dom_name, (dom_n, dom_ms, dom_flops) = max(per_cfg.items(), key=lambda kv: kv[1][1])
     dom_tflops = (dom_flops / dom_n) / (dom_ms / dom_n * 1e-3) / 1e12
     algo = algorithmic_conv_flops(spec, args.latent_frames, fpp)
+    dom_bytes = [conv_launch_bytes(sh) for (nm, _, _, sh) in launches if nm == dom_name]
 
     line = {
         "metric": "decoded frames/s at 704x1248 + conv TFLOP/s vs bf16 MFMA peak; peak HBM GiB",
@@ -158,10 +179,12 @@ def main():
                    "latent_frames": args.latent_frames, "video_frames": F, "frames_per_pass": fpp,
                    "global_batch": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": profiling.committed_traffic(dom_name), "traffic_unit": "HBM bytes per launch",
                      "launches_per_step": dom_n // args.steps,
                      "avg_launch_us": round(1000.0 * dom_ms / dom_n, 2),
-                     "flops_per_launch": dom_flops / dom_n},
+                     "flops_per_launch": dom_flops / dom_n,
+                     "algorithmic_bytes_per_launch": round(sum(dom_bytes) / max(len(dom_bytes), 1))},
         "conv": {"tflops": round(conv_flops / (conv_ms * 1e-3) / 1e12, 2),
                  "frac_of_peak": round(conv_flops / (conv_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "conv_ms_per_step": round(conv_ms / args.steps, 3),
@@ -169,6 +192,11 @@ def main():
                  "timed_tflop_per_step": round(conv_flops / args.steps / 1e12, 3),
                  "per_config": {k: {"launches": v[0], "ms": round(v[1], 3), "tflops": round(v[2] / (v[1] * 1e-3) / 1e12, 2)}
                                 for k, v in per_cfg.items()}},
+        "epilogues": {k: {"launches_per_step": v[0] // args.steps, "avg_launch_us": round(1000.0 * v[1] / v[0], 2),
+                          "gbs": round(v[2] / (v[1] * 1e-3) / 1e9, 1),
+                          "frac_of_hbm": round(v[2] / (v[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "ms_per_step": round(v[1] / args.steps, 3)}
+                      for k, v in per_mem.items()},
         "peak_hbm_gib": round(peak_alloc, 3),
         "peak_hbm_reserved_gib": round(peak_reserved, 3),
     }

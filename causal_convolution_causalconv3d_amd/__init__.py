@@ -106,6 +106,8 @@ def lib():
             "wvd_timing_launch": ([ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
             "wvd_conv_force_config": ([ctypes.c_int], ctypes.c_int),
+            "wvd_timing_read_mem": ([ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -124,7 +126,7 @@ def exported_symbols() -> Sequence[str]:
             "wvd_decoder_packed_bytes", "wvd_decoder_pack", "wvd_cache_bytes", "wvd_cache_init", "wvd_cache_reset",
             "wvd_cache_destroy", "wvd_cache_next_latent", "wvd_decode_workspace_bytes", "wvd_decode_chunk",
             "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read",
-            "wvd_timing_launch", "wvd_conv_force_config"]
+            "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem"]
 
 
 def _check(status: int):
@@ -392,6 +394,22 @@ def timing_read():
         L.wvd_timing_read(i, ctypes.byref(name), ctypes.byref(launches), ctypes.byref(ms), ctypes.byref(flops))
         if launches.value:
             out[name.value.decode()] = (launches.value, ms.value, flops.value)
+    return out
+
+
+def timing_read_mem():
+    """{kernel kind: (launches, total ms, total algorithmic bytes)} of the memory-bound kernels."""
+    L = lib()
+    n = L.wvd_timing_read_mem(-1, None, None, None, None)
+    out = {}
+    for i in range(n):
+        name = ctypes.c_char_p()
+        launches = ctypes.c_int64()
+        ms = ctypes.c_double()
+        nbytes = ctypes.c_double()
+        L.wvd_timing_read_mem(i, ctypes.byref(name), ctypes.byref(launches), ctypes.byref(ms), ctypes.byref(nbytes))
+        if launches.value:
+            out[name.value.decode()] = (launches.value, ms.value, nbytes.value)
     return out
 
 

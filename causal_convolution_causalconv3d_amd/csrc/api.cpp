@@ -86,11 +86,16 @@ bool same_grid(const wvd_tensor* a, const wvd_tensor* b) { return a->h == b->h &
 // Timing of the matrix-core conv launches.
 // ------------------------------------------------------------------------------------------
 struct TimingRecord {
-  int config;
+  int config;  // conv configuration, or -1 for a memory-bound kernel
+  int mem;     // MemKind of a memory-bound kernel, or -1
   hipEvent_t start, stop;
-  double flops;
+  double flops;  // conv: algorithmic FLOPs; memory-bound kernel: algorithmic bytes
   int shape[8];  // T, H, W, Ci, N, taps, phases, Th
 };
+// The memory-bound kernels of the path, timed like the convs (algorithmic bytes: every input
+// element read once, every output element written once).
+enum MemKind { MEM_NORM_SILU = 0, MEM_HEAD_STENCIL = 1, MEM_CONVERT = 2, MEM_KINDS = 3 };
+const char* const kMemKindNames[MEM_KINDS] = {"norm_silu", "head_stencil", "convert"};
 struct LaunchRecord {
   int config;
   float ms;
@@ -104,7 +109,9 @@ struct TimingState {
   std::vector<hipEvent_t> pool;
   std::vector<int64_t> launches;
   std::vector<double> ms, flops;
-  std::vector<LaunchRecord> log;  // every timed launch since the last reset
+  int64_t mem_launches[MEM_KINDS] = {};
+  double mem_ms[MEM_KINDS] = {}, mem_bytes[MEM_KINDS] = {};
+  std::vector<LaunchRecord> log;  // every timed conv launch since the last reset
 } g_timing;
 
 hipEvent_t pooled_event() {
@@ -138,10 +145,39 @@ wvd_status run_conv(const ConvProblem& p, hipStream_t s, double flops) {
   if (timed) {
     WVD_HIP(hipEventRecord(e1, s), "hipEventRecord");
     std::lock_guard<std::mutex> lk(g_timing.mu);
-    TimingRecord r{cfg, e0, e1, flops, {p.T, p.H, p.W, p.Ci, p.N, p.ntaps, p.phases, p.Th}};
+    TimingRecord r{cfg, -1, e0, e1, flops, {p.T, p.H, p.W, p.Ci, p.N, p.ntaps, p.phases, p.Th}};
     g_timing.pending.push_back(r);
   }
   return WVD_OK;
+}
+
+// A memory-bound launch (`launch` returns a hipError_t), timed when timing is on.
+template <class F>
+wvd_status run_mem(int kind, double bytes, hipStream_t s, const char* what, F&& launch) {
+  const bool timed = g_timing.on;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (timed) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    e0 = pooled_event();
+    e1 = pooled_event();
+    if (!e0 || !e1) return fail(WVD_ERR_HIP, "hipEventCreate failed");
+    WVD_HIP(hipEventRecord(e0, s), "hipEventRecord");
+  }
+  WVD_HIP(launch(), what);
+  if (timed) {
+    WVD_HIP(hipEventRecord(e1, s), "hipEventRecord");
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.pending.push_back(TimingRecord{-1, kind, e0, e1, bytes, {}});
+  }
+  return WVD_OK;
+}
+
+// Channel RMS norm (+ SiLU) over P positions of C channels (NTHWC bf16): reads x and gamma,
+// writes y.
+wvd_status run_norm(const bf16_t* x, const float* gamma, float eps, int silu, bf16_t* y, int64_t P, int C,
+                    hipStream_t s) {
+  return run_mem(MEM_NORM_SILU, 4.0 * (double)P * C + 4.0 * C, s, "norm launch",
+                 [&] { return launch_norm_silu(x, gamma, eps, silu, y, P, C, s); });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -380,9 +416,8 @@ extern "C" wvd_status wvd_rmsnorm_silu(const wvd_tensor* x, const float* gamma, 
   if (x->c != y->c || x->t != y->t || !same_grid(x, y)) return fail(WVD_ERR_SHAPE, "y must have x's shape");
   if (x->c % 8 != 0 || x->c > 512) return fail(WVD_ERR_UNSUPPORTED, "channels must be a multiple of 8, at most 512");
   if (!(eps >= 0.0f)) return fail(WVD_ERR_ARG, "eps must be >= 0");
-  return hip_status(launch_norm_silu((const bf16_t*)x->data, gamma, eps, apply_silu, (bf16_t*)y->data,
-                                     x->t * x->h * x->w, (int)x->c, (hipStream_t)stream),
-                    "norm launch");
+  return run_norm((const bf16_t*)x->data, gamma, eps, apply_silu, (bf16_t*)y->data, x->t * x->h * x->w, (int)x->c,
+                  (hipStream_t)stream);
 }
 
 // ==============================================================================================
@@ -419,7 +454,7 @@ wvd_status resblock_core(const ResblockArgs& r, hipStream_t s, F1 after_conv1, F
     WVD_TRY(run_conv(sc, s, conv_flops(P, w->cout, w->cin)));
     residual = r.sc;
   }
-  WVD_HIP(launch_norm_silu(r.x, w->gamma1, r.eps, 1, r.a, P, w->cin, s), "norm launch");
+  WVD_TRY(run_norm(r.x, w->gamma1, r.eps, 1, r.a, P, w->cin, s));
   ConvProblem c1 = plain_problem(r.a, r.hist1, r.T, r.H, r.W, w->cin, r.th1, w->conv1, w->cout, 3, 3, 3, w->bias1, r.h,
                                  nullptr);
   // conv2's input a2 = SiLU(norm2(h)): fused into conv1's epilogue when one workgroup holds every
@@ -434,7 +469,7 @@ wvd_status resblock_core(const ResblockArgs& r, hipStream_t s, F1 after_conv1, F
   WVD_TRY(after_conv1(r.a));
   const bf16_t* a2 = r.h;
   if (!fuse) {
-    WVD_HIP(launch_norm_silu(r.h, w->gamma2, r.eps, 1, r.a, P, w->cout, s), "norm launch");
+    WVD_TRY(run_norm(r.h, w->gamma2, r.eps, 1, r.a, P, w->cout, s));
     a2 = r.a;
   }
   ConvProblem c2 = plain_problem(a2, r.hist2, r.T, r.H, r.W, w->cout, r.th2, w->conv2, w->cout, 3, 3, 3, w->bias2,
@@ -1078,7 +1113,10 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
   // latents in NTHWC
   const bf16_t* zin = (const bf16_t*)z->data;
   if (z->layout == WVD_NCTHW) {
-    WVD_HIP(launch_convert(z->data, 1, 1, zc, 1, 0, d->z_channels, (int)n, d->latent_h, d->latent_w, s), "convert launch");
+    const double zb = 4.0 * (double)d->z_channels * n * d->latent_h * d->latent_w;
+    WVD_TRY(run_mem(MEM_CONVERT, zb, s, "convert launch", [&] {
+      return launch_convert(z->data, 1, 1, zc, 1, 0, d->z_channels, (int)n, d->latent_h, d->latent_w, s);
+    }));
     zin = zc;
   }
   int cur = 0;  // index of the stream buffer holding the activation
@@ -1101,7 +1139,7 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
       WVD_TRY(run_conv(sc, s, conv_flops(P, r.cout, r.cin)));
       residual = bsc;
     }
-    WVD_HIP(launch_norm_silu(x, F_(r.gamma1), d->eps, 1, ba, P, r.cin, s), "norm launch");
+    WVD_TRY(run_norm(x, F_(r.gamma1), d->eps, 1, ba, P, r.cin, s));
     ConvProblem c1 = plain_problem(ba, nullptr, (int)T, H, Wd, r.cin, 0, W_(r.w1), r.cout, 3, 3, 3, F_(r.b1), bh, nullptr);
     // norm2 + SiLU fused into conv1's epilogue when one workgroup holds all output channels
     const bool fuse = conv_can_fuse_norm((int)round_up(r.cout, 32));
@@ -1113,7 +1151,7 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     WVD_TRY(cached_conv(c1, r.slot1, ba, (int)T, conv_flops(P, r.cout, 27LL * r.cin)));
     const bf16_t* a2 = bh;
     if (!fuse) {
-      WVD_HIP(launch_norm_silu(bh, F_(r.gamma2), d->eps, 1, ba, P, r.cout, s), "norm launch");
+      WVD_TRY(run_norm(bh, F_(r.gamma2), d->eps, 1, ba, P, r.cout, s));
       a2 = ba;
     }
     ConvProblem c2 = plain_problem(a2, nullptr, (int)T, H, Wd, r.cout, 0, W_(r.w2), r.cout, 3, 3, 3, F_(r.b2), y, residual);
@@ -1173,7 +1211,7 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
   {
     const int64_t P = T * H * Wd;
     if (!act) {
-      WVD_HIP(launch_norm_silu(bx[cur], F_(p.norm_out), d->eps, 1, ba, P, c, s), "norm launch");
+      WVD_TRY(run_norm(bx[cur], F_(p.norm_out), d->eps, 1, ba, P, c, s));
       act = ba;
       zbuf = bx[cur ^ 1];
     }
@@ -1189,8 +1227,12 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     cp.fstride = (int)T;
     cp.To = (int)T * kHeadPlanes;
     WVD_TRY(cached_conv(cp, p.out_slot, act, (int)T, conv_flops(P, co, 27LL * c)));
-    WVD_HIP(launch_head_stencil(Z, co, F_(p.out_b), (bf16_t*)video->data, video->t, (int)frame_offset, (int)T, H, Wd, s),
-            "head launch");
+    // reads the 9 tap planes (16 bytes per plane and position), writes co bf16 channels
+    const double hb = (double)P * (kHeadPlanes * 16.0 + 2.0 * co);
+    WVD_TRY(run_mem(MEM_HEAD_STENCIL, hb, s, "head launch", [&] {
+      return launch_head_stencil(Z, co, F_(p.out_b), (bf16_t*)video->data, video->t, (int)frame_offset, (int)T, H, Wd,
+                                 s);
+    }));
   }
   cache->next_latent += n;
   cache->next_frame += fr.video;
@@ -1224,8 +1266,26 @@ extern "C" wvd_status wvd_timing_reset(void) {
   g_timing.launches.assign(conv_config_count(), 0);
   g_timing.ms.assign(conv_config_count(), 0.0);
   g_timing.flops.assign(conv_config_count(), 0.0);
+  for (int k = 0; k < MEM_KINDS; ++k) {
+    g_timing.mem_launches[k] = 0;
+    g_timing.mem_ms[k] = 0.0;
+    g_timing.mem_bytes[k] = 0.0;
+  }
   g_timing.log.clear();
   return WVD_OK;
+}
+
+extern "C" int wvd_timing_read_mem(int i, const char** name, int64_t* launches, double* ms, double* bytes) {
+  const char* nm = nullptr;
+  wvd_timing_read(0, &nm, nullptr, nullptr, nullptr);  // drains the pending events
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (!name) return MEM_KINDS;
+  if (i < 0 || i >= MEM_KINDS) return -1;
+  *name = kMemKindNames[i];
+  if (launches) *launches = g_timing.mem_launches[i];
+  if (ms) *ms = g_timing.mem_ms[i];
+  if (bytes) *bytes = g_timing.mem_bytes[i];
+  return MEM_KINDS;
 }
 
 extern "C" int wvd_timing_launch(int i, int* config, double* ms, double* flops, int shape[8]) {
@@ -1253,8 +1313,12 @@ extern "C" int wvd_timing_read(int i, const char** name, int64_t* launches, doub
   }
   for (auto& r : g_timing.pending) {
     float t = 0.0f;
-    if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&t, r.start, r.stop) == hipSuccess &&
-        r.config >= 0 && r.config < n) {
+    const bool got = hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&t, r.start, r.stop) == hipSuccess;
+    if (got && r.mem >= 0 && r.mem < MEM_KINDS) {
+      g_timing.mem_launches[r.mem] += 1;
+      g_timing.mem_ms[r.mem] += t;
+      g_timing.mem_bytes[r.mem] += r.flops;
+    } else if (got && r.config >= 0 && r.config < n) {
       g_timing.launches[r.config] += 1;
       g_timing.ms[r.config] += t;
       g_timing.flops[r.config] += r.flops;

@@ -70,6 +70,7 @@ struct ConvProblem {
   const float* norm_gamma;  // [N] or null
   float norm_eps;
   int norm_silu;
+  int time_tiles;  // set by the launcher: the halo kernel's tile order
 };
 
 // force_config >= 0 runs that configuration (hipErrorNotSupported when it cannot run p).

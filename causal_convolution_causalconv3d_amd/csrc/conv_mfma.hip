@@ -320,8 +320,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProb
   const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
   const int mt = lin / numN, nt = lin - (lin / numN) * numN;
   const int n0 = nt * BN;
-  const int tf = mt / tpf;
-  const int rem = mt - tf * tpf;
+  // Tile order: frame-major (a frame's tiles next to each other), or with time_tiles the same
+  // tile of consecutive frames next to each other (an input patch then serves the temporal taps
+  // of three neighbouring workgroups while it is in L2).
+  const int tf = p.time_tiles ? mt % p.T : mt / tpf;
+  const int rem = p.time_tiles ? mt / p.T : mt - tf * tpf;
   const int rt = rem / numC;
   const int h0 = rt * TR, w0 = (rem - rt * numC) * 32;
   const int dt0 = -2 * (p.kt >> 1);
@@ -526,15 +529,18 @@ struct ConfigEntry {
   const char* name;
   int nb, mb, waves;
   int halo;  // conv_halo_kernel's KS (WAVES*MB rows x 32 columns per tile), or 0
+  int time_tiles;  // halo tile order (ConvProblem::time_tiles)
   void (*kernel)(const ConvProblem);
 };
 
 #define WVD_CONV_CONFIG(NB, MB, W) \
-  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, conv_mfma_kernel<NB, MB, W> }
+  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, conv_mfma_kernel<NB, MB, W> }
+// 3x3-tap halo convs order tiles time-fastest (measured 2-8% faster than frame-major on every
+// 3x3x3 layer: fewer input re-reads past L2); the phase convs have no temporal taps.
 #define WVD_HALO_CONFIG(NB, MB, W) \
-  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, conv_halo_kernel<NB, MB, W, 3> }
+  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_kernel<NB, MB, W, 3> }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, conv_halo_kernel<NB, MB, W, 2> }
+  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_kernel<NB, MB, W, 2> }
 
 // Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
 // bigger per-wave tiles at one wave per SIMD: the second wave issues matrix work while the first
@@ -630,7 +636,9 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   const int64_t blocks = blocks_for(c, p.T, p.H, p.W, p.Npad);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (config_id) *config_id = id;
-  hipLaunchKernelGGL(c.kernel, dim3((unsigned)blocks, 1, p.phases), dim3(c.waves * 64), 0, s, p);
+  ConvProblem q = p;
+  q.time_tiles = c.time_tiles;
+  hipLaunchKernelGGL(c.kernel, dim3((unsigned)blocks, 1, p.phases), dim3(c.waves * 64), 0, s, q);
   return hipGetLastError();
 }
 

@@ -1,0 +1,199 @@
+"""Measurement support: rocprofv3 summaries and the HBM traffic of the conv kernels.
+
+* ``copy_calibration_run(mib)`` runs a plain elementwise copy (y = -x, fp32) over ``mib`` MiB three
+  times. Under ``rocprofv3 --pmc FETCH_SIZE`` (then ``--pmc WRITE_SIZE``) its per-dispatch
+  counters give the factor between what the counters report and the bytes really moved, which
+  then scales the counters of the conv kernel.
+* ``kernel_sources_sha256()`` hashes the conv kernels' sources; a traffic figure is only valid
+  for the sources it was measured on.
+* ``committed_traffic(config)`` returns the HBM bytes per launch recorded for a conv
+  configuration in ``profiles/<config>_hbm_traffic_*.md`` when the recorded source hash matches
+  the current sources, else None.
+
+Command line (prints markdown):
+  python -m causal_convolution_causalconv3d_amd.profiling stats <rocprof kernel_stats.csv> [--command CMD]
+  python -m causal_convolution_causalconv3d_amd.profiling traffic --config NAME --fetch DIR --write DIR
+      --copy-fetch DIR --copy-write DIR --copy-mib N [--command CMD ...]
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+import sys
+from typing import Dict, List, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+KERNEL_SOURCES = ("conv_mfma.hip", "conv_epilogue.h", "common.h")
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _keyvals(path: str) -> Dict[str, str]:
+    out = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^\s*[-*]?\s*`?([a-z_0-9]+)`?\s*:\s*`?([^`\s]+)`?\s*$", line)
+            if m:
+                out[m.group(1)] = m.group(2)
+    return out
+
+
+def committed_traffic(config: str) -> Optional[int]:
+    """HBM bytes per launch of `config` from its committed traffic summary, if still valid."""
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"{config}_hbm_traffic_*.md"))):
+        kv = _keyvals(path)
+        if kv.get("config") == config and kv.get("kernel_sources_sha256") == kernel_sources_sha256():
+            try:
+                return int(float(kv["hbm_bytes_per_launch"]))
+            except (KeyError, ValueError):
+                return None
+    return None
+
+
+def copy_calibration_run(mib: int) -> None:
+    import torch
+
+    n = mib * (1 << 20) // 4
+    x = torch.randn(n, device="cuda")
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(f"copy calibration: 3 dispatches of y = -x over {mib} MiB ({n * 4} bytes read and written each)", flush=True)
+
+
+def kernel_symbol(config: str) -> str:
+    """The kernel's demangled name prefix for a configuration name."""
+    m = re.fullmatch(r"conv_(mfma|halo|phase_halo)_n(\d+)_m(\d+)_w(\d+)", config)
+    if not m:
+        raise ValueError(f"unknown conv configuration {config}")
+    kind, nb, mb, w = m.groups()
+    if kind == "mfma":
+        return f"conv_mfma_kernel<{nb}, {mb}, {w}>"
+    return f"conv_halo_kernel<{nb}, {mb}, {w}, {2 if kind == 'phase_halo' else 3}>"
+
+
+def _counter_rows(d: str) -> List[dict]:
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(d: str, counter: str, match) -> List[float]:
+    acc: Dict[str, float] = {}
+    for r in _counter_rows(d):
+        if r["Counter_Name"] != counter or not match(r["Kernel_Name"]):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    return list(acc.values())
+
+
+def traffic_summary(config: str, fetch: str, write: str, copy_fetch: str, copy_write: str, copy_mib: int,
+                    commands: List[str]) -> str:
+    sym = kernel_symbol(config)
+    is_kernel = lambda name: sym in name  # noqa: E731
+    is_copy = lambda name: "neg" in name  # noqa: E731
+    kf = _per_dispatch(fetch, "FETCH_SIZE", is_kernel)
+    kw = _per_dispatch(write, "WRITE_SIZE", is_kernel)
+    cf = _per_dispatch(copy_fetch, "FETCH_SIZE", is_copy)
+    cw = _per_dispatch(copy_write, "WRITE_SIZE", is_copy)
+    if not (kf and kw and cf and cw):
+        raise RuntimeError("missing dispatches in the counter files")
+    copy_bytes = copy_mib * (1 << 20)
+    # the copy's last dispatches (after the warm-up one)
+    cf_kib, cw_kib = sum(cf[-3:]) / len(cf[-3:]), sum(cw[-3:]) / len(cw[-3:])
+    f_scale = copy_bytes / (cf_kib * 1024.0)
+    w_scale = copy_bytes / (cw_kib * 1024.0)
+    kf_kib, kw_kib = sum(kf) / len(kf), sum(kw) / len(kw)
+    fetch_b = kf_kib * 1024.0 * f_scale
+    write_b = kw_kib * 1024.0 * w_scale
+    lines = [
+        f"# HBM traffic of {config} in the streaming decode (704x1248, 4 latent frames per pass)",
+        "",
+        "Counters: rocprofv3 `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE` (KiB per dispatch), one run each,",
+        "averaged over every dispatch of the kernel; scaled by the same counters on a plain copy kernel",
+        f"(y = -x, fp32, {copy_mib} MiB read and written per dispatch, mean of its last 3 dispatches).",
+        "",
+        "Commands:",
+        "",
+    ]
+    lines += [f"    {c}" for c in commands]
+    lines += [
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| kernel dispatches (fetch run / write run) | {len(kf)} / {len(kw)} |",
+        f"| FETCH_SIZE per dispatch (KiB, raw) | {kf_kib:.1f} |",
+        f"| WRITE_SIZE per dispatch (KiB, raw) | {kw_kib:.1f} |",
+        f"| copy FETCH_SIZE per dispatch (KiB) / true | {cf_kib:.1f} / {copy_bytes / 1024:.1f} |",
+        f"| copy WRITE_SIZE per dispatch (KiB) / true | {cw_kib:.1f} / {copy_bytes / 1024:.1f} |",
+        f"| fetch scale / write scale | {f_scale:.4f} / {w_scale:.4f} |",
+        f"| HBM read per launch (bytes, scaled) | {fetch_b:.4g} |",
+        f"| HBM write per launch (bytes, scaled) | {write_b:.4g} |",
+        "",
+        f"- config: `{config}`",
+        f"- kernel_sources_sha256: `{kernel_sources_sha256()}`",
+        f"- hbm_bytes_per_launch: `{int(round(fetch_b + write_b))}`",
+        "",
+    ]
+    return "\n".join(lines)
+
+
+def stats_summary(path: str, command: str, top: int = 25) -> str:
+    with open(path) as f:
+        rows = list(csv.DictReader(f))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["Command:", "", f"    {command}", "",
+           "| kernel | calls | total ms | avg us | share |", "|---|---:|---:|---:|---:|"]
+    for r in rows[:top]:
+        name = r["Name"]
+        name = re.sub(r"\(wvd::ConvProblem\)$", "", name)
+        name = name.replace("void wvd::(anonymous namespace)::", "")
+        if len(name) > 90:
+            name = name[:87] + "..."
+        t = float(r["TotalDurationNs"])
+        out.append(f"| `{name}` | {r['Calls']} | {t / 1e6:.2f} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{100.0 * t / total:.1f}% |")
+    out.append(f"| all kernels | {sum(int(r['Calls']) for r in rows)} | {total / 1e6:.2f} | | 100% |")
+    return "\n".join(out) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="python -m causal_convolution_causalconv3d_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    st = sub.add_parser("stats")
+    st.add_argument("csv")
+    st.add_argument("--command", default="")
+    tr = sub.add_parser("traffic")
+    tr.add_argument("--config", required=True)
+    for k in ("fetch", "write", "copy-fetch", "copy-write"):
+        tr.add_argument(f"--{k}", required=True)
+    tr.add_argument("--copy-mib", type=int, required=True)
+    tr.add_argument("--command", action="append", default=[])
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        sys.stdout.write(stats_summary(a.csv, a.command))
+    else:
+        sys.stdout.write(traffic_summary(a.config, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.command))
+
+
+if __name__ == "__main__":
+    main()

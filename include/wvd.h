@@ -221,8 +221,9 @@ int64_t wvd_chunk_video_frames(const wvd_decoder_desc* d, int64_t n, int first, 
 
 /* ============================================================================================
  * Kernel timing (measurement support): when enabled, the library records a HIP event pair
- * around every launch of the matrix-core convolution kernel on the launch stream and sums the
- * elapsed times and the algorithmic FLOPs per kernel configuration. wvd_timing_read
+ * around every launch of the matrix-core convolution kernel (and of the memory-bound kernels) on
+ * the launch stream and sums the elapsed times and the algorithmic FLOPs (bytes) per kernel
+ * configuration (kind). wvd_timing_read
  * synchronises the events. Not for use while another thread launches.
  * ========================================================================================== */
 wvd_status wvd_timing_enable(int on);
@@ -235,6 +236,11 @@ int wvd_timing_read(int i, const char** name, int64_t* launches, double* ms, dou
  * algorithmic FLOPs and problem shape {T, H, W, Ci, N, taps, phases, history frames}. Returns the
  * number of recorded launches (call with i = -1 to count). */
 int wvd_timing_launch(int i, int* config, double* ms, double* flops, int shape[8]);
+/* The memory-bound kernels (channel RMS norm + SiLU, the head's tap stencil, the latent layout
+ * conversion), timed the same way: for kind i (0..count-1) a name, the launch count, the summed
+ * milliseconds and the summed algorithmic bytes (every input element read once, every output
+ * element written once). Returns the count of kinds when name is null. */
+int wvd_timing_read_mem(int i, const char** name, int64_t* launches, double* ms, double* bytes);
 /* Testing and tuning support: run every following matrix-core convolution launch with
  * configuration `config` (an index of wvd_timing_read), or with the automatic choice again
  * when config is -1. A launch the forced configuration cannot run (a halo-tile configuration on
