@@ -31,6 +31,13 @@ namespace {
 
 constexpr int LDS_ROW = 40;  // bf16 per LDS row: 32 channels + 8 pad (80 bytes: no bank conflicts)
 
+// Staging pieces are 16 bytes (8 channels of one weight row or patch position), four lanes per
+// row so that a wave's global loads cover whole 64-byte runs. A lane without a piece (the last
+// round of a tile whose piece count is not a multiple of the workgroup size) loads a valid
+// address and stores into the unused 16-byte pad of a row, one pad per such lane: no branch,
+// and no pile-up of many lanes on one LDS address (a same-address store serialises).
+__device__ __forceinline__ int pad_slot(int row) { return row * LDS_ROW + 32; }  // in bf16
+
 template <int NB, int MB, int WAVES>
 __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProblem p) {
   constexpr int BN = NB * 32;
@@ -164,11 +171,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
     }
   };
   // Weight rows past Npad (only in a partial last N tile) read row Npad-1: those columns are
-  // never stored. Threads past the tile's pieces repeat the last piece (same data, same address).
+  // never stored. Lanes past the tile's pieces go to pad slots (see pad_slot).
   auto load_w = [&](u32x4 (&dst)[WLOADS], const Cursor& c) {
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
-      const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
+      const int q = (tid + i * NT) % WPIECES;
       const int row = min(q >> 2, p.Npad - 1 - n0), piece = q & 3;
       dst[i] = *(const u32x4*)(wbase + row * wrow + c.tap * p.Cip + c.chunk * 32 + piece * 8);
     }
@@ -176,9 +183,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   auto store_w = [&](const u32x4 (&src)[WLOADS], int buf) {
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
-      const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
-      const int row = q >> 2, piece = q & 3;
-      *(u32x4*)(&lds[buf][row * LDS_ROW + piece * 8]) = src[i];
+      const int q = tid + i * NT;
+      const int at = q < WPIECES ? (q >> 2) * LDS_ROW + (q & 3) * 8 : pad_slot((q - WPIECES) % BN);
+      *(u32x4*)(&lds[buf][at]) = src[i];
     }
   };
   auto read_w = [&](u32x4 (&dst)[2][NB], int buf) {
@@ -282,21 +289,27 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
 constexpr int PROW = 40;  // bf16 per patch position: 32 channels + 8 pad
 
 template <int NB, int MB, int WAVES, int KS>
-__global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProblem p) {
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_kernel(const ConvProblem p) {
   static_assert(KS == 2 || KS == 3, "3x3 taps, or 2x2 phase taps");
   constexpr int SPS = KS * KS;              // steps per stage
   constexpr int STORE_S = SPS == 9 ? 4 : 2;  // the step that stores the next stage's patch
   constexpr int BN = NB * 32;
   constexpr int TR = WAVES * MB;
   constexpr int PR = TR + 2, PC = 34;
-  constexpr int PATCH = PR * PC * PROW + 8;  // + one 16-byte slot for the surplus pieces
+  constexpr int PATCH = PR * PC * PROW;
   constexpr int NT = WAVES * 64;
   constexpr int WPIECES = BN * 4;
   constexpr int WLOADS = (WPIECES + NT - 1) / NT;
   constexpr int PPIECES = PR * PC * 4;  // 16-byte pieces of one patch
   constexpr int PLOADS = (PPIECES + NT - 1) / NT;
   static_assert(NT % 4 == 0, "a thread's pieces share one channel group");
-  __shared__ __attribute__((aligned(16))) bf16_t lds_w[4][BN * LDS_ROW];
+  static_assert(PLOADS * NT - PPIECES <= PR * PC, "a pad slot for every lane without a patch piece");
+  // Weight stages: step j's slice sits in stage j % NWS. Three suffice (stage (k + 2) % 3 is
+  // written at the end of step k; its last reader, step k - 1, is past the barrier of step
+  // k - 1); with 9 steps per stage the index is then a compile-time constant. 2x2 taps (4 steps
+  // per stage) use four for the same reason.
+  constexpr int NWS = (SPS % 3 == 0) ? 3 : 4;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w[NWS][BN * LDS_ROW];
   __shared__ __attribute__((aligned(16))) bf16_t lds_p[2][PATCH];
 
   const int tid = threadIdx.x;
@@ -344,7 +357,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProb
     boff[mb] = (uint32_t)((((r + pa) * PC + l32 + pb) * PROW + half * 16) * 2);
   }
 
-  // This thread's patch pieces: position (pr, pc) of the patch, channel group tid & 3.
+  // This thread's patch pieces: position (piece / 4) of the patch, channel group tid & 3; a lane
+  // without a piece loads zeros and stores into a position's unused pad.
   const int ch8 = (tid & 3) * 8;
   int goff[PLOADS];       // byte offset in a frame (chunk 0), or -1 outside the frame
   uint32_t poff[PLOADS];  // byte offset in a patch buffer
@@ -356,7 +370,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProb
     const int hh = h0 - 1 + pr, ww = w0 - 1 + pc;
     const bool inb = (piece < PPIECES) & (hh >= 0) & (hh < p.H) & (ww >= 0) & (ww < p.W);
     goff[i] = inb ? ((hh * p.W + ww) * p.Ci + ch8) * 2 : -1;
-    poff[i] = piece < PPIECES ? (uint32_t)((pos * PROW + ch8) * 2) : (uint32_t)((PATCH - 8) * 2);
+    poff[i] = (uint32_t)((piece < PPIECES ? pos * PROW + ch8 : pad_slot(piece - PPIECES)) * 2);
   }
 
   const int nchunks = p.Cip >> 5;
@@ -403,7 +417,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProb
   auto load_w = [&](u32x4 (&dst)[WLOADS], int col) {
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
-      const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
+      const int q = (tid + i * NT) % WPIECES;
       const int row = min(q >> 2, p.Npad - 1 - n0), piece = q & 3;
       dst[i] = *(const u32x4*)(wbase + row * wrow + col + piece * 8);
     }
@@ -411,9 +425,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProb
   auto store_w = [&](const u32x4 (&src)[WLOADS], int buf) {
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i) {
-      const int q = (tid + i * NT < WPIECES) ? tid + i * NT : WPIECES - 1;
-      const int row = q >> 2, piece = q & 3;
-      *(u32x4*)(&lds_w[buf][row * LDS_ROW + piece * 8]) = src[i];
+      const int q = tid + i * NT;
+      const int at = q < WPIECES ? (q >> 2) * LDS_ROW + (q & 3) * 8 : pad_slot((q - WPIECES) % BN);
+      *(u32x4*)(&lds_w[buf][at]) = src[i];
     }
   };
   // fragments of K half q (channels half*16 + q*8 .. + 7 of the chunk) of spatial tap `tap`
@@ -445,7 +459,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProb
                                                               __builtin_bit_cast(bf16x8, a[mb]), acc[nb][mb], 0, 0, 0);
   };
 
-  // Pipeline. Weights: step j's slice sits in LDS stage j % 4; during step k the weights of step
+  // Pipeline. Weights: step j's slice sits in LDS stage j % NWS; during step k the weights of step
   // k + 3 are loaded into registers and those of step k + 2 (loaded during step k - 1) are
   // stored at the step's end. Patches: stage g's patch sits in buffer g % 2; the next stage's
   // patch is loaded at step 0 of a stage and stored at step 4 (its buffer was last read in
@@ -472,7 +486,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProb
     // half step 0 (step k + 3 lies in this stage or the next: SPS >= 4)
     load_w(wreg[KP ^ 1], S + 3 < SPS ? cur.col + (S + 3) * p.Cip : nxt.col + (S + 3 - SPS) * p.Cip);
     if constexpr (S == 0) load_patch(preg, nxt, g + 1 < ng);
-    read_a(wf[1], k & 3, 1);
+    read_a(wf[1], S % NWS, 1);
     read_b(bf[1], P, S, 1);
     compute(wf[0], bf[0]);
 #pragma unroll
@@ -484,7 +498,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProb
     }
     __builtin_amdgcn_sched_barrier(0);
     // half step 1
-    read_a(wf[0], (k + 1) & 3, 0);
+    read_a(wf[0], (S + 1) % NWS, 0);
     if constexpr (S < SPS - 1) read_b(bf[0], P, S + 1, 0);
     else read_b(bf[0], P ^ 1, 0, 0);
     compute(wf[1], bf[1]);
@@ -495,7 +509,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_halo_kernel(const ConvProb
       __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    store_w(wreg[KP], (k + 2) & 3);
+    store_w(wreg[KP], (S + 2) % NWS);
     if constexpr (S == STORE_S) store_patch(preg, P ^ 1);
     __syncthreads();
   };
@@ -545,19 +559,29 @@ struct ConfigEntry {
 // Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
 // bigger per-wave tiles at one wave per SIMD: the second wave issues matrix work while the first
 // waits on memory.
+// Configuration ids: indices into kConfigs (also the timing and force-config indices).
+enum ConfigId {
+  LIN_N6_W8,     // 192 x 256, 2 waves/SIMD
+  LIN_N6_W4,     // 192 x 128, 2 workgroups/CU
+  LIN_N3_W8,     // 96 x 256, 2 waves/SIMD
+  LIN_N3_W4,     // 96 x 128: small grids
+  LIN_N1_M4_W4,  // 32 x 512: a few output channels
+  LIN_N3_M2_W8,  // 96 x 512, 2 waves/SIMD: long reductions (3x3x3 taps)
+  HALO_N6_W8,    // 192 x (8 rows x 32 columns)
+  HALO_N3_W8,    // 96 x (16 rows x 32 columns)
+  HALO_N3_W4,    // 96 x (8 rows x 32 columns), two workgroups per CU
+  PHASE_N6_W8,   // x2 upsampling phases: 192 x (8 rows x 32 columns)
+  PHASE_N3_W8,   // x2 upsampling phases: 96 x (16 rows x 32 columns)
+  NUM_CONFIGS
+};
 const ConfigEntry kConfigs[] = {
-    WVD_CONV_CONFIG(6, 1, 8),  // 192 x 256, 2 waves/SIMD
-    WVD_CONV_CONFIG(6, 1, 4),  // 192 x 128, 2 workgroups/CU
-    WVD_CONV_CONFIG(3, 1, 8),  // 96 x 256, 2 waves/SIMD
-    WVD_CONV_CONFIG(3, 1, 4),  // 96 x 128: small grids
-    WVD_CONV_CONFIG(1, 4, 4),  // 32 x 512: a few output channels
-    WVD_CONV_CONFIG(3, 2, 8),  // 96 x 512, 2 waves/SIMD: long reductions (3x3x3 taps)
-    WVD_HALO_CONFIG(6, 1, 8),  // 192 x (8 rows x 32 columns)
-    WVD_HALO_CONFIG(3, 2, 8),  // 96 x (16 rows x 32 columns)
-    WVD_PHASE_HALO_CONFIG(6, 1, 8),  // x2 upsampling phases: 192 x (8 rows x 32 columns)
-    WVD_PHASE_HALO_CONFIG(3, 2, 8),  // x2 upsampling phases: 96 x (16 rows x 32 columns)
+    WVD_CONV_CONFIG(6, 1, 8),       WVD_CONV_CONFIG(6, 1, 4),       WVD_CONV_CONFIG(3, 1, 8),
+    WVD_CONV_CONFIG(3, 1, 4),       WVD_CONV_CONFIG(1, 4, 4),       WVD_CONV_CONFIG(3, 2, 8),
+    WVD_HALO_CONFIG(6, 1, 8),       WVD_HALO_CONFIG(3, 2, 8),       WVD_HALO_CONFIG(3, 2, 4),
+    WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
 constexpr int kMaxFusedNormN = 192;  // the widest channel tile
 
 // Workgroups of a problem: per frame ceil(H*W / BM) position tiles (halo kernels: ceil(H / rows)
@@ -575,32 +599,37 @@ int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t H, int64_t W, int Np
 
 // Convolutions with 3x3 spatial taps take the halo kernel with 96 x (16 x 32) tiles (measured the
 // fastest on every 3x3x3 layer of the decoder, 384-channel ones included: two position blocks per
-// wave halve the weight fragment reads per matrix op), or its 192-wide variant when a fused norm
-// needs more channels in one tile. Otherwise: the largest linear tile whose grid still gives every
-// CU a workgroup per phase; a 96-wide channel tile takes two position blocks per wave on long
-// reductions, one on short ones.
+// wave halve the weight fragment reads per matrix op), its 8-row variant when 16-row tiles would
+// leave a ragged last row of tiles but 8-row ones do not (two workgroups per CU; measured 10 %
+// faster at 88 rows), or the 192-wide variant when a fused norm needs more channels in one tile.
+// Otherwise: the largest linear tile whose grid still gives every CU a workgroup per phase; a
+// 96-wide channel tile takes two position blocks per wave on long reductions, one on short ones.
 int choose_config(const ConvProblem& p, bool one_n_tile) {
   const int64_t cus = 256;
   const int64_t T = p.T, H = p.H, W = p.W;
   const int Npad = p.Npad, phases = p.phases;
-  if (Npad <= 32) return 4;
-  if (phases == 1 && p.kh == 3 && p.kw == 3) return (one_n_tile && Npad > 96) ? 6 : 7;
+  if (Npad <= 32) return LIN_N1_M4_W4;
+  if (phases == 1 && p.kh == 3 && p.kw == 3) {
+    if (one_n_tile && Npad > 96) return HALO_N6_W8;
+    return (H % 16 != 0 && H % 8 == 0) ? HALO_N3_W4 : HALO_N3_W8;
+  }
   // The phase convs (K = 4 taps x C) have short reductions: the halo kernel wins from 192
   // channels up; at 96 (with the fused norm) the linear kernel's smaller LDS footprint and
   // overlapping workgroups do better.
-  if (phases == 4 && p.kh == 2 && p.kw == 2 && Npad >= 192 && !one_n_tile) return 9;
-  const int n96 = (p.ntaps >= 9 && blocks_for(kConfigs[5], T, H, W, Npad) * phases >= cus) ? 5 : 2;
+  if (phases == 4 && p.kh == 2 && p.kw == 2 && Npad >= 192 && !one_n_tile) return PHASE_N3_W8;
+  const auto fills = [&](int id) { return blocks_for(kConfigs[id], T, H, W, Npad) * phases >= cus; };
+  const int n96 = (p.ntaps >= 9 && fills(LIN_N3_M2_W8)) ? LIN_N3_M2_W8 : LIN_N3_W8;
   if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup
-    if (Npad <= 96) return blocks_for(kConfigs[2], T, H, W, Npad) * phases >= cus ? n96 : 3;
-    return blocks_for(kConfigs[0], T, H, W, Npad) * phases >= cus ? 0 : 1;
+    if (Npad <= 96) return fills(LIN_N3_W8) ? n96 : LIN_N3_W4;
+    return fills(LIN_N6_W8) ? LIN_N6_W8 : LIN_N6_W4;
   }
   if (Npad % 192 == 0) {
-    if (blocks_for(kConfigs[0], T, H, W, Npad) * phases >= cus) return 0;
-    if (blocks_for(kConfigs[1], T, H, W, Npad) * phases >= cus) return 1;
-    return 3;
+    if (fills(LIN_N6_W8)) return LIN_N6_W8;
+    if (fills(LIN_N6_W4)) return LIN_N6_W4;
+    return LIN_N3_W4;
   }
-  if (Npad % 96 == 0 && blocks_for(kConfigs[2], T, H, W, Npad) * phases >= cus) return n96;
-  return 3;
+  if (Npad % 96 == 0 && fills(LIN_N3_W8)) return n96;
+  return LIN_N3_W4;
 }
 
 }  // namespace
