@@ -539,6 +539,273 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_kernel(const 
   conv_epilogue<NB, MB>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
 }
 
+// LDS-DMA variant of the 3x3-tap halo kernel. Same tiles, K order, fragments and epilogue; the
+// staging goes straight from memory into LDS with buffer loads that write LDS (each lane's 16
+// bytes land at the instruction's LDS base + 16 * lane), so no registers, no LDS store
+// instructions and no address arithmetic per piece. A weight row and a patch position are five
+// 16-byte slots (32 channels and the pad); a lane that draws a pad slot, a slot past the rows, a
+// position outside the frame or a channel past Ci reads out of range and writes zeros.
+// Weights sit in six LDS slots, one per K step (step j in slot j % 6), and are fetched five
+// steps ahead: slot (k + 5) % 6 last held step k - 1, which every wave finished before the
+// barrier of step k - 1. The next stage's patch is fetched at step 0 of a stage into the other
+// buffer (last read in the previous stage). Before the barrier of step k a wave waits until its
+// own fetches up to step k - 3 have landed (a count of the fetches it issued since, fixed at
+// compile time): that covers the weights of step k + 2 (read from step k + 1 on) and, from step
+// 3, the next patch (read from step 8 on). Each slot and buffer is its own LDS array, so the
+// compiler's own waits before LDS reads only cover fetches into the array being read.
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 fields: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8; expcnt 7 and lgkmcnt 15 do not wait).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+template <int NB, int MB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(const ConvProblem p) {
+  constexpr int SPS = 9;
+  constexpr int BN = NB * 32;
+  constexpr int TR = WAVES * MB;
+  constexpr int PR = TR + 2, PC = 34;
+  constexpr int PSLOTS = PR * PC * 5;                                // 16-byte slots of a patch
+  constexpr int PIW = (PSLOTS + 64 * WAVES - 1) / (64 * WAVES);      // patch fetches per wave
+  constexpr int WSLOTS = BN * 5;                                     // 16-byte slots of a weight step
+  constexpr int WIW = (WSLOTS + 64 * WAVES - 1) / (64 * WAVES);      // weight fetches per wave
+  constexpr int PBYTES = PIW * WAVES * 1024, WBYTES = WIW * WAVES * 1024;
+  static_assert(2 * PBYTES + 6 * WBYTES <= 163840, "LDS");
+  __shared__ __attribute__((aligned(16))) bf16_t lds_p0[PBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_p1[PBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w0[WBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w1[WBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w2[WBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w3[WBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w4[WBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w5[WBYTES / 2];
+  auto wslot = [&](auto I) -> bf16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return lds_w0;
+    else if constexpr (i == 1) return lds_w1;
+    else if constexpr (i == 2) return lds_w2;
+    else if constexpr (i == 3) return lds_w3;
+    else if constexpr (i == 4) return lds_w4;
+    else return lds_w5;
+  };
+  auto pbuf = [&](auto I) -> bf16_t* {
+    if constexpr (decltype(I)::value == 0) return lds_p0;
+    else return lds_p1;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int numR = (p.H + TR - 1) / TR, numC = (p.W + 31) / 32;
+  const int tpf = numR * numC;
+  const int numN = (p.Npad + BN - 1) / BN;
+  const int total = p.T * tpf * numN;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int q8 = total >> 3, r8 = total & 7;
+  const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
+  const int mt = lin / numN, nt = lin - (lin / numN) * numN;
+  const int n0 = nt * BN;
+  const int tf = p.time_tiles ? mt % p.T : mt / tpf;
+  const int rem = p.time_tiles ? mt / p.T : mt - tf * tpf;
+  const int rt = rem / numC;
+  const int h0 = rt * TR, w0 = (rem - rt * numC) * 32;
+  const int dt0 = -2 * (p.kt >> 1);
+
+  int ph[MB], pw[MB];
+  bool pv[MB];
+  uint32_t boff[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = wave * MB + mb;
+    ph[mb] = h0 + r;
+    pw[mb] = w0 + l32;
+    pv[mb] = (ph[mb] < p.H) & (pw[mb] < p.W);
+    boff[mb] = (uint32_t)(((r * PC + l32) * PROW + half * 16) * 2);
+  }
+
+  const int nchunks = p.Cip >> 5;
+  const int ng = nchunks * p.kt;
+  const int64_t frame_elems = (int64_t)p.H * p.W * p.Ci;
+  const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
+  const int64_t wrow = (int64_t)p.ntaps * p.Cip;
+  const bf16_t* wbase = p.wpk + (int64_t)n0 * wrow;
+  const int wrows = min(BN, p.Npad - n0);
+  const uint32_t wbytes = (uint32_t)((int64_t)(p.Npad - n0) * wrow * 2);
+
+  // This lane's patch slots: byte offset in a frame for chunk 0 (or frame_bytes: always zero)
+  // and the slot's channel group (for the Ci tail of the last chunk).
+  uint32_t pgo[PIW];
+  int pch[PIW];
+#pragma unroll
+  for (int i = 0; i < PIW; ++i) {
+    const int j = (i * WAVES + wave) * 64 + lane;
+    const int pos = j / 5, part = j - (j / 5) * 5;
+    const int pr = pos / PC, pc = pos - (pos / PC) * PC;
+    const int hh = h0 - 1 + pr, ww = w0 - 1 + pc;
+    const bool ok = (part < 4) & (pos < PR * PC) & (hh >= 0) & (hh < p.H) & (ww >= 0) & (ww < p.W);
+    pgo[i] = ok ? (uint32_t)(((hh * p.W + ww) * p.Ci + part * 8) * 2) : frame_bytes;
+    pch[i] = part * 8;
+  }
+  // This lane's weight slots: byte offset of (row, 8-channel group) in the tile's packed rows,
+  // or wbytes (always zero) for pads and slots past the rows.
+  uint32_t wgo[WIW];
+#pragma unroll
+  for (int i = 0; i < WIW; ++i) {
+    const int j = (i * WAVES + wave) * 64 + lane;
+    const int row = j / 5, part = j - (j / 5) * 5;
+    wgo[i] = ((part < 4) & (row < wrows)) ? (uint32_t)((row * wrow + part * 8) * 2) : wbytes;
+  }
+  const __amdgpu_buffer_rsrc_t rs_w =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, (int)wbytes, 0x00020000);
+
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+  typedef __attribute__((address_space(3))) void lds_void;
+  u32x4 wf[2][NB];
+  u32x4 bf[2][MB];
+
+  struct Stage {
+    int chunk, i, col;
+  };
+  auto stage_at = [&](int chunk, int i) -> Stage { return {chunk, i, i * SPS * p.Cip + chunk * 32}; };
+  auto next_stage = [&](const Stage& c) -> Stage {
+    if (c.chunk * p.kt + c.i + 1 >= ng) return c;
+    return (c.i + 1 == p.kt) ? stage_at(c.chunk + 1, 0) : stage_at(c.chunk, c.i + 1);
+  };
+
+  // fetch a stage's patch into buffer BUF (live == false: zeros)
+  auto fetch_patch = [&](auto BUF, const Stage& c, bool live) {
+    const int sf = tf + dt0 + c.i;
+    const bool fok = live & (sf >= -p.Th);
+    const bf16_t* fbase = (sf >= 0) ? p.x + (int64_t)sf * frame_elems
+                                    : ((sf >= -p.Th) ? p.hist + (int64_t)(sf + p.Th) * frame_elems : p.x);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)fbase, (short)0, fok ? (int)frame_bytes : 0, 0x00020000);
+    char* base = (char*)pbuf(BUF);
+#pragma unroll
+    for (int i = 0; i < PIW; ++i) {
+      const uint32_t vo = (c.chunk * 32 + pch[i] < p.Ci) ? pgo[i] + c.chunk * 64 : frame_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + (i * WAVES + wave) * 1024), 16, (int)vo, 0, 0, 0);
+    }
+  };
+  // fetch the weights of one K step (column col of the packed rows) into slot SLOT
+  auto fetch_w = [&](auto SLOT, int col) {
+    char* base = (char*)wslot(SLOT);
+#pragma unroll
+    for (int i = 0; i < WIW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_void*)(base + (i * WAVES + wave) * 1024), 16,
+                                               (int)(wgo[i] + col * 2), 0, 0, 0);
+  };
+  auto read_a = [&](u32x4 (&dst)[NB], auto SLOT, int q) {
+    const bf16_t* w = wslot(SLOT);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) dst[nb] = *(const u32x4*)(&w[(nb * 32 + l32) * LDS_ROW + half * 16 + q * 8]);
+  };
+  auto read_b = [&](u32x4 (&dst)[MB], auto BUF, int tap, int q) {
+    const int j = tap / 3, k = tap - (tap / 3) * 3;
+    const char* base = (const char*)pbuf(BUF);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) dst[mb] = *(const u32x4*)(base + boff[mb] + ((j * PC + k) * PROW + q * 8) * 2);
+  };
+
+  floatx16 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
+  auto compute = [&](const u32x4 (&w)[NB], const u32x4 (&a)[MB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[nb]),
+                                                              __builtin_bit_cast(bf16x8, a[mb]), acc[nb][mb], 0, 0, 0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+
+  Stage cur = stage_at(0, 0);
+  Stage nxt = next_stage(cur);
+  fetch_patch(I0{}, cur, true);
+  fetch_w(I0{}, cur.col);
+  fetch_w(I1{}, cur.col + p.Cip);
+  fetch_w(I2{}, cur.col + 2 * p.Cip);
+  fetch_w(I3{}, cur.col + 3 * p.Cip);
+  fetch_w(I4{}, cur.col + 4 * p.Cip);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  read_a(wf[0], I0{}, 0);
+  read_b(bf[0], I0{}, 0, 0);
+
+  constexpr int NM = MB * NB;
+  auto step = [&](auto PP, auto SS, int g) {
+    constexpr int P = decltype(PP)::value;  // stage parity: patch buffer
+    constexpr int S = decltype(SS)::value;  // spatial tap
+    constexpr int K6 = (3 * P + S) % 6;     // k mod 6 (k = 9g + S)
+    __builtin_amdgcn_sched_barrier(0);
+    // step k + 5 lies in this stage or the next one
+    fetch_w(std::integral_constant<int, (K6 + 5) % 6>{},
+            S + 5 < SPS ? cur.col + (S + 5) * p.Cip : nxt.col + (S + 5 - SPS) * p.Cip);
+    if constexpr (S == 0) fetch_patch(std::integral_constant<int, P ^ 1>{}, nxt, g + 1 < ng);
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(wf[1], std::integral_constant<int, K6>{}, 1);
+    read_b(bf[1], std::integral_constant<int, P>{}, S, 1);
+    compute(wf[0], bf[0]);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(wf[0], std::integral_constant<int, (K6 + 1) % 6>{}, 0);
+    if constexpr (S < SPS - 1) read_b(bf[0], std::integral_constant<int, P>{}, S + 1, 0);
+    else read_b(bf[0], std::integral_constant<int, P ^ 1>{}, 0, 0);
+    compute(wf[1], bf[1]);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // own fetches of steps <= k - 3 have landed: the ones issued in steps k - 2 .. k may not
+    constexpr int N = 3 * WIW + (S <= 2 ? PIW : 0);
+    static_assert(N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+    __builtin_amdgcn_s_barrier();
+  };
+  auto stage = [&](auto PP, int g) {
+    step(PP, I0{}, g);
+    step(PP, I1{}, g);
+    step(PP, I2{}, g);
+    step(PP, I3{}, g);
+    step(PP, I4{}, g);
+    step(PP, std::integral_constant<int, 5>{}, g);
+    step(PP, std::integral_constant<int, 6>{}, g);
+    step(PP, std::integral_constant<int, 7>{}, g);
+    step(PP, std::integral_constant<int, 8>{}, g);
+    cur = nxt;
+    nxt = next_stage(nxt);
+  };
+  int g = 0;
+  for (; g + 1 < ng; g += 2) {
+    stage(I0{}, g);
+    stage(I1{}, g + 1);
+  }
+  if (g < ng) stage(I0{}, g);
+  // fetches past the end (into slots nobody reads) must land before the workgroup exits
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  conv_epilogue<NB, MB>(p, acc, ph, pw, pv, tf, n0, 0, 0, half);
+}
+
 struct ConfigEntry {
   const char* name;
   int nb, mb, waves;
@@ -553,6 +820,8 @@ struct ConfigEntry {
 // 3x3x3 layer: fewer input re-reads past L2); the phase convs have no temporal taps.
 #define WVD_HALO_CONFIG(NB, MB, W) \
   { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_kernel<NB, MB, W, 3> }
+#define WVD_HALO_DMA_CONFIG(NB, MB, W) \
+  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_dma_kernel<NB, MB, W> }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
   { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_kernel<NB, MB, W, 2> }
 
@@ -572,13 +841,16 @@ enum ConfigId {
   HALO_N3_W4,    // 96 x (8 rows x 32 columns), two workgroups per CU
   PHASE_N6_W8,   // x2 upsampling phases: 192 x (8 rows x 32 columns)
   PHASE_N3_W8,   // x2 upsampling phases: 96 x (16 rows x 32 columns)
+  HALO_DMA_N3_W8,  // HALO_N3_W8 with LDS-DMA staging
+  HALO_DMA_N6_W8,  // HALO_N6_W8 with LDS-DMA staging
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
     WVD_CONV_CONFIG(6, 1, 8),       WVD_CONV_CONFIG(6, 1, 4),       WVD_CONV_CONFIG(3, 1, 8),
     WVD_CONV_CONFIG(3, 1, 4),       WVD_CONV_CONFIG(1, 4, 4),       WVD_CONV_CONFIG(3, 2, 8),
     WVD_HALO_CONFIG(6, 1, 8),       WVD_HALO_CONFIG(3, 2, 8),       WVD_HALO_CONFIG(3, 2, 4),
-    WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8),
+    WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_CONFIG(3, 2, 8),
+    WVD_HALO_DMA_CONFIG(6, 1, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -597,11 +869,11 @@ int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t H, int64_t W, int Np
   return T * ((H * W + bm - 1) / bm) * nt;
 }
 
-// Convolutions with 3x3 spatial taps take the halo kernel with 96 x (16 x 32) tiles (measured the
-// fastest on every 3x3x3 layer of the decoder, 384-channel ones included: two position blocks per
-// wave halve the weight fragment reads per matrix op), its 8-row variant when 16-row tiles would
-// leave a ragged last row of tiles but 8-row ones do not (two workgroups per CU; measured 10 %
-// faster at 88 rows), or the 192-wide variant when a fused norm needs more channels in one tile.
+// Convolutions with 3x3 spatial taps take the LDS-DMA halo kernel with 96 x (16 x 32) tiles
+// (measured the fastest on every 3x3x3 layer of the decoder, 384-channel ones included: two
+// position blocks per wave halve the weight fragment reads per matrix op; DMA staging 5-12 %
+// faster than register staging), or its 192-wide variant when a fused norm needs more channels
+// in one tile.
 // Otherwise: the largest linear tile whose grid still gives every CU a workgroup per phase; a
 // 96-wide channel tile takes two position blocks per wave on long reductions, one on short ones.
 int choose_config(const ConvProblem& p, bool one_n_tile) {
@@ -609,10 +881,7 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   const int64_t T = p.T, H = p.H, W = p.W;
   const int Npad = p.Npad, phases = p.phases;
   if (Npad <= 32) return LIN_N1_M4_W4;
-  if (phases == 1 && p.kh == 3 && p.kw == 3) {
-    if (one_n_tile && Npad > 96) return HALO_N6_W8;
-    return (H % 16 != 0 && H % 8 == 0) ? HALO_N3_W4 : HALO_N3_W8;
-  }
+  if (phases == 1 && p.kh == 3 && p.kw == 3) return (one_n_tile && Npad > 96) ? HALO_DMA_N6_W8 : HALO_DMA_N3_W8;
   // The phase convs (K = 4 taps x C) have short reductions: the halo kernel wins from 192
   // channels up; at 96 (with the fused norm) the linear kernel's smaller LDS footprint and
   // overlapping workgroups do better.

@@ -272,8 +272,8 @@ def test_resblock_halo_configs_match_oracle(C):
     hd = to_dev_nthwc(cfg["hist"])
     xd = to_dev_nthwc(cfg["x"])
     try:
-        for name in ("conv_halo_n6_m1_w8", "conv_halo_n3_m2_w8"):
-            if C > 96 and name == "conv_halo_n3_m2_w8":
+        for name in ("conv_halo_n6_m1_w8", "conv_halo_n3_m2_w8", "conv_halo_dma_n6_m1_w8", "conv_halo_dma_n3_m2_w8"):
+            if C > 96 and "n3_m2" in name:
                 continue  # a 96-wide tile cannot hold a 192-channel norm
             wvd.conv_force_config(name)
             y = wvd.resblock(xd, wts, 1e-6, hist1=hd, hist2=hd)
