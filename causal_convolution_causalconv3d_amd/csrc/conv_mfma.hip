@@ -557,9 +557,15 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_kernel(const 
 // expcnt 6:4, lgkmcnt 11:8; expcnt 7 and lgkmcnt 15 do not wait).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-template <int NB, int MB, int WAVES>
+template <int NB, int MB, int WAVES, int KS>
 __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(const ConvProblem p) {
-  constexpr int SPS = 9;
+  static_assert(KS == 2 || KS == 3, "3x3 taps, or 2x2 phase taps");
+  constexpr int SPS = KS * KS;
+  // weight fetch distance D (steps ahead), slots NWS (> D, and k mod NWS a compile-time
+  // function of the stage parity and the tap), barrier wait window WW = D - 2 steps (must not
+  // exceed SPS - 2 so that the patch fetched at step 0 is in place for step SPS - 1)
+  constexpr int D = (SPS == 9) ? 5 : 4, NWS = (SPS == 9) ? 6 : 8, WW = D - 2;
+  static_assert(WW <= SPS - 2 && D < NWS && (2 * SPS) % NWS == 0, "fetch distance, slots and wait window");
   constexpr int BN = NB * 32;
   constexpr int TR = WAVES * MB;
   constexpr int PR = TR + 2, PC = 34;
@@ -568,7 +574,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   constexpr int WSLOTS = BN * 5;                                     // 16-byte slots of a weight step
   constexpr int WIW = (WSLOTS + 64 * WAVES - 1) / (64 * WAVES);      // weight fetches per wave
   constexpr int PBYTES = PIW * WAVES * 1024, WBYTES = WIW * WAVES * 1024;
-  static_assert(2 * PBYTES + 6 * WBYTES <= 163840, "LDS");
+  static_assert(2 * PBYTES + NWS * WBYTES <= 163840, "LDS");
   __shared__ __attribute__((aligned(16))) bf16_t lds_p0[PBYTES / 2];
   __shared__ __attribute__((aligned(16))) bf16_t lds_p1[PBYTES / 2];
   __shared__ __attribute__((aligned(16))) bf16_t lds_w0[WBYTES / 2];
@@ -577,14 +583,19 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   __shared__ __attribute__((aligned(16))) bf16_t lds_w3[WBYTES / 2];
   __shared__ __attribute__((aligned(16))) bf16_t lds_w4[WBYTES / 2];
   __shared__ __attribute__((aligned(16))) bf16_t lds_w5[WBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w6[NWS > 6 ? WBYTES / 2 : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_w7[NWS > 6 ? WBYTES / 2 : 8];
   auto wslot = [&](auto I) -> bf16_t* {
     constexpr int i = decltype(I)::value;
+    static_assert(i >= 0 && i < NWS, "slot");
     if constexpr (i == 0) return lds_w0;
     else if constexpr (i == 1) return lds_w1;
     else if constexpr (i == 2) return lds_w2;
     else if constexpr (i == 3) return lds_w3;
     else if constexpr (i == 4) return lds_w4;
-    else return lds_w5;
+    else if constexpr (i == 5) return lds_w5;
+    else if constexpr (i == 6) return lds_w6;
+    else return lds_w7;
   };
   auto pbuf = [&](auto I) -> bf16_t* {
     if constexpr (decltype(I)::value == 0) return lds_p0;
@@ -596,6 +607,9 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
+  const int phase = blockIdx.z;
+  const int pa = (KS == 2) ? (phase >> 1) : 0;
+  const int pb = (KS == 2) ? (phase & 1) : 0;
 
   const int numR = (p.H + TR - 1) / TR, numC = (p.W + 31) / 32;
   const int tpf = numR * numC;
@@ -613,6 +627,8 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   const int h0 = rt * TR, w0 = (rem - rt * numC) * 32;
   const int dt0 = -2 * (p.kt >> 1);
 
+  // operand of tap (0, 0): patch position (r + 1 + dh0, l32 + 1 + dw0), first tap offset
+  // (-1, -1), or (a - 1, b - 1) for phase (a, b) of the x2 upsampling
   int ph[MB], pw[MB];
   bool pv[MB];
   uint32_t boff[MB];
@@ -622,7 +638,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
     ph[mb] = h0 + r;
     pw[mb] = w0 + l32;
     pv[mb] = (ph[mb] < p.H) & (pw[mb] < p.W);
-    boff[mb] = (uint32_t)(((r * PC + l32) * PROW + half * 16) * 2);
+    boff[mb] = (uint32_t)((((r + pa) * PC + l32 + pb) * PROW + half * 16) * 2);
   }
 
   const int nchunks = p.Cip >> 5;
@@ -630,7 +646,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   const int64_t frame_elems = (int64_t)p.H * p.W * p.Ci;
   const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
   const int64_t wrow = (int64_t)p.ntaps * p.Cip;
-  const bf16_t* wbase = p.wpk + (int64_t)n0 * wrow;
+  const bf16_t* wbase = p.wpk + ((int64_t)phase * p.Npad + n0) * wrow;
   const int wrows = min(BN, p.Npad - n0);
   const uint32_t wbytes = (uint32_t)((int64_t)(p.Npad - n0) * wrow * 2);
 
@@ -703,7 +719,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
     for (int nb = 0; nb < NB; ++nb) dst[nb] = *(const u32x4*)(&w[(nb * 32 + l32) * LDS_ROW + half * 16 + q * 8]);
   };
   auto read_b = [&](u32x4 (&dst)[MB], auto BUF, int tap, int q) {
-    const int j = tap / 3, k = tap - (tap / 3) * 3;
+    const int j = tap / KS, k = tap - (tap / KS) * KS;
     const char* base = (const char*)pbuf(BUF);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) dst[mb] = *(const u32x4*)(base + boff[mb] + ((j * PC + k) * PROW + q * 8) * 2);
@@ -733,11 +749,12 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   Stage cur = stage_at(0, 0);
   Stage nxt = next_stage(cur);
   fetch_patch(I0{}, cur, true);
+  // steps 0 .. D - 1, all in the first stage
   fetch_w(I0{}, cur.col);
   fetch_w(I1{}, cur.col + p.Cip);
   fetch_w(I2{}, cur.col + 2 * p.Cip);
   fetch_w(I3{}, cur.col + 3 * p.Cip);
-  fetch_w(I4{}, cur.col + 4 * p.Cip);
+  if constexpr (D == 5) fetch_w(I4{}, cur.col + 4 * p.Cip);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_barrier();
   read_a(wf[0], I0{}, 0);
@@ -747,11 +764,11 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   auto step = [&](auto PP, auto SS, int g) {
     constexpr int P = decltype(PP)::value;  // stage parity: patch buffer
     constexpr int S = decltype(SS)::value;  // spatial tap
-    constexpr int K6 = (3 * P + S) % 6;     // k mod 6 (k = 9g + S)
+    constexpr int K6 = (P * SPS + S) % NWS;  // k mod NWS (k = SPS * g + S)
     __builtin_amdgcn_sched_barrier(0);
-    // step k + 5 lies in this stage or the next one
-    fetch_w(std::integral_constant<int, (K6 + 5) % 6>{},
-            S + 5 < SPS ? cur.col + (S + 5) * p.Cip : nxt.col + (S + 5 - SPS) * p.Cip);
+    // step k + D lies in this stage or the next one (D < 2 * SPS - S)
+    fetch_w(std::integral_constant<int, (K6 + D) % NWS>{},
+            S + D < SPS ? cur.col + (S + D) * p.Cip : nxt.col + (S + D - SPS) * p.Cip);
     if constexpr (S == 0) fetch_patch(std::integral_constant<int, P ^ 1>{}, nxt, g + 1 < ng);
     __builtin_amdgcn_sched_barrier(0);
     read_a(wf[1], std::integral_constant<int, K6>{}, 1);
@@ -764,7 +781,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
       __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    read_a(wf[0], std::integral_constant<int, (K6 + 1) % 6>{}, 0);
+    read_a(wf[0], std::integral_constant<int, (K6 + 1) % NWS>{}, 0);
     if constexpr (S < SPS - 1) read_b(bf[0], std::integral_constant<int, P>{}, S + 1, 0);
     else read_b(bf[0], std::integral_constant<int, P ^ 1>{}, 0, 0);
     compute(wf[1], bf[1]);
@@ -775,8 +792,8 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
       __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // own fetches of steps <= k - 3 have landed: the ones issued in steps k - 2 .. k may not
-    constexpr int N = 3 * WIW + (S <= 2 ? PIW : 0);
+    // own fetches of steps <= k - WW have landed: the ones issued in steps k - WW + 1 .. k may not
+    constexpr int N = WW * WIW + (S < WW ? PIW : 0);
     static_assert(N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
     __builtin_amdgcn_s_barrier();
@@ -786,11 +803,13 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
     step(PP, I1{}, g);
     step(PP, I2{}, g);
     step(PP, I3{}, g);
-    step(PP, I4{}, g);
-    step(PP, std::integral_constant<int, 5>{}, g);
-    step(PP, std::integral_constant<int, 6>{}, g);
-    step(PP, std::integral_constant<int, 7>{}, g);
-    step(PP, std::integral_constant<int, 8>{}, g);
+    if constexpr (SPS == 9) {
+      step(PP, I4{}, g);
+      step(PP, std::integral_constant<int, 5>{}, g);
+      step(PP, std::integral_constant<int, 6>{}, g);
+      step(PP, std::integral_constant<int, 7>{}, g);
+      step(PP, std::integral_constant<int, 8>{}, g);
+    }
     cur = nxt;
     nxt = next_stage(nxt);
   };
@@ -803,7 +822,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   // fetches past the end (into slots nobody reads) must land before the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  conv_epilogue<NB, MB>(p, acc, ph, pw, pv, tf, n0, 0, 0, half);
+  conv_epilogue<NB, MB>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
 }
 
 struct ConfigEntry {
@@ -821,7 +840,9 @@ struct ConfigEntry {
 #define WVD_HALO_CONFIG(NB, MB, W) \
   { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_kernel<NB, MB, W, 3> }
 #define WVD_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_dma_kernel<NB, MB, W> }
+  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_dma_kernel<NB, MB, W, 3> }
+#define WVD_PHASE_HALO_DMA_CONFIG(NB, MB, W) \
+  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_dma_kernel<NB, MB, W, 2> }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
   { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_kernel<NB, MB, W, 2> }
 
@@ -843,6 +864,7 @@ enum ConfigId {
   PHASE_N3_W8,   // x2 upsampling phases: 96 x (16 rows x 32 columns)
   HALO_DMA_N3_W8,  // HALO_N3_W8 with LDS-DMA staging
   HALO_DMA_N6_W8,  // HALO_N6_W8 with LDS-DMA staging
+  PHASE_DMA_N3_W8,  // PHASE_N3_W8 with LDS-DMA staging
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -850,7 +872,7 @@ const ConfigEntry kConfigs[] = {
     WVD_CONV_CONFIG(3, 1, 4),       WVD_CONV_CONFIG(1, 4, 4),       WVD_CONV_CONFIG(3, 2, 8),
     WVD_HALO_CONFIG(6, 1, 8),       WVD_HALO_CONFIG(3, 2, 8),       WVD_HALO_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_CONFIG(3, 2, 8),
-    WVD_HALO_DMA_CONFIG(6, 1, 8),
+    WVD_HALO_DMA_CONFIG(6, 1, 8),    WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -882,10 +904,10 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   const int Npad = p.Npad, phases = p.phases;
   if (Npad <= 32) return LIN_N1_M4_W4;
   if (phases == 1 && p.kh == 3 && p.kw == 3) return (one_n_tile && Npad > 96) ? HALO_DMA_N6_W8 : HALO_DMA_N3_W8;
-  // The phase convs (K = 4 taps x C) have short reductions: the halo kernel wins from 192
-  // channels up; at 96 (with the fused norm) the linear kernel's smaller LDS footprint and
-  // overlapping workgroups do better.
-  if (phases == 4 && p.kh == 2 && p.kw == 2 && Npad >= 192 && !one_n_tile) return PHASE_N3_W8;
+  // The phase convs (K = 4 taps x C) have short reductions: the DMA halo kernel wins from 192
+  // channels up; at 96 (with the fused norm: a heavy epilogue) the linear kernel's smaller LDS
+  // footprint lets workgroups overlap, measured 10 % faster.
+  if (phases == 4 && p.kh == 2 && p.kw == 2 && Npad >= 192 && !one_n_tile) return PHASE_DMA_N3_W8;
   const auto fills = [&](int id) { return blocks_for(kConfigs[id], T, H, W, Npad) * phases >= cus; };
   const int n96 = (p.ntaps >= 9 && fills(LIN_N3_M2_W8)) ? LIN_N3_M2_W8 : LIN_N3_W8;
   if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup

@@ -124,7 +124,7 @@ def test_bf16_conv_every_config_matches_oracle(case):
             ran += 1
     finally:
         wvd.conv_force_config(None)
-    assert ran >= len(names) - 2
+    assert ran == len([n for n in names if not n.startswith("conv_phase_halo")])
 
 
 @pytest.mark.parametrize("C,T,H,W", [(96, 2, 19, 37), (192, 1, 9, 40), (384, 2, 5, 7)])
