@@ -64,6 +64,42 @@ def algorithmic_conv_flops(spec: wl.DecoderSpec, latent_frames: int, fpp: int, h
     return total
 
 
+def achievable_peaks():
+    """What this chip sustains, as context for the spec peaks: a large bf16 library GEMM (torch.matmul,
+    8192^3, random data) in TFLOP/s and a plain device copy (2 GiB) in GB/s. Run after the timed
+    region; not part of any step."""
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    nbytes = 2 << 30
+    x = torch.empty(nbytes // 4, device="cuda", dtype=torch.float32).normal_(generator=g)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_tflops": round(gemm_tflops, 1), "copy_gbs": round(copy_gbs, 1),
+            "what": "torch.matmul bf16 8192^3 (hipBLASLt) and a 2 GiB device copy, 20 reps each, after the timed region"}
+
+
 def cpu_baseline(seconds_hint: float = 15.0):
     """The oracle (as it stands) on a bounded sample of the same decode: a 20x28 latent crop,
     one pass of 2 latent frames (8 video frames of 320x448), scaled to full-frame frames/s by the
@@ -197,6 +233,7 @@ def main():
                           "frac_of_hbm": round(v[2] / (v[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                           "ms_per_step": round(v[1] / args.steps, 3)}
                       for k, v in per_mem.items()},
+        "achievable": achievable_peaks(),
         "peak_hbm_gib": round(peak_alloc, 3),
         "peak_hbm_reserved_gib": round(peak_reserved, 3),
     }

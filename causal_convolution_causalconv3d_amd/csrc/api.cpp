@@ -459,7 +459,7 @@ wvd_status resblock_core(const ResblockArgs& r, hipStream_t s, F1 after_conv1, F
                                  nullptr);
   // conv2's input a2 = SiLU(norm2(h)): fused into conv1's epilogue when one workgroup holds every
   // output channel of a position (then h is never stored), else a separate pass
-  const bool fuse = conv_can_fuse_norm((int)round_up(w->cout, 32));
+  const bool fuse = conv_can_fuse_norm(w->cout, w->bias1, w->gamma2);
   if (fuse) {
     c1.norm_gamma = w->gamma2;
     c1.norm_eps = r.eps;
@@ -1142,7 +1142,7 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     WVD_TRY(run_norm(x, F_(r.gamma1), d->eps, 1, ba, P, r.cin, s));
     ConvProblem c1 = plain_problem(ba, nullptr, (int)T, H, Wd, r.cin, 0, W_(r.w1), r.cout, 3, 3, 3, F_(r.b1), bh, nullptr);
     // norm2 + SiLU fused into conv1's epilogue when one workgroup holds all output channels
-    const bool fuse = conv_can_fuse_norm((int)round_up(r.cout, 32));
+    const bool fuse = conv_can_fuse_norm(r.cout, F_(r.b1), F_(r.gamma2));
     if (fuse) {
       c1.norm_gamma = F_(r.gamma2);
       c1.norm_eps = d->eps;
@@ -1169,7 +1169,7 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
       WVD_TRY(resblock(r));
       c = r.cout;
     }
-    const bool fuse_out = si == L - 1 && conv_can_fuse_norm((int)round_up(c, 32));
+    const bool fuse_out = si == L - 1 && conv_can_fuse_norm(c, F_(st.sb), F_(p.norm_out));
     const float* ng = fuse_out ? F_(p.norm_out) : nullptr;
     const bf16_t* x = bx[cur];
     if (st.temporal) {

@@ -66,7 +66,7 @@ struct ConvProblem {
   int To, Ho, Wo, nsplit, fbase, fmul, fstride, hmul, wmul;
   int y_f32;
   // Optional fused channel RMS norm (+ SiLU) of the output (bf16 output, no residual, one
-  // channel tile: Npad <= conv_can_fuse_norm's limit): y = SiLU(gamma * v / sqrt(mean_c v^2 + eps)).
+  // channel tile, see conv_can_fuse_norm): y = SiLU(gamma * v / sqrt(mean_c v^2 + eps)).
   const float* norm_gamma;  // [N] or null
   float norm_eps;
   int norm_silu;
@@ -75,7 +75,9 @@ struct ConvProblem {
 
 // force_config >= 0 runs that configuration (hipErrorNotSupported when it cannot run p).
 hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id, int force_config = -1);
-bool conv_can_fuse_norm(int Npad);
+// Whether a conv with N output channels can apply RMS norm (+ SiLU) with gamma in its epilogue:
+// one channel tile, N % 8 == 0, bias (may be null) and gamma 16-byte aligned.
+bool conv_can_fuse_norm(int N, const float* bias, const float* gamma);
 const char* conv_config_name(int config_id);
 int conv_config_count();
 

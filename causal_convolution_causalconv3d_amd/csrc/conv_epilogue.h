@@ -6,33 +6,62 @@
 
 namespace wvd {
 
-// The lane holds, per (nb, mb, g), channels n0 + nb*32 + g*8 + half*4 + {0..3} of position
+// Four consecutive per-channel values v[n .. n+3] (n a multiple of 4) as one 16-byte load when the
+// array is 16-byte aligned and all four exist, else element by element; entries >= N are 0.
+__device__ __forceinline__ float4 load4(const float* v, int n, int N) {
+  if (!v) return make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if ((((uintptr_t)v & 15u) == 0) & (n + 3 < N)) return *(const float4*)(v + n);
+  float4 r;
+  r.x = n + 0 < N ? v[n + 0] : 0.0f;
+  r.y = n + 1 < N ? v[n + 1] : 0.0f;
+  r.z = n + 2 < N ? v[n + 2] : 0.0f;
+  r.w = n + 3 < N ? v[n + 3] : 0.0f;
+  return r;
+}
+
+// NORM selects the fused RMS norm (+ SiLU) epilogue (p.norm_gamma set), instantiated separately so
+// that its registers do not weigh on the plain kernels. The lane holds, per (nb, mb, g), channels n0 + nb*32 + g*8 + half*4 + {0..3} of position
 // (ph[mb], pw[mb]) of frame tf (valid when pv[mb]); (pa, pb) is the output phase. Scheduling
 // barriers keep one (mb, nb) block in flight at a time so the accumulators are not all copied
 // out of the AGPRs at once.
-template <int NB, int MB>
+template <int NB, int MB, bool NORM>
 __device__ __forceinline__ void conv_epilogue(const ConvProblem& p, floatx16 (&acc)[NB][MB], const int (&ph)[MB],
                                               const int (&pw)[MB], const bool (&pv)[MB], int tf, int n0, int pa,
                                               int pb, int half) {
-  if (p.norm_gamma) {
+  if constexpr (NORM) {
     // Fused channel RMS norm (+ SiLU) of the conv output: the workgroup holds every channel of
     // its positions (one N tile), split between lanes l and l ^ 32, so the per-position sum of
     // squares is this lane's part plus one cross-lane exchange. fp32 statistics on the unrounded
     // sums, one bf16 rounding of the activated value.
+    // (launched only with N % 8 == 0 and 16-byte aligned bias and gamma, so an 8-channel group c
+    // .. c+7 is wholly in or out of range: wave-uniform tests; channels in [N, Npad) have zero
+    // weights and bias, so their accumulators are 0)
     const float inv_n = 1.0f / (float)p.N;
+    float ssm[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float ss = 0.0f;
+    for (int mb = 0; mb < MB; ++mb) ssm[mb] = 0.0f;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) {
+        const int c = nb * 32 + g * 8;
+        if (c >= p.N) continue;
+        const float4 b4 = p.bias ? *(const float4*)(p.bias + c + half * 4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int n = nb * 32 + g * 8 + half * 4 + e;
-            const float v = n < p.N ? acc[nb][mb][g * 4 + e] + (p.bias ? p.bias[n] : 0.0f) : 0.0f;
-            ss = fmaf(v, v, ss);
+            const float v = acc[nb][mb][g * 4 + e] + bv[e];
+            acc[nb][mb][g * 4 + e] = v;
+            ssm[mb] = fmaf(v, v, ssm[mb]);
           }
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float ss = ssm[mb];
       ss += __shfl_xor(ss, 32, 64);
       const float r = rsqrtf(ss * inv_n + p.norm_eps);
       const bool valid = pv[mb];
@@ -44,13 +73,13 @@ __device__ __forceinline__ void conv_epilogue(const ConvProblem& p, floatx16 (&a
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = nb * 32 + g * 8 + half * 4;
-          if (!valid || n >= p.N) continue;
+          if ((nb * 32 + g * 8 >= p.N) || !valid) continue;
           const float4 gm = *(const float4*)(p.norm_gamma + n);
           const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[e] = (acc[nb][mb][g * 4 + e] + (p.bias ? p.bias[n + e] : 0.0f)) * r * gv[e];
+            v[e] = acc[nb][mb][g * 4 + e] * r * gv[e];
             if (p.norm_silu) v[e] = silu_f32(v[e]);
           }
           const int f = p.fbase + p.fmul * tf + p.fstride * (n / p.nsplit);
@@ -77,9 +106,11 @@ __device__ __forceinline__ void conv_epilogue(const ConvProblem& p, floatx16 (&a
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + nb * 32 + g * 8 + half * 4;
         if (!valid || n >= p.N) continue;
+        const float4 b4 = load4(p.bias, n, p.N);
+        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][g * 4 + e] + ((p.bias && n + e < p.N) ? p.bias[n + e] : 0.0f);
+        for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][g * 4 + e] + bv[e];
         // the 4 channels share a frame and are contiguous (nsplit is a multiple of 4)
         const int f = p.fbase + p.fmul * tf + p.fstride * (n / p.nsplit);
         const int nc = n % p.nsplit;

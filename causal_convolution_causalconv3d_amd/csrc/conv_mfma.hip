@@ -38,7 +38,7 @@ constexpr int LDS_ROW = 40;  // bf16 per LDS row: 32 channels + 8 pad (80 bytes:
 // and no pile-up of many lanes on one LDS address (a same-address store serialises).
 __device__ __forceinline__ int pad_slot(int row) { return row * LDS_ROW + 32; }  // in bf16
 
-template <int NB, int MB, int WAVES>
+template <int NB, int MB, int WAVES, bool NORM>
 __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProblem p) {
   constexpr int BN = NB * 32;
   constexpr int BM = WAVES * MB * 32;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
     step(std::integral_constant<int, 5>{}, k + 5);
   }
 
-  conv_epilogue<NB, MB>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
+  conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
 }
 
 // Halo-tile variant for KS x KS spatial taps: KS = 3 (phases == 1, kh == kw == 3, any kt) or
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
 // as in conv_mfma_kernel.
 constexpr int PROW = 40;  // bf16 per patch position: 32 channels + 8 pad
 
-template <int NB, int MB, int WAVES, int KS>
+template <int NB, int MB, int WAVES, int KS, bool NORM>
 __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_kernel(const ConvProblem p) {
   static_assert(KS == 2 || KS == 3, "3x3 taps, or 2x2 phase taps");
   constexpr int SPS = KS * KS;              // steps per stage
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_kernel(const 
   }
   if (g < ng) stage(std::integral_constant<int, 0>{}, g);
 
-  conv_epilogue<NB, MB>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
+  conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
 }
 
 // LDS-DMA variant of the 3x3-tap halo kernel. Same tiles, K order, fragments and epilogue; the
@@ -557,18 +557,22 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_kernel(const 
 // expcnt 6:4, lgkmcnt 11:8; expcnt 7 and lgkmcnt 15 do not wait).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-template <int NB, int MB, int WAVES, int KS>
+template <int NB, int MB, int WAVES, int KS, bool NORM>
 __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(const ConvProblem p) {
   static_assert(KS == 2 || KS == 3, "3x3 taps, or 2x2 phase taps");
   constexpr int SPS = KS * KS;
   // weight fetch distance D (steps ahead), slots NWS (> D, and k mod NWS a compile-time
   // function of the stage parity and the tap), barrier wait window WW = D - 2 steps (must not
   // exceed SPS - 2 so that the patch fetched at step 0 is in place for step SPS - 1)
-  constexpr int D = (SPS == 9) ? 5 : 4, NWS = (SPS == 9) ? 6 : 8, WW = D - 2;
+  // (2x2 taps with 4 waves: D = 3 and 4 slots, so that two workgroups fit in one CU's LDS)
+  constexpr bool SMALL = (SPS == 4 && WAVES == 4);
+  constexpr int D = (SPS == 9) ? 5 : (SMALL ? 3 : 4), NWS = (SPS == 9) ? 6 : (SMALL ? 4 : 8), WW = D - 2;
   static_assert(WW <= SPS - 2 && D < NWS && (2 * SPS) % NWS == 0, "fetch distance, slots and wait window");
   constexpr int BN = NB * 32;
   constexpr int TR = WAVES * MB;
-  constexpr int PR = TR + 2, PC = 34;
+  // patch: the tile with a 1-pixel halo; 2x2 phase taps need one side only (the side set by
+  // the phase), so their patch starts at (h0 - 1 + a, w0 - 1 + b) and is one row and column smaller
+  constexpr int PR = TR + (KS == 3 ? 2 : 1), PC = (KS == 3 ? 34 : 33);
   constexpr int PSLOTS = PR * PC * 5;                                // 16-byte slots of a patch
   constexpr int PIW = (PSLOTS + 64 * WAVES - 1) / (64 * WAVES);      // patch fetches per wave
   constexpr int WSLOTS = BN * 5;                                     // 16-byte slots of a weight step
@@ -638,7 +642,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
     ph[mb] = h0 + r;
     pw[mb] = w0 + l32;
     pv[mb] = (ph[mb] < p.H) & (pw[mb] < p.W);
-    boff[mb] = (uint32_t)((((r + pa) * PC + l32 + pb) * PROW + half * 16) * 2);
+    boff[mb] = (uint32_t)(((r * PC + l32) * PROW + half * 16) * 2);
   }
 
   const int nchunks = p.Cip >> 5;
@@ -659,7 +663,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
     const int j = (i * WAVES + wave) * 64 + lane;
     const int pos = j / 5, part = j - (j / 5) * 5;
     const int pr = pos / PC, pc = pos - (pos / PC) * PC;
-    const int hh = h0 - 1 + pr, ww = w0 - 1 + pc;
+    const int hh = h0 - 1 + pa + pr, ww = w0 - 1 + pb + pc;
     const bool ok = (part < 4) & (pos < PR * PC) & (hh >= 0) & (hh < p.H) & (ww >= 0) & (ww < p.W);
     pgo[i] = ok ? (uint32_t)(((hh * p.W + ww) * p.Ci + part * 8) * 2) : frame_bytes;
     pch[i] = part * 8;
@@ -822,7 +826,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   // fetches past the end (into slots nobody reads) must land before the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  conv_epilogue<NB, MB>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
+  conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
 }
 
 struct ConfigEntry {
@@ -830,21 +834,27 @@ struct ConfigEntry {
   int nb, mb, waves;
   int halo;  // conv_halo_kernel's KS (WAVES*MB rows x 32 columns per tile), or 0
   int time_tiles;  // halo tile order (ConvProblem::time_tiles)
-  void (*kernel)(const ConvProblem);
+  void (*kernel)(const ConvProblem);       // plain epilogue (bias, residual, fp32 planes)
+  void (*kernel_norm)(const ConvProblem);  // fused RMS norm (+ SiLU) epilogue
 };
 
 #define WVD_CONV_CONFIG(NB, MB, W) \
-  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, conv_mfma_kernel<NB, MB, W> }
+  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
+    conv_mfma_kernel<NB, MB, W, true> }
 // 3x3-tap halo convs order tiles time-fastest (measured 2-8% faster than frame-major on every
 // 3x3x3 layer: fewer input re-reads past L2); the phase convs have no temporal taps.
 #define WVD_HALO_CONFIG(NB, MB, W) \
-  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_kernel<NB, MB, W, 3> }
+  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_kernel<NB, MB, W, 3, false>, \
+    conv_halo_kernel<NB, MB, W, 3, true> }
 #define WVD_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_dma_kernel<NB, MB, W, 3> }
+  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_dma_kernel<NB, MB, W, 3, false>, \
+    conv_halo_dma_kernel<NB, MB, W, 3, true> }
 #define WVD_PHASE_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_dma_kernel<NB, MB, W, 2> }
+  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_dma_kernel<NB, MB, W, 2, false>, \
+    conv_halo_dma_kernel<NB, MB, W, 2, true> }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_kernel<NB, MB, W, 2> }
+  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
+    conv_halo_kernel<NB, MB, W, 2, true> }
 
 // Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
 // bigger per-wave tiles at one wave per SIMD: the second wave issues matrix work while the first
@@ -865,6 +875,7 @@ enum ConfigId {
   HALO_DMA_N3_W8,  // HALO_N3_W8 with LDS-DMA staging
   HALO_DMA_N6_W8,  // HALO_N6_W8 with LDS-DMA staging
   PHASE_DMA_N3_W8,  // PHASE_N3_W8 with LDS-DMA staging
+  PHASE_DMA_N3_W4,  // x2 upsampling phases: 96 x (8 rows x 32 columns), two workgroups per CU
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -872,11 +883,12 @@ const ConfigEntry kConfigs[] = {
     WVD_CONV_CONFIG(3, 1, 4),       WVD_CONV_CONFIG(1, 4, 4),       WVD_CONV_CONFIG(3, 2, 8),
     WVD_HALO_CONFIG(6, 1, 8),       WVD_HALO_CONFIG(3, 2, 8),       WVD_HALO_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_CONFIG(3, 2, 8),
-    WVD_HALO_DMA_CONFIG(6, 1, 8),    WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8),
+    WVD_HALO_DMA_CONFIG(6, 1, 8),    WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
 constexpr int kMaxFusedNormN = 192;  // the widest channel tile
+constexpr int round_up_int(int v, int m) { return (v + m - 1) / m * m; }
 
 // Workgroups of a problem: per frame ceil(H*W / BM) position tiles (halo kernels: ceil(H / rows)
 // x ceil(W / 32)), times the channel tiles.
@@ -908,6 +920,7 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   // channels up; at 96 (with the fused norm: a heavy epilogue) the linear kernel's smaller LDS
   // footprint lets workgroups overlap, measured 10 % faster.
   if (phases == 4 && p.kh == 2 && p.kw == 2 && Npad >= 192 && !one_n_tile) return PHASE_DMA_N3_W8;
+  if (phases == 4 && p.kh == 2 && p.kw == 2 && Npad <= 96) return PHASE_DMA_N3_W4;
   const auto fills = [&](int id) { return blocks_for(kConfigs[id], T, H, W, Npad) * phases >= cus; };
   const int n96 = (p.ntaps >= 9 && fills(LIN_N3_M2_W8)) ? LIN_N3_M2_W8 : LIN_N3_W8;
   if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup
@@ -925,7 +938,10 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
 
 }  // namespace
 
-bool conv_can_fuse_norm(int Npad) { return Npad <= kMaxFusedNormN; }
+bool conv_can_fuse_norm(int N, const float* bias, const float* gamma) {
+  const auto a16 = [](const void* q) { return ((uintptr_t)q & 15u) == 0; };
+  return round_up_int(N, 32) <= kMaxFusedNormN && N % 8 == 0 && a16(bias) && a16(gamma) && gamma;
+}
 
 const char* conv_config_name(int id) { return (id >= 0 && id < kNumConfigs) ? kConfigs[id].name : "?"; }
 int conv_config_count() { return kNumConfigs; }
@@ -946,7 +962,8 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   if (p.T == 0 || HW == 0) return hipSuccess;
   // one frame is addressed with 32-bit byte offsets
   if (HW * p.Ci * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  if (p.norm_gamma && (p.Npad > kMaxFusedNormN || p.res || p.y_f32 || p.nsplit != p.N)) return hipErrorInvalidValue;
+  if (p.norm_gamma && (!conv_can_fuse_norm(p.N, p.bias, p.norm_gamma) || p.res || p.y_f32 || p.nsplit != p.N))
+    return hipErrorInvalidValue;
   int id = choose_config(p, p.norm_gamma != nullptr);
   if (force_config >= 0) {
     if (!conv_config_fits(p, force_config)) return hipErrorNotSupported;
@@ -958,7 +975,8 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   if (config_id) *config_id = id;
   ConvProblem q = p;
   q.time_tiles = c.time_tiles;
-  hipLaunchKernelGGL(c.kernel, dim3((unsigned)blocks, 1, p.phases), dim3(c.waves * 64), 0, s, q);
+  hipLaunchKernelGGL(p.norm_gamma ? c.kernel_norm : c.kernel, dim3((unsigned)blocks, 1, p.phases), dim3(c.waves * 64),
+                     0, s, q);
   return hipGetLastError();
 }
 
