@@ -74,16 +74,17 @@ def copy_calibration_run(mib: int) -> None:
 
 
 def kernel_symbol(config: str) -> str:
-    """The kernel's demangled name prefix for a configuration name."""
+    """The demangled name prefix shared by a configuration's kernels (its plain and fused-norm
+    epilogue instantiations)."""
     m = re.fullmatch(r"conv_(mfma|halo|phase_halo|halo_dma|phase_halo_dma)_n(\d+)_m(\d+)_w(\d+)", config)
     if not m:
         raise ValueError(f"unknown conv configuration {config}")
     kind, nb, mb, w = m.groups()
     if kind == "mfma":
-        return f"conv_mfma_kernel<{nb}, {mb}, {w}>"
+        return f"conv_mfma_kernel<{nb}, {mb}, {w}, "
     ks = 2 if kind.startswith("phase") else 3
     base = "conv_halo_dma_kernel" if kind.endswith("dma") else "conv_halo_kernel"
-    return f"{base}<{nb}, {mb}, {w}, {ks}>"
+    return f"{base}<{nb}, {mb}, {w}, {ks}, "
 
 
 def _counter_rows(d: str) -> List[dict]:
