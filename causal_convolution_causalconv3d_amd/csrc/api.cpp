@@ -94,8 +94,8 @@ struct TimingRecord {
 };
 // The memory-bound kernels of the path, timed like the convs (algorithmic bytes: every input
 // element read once, every output element written once).
-enum MemKind { MEM_NORM_SILU = 0, MEM_HEAD_STENCIL = 1, MEM_CONVERT = 2, MEM_KINDS = 3 };
-const char* const kMemKindNames[MEM_KINDS] = {"norm_silu", "head_stencil", "convert"};
+enum MemKind { MEM_NORM_SILU = 0, MEM_HEAD_STENCIL = 1, MEM_CONVERT = 2, MEM_HEAD_FUSED = 3, MEM_KINDS = 4 };
+const char* const kMemKindNames[MEM_KINDS] = {"norm_silu", "head_stencil", "convert", "head_fused"};
 struct LaunchRecord {
   int config;
   float ms;
@@ -1216,6 +1216,25 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
       zbuf = bx[cur ^ 1];
     }
     const int co = d->out_channels;
+    if (head_fused_supported((int)round_up(c, 32))) {
+      // tap conv + stencil in one kernel (no tap planes in memory); reads the activation (and
+      // its history) once, writes co bf16 channels
+      const int slot = p.out_slot;
+      const bf16_t* hist = slot_hist(slot);
+      const int Th = cache->valid[slot];
+      const double hb = (double)(T + std::min(Th, 2)) * H * Wd * c * 2.0 + (double)P * co * 2.0;
+      WVD_TRY(run_mem(MEM_HEAD_FUSED, hb, s, "head launch", [&] {
+        return launch_head_fused(act, hist, Th, (int)T, H, Wd, c, (int)round_up(c, 32), (const bf16_t*)W_(p.out_w),
+                                 F_(p.out_b), co, (bf16_t*)video->data, video->t, (int)frame_offset, s);
+      }));
+      int v = cache->valid[slot];
+      WVD_TRY(update_slot((char*)slot_ptr(slot), v, act, (int)T, p.slots[slot].frame_bytes, s));
+      cache->valid[slot] = v;
+      cache->next_latent += n;
+      cache->next_frame += fr.video;
+      if (first) cache->rule = first_frame_rule != 0;
+      return WVD_OK;
+    }
     float* Z = (float*)zbuf;
     // n = tap*4 + o: each lane's 4 accumulator channels are one tap's 4 colour slots, stored as
     // one float4 into plane `tap`: frame f = t + T*tap of a [9T][H][W][4] tensor

@@ -104,6 +104,12 @@ hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t 
 hipError_t launch_pack_head(const void* w, int w_bf16, int Co, int Ci, int Npad, int Cip, bf16_t* out, hipStream_t s);
 // video[o][fbase + t][h][w] = bias[o] + sum_{j,k} Z[j*3+k][t][h+j-1][w+k-1][o] (zero outside the frame),
 // Z fp32 [9][T][H][W][4] tap planes; video bf16 NCTHW with `frames` frames per channel plane.
+// The head's tap conv and stencil fused (input channels padded to Cip <= 192): x [T][H][W][C]
+// bf16 with Th history frames, packed head weights [64][3][Cip], video NCTHW bf16.
+bool head_fused_supported(int Cip);
+hipError_t launch_head_fused(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
+                             const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
+                             hipStream_t s);
 hipError_t launch_head_stencil(const float* Z, int Co, const float* bias, bf16_t* video, int64_t frames, int fbase,
                                int T, int H, int W, hipStream_t s);
 

@@ -68,12 +68,178 @@ __global__ __launch_bounds__(256) void head_stencil_kernel(const float4* __restr
     if (o < Co) video[(int64_t)o * frames * HW + pix] = (bf16_t)f32_to_bf16(acc[o] + (bias ? bias[o] : 0.0f));
 }
 
+// Fused head: the tap conv and the stencil in one kernel, so the fp32 tap planes never go to
+// memory. A workgroup computes Z (36 tap channels: tap*4 + colour) for a 16 x 32 tile of one
+// frame that overlaps its neighbours by one pixel on every side, keeps Z in LDS, and sums the
+// 9-tap stencil for the 14 x 30 interior straight into the video. Z at positions outside the
+// frame is 0 (their activations read as 0), which is the conv's zero padding. Weights (64 rows:
+// 36 used; 3 temporal taps x Cip channels) stay in LDS for the whole reduction, so the K loop has
+// no barriers; the activation operands come from memory into registers through range-checked
+// buffer loads, one K step ahead. The K order (32-channel chunk outermost, temporal tap inside,
+// K halves in order) is the tap conv's, so Z is the same as the two-kernel path computes.
+constexpr int HF_ROWS = 16, HF_COLS = 32;                      // computed tile
+constexpr int HF_OROWS = HF_ROWS - 2, HF_OCOLS = HF_COLS - 2;   // output tile
+constexpr int HF_N = 64;                                        // Z rows in the matrix-core tile
+constexpr int HF_Z = 36;                                        // Z channels kept
+constexpr int HF_MAXCIP = 192;
+constexpr int HF_WROW = 3 * HF_MAXCIP + 8;  // bf16 per LDS weight row: 1168 bytes, 73 16-byte units (odd)
+constexpr int HF_LDS = (HF_N * HF_WROW * 2 > HF_ROWS * HF_COLS * HF_Z * 4) ? HF_N * HF_WROW * 2
+                                                                          : HF_ROWS * HF_COLS * HF_Z * 4;
+
+__global__ __launch_bounds__(512, 1) void head_fused_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ hist,
+                                                            int Th, int T, int H, int W, int C, int Cip,
+                                                            const bf16_t* __restrict__ wpk, const float* __restrict__ bias,
+                                                            int Co, bf16_t* __restrict__ video, int64_t frames, int fbase) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[HF_LDS];
+  bf16_t* wl = (bf16_t*)lds;   // [64][HF_WROW] during the K loop
+  float* zl = (float*)lds;     // [16][32][36] afterwards
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int numR = (H + HF_OROWS - 1) / HF_OROWS, numC = (W + HF_OCOLS - 1) / HF_OCOLS;
+  const int total = T * numR * numC;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int q8 = total >> 3, r8 = total & 7;
+  const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
+  const int t = lin % T, tile = lin / T;  // time-fastest: a patch serves the temporal taps of neighbours
+  const int rt = tile / numC;
+  const int h0 = rt * HF_OROWS, w0 = (tile - rt * numC) * HF_OCOLS;  // first output pixel
+
+  // weights into LDS: [n][i*Cip + c] from the packed [64][3][Cip]
+  const int wk = 3 * Cip;
+  for (int q = tid; q < HF_N * (wk / 8); q += 512) {
+    const int n = q / (wk / 8), k8 = q - n * (wk / 8);
+    *(u32x4*)(&wl[n * HF_WROW + k8 * 8]) = *(const u32x4*)(wpk + (int64_t)n * wk + k8 * 8);
+  }
+
+  // this lane's positions: tile rows 2*wave + mb (image row h0 - 1 + that), column l32
+  const int64_t frame_elems = (int64_t)H * W * C;
+  const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
+  uint32_t poff[2];
+  bool pin[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int hh = h0 - 1 + 2 * wave + mb, ww = w0 - 1 + l32;
+    pin[mb] = (hh >= 0) & (hh < H) & (ww >= 0) & (ww < W);
+    poff[mb] = pin[mb] ? (uint32_t)(((int64_t)hh * W + ww) * C * 2) : 0u;
+  }
+  const int nchunks = Cip >> 5;
+  const int nk = 3 * nchunks;
+  auto load_step = [&](u32x4 (&dst)[2][2], int s) {
+    const int chunk = s / 3, i = s - chunk * 3;
+    const int sf = t - 2 + i;  // source frame; negative: history
+    const bf16_t* fb = (sf >= 0) ? x + (int64_t)sf * frame_elems
+                                 : ((sf >= -Th) ? hist + (int64_t)(sf + Th) * frame_elems : x);
+    const bool fok = (sf >= -Th) & (s < nk);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)fb, (short)0, fok ? (int)frame_bytes : 0, 0x00020000);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ch = chunk * 32 + half * 16 + q * 8;
+        const int vo = (pin[mb] & (ch < C)) ? (int)(poff[mb] + ch * 2) : (int)frame_bytes;
+        dst[mb][q] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0);
+      }
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
+
+  u32x4 areg[2][2][2];
+  load_step(areg[0], 0);
+  __syncthreads();  // weights in place
+  for (int s = 0; s < nk; s += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int st = s + u;
+      load_step(areg[u ^ 1], st + 1);  // past the end: zeros, never used
+      if (st < nk) {
+        const int chunk = st / 3, i = st - chunk * 3;
+        const int k0 = i * Cip + chunk * 32;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              const u32x4 a = *(const u32x4*)(&wl[(nb * 32 + l32) * HF_WROW + k0 + half * 16 + q * 8]);
+              acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                    __builtin_bit_cast(bf16x8, areg[u][mb][q]),
+                                                                    acc[nb][mb], 0, 0, 0);
+            }
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with the weights: the LDS now takes Z
+
+  // Z[row][col][n] for n < 36 (lane: channels nb*32 + g*8 + half*4 + {0..3} of its position)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    float* zp = zl + ((2 * wave + mb) * HF_COLS + l32) * HF_Z;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = g * 8 + half * 4;
+      *(float4*)(zp + n) = make_float4(acc[0][mb][g * 4], acc[0][mb][g * 4 + 1], acc[0][mb][g * 4 + 2],
+                                       acc[0][mb][g * 4 + 3]);
+    }
+    if (half == 0) *(float4*)(zp + 32) = make_float4(acc[1][mb][0], acc[1][mb][1], acc[1][mb][2], acc[1][mb][3]);
+  }
+  __syncthreads();
+
+  // the stencil: output pixel (h0 + orow, w0 + ocol) sums tap (j, k) of tile position
+  // (orow + j, ocol + k); fp32 sums in (j, k) order, one rounding
+  if (tid < HF_OROWS * HF_OCOLS) {
+    const int orow = tid / HF_OCOLS, ocol = tid - orow * HF_OCOLS;
+    const int h = h0 + orow, w = w0 + ocol;
+    if (h < H && w < W) {
+      float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const float4 z = *(const float4*)(zl + ((orow + j) * HF_COLS + ocol + k) * HF_Z + (j * 3 + k) * 4);
+          a0 += z.x;
+          a1 += z.y;
+          a2 += z.z;
+          a3 += z.w;
+        }
+      const int64_t HW = (int64_t)H * W;
+      const int64_t pix = (int64_t)(fbase + t) * HW + (int64_t)h * W + w;
+      const float av[4] = {a0, a1, a2, a3};
+#pragma unroll
+      for (int o = 0; o < 4; ++o)
+        if (o < Co) video[(int64_t)o * frames * HW + pix] = (bf16_t)f32_to_bf16(av[o] + (bias ? bias[o] : 0.0f));
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pack_head(const void* w, int w_bf16, int Co, int Ci, int Npad, int Cip, bf16_t* out, hipStream_t s) {
   const int64_t n = (int64_t)Npad * 3 * Cip;
   hipLaunchKernelGGL(pack_head_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, w, w_bf16, Co, Ci, Npad,
                      Cip, out);
+  return hipGetLastError();
+}
+
+bool head_fused_supported(int Cip) { return Cip % 32 == 0 && Cip <= HF_MAXCIP; }
+
+hipError_t launch_head_fused(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
+                             const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
+                             hipStream_t s) {
+  if (T == 0 || H == 0 || W == 0) return hipSuccess;
+  if (!head_fused_supported(Cip) || C > Cip || (int64_t)H * W * C * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)T * ((H + HF_OROWS - 1) / HF_OROWS) * ((W + HF_OCOLS - 1) / HF_OCOLS);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(head_fused_kernel, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, Cip, wpk, bias,
+                     Co, video, frames, fbase);
   return hipGetLastError();
 }
 
