@@ -916,11 +916,10 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   const int Npad = p.Npad, phases = p.phases;
   if (Npad <= 32) return LIN_N1_M4_W4;
   if (phases == 1 && p.kh == 3 && p.kw == 3) return (one_n_tile && Npad > 96) ? HALO_DMA_N6_W8 : HALO_DMA_N3_W8;
-  // The phase convs (K = 4 taps x C) have short reductions: the DMA halo kernel wins from 192
-  // channels up; at 96 (with the fused norm: a heavy epilogue) the linear kernel's smaller LDS
-  // footprint lets workgroups overlap, measured 10 % faster.
-  if (phases == 4 && p.kh == 2 && p.kw == 2 && Npad >= 192 && !one_n_tile) return PHASE_DMA_N3_W8;
-  if (phases == 4 && p.kh == 2 && p.kw == 2 && Npad <= 96) return PHASE_DMA_N3_W4;
+  // The phase convs (K = 4 taps x C) have short reductions and heavy epilogues: the 4-wave DMA
+  // halo tile (80 KB of LDS, two workgroups per CU so one's epilogue overlaps the other's matrix
+  // work) measured fastest at 96, 192 and 384 channels (4-13 % over the 8-wave tile).
+  if (phases == 4 && p.kh == 2 && p.kw == 2 && (Npad <= 96 || !one_n_tile)) return PHASE_DMA_N3_W4;
   const auto fills = [&](int id) { return blocks_for(kConfigs[id], T, H, W, Npad) * phases >= cus; };
   const int n96 = (p.ntaps >= 9 && fills(LIN_N3_M2_W8)) ? LIN_N3_M2_W8 : LIN_N3_W8;
   if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup
