@@ -611,18 +611,21 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int phase = blockIdx.z;
-  const int pa = (KS == 2) ? (phase >> 1) : 0;
-  const int pb = (KS == 2) ? (phase & 1) : 0;
-
+  // The x2 phase convs deal their four phases (the fastest index) from the same XCD range: the
+  // four workgroups of a tile run side by side, share its input patch in L2 and write
+  // neighbouring output positions close in time.
+  constexpr int NPH = (KS == 2) ? 4 : 1;
   const int numR = (p.H + TR - 1) / TR, numC = (p.W + 31) / 32;
   const int tpf = numR * numC;
   const int numN = (p.Npad + BN - 1) / BN;
-  const int total = p.T * tpf * numN;
+  const int total = p.T * tpf * numN * NPH;
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
   const int q8 = total >> 3, r8 = total & 7;
-  const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
+  const int lin_p = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
+  const int phase = lin_p % NPH, lin = lin_p / NPH;
+  const int pa = (KS == 2) ? (phase >> 1) : 0;
+  const int pb = (KS == 2) ? (phase & 1) : 0;
   const int mt = lin / numN, nt = lin - (lin / numN) * numN;
   const int n0 = nt * BN;
   const int tf = p.time_tiles ? mt % p.T : mt / tpf;
@@ -834,26 +837,27 @@ struct ConfigEntry {
   int nb, mb, waves;
   int halo;  // conv_halo_kernel's KS (WAVES*MB rows x 32 columns per tile), or 0
   int time_tiles;  // halo tile order (ConvProblem::time_tiles)
+  int phase_in_x;  // the x2 phases are part of the linear block index (grid z = 1)
   void (*kernel)(const ConvProblem);       // plain epilogue (bias, residual, fp32 planes)
   void (*kernel_norm)(const ConvProblem);  // fused RMS norm (+ SiLU) epilogue
 };
 
 #define WVD_CONV_CONFIG(NB, MB, W) \
-  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
+  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
     conv_mfma_kernel<NB, MB, W, true> }
 // 3x3-tap halo convs order tiles time-fastest (measured 2-8% faster than frame-major on every
 // 3x3x3 layer: fewer input re-reads past L2); the phase convs have no temporal taps.
 #define WVD_HALO_CONFIG(NB, MB, W) \
-  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_kernel<NB, MB, W, 3, false>, \
+  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, conv_halo_kernel<NB, MB, W, 3, false>, \
     conv_halo_kernel<NB, MB, W, 3, true> }
 #define WVD_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, conv_halo_dma_kernel<NB, MB, W, 3, false>, \
+  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, conv_halo_dma_kernel<NB, MB, W, 3, false>, \
     conv_halo_dma_kernel<NB, MB, W, 3, true> }
 #define WVD_PHASE_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_dma_kernel<NB, MB, W, 2, false>, \
+  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, conv_halo_dma_kernel<NB, MB, W, 2, false>, \
     conv_halo_dma_kernel<NB, MB, W, 2, true> }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
+  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
     conv_halo_kernel<NB, MB, W, 2, true> }
 
 // Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
@@ -974,8 +978,10 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   if (config_id) *config_id = id;
   ConvProblem q = p;
   q.time_tiles = c.time_tiles;
-  hipLaunchKernelGGL(p.norm_gamma ? c.kernel_norm : c.kernel, dim3((unsigned)blocks, 1, p.phases), dim3(c.waves * 64),
-                     0, s, q);
+  const int64_t gx = c.phase_in_x ? blocks * p.phases : blocks;
+  if (gx > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(p.norm_gamma ? c.kernel_norm : c.kernel, dim3((unsigned)gx, 1, c.phase_in_x ? 1 : p.phases),
+                     dim3(c.waves * 64), 0, s, q);
   return hipGetLastError();
 }
 
