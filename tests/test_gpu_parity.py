@@ -387,6 +387,28 @@ def test_small_decoder_matches_oracle_and_is_pass_size_invariant(rule):
     assert q >= 55.0
 
 
+WIDE_TAIL_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 32, 224))
+
+
+def test_wide_last_stage_decoder_matches_oracle():
+    """A last stage wider than one fused-epilogue tile (224 channels): norm_out runs as its own
+    pass and the head as the tap-plane conv + stencil kernels (the fused paths' fallbacks)."""
+    hw = (2, 3)
+    z, params = wl.decoder_weights(WIDE_TAIL_GPU, seed=54, latent_frames=3, latent_hw=hw)
+    ref = oracle.decode(z[0], oracle.as_numpy_params(params), WIDE_TAIL_GPU, frames_per_pass=3)
+    dec = _gpu_decoder(WIDE_TAIL_GPU, params, hw)
+    zd = z.to(torch.bfloat16).cuda()
+    v3 = dec.decode(zd, frames_per_pass=3)
+    v1 = dec.decode(zd, frames_per_pass=1)
+    torch.cuda.synchronize()
+    assert torch.equal(v1, v3)
+    got = v3[0].float().cpu().numpy()
+    assert got.shape == ref.shape
+    q = psnr(got, ref)
+    log(f"wide-tail decoder psnr {q:.2f} dB")
+    assert q >= 55.0
+
+
 def test_full_channel_decoder_small_latent_matches_oracle():
     spec = wl.FULL_DECODER
     hw = (3, 5)
