@@ -70,6 +70,7 @@ struct ConvProblem {
   float norm_eps;
   int norm_silu;
   int time_tiles;  // set by the launcher: the halo kernel's tile order
+  int staged;      // set by the launcher: store the output through LDS (see conv_epilogue_staged)
 };
 
 // force_config >= 0 runs that configuration (hipErrorNotSupported when it cannot run p).

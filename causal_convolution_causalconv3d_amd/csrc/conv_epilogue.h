@@ -140,4 +140,148 @@ __device__ __forceinline__ void conv_epilogue(const ConvProblem& p, floatx16 (&a
   }
 }
 
+// Output index of channel n (a multiple of 4) at output row orow, column ocol of frame tf.
+__device__ __forceinline__ int64_t out_index(const ConvProblem& p, int tf, int n, int orow, int ocol) {
+  const int fs = p.fstride ? n / p.nsplit : 0;
+  const int f = p.fbase + p.fmul * tf + p.fstride * fs;
+  const int nc = n - fs * p.nsplit;
+  return (((int64_t)f * p.Ho + orow) * p.Wo + ocol) * p.nsplit + nc;
+}
+
+// Epilogue through LDS (p.staged: bf16 output, N and nsplit multiples of 8, y and res 16-byte
+// aligned). The accumulator layout scatters a store instruction over 32 positions (8 bytes per
+// lane, one position's channels 2 * nsplit bytes apart), so instead each wave writes its values
+// into a private LDS area, one row of 32 positions and up to 96 channels at a time, and then
+// stores 16 contiguous bytes per lane, consecutive lanes on consecutive addresses. The residual
+// comes in the same coalesced way and is added in fp32 before the single rounding. `stage` holds
+// 32 * PS bytes for this wave alone (PS = 16-byte padded position stride); the same values and
+// rounding as conv_epilogue.
+template <int NB>
+struct StagedShape {
+  static constexpr int NBP = NB >= 3 ? 3 : NB;  // 32-channel blocks per pass
+  static constexpr int CHP = NBP * 4;           // 16-byte chunks of a position in one pass
+  static constexpr int PS = NBP * 64 + 16;      // LDS bytes per position
+  static constexpr int CPL = 32 * CHP / 64;     // chunks per lane and pass
+  static constexpr int BYTES = 32 * PS;         // one wave's LDS area
+  static_assert(NB % NBP == 0 && (32 * CHP) % 64 == 0, "pass shape");
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NB, int MB, bool NORM>
+__device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, floatx16 (&acc)[NB][MB], const int (&ph)[MB],
+                                                     int w0, int tf, int n0, int pa, int pb, int lane, char* stage) {
+  using S = StagedShape<NB>;
+  constexpr int NPG = NB / S::NBP;  // passes per row
+  const int half = lane >> 5, l32 = lane & 31;
+  float rs[MB];  // the norm's 1 / rms per row
+  if constexpr (NORM) {
+    // bias, then the per-position sum of squares over all channels (see conv_epilogue)
+    const float inv_n = 1.0f / (float)p.N;
+    float ssm[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) ssm[mb] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = nb * 32 + g * 8;
+        if (c >= p.N) continue;
+        const float4 b4 = p.bias ? *(const float4*)(p.bias + c + half * 4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = acc[nb][mb][g * 4 + e] + bv[e];
+            acc[nb][mb][g * 4 + e] = v;
+            ssm[mb] = fmaf(v, v, ssm[mb]);
+          }
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const float ss = ssm[mb] + __shfl_xor(ssm[mb], 32, 64);
+      rs[mb] = rsqrtf(ss * inv_n + p.norm_eps);
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (ph[mb] >= p.H) continue;  // the whole row is outside the frame (wave-uniform)
+    const int orow = p.hmul * ph[mb] + pa;
+#pragma unroll
+    for (int pg = 0; pg < NPG; ++pg) {
+      const int cb = n0 + pg * S::NBP * 32;
+      if (cb >= p.N) continue;
+      __builtin_amdgcn_sched_barrier(0);
+      if (!NORM && p.res) {
+        uint4 r[S::CPL];
+#pragma unroll
+        for (int i = 0; i < S::CPL; ++i) {
+          const int j = i * 64 + lane, q = j / S::CHP, c = j - (j / S::CHP) * S::CHP;
+          const int n = cb + c * 8, w = w0 + q;
+          r[i] = (w < p.W && n < p.N) ? *(const uint4*)(p.res + out_index(p, tf, n, orow, p.wmul * w + pb))
+                                      : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < S::CPL; ++i) {
+          const int j = i * 64 + lane, q = j / S::CHP, c = j - (j / S::CHP) * S::CHP;
+          *(uint4*)(stage + q * S::PS + c * 16) = r[i];
+        }
+        wave_lds_sync();
+      }
+#pragma unroll
+      for (int nl = 0; nl < S::NBP; ++nl) {
+        const int nb = pg * S::NBP + nl;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + nb * 32 + g * 8 + half * 4;
+          if (n0 + nb * 32 + g * 8 >= p.N) continue;  // N % 8 == 0: wave-uniform
+          float v[4];
+          if constexpr (NORM) {
+            const float4 gm = *(const float4*)(p.norm_gamma + n);
+            const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = acc[nb][mb][g * 4 + e] * rs[mb] * gv[e];
+              if (p.norm_silu) v[e] = silu_f32(v[e]);
+            }
+          } else {
+            const float4 b4 = load4(p.bias, n, p.N);
+            const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][g * 4 + e] + bv[e];
+          }
+          uint2* a = (uint2*)(stage + l32 * S::PS + (nl * 32 + g * 8 + half * 4) * 2);
+          if (!NORM && p.res) {
+            const uint2 r = *a;
+            v[0] += bf16_lo(r.x);
+            v[1] += bf16_hi(r.x);
+            v[2] += bf16_lo(r.y);
+            v[3] += bf16_hi(r.y);
+          }
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *a = o;
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < S::CPL; ++i) {
+        const int j = i * 64 + lane, q = j / S::CHP, c = j - (j / S::CHP) * S::CHP;
+        const int n = cb + c * 8, w = w0 + q;
+        const uint4 o = *(const uint4*)(stage + q * S::PS + c * 16);
+        if (w < p.W && n < p.N) *(uint4*)((bf16_t*)p.y + out_index(p, tf, n, orow, p.wmul * w + pb)) = o;
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
 }  // namespace wvd

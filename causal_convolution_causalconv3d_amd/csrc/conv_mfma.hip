@@ -829,7 +829,17 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
   // fetches past the end (into slots nobody reads) must land before the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
+  if (p.staged) {
+    // Every wave's fetches have landed and the patch is read no more: the two patch buffers
+    // become the waves' output staging areas (half of the waves in each).
+    __builtin_amdgcn_s_barrier();
+    constexpr int SW = WAVES / 2;
+    static_assert(SW * StagedShape<NB>::BYTES <= PBYTES, "staging areas");
+    char* st = (wave < SW ? (char*)lds_p0 : (char*)lds_p1) + (wave % SW) * StagedShape<NB>::BYTES;
+    conv_epilogue_staged<NB, MB, NORM>(p, acc, ph, w0, tf, n0, pa, pb, lane, st);
+  } else {
+    conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
+  }
 }
 
 struct ConfigEntry {
@@ -838,26 +848,27 @@ struct ConfigEntry {
   int halo;  // conv_halo_kernel's KS (WAVES*MB rows x 32 columns per tile), or 0
   int time_tiles;  // halo tile order (ConvProblem::time_tiles)
   int phase_in_x;  // the x2 phases are part of the linear block index (grid z = 1)
+  int staged;      // the kernel has the LDS-staged epilogue (used when ConvProblem allows it)
   void (*kernel)(const ConvProblem);       // plain epilogue (bias, residual, fp32 planes)
   void (*kernel_norm)(const ConvProblem);  // fused RMS norm (+ SiLU) epilogue
 };
 
 #define WVD_CONV_CONFIG(NB, MB, W) \
-  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
+  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
     conv_mfma_kernel<NB, MB, W, true> }
 // 3x3-tap halo convs order tiles time-fastest (measured 2-8% faster than frame-major on every
 // 3x3x3 layer: fewer input re-reads past L2); the phase convs have no temporal taps.
 #define WVD_HALO_CONFIG(NB, MB, W) \
-  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, conv_halo_kernel<NB, MB, W, 3, false>, \
+  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 0, conv_halo_kernel<NB, MB, W, 3, false>, \
     conv_halo_kernel<NB, MB, W, 3, true> }
 #define WVD_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, conv_halo_dma_kernel<NB, MB, W, 3, false>, \
+  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, conv_halo_dma_kernel<NB, MB, W, 3, false>, \
     conv_halo_dma_kernel<NB, MB, W, 3, true> }
 #define WVD_PHASE_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, conv_halo_dma_kernel<NB, MB, W, 2, false>, \
+  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, conv_halo_dma_kernel<NB, MB, W, 2, false>, \
     conv_halo_dma_kernel<NB, MB, W, 2, true> }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
+  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
     conv_halo_kernel<NB, MB, W, 2, true> }
 
 // Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
@@ -978,6 +989,8 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   if (config_id) *config_id = id;
   ConvProblem q = p;
   q.time_tiles = c.time_tiles;
+  q.staged = c.staged && !p.y_f32 && p.N % 8 == 0 && p.nsplit % 8 == 0 && ((uintptr_t)p.y & 15) == 0 &&
+             ((uintptr_t)p.res & 15) == 0;
   const int64_t gx = c.phase_in_x ? blocks * p.phases : blocks;
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(p.norm_gamma ? c.kernel_norm : c.kernel, dim3((unsigned)gx, 1, c.phase_in_x ? 1 : p.phases),
