@@ -557,15 +557,21 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_kernel(const 
 // expcnt 6:4, lgkmcnt 11:8; expcnt 7 and lgkmcnt 15 do not wait).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
+// Waves per SIMD a DMA kernel is compiled for: two, or four for the one-row phase tiles (their
+// light main loop leaves the SIMDs to the epilogue's vector work, which other waves then overlap).
+template <int MB, int KS>
+constexpr int dma_waves_per_simd() { return (KS == 2 && MB == 1) ? 4 : 2; }
+
 template <int NB, int MB, int WAVES, int KS, bool NORM>
-__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(const ConvProblem p) {
+__global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAVES)) void conv_halo_dma_kernel(
+    const ConvProblem p) {
   static_assert(KS == 2 || KS == 3, "3x3 taps, or 2x2 phase taps");
   constexpr int SPS = KS * KS;
   // weight fetch distance D (steps ahead), slots NWS (> D, and k mod NWS a compile-time
   // function of the stage parity and the tap), barrier wait window WW = D - 2 steps (must not
   // exceed SPS - 2 so that the patch fetched at step 0 is in place for step SPS - 1)
-  // (2x2 taps with 4 waves: D = 3 and 4 slots, so that two workgroups fit in one CU's LDS)
-  constexpr bool SMALL = (SPS == 4 && WAVES == 4);
+  // (2x2 taps on 8-row tiles: D = 3 and 4 slots, so that two workgroups fit in one CU's LDS)
+  constexpr bool SMALL = (SPS == 4 && WAVES * MB == 8);
   constexpr int D = (SPS == 9) ? 5 : (SMALL ? 3 : 4), NWS = (SPS == 9) ? 6 : (SMALL ? 4 : 8), WW = D - 2;
   static_assert(WW <= SPS - 2 && D < NWS && (2 * SPS) % NWS == 0, "fetch distance, slots and wait window");
   constexpr int BN = NB * 32;
@@ -833,9 +839,17 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_dma_kernel(co
     // Every wave's fetches have landed and the patch is read no more: the two patch buffers
     // become the waves' output staging areas (half of the waves in each).
     __builtin_amdgcn_s_barrier();
-    constexpr int SW = WAVES / 2;
-    static_assert(SW * StagedShape<NB>::BYTES <= PBYTES, "staging areas");
-    char* st = (wave < SW ? (char*)lds_p0 : (char*)lds_p1) + (wave % SW) * StagedShape<NB>::BYTES;
+    // (as many areas as fit in each patch buffer, the rest in weight slots, all idle now)
+    constexpr int SB = StagedShape<NB>::BYTES, PCAP = PBYTES / SB, WCAP = WBYTES / SB;
+    static_assert(2 * PCAP + 2 * WCAP >= WAVES, "staging areas");
+    char* st;
+    if (wave < PCAP) st = (char*)lds_p0 + wave * SB;
+    else if (wave < 2 * PCAP) st = (char*)lds_p1 + (wave - PCAP) * SB;
+    else {
+      const int r = wave - 2 * PCAP, q = r % (WCAP > 0 ? WCAP : 1);
+      char* w = (r / (WCAP > 0 ? WCAP : 1) == 0) ? (char*)wslot(I0{}) : (char*)wslot(I1{});
+      st = w + q * SB;
+    }
     conv_epilogue_staged<NB, MB, NORM>(p, acc, ph, w0, tf, n0, pa, pb, lane, st);
   } else {
     conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
@@ -891,6 +905,7 @@ enum ConfigId {
   HALO_DMA_N6_W8,  // HALO_N6_W8 with LDS-DMA staging
   PHASE_DMA_N3_W8,  // PHASE_N3_W8 with LDS-DMA staging
   PHASE_DMA_N3_W4,  // x2 upsampling phases: 96 x (8 rows x 32 columns), two workgroups per CU
+  PHASE_DMA_N3_M1_W8,  // the same tile, one row per wave: two 8-wave workgroups per CU
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -899,6 +914,7 @@ const ConfigEntry kConfigs[] = {
     WVD_HALO_CONFIG(6, 1, 8),       WVD_HALO_CONFIG(3, 2, 8),       WVD_HALO_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_CONFIG(3, 2, 8),
     WVD_HALO_DMA_CONFIG(6, 1, 8),    WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
+    WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -931,10 +947,13 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   const int Npad = p.Npad, phases = p.phases;
   if (Npad <= 32) return LIN_N1_M4_W4;
   if (phases == 1 && p.kh == 3 && p.kw == 3) return (one_n_tile && Npad > 96) ? HALO_DMA_N6_W8 : HALO_DMA_N3_W8;
-  // The phase convs (K = 4 taps x C) have short reductions and heavy epilogues: the 4-wave DMA
-  // halo tile (80 KB of LDS, two workgroups per CU so one's epilogue overlaps the other's matrix
-  // work) measured fastest at 96, 192 and 384 channels (4-13 % over the 8-wave tile).
-  if (phases == 4 && p.kh == 2 && p.kw == 2 && (Npad <= 96 || !one_n_tile)) return PHASE_DMA_N3_W4;
+  // The phase convs (K = 4 taps x C) have short reductions and heavy epilogues, so they run 8-row
+  // DMA halo tiles with 80 KB of LDS, two workgroups per CU, whose epilogues overlap other waves'
+  // matrix work: one row per wave (four waves per SIMD) measured fastest at 96 and 192 channels
+  // (5-9 % over two rows per wave on 4 waves), two rows per wave at 384 (8 %).
+  if (phases == 4 && p.kh == 2 && p.kw == 2 && (Npad <= 96 || (!one_n_tile && Npad <= 192)))
+    return PHASE_DMA_N3_M1_W8;
+  if (phases == 4 && p.kh == 2 && p.kw == 2 && !one_n_tile) return PHASE_DMA_N3_W4;
   const auto fills = [&](int id) { return blocks_for(kConfigs[id], T, H, W, Npad) * phases >= cus; };
   const int n96 = (p.ntaps >= 9 && fills(LIN_N3_M2_W8)) ? LIN_N3_M2_W8 : LIN_N3_W8;
   if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup
