@@ -19,6 +19,15 @@ __device__ __forceinline__ float4 load4(const float* v, int n, int N) {
   return r;
 }
 
+// A per-channel array pointer the compiler must treat as new at each call: the epilogue runs
+// once per tile inside a tile loop, and loads of bias and gamma hoisted out of that loop would
+// hold their registers through the whole reduction.
+template <typename T>
+__device__ __forceinline__ const T* opaque(const T* ptr) {
+  asm volatile("" : "+s"(ptr));
+  return ptr;
+}
+
 // NORM selects the fused RMS norm (+ SiLU) epilogue (p.norm_gamma set), instantiated separately so
 // that its registers do not weigh on the plain kernels. The lane holds, per (nb, mb, g), channels n0 + nb*32 + g*8 + half*4 + {0..3} of position
 // (ph[mb], pw[mb]) of frame tf (valid when pv[mb]); (pa, pb) is the output phase. Scheduling
@@ -28,6 +37,9 @@ template <int NB, int MB, bool NORM>
 __device__ __forceinline__ void conv_epilogue(const ConvProblem& p, floatx16 (&acc)[NB][MB], const int (&ph)[MB],
                                               const int (&pw)[MB], const bool (&pv)[MB], int tf, int n0, int pa,
                                               int pb, int half) {
+  const float* bias = opaque(p.bias);
+  const float* gamma = opaque(p.norm_gamma);
+  asm volatile("" : "+v"(half));
   if constexpr (NORM) {
     // Fused channel RMS norm (+ SiLU) of the conv output: the workgroup holds every channel of
     // its positions (one N tile), split between lanes l and l ^ 32, so the per-position sum of
@@ -47,7 +59,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvProblem& p, floatx16 (&a
       for (int g = 0; g < 4; ++g) {
         const int c = nb * 32 + g * 8;
         if (c >= p.N) continue;
-        const float4 b4 = p.bias ? *(const float4*)(p.bias + c + half * 4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float4 b4 = bias ? *(const float4*)(bias + c + half * 4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -74,7 +86,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvProblem& p, floatx16 (&a
         for (int g = 0; g < 4; ++g) {
           const int n = nb * 32 + g * 8 + half * 4;
           if ((nb * 32 + g * 8 >= p.N) || !valid) continue;
-          const float4 gm = *(const float4*)(p.norm_gamma + n);
+          const float4 gm = *(const float4*)(gamma + n);
           const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
           float v[4];
 #pragma unroll
@@ -106,7 +118,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvProblem& p, floatx16 (&a
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + nb * 32 + g * 8 + half * 4;
         if (!valid || n >= p.N) continue;
-        const float4 b4 = load4(p.bias, n, p.N);
+        const float4 b4 = load4(bias, n, p.N);
         const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
         float v[4];
 #pragma unroll
@@ -155,15 +167,15 @@ __device__ __forceinline__ int64_t out_index(const ConvProblem& p, int tf, int n
 // stores 16 contiguous bytes per lane, consecutive lanes on consecutive addresses. The residual
 // comes in the same coalesced way and is added in fp32 before the single rounding. `stage` holds
 // 32 * PS bytes for this wave alone (PS = 16-byte padded position stride); the same values and
-// rounding as conv_epilogue.
-template <int NB>
+// rounding as conv_epilogue. A pass covers NBP 32-channel blocks (NBP divides NB).
+template <int NBP_>
 struct StagedShape {
-  static constexpr int NBP = NB >= 3 ? 3 : NB;  // 32-channel blocks per pass
+  static constexpr int NBP = NBP_;              // 32-channel blocks per pass
   static constexpr int CHP = NBP * 4;           // 16-byte chunks of a position in one pass
   static constexpr int PS = NBP * 64 + 16;      // LDS bytes per position
   static constexpr int CPL = 32 * CHP / 64;     // chunks per lane and pass
   static constexpr int BYTES = 32 * PS;         // one wave's LDS area
-  static_assert(NB % NBP == 0 && (32 * CHP) % 64 == 0, "pass shape");
+  static_assert((32 * CHP) % 64 == 0, "pass shape");
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -172,10 +184,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NB, int MB, bool NORM>
+template <int NB, int MB, bool NORM, int NBP>
 __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, floatx16 (&acc)[NB][MB], const int (&ph)[MB],
                                                      int w0, int tf, int n0, int pa, int pb, int lane, char* stage) {
-  using S = StagedShape<NB>;
+  const float* bias = opaque(p.bias);
+  const float* gamma = opaque(p.norm_gamma);
+  asm volatile("" : "+v"(lane));  // (the chunk indices below are per call, not hoisted)
+  using S = StagedShape<NBP>;
+  static_assert(NB % NBP == 0, "pass shape");
   constexpr int NPG = NB / S::NBP;  // passes per row
   const int half = lane >> 5, l32 = lane & 31;
   float rs[MB];  // the norm's 1 / rms per row
@@ -192,7 +208,7 @@ __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, float
       for (int g = 0; g < 4; ++g) {
         const int c = nb * 32 + g * 8;
         if (c >= p.N) continue;
-        const float4 b4 = p.bias ? *(const float4*)(p.bias + c + half * 4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float4 b4 = bias ? *(const float4*)(bias + c + half * 4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -244,7 +260,7 @@ __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, float
           if (n0 + nb * 32 + g * 8 >= p.N) continue;  // N % 8 == 0: wave-uniform
           float v[4];
           if constexpr (NORM) {
-            const float4 gm = *(const float4*)(p.norm_gamma + n);
+            const float4 gm = *(const float4*)(gamma + n);
             const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -252,7 +268,7 @@ __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, float
               if (p.norm_silu) v[e] = silu_f32(v[e]);
             }
           } else {
-            const float4 b4 = load4(p.bias, n, p.N);
+            const float4 b4 = load4(bias, n, p.N);
             const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = acc[nb][mb][g * 4 + e] + bv[e];

@@ -585,6 +585,13 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
   constexpr int WIW = (WSLOTS + 64 * WAVES - 1) / (64 * WAVES);      // weight fetches per wave
   constexpr int PBYTES = PIW * WAVES * 1024, WBYTES = WIW * WAVES * 1024;
   static_assert(2 * PBYTES + NWS * WBYTES <= 163840, "LDS");
+  // Output staging at a tile's end (conv_epilogue_staged): the patch buffer of the tile's last
+  // stage is idle (the other one holds the next tile's first patch, possibly still in flight).
+  // NBP: the widest pass (96, 64 or 32 channels) whose per-wave areas all fit in it. (One known
+  // LDS array, so the compiler's waits before the staging accesses do not cover the prefetch.)
+  constexpr auto staging_fits = [](int nbp) constexpr { return PBYTES / (32 * (nbp * 64 + 16)) >= WAVES; };
+  constexpr int NBP = (NB % 3 == 0 && staging_fits(3)) ? 3 : ((NB % 2 == 0 && staging_fits(2)) ? 2 : 1);
+  static_assert(staging_fits(NBP), "staging areas");
   __shared__ __attribute__((aligned(16))) bf16_t lds_p0[PBYTES / 2];
   __shared__ __attribute__((aligned(16))) bf16_t lds_p1[PBYTES / 2];
   __shared__ __attribute__((aligned(16))) bf16_t lds_w0[WBYTES / 2];
@@ -611,101 +618,122 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
     if constexpr (decltype(I)::value == 0) return lds_p0;
     else return lds_p1;
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  // The x2 phase convs deal their four phases (the fastest index) from the same XCD range: the
-  // four workgroups of a tile run side by side, share its input patch in L2 and write
-  // neighbouring output positions close in time.
+
+  // Walking several tiles per workgroup keeps the tile loop's state live through the epilogue,
+  // which the fused-norm epilogue cannot afford without spilling; those kernels take one tile.
+  constexpr bool PERSIST = !NORM;
+  // Tiles. The x2 phase convs deal their four phases as the fastest index: the four tiles of a
+  // position run side by side, share its input patch in L2 and write neighbouring outputs close
+  // in time. Each XCD owns a contiguous range of tiles (workgroup b runs on XCD b % 8); within
+  // it workgroup `local` takes tiles local, local + G8, local + 2 G8, ... (G8 workgroups per XCD,
+  // gridDim.x a multiple of 8), so an XCD always works on a window of neighbouring tiles. With
+  // more than one tile per workgroup, the first stage of the next tile (its patch and the
+  // weights of its first D steps) is fetched during the last stage of the current one, and its
+  // matrix work starts right after the epilogue, while that epilogue's stores drain.
   constexpr int NPH = (KS == 2) ? 4 : 1;
   const int numR = (p.H + TR - 1) / TR, numC = (p.W + 31) / 32;
   const int tpf = numR * numC;
   const int numN = (p.Npad + BN - 1) / BN;
   const int total = p.T * tpf * numN * NPH;
-  const int b = blockIdx.x;
-  const int xcd = b & 7, local = b >> 3;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, G8 = gridDim.x >> 3;
   const int q8 = total >> 3, r8 = total & 7;
-  const int lin_p = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
-  const int phase = lin_p % NPH, lin = lin_p / NPH;
-  const int pa = (KS == 2) ? (phase >> 1) : 0;
-  const int pb = (KS == 2) ? (phase & 1) : 0;
-  const int mt = lin / numN, nt = lin - (lin / numN) * numN;
-  const int n0 = nt * BN;
-  const int tf = p.time_tiles ? mt % p.T : mt / tpf;
-  const int rem = p.time_tiles ? mt / p.T : mt - tf * tpf;
-  const int rt = rem / numC;
-  const int h0 = rt * TR, w0 = (rem - rt * numC) * 32;
+  const int xs = xcd * q8 + (xcd < r8 ? xcd : r8), xl = q8 + (xcd < r8 ? 1 : 0);
+  if (local >= xl) return;  // no tile for this workgroup (uniform)
+  struct Tile {
+    int tf, h0, w0, n0, phase;
+  };
+  auto decode = [&](int it) -> Tile {
+    const int lin_p = xs + it;
+    const int phase = lin_p % NPH, lin = lin_p / NPH;
+    const int mt = lin / numN, nt = lin - (lin / numN) * numN;
+    const int tf = p.time_tiles ? mt % p.T : mt / tpf;
+    const int rem = p.time_tiles ? mt / p.T : mt - tf * tpf;
+    const int rt = rem / numC;
+    return {tf, rt * TR, (rem - rt * numC) * 32, nt * BN, phase};
+  };
   const int dt0 = -2 * (p.kt >> 1);
-
-  // operand of tap (0, 0): patch position (r + 1 + dh0, l32 + 1 + dw0), first tap offset
-  // (-1, -1), or (a - 1, b - 1) for phase (a, b) of the x2 upsampling
-  int ph[MB], pw[MB];
-  bool pv[MB];
-  uint32_t boff[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int r = wave * MB + mb;
-    ph[mb] = h0 + r;
-    pw[mb] = w0 + l32;
-    pv[mb] = (ph[mb] < p.H) & (pw[mb] < p.W);
-    boff[mb] = (uint32_t)(((r * PC + l32) * PROW + half * 16) * 2);
-  }
-
   const int nchunks = p.Cip >> 5;
   const int ng = nchunks * p.kt;
   const int64_t frame_elems = (int64_t)p.H * p.W * p.Ci;
   const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
   const int64_t wrow = (int64_t)p.ntaps * p.Cip;
-  const bf16_t* wbase = p.wpk + ((int64_t)phase * p.Npad + n0) * wrow;
-  const int wrows = min(BN, p.Npad - n0);
-  const uint32_t wbytes = (uint32_t)((int64_t)(p.Npad - n0) * wrow * 2);
+  // the tile's packed weight rows (phase, n0 ..): rows past Npad lie past the range and read 0
+  auto weight_rsrc = [&](const Tile& t) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(p.wpk + ((int64_t)t.phase * p.Npad + t.n0) * wrow), (short)0,
+                                             (int)((int64_t)(p.Npad - t.n0) * wrow * 2), 0x00020000);
+  };
 
+  // B operand of tap (0, 0): patch position (r + 1 + dh0, l32 + 1 + dw0) (tile independent)
+  uint32_t boff[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    boff[mb] = (uint32_t)((((wave * MB + mb) * PC + l32) * PROW + half * 16) * 2);
   // This lane's patch slots: byte offset in a frame for chunk 0 (or frame_bytes: always zero)
   // and the slot's channel group (for the Ci tail of the last chunk).
   uint32_t pgo[PIW];
   int pch[PIW];
+  // (recomputed from an opaque copy of the thread index at each tile: hoisting the
+  // tile-independent part out of the tile loop would hold 2 * PIW more registers through it)
+  auto patch_offsets = [&](const Tile& t) __attribute__((always_inline)) {
+    const int pa = (KS == 2) ? (t.phase >> 1) : 0, pb = (KS == 2) ? (t.phase & 1) : 0;
+    int ltid = tid;
+    asm volatile("" : "+v"(ltid));
 #pragma unroll
-  for (int i = 0; i < PIW; ++i) {
-    const int j = (i * WAVES + wave) * 64 + lane;
-    const int pos = j / 5, part = j - (j / 5) * 5;
-    const int pr = pos / PC, pc = pos - (pos / PC) * PC;
-    const int hh = h0 - 1 + pa + pr, ww = w0 - 1 + pb + pc;
-    const bool ok = (part < 4) & (pos < PR * PC) & (hh >= 0) & (hh < p.H) & (ww >= 0) & (ww < p.W);
-    pgo[i] = ok ? (uint32_t)(((hh * p.W + ww) * p.Ci + part * 8) * 2) : frame_bytes;
-    pch[i] = part * 8;
-  }
-  // This lane's weight slots: byte offset of (row, 8-channel group) in the tile's packed rows,
-  // or wbytes (always zero) for pads and slots past the rows.
+    for (int i = 0; i < PIW; ++i) {
+      const int j = i * WAVES * 64 + ltid;
+      const int pos = j / 5, part = j - (j / 5) * 5;
+      const int pr = pos / PC, pc = pos - (pos / PC) * PC;
+      const int hh = t.h0 - 1 + pa + pr, ww = t.w0 - 1 + pb + pc;
+      const bool ok = (part < 4) & (pos < PR * PC) & (hh >= 0) & (hh < p.H) & (ww >= 0) & (ww < p.W);
+      pgo[i] = ok ? (uint32_t)(((hh * p.W + ww) * p.Ci + part * 8) * 2) : frame_bytes;
+      pch[i] = part * 8;
+    }
+  };
+  // This lane's weight slots: byte offset of (row, 8-channel group) in the packed rows; pads
+  // read past any tile's range (zero).
   uint32_t wgo[WIW];
 #pragma unroll
   for (int i = 0; i < WIW; ++i) {
     const int j = (i * WAVES + wave) * 64 + lane;
     const int row = j / 5, part = j - (j / 5) * 5;
-    wgo[i] = ((part < 4) & (row < wrows)) ? (uint32_t)((row * wrow + part * 8) * 2) : wbytes;
+    wgo[i] = (part < 4) ? (uint32_t)((row * wrow + part * 8) * 2) : 0x7ffffff0u;
   }
-  const __amdgpu_buffer_rsrc_t rs_w =
-      __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, (int)wbytes, 0x00020000);
 
   typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
   typedef __attribute__((address_space(3))) void lds_void;
   u32x4 wf[2][NB];
   u32x4 bf[2][MB];
 
+  // A stage of the K loop: 32-channel chunk, temporal tap i, weight column; nt: in the next tile
   struct Stage {
-    int chunk, i, col;
+    int chunk, i, col, nt;
   };
-  auto stage_at = [&](int chunk, int i) -> Stage { return {chunk, i, i * SPS * p.Cip + chunk * 32}; };
+  auto stage_at = [&](int chunk, int i, int nt) -> Stage { return {chunk, i, i * SPS * p.Cip + chunk * 32, nt}; };
   auto next_stage = [&](const Stage& c) -> Stage {
-    if (c.chunk * p.kt + c.i + 1 >= ng) return c;
-    return (c.i + 1 == p.kt) ? stage_at(c.chunk + 1, 0) : stage_at(c.chunk, c.i + 1);
+    if (c.chunk * p.kt + c.i + 1 >= ng) return stage_at(0, 0, 1);
+    return (c.i + 1 == p.kt) ? stage_at(c.chunk + 1, 0, c.nt) : stage_at(c.chunk, c.i + 1, c.nt);
   };
 
-  // fetch a stage's patch into buffer BUF (live == false: zeros)
-  auto fetch_patch = [&](auto BUF, const Stage& c, bool live) {
-    const int sf = tf + dt0 + c.i;
+  int it = local;                    // the current tile (index in the XCD range)
+  bool more = PERSIST && it + G8 < xl;  // whether there is a next tile
+  Tile tc = decode(it);
+  Tile tn = more ? decode(it + G8) : tc;
+  __amdgpu_buffer_rsrc_t rs_cur = weight_rsrc(tc), rs_nxt = weight_rsrc(tn);
+
+  // fetch a stage's patch (of the current or the next tile) into buffer BUF (live == false: zeros)
+  auto fetch_patch = [&](auto BUF, const Stage& c, bool live) __attribute__((always_inline)) {
+    const int sf = (c.nt ? tn.tf : tc.tf) + dt0 + c.i;
     const bool fok = live & (sf >= -p.Th);
     const bf16_t* fbase = (sf >= 0) ? p.x + (int64_t)sf * frame_elems
                                     : ((sf >= -p.Th) ? p.hist + (int64_t)(sf + p.Th) * frame_elems : p.x);
@@ -719,11 +747,11 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
     }
   };
   // fetch the weights of one K step (column col of the packed rows) into slot SLOT
-  auto fetch_w = [&](auto SLOT, int col) {
+  auto fetch_w = [&](auto SLOT, int col, __amdgpu_buffer_rsrc_t rs) {
     char* base = (char*)wslot(SLOT);
 #pragma unroll
     for (int i = 0; i < WIW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_void*)(base + (i * WAVES + wave) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + (i * WAVES + wave) * 1024), 16,
                                                (int)(wgo[i] + col * 2), 0, 0, 0);
   };
   auto read_a = [&](u32x4 (&dst)[NB], auto SLOT, int q) {
@@ -739,12 +767,14 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
   };
 
   floatx16 acc[NB][MB];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
+  };
   auto compute = [&](const u32x4 (&w)[NB], const u32x4 (&a)[MB]) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -753,36 +783,41 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[nb]),
                                                               __builtin_bit_cast(bf16x8, a[mb]), acc[nb][mb], 0, 0, 0);
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
 
-  Stage cur = stage_at(0, 0);
+  // prologue: the first tile's first stage (patch and steps 0 .. D - 1, all in stage 0)
+  patch_offsets(tc);
+  Stage cur = stage_at(0, 0, 0);
   Stage nxt = next_stage(cur);
   fetch_patch(I0{}, cur, true);
-  // steps 0 .. D - 1, all in the first stage
-  fetch_w(I0{}, cur.col);
-  fetch_w(I1{}, cur.col + p.Cip);
-  fetch_w(I2{}, cur.col + 2 * p.Cip);
-  fetch_w(I3{}, cur.col + 3 * p.Cip);
-  if constexpr (D == 5) fetch_w(I4{}, cur.col + 4 * p.Cip);
+  fetch_w(I0{}, cur.col, rs_cur);
+  fetch_w(I1{}, cur.col + p.Cip, rs_cur);
+  fetch_w(I2{}, cur.col + 2 * p.Cip, rs_cur);
+  if constexpr (D >= 4) fetch_w(I3{}, cur.col + 3 * p.Cip, rs_cur);
+  if constexpr (D == 5) fetch_w(I4{}, cur.col + 4 * p.Cip, rs_cur);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_barrier();
   read_a(wf[0], I0{}, 0);
   read_b(bf[0], I0{}, 0, 0);
+  zero_acc();
 
   constexpr int NM = MB * NB;
-  auto step = [&](auto PP, auto SS, int g) {
+  auto step = [&](auto PP, auto SS) __attribute__((always_inline)) {
     constexpr int P = decltype(PP)::value;  // stage parity: patch buffer
     constexpr int S = decltype(SS)::value;  // spatial tap
     constexpr int K6 = (P * SPS + S) % NWS;  // k mod NWS (k = SPS * g + S)
     __builtin_amdgcn_sched_barrier(0);
-    // step k + D lies in this stage or the next one (D < 2 * SPS - S)
-    fetch_w(std::integral_constant<int, (K6 + D) % NWS>{},
-            S + D < SPS ? cur.col + (S + D) * p.Cip : nxt.col + (S + D - SPS) * p.Cip);
-    if constexpr (S == 0) fetch_patch(std::integral_constant<int, P ^ 1>{}, nxt, g + 1 < ng);
+    // step k + D lies in this stage or the next one (D < 2 * SPS - S), which may be the next
+    // tile's first stage
+    if constexpr (S + D < SPS) {
+      fetch_w(std::integral_constant<int, (K6 + D) % NWS>{}, cur.col + (S + D) * p.Cip, rs_cur);
+    } else {
+      fetch_w(std::integral_constant<int, (K6 + D) % NWS>{}, nxt.col + (S + D - SPS) * p.Cip,
+              nxt.nt ? rs_nxt : rs_cur);
+    }
+    if constexpr (S == 0) {
+      if (PERSIST && nxt.nt) patch_offsets(tn);  // the current tile fetches no more patches
+      fetch_patch(std::integral_constant<int, P ^ 1>{}, nxt, !nxt.nt || more);
+    }
     __builtin_amdgcn_sched_barrier(0);
     read_a(wf[1], std::integral_constant<int, K6>{}, 1);
     read_b(bf[1], std::integral_constant<int, P>{}, S, 1);
@@ -811,50 +846,122 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
     __builtin_amdgcn_s_barrier();
   };
-  auto stage = [&](auto PP, int g) {
-    step(PP, I0{}, g);
-    step(PP, I1{}, g);
-    step(PP, I2{}, g);
-    step(PP, I3{}, g);
+  auto stage = [&](auto PP) __attribute__((always_inline)) {
+    step(PP, I0{});
+    step(PP, I1{});
+    step(PP, I2{});
+    step(PP, I3{});
     if constexpr (SPS == 9) {
-      step(PP, I4{}, g);
-      step(PP, std::integral_constant<int, 5>{}, g);
-      step(PP, std::integral_constant<int, 6>{}, g);
-      step(PP, std::integral_constant<int, 7>{}, g);
-      step(PP, std::integral_constant<int, 8>{}, g);
+      step(PP, I4{});
+      step(PP, std::integral_constant<int, 5>{});
+      step(PP, std::integral_constant<int, 6>{});
+      step(PP, std::integral_constant<int, 7>{});
+      step(PP, std::integral_constant<int, 8>{});
     }
     cur = nxt;
-    nxt = next_stage(nxt);
+    if (!nxt.nt) nxt = next_stage(nxt);  // (past a tile's last stage nxt is set at the switch)
   };
-  int g = 0;
-  for (; g + 1 < ng; g += 2) {
-    stage(I0{}, g);
-    stage(I1{}, g + 1);
-  }
-  if (g < ng) stage(I0{}, g);
-  // fetches past the end (into slots nobody reads) must land before the workgroup exits
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-
-  if (p.staged) {
-    // Every wave's fetches have landed and the patch is read no more: the two patch buffers
-    // become the waves' output staging areas (half of the waves in each).
-    __builtin_amdgcn_s_barrier();
-    // (as many areas as fit in each patch buffer, the rest in weight slots, all idle now)
-    constexpr int SB = StagedShape<NB>::BYTES, PCAP = PBYTES / SB, WCAP = WBYTES / SB;
-    static_assert(2 * PCAP + 2 * WCAP >= WAVES, "staging areas");
-    char* st;
-    if (wave < PCAP) st = (char*)lds_p0 + wave * SB;
-    else if (wave < 2 * PCAP) st = (char*)lds_p1 + (wave - PCAP) * SB;
-    else {
-      const int r = wave - 2 * PCAP, q = r % (WCAP > 0 ? WCAP : 1);
-      char* w = (r / (WCAP > 0 ? WCAP : 1) == 0) ? (char*)wslot(I0{}) : (char*)wslot(I1{});
-      st = w + q * SB;
+  using SShape = StagedShape<NBP>;
+  // After each stage: at a tile's end (its last stage of parity PL) the epilogue, then the
+  // switch to the next tile, whose first stage (parity PL ^ 1) is already fetched. Returns
+  // whether the workgroup is done.
+  if constexpr (!PERSIST) {
+    // One tile: its stages, then the epilogue with both patch buffers (and two weight slots if
+    // needed) as staging areas once every fetch has landed.
+    int g = 0;
+    for (; g + 1 < ng; g += 2) {
+      stage(I0{});
+      stage(I1{});
     }
-    conv_epilogue_staged<NB, MB, NORM>(p, acc, ph, w0, tf, n0, pa, pb, lane, st);
-  } else {
-    conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
+    if (g < ng) stage(I0{});
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    const int pa = (KS == 2) ? (tc.phase >> 1) : 0, pb = (KS == 2) ? (tc.phase & 1) : 0;
+    int ph[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) ph[mb] = tc.h0 + wave * MB + mb;
+    if (p.staged) {
+      __builtin_amdgcn_s_barrier();
+      constexpr auto fits1 = [](int nbp) constexpr {
+        const int sb = 32 * (nbp * 64 + 16);
+        return 2 * (PBYTES / sb) + 2 * (WBYTES / sb) >= WAVES;
+      };
+      constexpr int NBP1 = (NB % 3 == 0 && fits1(3)) ? 3 : ((NB % 2 == 0 && fits1(2)) ? 2 : 1);
+      constexpr int SB = StagedShape<NBP1>::BYTES, PCAP = PBYTES / SB, WCAP = WBYTES / SB > 0 ? WBYTES / SB : 1;
+      static_assert(fits1(NBP1), "staging areas");
+      char* st;
+      if (wave < PCAP) st = (char*)lds_p0 + wave * SB;
+      else if (wave < 2 * PCAP) st = (char*)lds_p1 + (wave - PCAP) * SB;
+      else {
+        const int r = wave - 2 * PCAP;
+        st = ((r / WCAP == 0) ? (char*)wslot(I0{}) : (char*)wslot(I1{})) + (r % WCAP) * SB;
+      }
+      conv_epilogue_staged<NB, MB, NORM, NBP1>(p, acc, ph, tc.w0, tc.tf, tc.n0, pa, pb, lane, st);
+    } else {
+      int pw[MB];
+      bool pv[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        pw[mb] = tc.w0 + l32;
+        pv[mb] = (ph[mb] < p.H) & (pw[mb] < p.W);
+      }
+      conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tc.tf, tc.n0, pa, pb, half);
+    }
+    return;
   }
+  int g = 0;  // stage within the tile
+  auto after_stage = [&](auto PL) __attribute__((always_inline)) -> bool {
+    constexpr int L = decltype(PL)::value;
+    if (++g < ng) return false;
+    g = 0;
+    const int pa = (KS == 2) ? (tc.phase >> 1) : 0, pb = (KS == 2) ? (tc.phase & 1) : 0;
+    int ph[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) ph[mb] = tc.h0 + wave * MB + mb;
+    if (p.staged) {
+      conv_epilogue_staged<NB, MB, NORM, NBP>(p, acc, ph, tc.w0, tc.tf, tc.n0, pa, pb, lane,
+                                              (char*)pbuf(PL) + wave * SShape::BYTES);
+    } else {
+      int pw[MB];
+      bool pv[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        pw[mb] = tc.w0 + l32;
+        pv[mb] = (ph[mb] < p.H) & (pw[mb] < p.W);
+      }
+      conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tc.tf, tc.n0, pa, pb, half);
+    }
+    if (!more) return true;
+    it += G8;
+    more = PERSIST && it + G8 < xl;
+    tc = tn;
+    rs_cur = rs_nxt;
+    if (more) {
+      tn = decode(it + G8);
+      rs_nxt = weight_rsrc(tn);
+    }
+    cur.nt = 0;
+    nxt = next_stage(cur);
+    zero_acc();
+    // every wave is done with the staging areas before the next tile's fetches reuse them
+    __builtin_amdgcn_s_barrier();
+    read_a(wf[0], std::integral_constant<int, ((L ^ 1) * SPS) % NWS>{}, 0);
+    read_b(bf[0], std::integral_constant<int, L ^ 1>{}, 0, 0);
+    return false;
+  };
+  for (;;) {
+    stage(I0{});
+    if (after_stage(I0{})) break;
+    stage(I1{});
+    if (after_stage(I1{})) break;
+  }
+  // fetches past the end (into slots and buffers nobody reads) land before the workgroup exits
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
+
+// DMA conv kernels without a fused norm run persistent workgroups (one per resident slot,
+// several tiles each).
+constexpr bool kPersistentDmaTiles = true;
+constexpr int kNumCUs = 256;
 
 struct ConfigEntry {
   const char* name;
@@ -863,26 +970,29 @@ struct ConfigEntry {
   int time_tiles;  // halo tile order (ConvProblem::time_tiles)
   int phase_in_x;  // the x2 phases are part of the linear block index (grid z = 1)
   int staged;      // the kernel has the LDS-staged epilogue (used when ConvProblem allows it)
+  int wgs_per_cu;  // workgroups resident per CU (a DMA kernel then walks several tiles each)
   void (*kernel)(const ConvProblem);       // plain epilogue (bias, residual, fp32 planes)
   void (*kernel_norm)(const ConvProblem);  // fused RMS norm (+ SiLU) epilogue
 };
 
 #define WVD_CONV_CONFIG(NB, MB, W) \
-  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
+  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, 0, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
     conv_mfma_kernel<NB, MB, W, true> }
 // 3x3-tap halo convs order tiles time-fastest (measured 2-8% faster than frame-major on every
 // 3x3x3 layer: fewer input re-reads past L2); the phase convs have no temporal taps.
 #define WVD_HALO_CONFIG(NB, MB, W) \
-  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 0, conv_halo_kernel<NB, MB, W, 3, false>, \
+  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 0, 0, conv_halo_kernel<NB, MB, W, 3, false>, \
     conv_halo_kernel<NB, MB, W, 3, true> }
 #define WVD_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, conv_halo_dma_kernel<NB, MB, W, 3, false>, \
+  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, dma_waves_per_simd<MB, 3>() * 4 / W, \
+    conv_halo_dma_kernel<NB, MB, W, 3, false>, \
     conv_halo_dma_kernel<NB, MB, W, 3, true> }
 #define WVD_PHASE_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, conv_halo_dma_kernel<NB, MB, W, 2, false>, \
+  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<MB, 2>() * 4 / W, \
+    conv_halo_dma_kernel<NB, MB, W, 2, false>, \
     conv_halo_dma_kernel<NB, MB, W, 2, true> }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
+  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
     conv_halo_kernel<NB, MB, W, 2, true> }
 
 // Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
@@ -1010,7 +1120,13 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   q.time_tiles = c.time_tiles;
   q.staged = c.staged && !p.y_f32 && p.N % 8 == 0 && p.nsplit % 8 == 0 && ((uintptr_t)p.y & 15) == 0 &&
              ((uintptr_t)p.res & 15) == 0;
-  const int64_t gx = c.phase_in_x ? blocks * p.phases : blocks;
+  int64_t gx = c.phase_in_x ? blocks * p.phases : blocks;
+  if (c.wgs_per_cu) {
+    // DMA kernels: a multiple of 8 workgroups (XCD ranges); with persistent tiles no more than
+    // fit on the chip at once, each walking its share of the tiles
+    gx = (gx + 7) / 8 * 8;
+    if (kPersistentDmaTiles && !p.norm_gamma) gx = std::min<int64_t>(gx, (int64_t)kNumCUs * c.wgs_per_cu);
+  }
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(p.norm_gamma ? c.kernel_norm : c.kernel, dim3((unsigned)gx, 1, c.phase_in_x ? 1 : p.phases),
                      dim3(c.waves * 64), 0, s, q);
