@@ -106,6 +106,7 @@ def lib():
             "wvd_timing_launch": ([ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double),
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
             "wvd_conv_force_config": ([ctypes.c_int], ctypes.c_int),
+            "wvd_conv_max_workgroups": ([ctypes.c_int], ctypes.c_int),
             "wvd_timing_read_mem": ([ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         }
@@ -126,7 +127,7 @@ def exported_symbols() -> Sequence[str]:
             "wvd_decoder_packed_bytes", "wvd_decoder_pack", "wvd_cache_bytes", "wvd_cache_init", "wvd_cache_reset",
             "wvd_cache_destroy", "wvd_cache_next_latent", "wvd_decode_workspace_bytes", "wvd_decode_chunk",
             "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read",
-            "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem"]
+            "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem", "wvd_conv_max_workgroups"]
 
 
 def _check(status: int):
@@ -432,6 +433,12 @@ def conv_force_config(config):
     elif isinstance(config, str):
         config = conv_config_names().index(config)
     _check(lib().wvd_conv_force_config(int(config)))
+
+
+def conv_max_workgroups(n):
+    """Cap the workgroups of the following multi-tile halo conv launches at n (0 or None: default);
+    every workgroup then walks a longer run of tiles (testing)."""
+    _check(lib().wvd_conv_max_workgroups(int(n or 0)))
 
 
 def timing_launches():

@@ -125,8 +125,10 @@ hipEvent_t pooled_event() {
   return e;
 }
 
-// Configuration forced by wvd_conv_force_config (-1: automatic choice).
+// Configuration forced by wvd_conv_force_config (-1: automatic choice) and the workgroup cap of
+// wvd_conv_max_workgroups (0: none).
 std::atomic<int> g_force_config{-1};
+std::atomic<int> g_max_workgroups{0};
 
 wvd_status run_conv(const ConvProblem& p, hipStream_t s, double flops) {
   const bool timed = g_timing.on;
@@ -139,7 +141,7 @@ wvd_status run_conv(const ConvProblem& p, hipStream_t s, double flops) {
     WVD_HIP(hipEventRecord(e0, s), "hipEventRecord");
   }
   int cfg = -1;
-  const hipError_t le = launch_conv_mfma(p, s, &cfg, g_force_config.load());
+  const hipError_t le = launch_conv_mfma(p, s, &cfg, g_force_config.load(), g_max_workgroups.load());
   if (le == hipErrorNotSupported) return fail(WVD_ERR_UNSUPPORTED, "forced conv configuration cannot run this problem");
   WVD_HIP(le, "conv_mfma launch");
   if (timed) {
@@ -1265,6 +1267,12 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
 extern "C" wvd_status wvd_conv_force_config(int config) {
   if (config < -1 || config >= conv_config_count()) return fail(WVD_ERR_ARG, "conv config index out of range");
   g_force_config.store(config);
+  return WVD_OK;
+}
+
+extern "C" wvd_status wvd_conv_max_workgroups(int n) {
+  if (n < 0) return fail(WVD_ERR_ARG, "negative workgroup cap");
+  g_max_workgroups.store(n);
   return WVD_OK;
 }
 

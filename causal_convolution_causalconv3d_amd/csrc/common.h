@@ -73,8 +73,10 @@ struct ConvProblem {
   int staged;      // set by the launcher: store the output through LDS (see conv_epilogue_staged)
 };
 
-// force_config >= 0 runs that configuration (hipErrorNotSupported when it cannot run p).
-hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id, int force_config = -1);
+// force_config >= 0 runs that configuration (hipErrorNotSupported when it cannot run p);
+// max_workgroups > 0 caps the workgroups of a DMA kernel launch, each then walking more tiles.
+hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id, int force_config = -1,
+                            int max_workgroups = 0);
 // Whether a conv with N output channels can apply RMS norm (+ SiLU) with gamma in its epilogue:
 // one channel tile, N % 8 == 0, bias (may be null) and gamma 16-byte aligned.
 bool conv_can_fuse_norm(int N, const float* bias, const float* gamma);

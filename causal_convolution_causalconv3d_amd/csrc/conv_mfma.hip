@@ -1100,7 +1100,8 @@ bool conv_config_fits(const ConvProblem& p, int id) {
   return true;
 }
 
-hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id, int force_config) {
+hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id, int force_config,
+                            int max_workgroups) {
   const int64_t HW = (int64_t)p.H * p.W;
   if (p.T == 0 || HW == 0) return hipSuccess;
   // one frame is addressed with 32-bit byte offsets
@@ -1125,7 +1126,10 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
     // DMA kernels: a multiple of 8 workgroups (XCD ranges); with persistent tiles no more than
     // fit on the chip at once, each walking its share of the tiles
     gx = (gx + 7) / 8 * 8;
-    if (kPersistentDmaTiles && !p.norm_gamma) gx = std::min<int64_t>(gx, (int64_t)kNumCUs * c.wgs_per_cu);
+    if (kPersistentDmaTiles && !p.norm_gamma) {
+      gx = std::min<int64_t>(gx, (int64_t)kNumCUs * c.wgs_per_cu);
+      if (max_workgroups > 0) gx = std::min<int64_t>(gx, std::max(8, max_workgroups / 8 * 8));
+    }
   }
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(p.norm_gamma ? c.kernel_norm : c.kernel, dim3((unsigned)gx, 1, c.phase_in_x ? 1 : p.phases),

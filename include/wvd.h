@@ -248,6 +248,12 @@ int wvd_timing_read_mem(int i, const char** name, int64_t* launches, double* ms,
  * fails with WVD_ERR_UNSUPPORTED. WVD_ERR_ARG for an index out of range. Process-wide; not for
  * use while another thread launches. */
 wvd_status wvd_conv_force_config(int config);
+/* Testing support: cap the workgroups of every following halo-tile (LDS-DMA) convolution launch
+ * that walks several tiles per workgroup (those without a fused norm) at n, rounded down to a
+ * multiple of 8 and at least 8, so that each workgroup walks a longer run of tiles; 0 restores
+ * the default (one workgroup per resident slot). Results are the same for any n. WVD_ERR_ARG for
+ * n < 0. Process-wide; not for use while another thread launches. */
+wvd_status wvd_conv_max_workgroups(int n);
 
 #ifdef __cplusplus
 }

@@ -192,6 +192,63 @@ def test_bf16_conv_residual_and_hist_out():
     assert torch.equal(hout1[:, 0], hd[:, 0]) and torch.equal(hout1[:, 1], xd[:, 0])
 
 
+WALK_CASES = [
+    # Ci, Co, T, H, W, Th: 3x3x3 convs with enough tiles that 8 workgroups each walk several
+    (96, 96, 3, 40, 70, 2),    # an odd number of K stages (3 chunks x 3 temporal taps)
+    (64, 192, 2, 35, 66, 1),   # an even number of stages, two 96-channel tiles
+    (48, 96, 2, 33, 40, 0),    # a partial 32-channel chunk
+]
+
+
+@pytest.mark.parametrize("case", WALK_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_conv_tile_walk_matches_one_tile_per_workgroup_and_oracle(case):
+    """Halo-tile convs whose workgroups each walk a run of tiles (capped at 8 workgroups) give the
+    same bits as the default launch, and match the oracle (with a residual added)."""
+    Ci, Co, T, H, W, Th = case
+    seed = Ci + 3 * Co + 5 * T + 7 * H + 11 * W + Th
+    x = wl.bf16_values(_rand((1, Ci, T, H, W), seed))
+    res = wl.bf16_values(_rand((1, Co, T, H, W), seed + 1))
+    w = wl.bf16_values(wl.kaiming(torch.Generator().manual_seed(seed + 2), (Co, Ci, 3, 3, 3)))
+    b = 0.1 * _rand((Co,), seed + 3)
+    hist = wl.bf16_values(_rand((1, Ci, Th, H, W), seed + 4)) if Th else None
+    ref = oracle.add(oracle.causal_conv3d(x[0], w, b, None if hist is None else hist[0]), res[0])
+    xd, wp, bd, rd = to_dev_nthwc(x), wvd.conv_pack(w.cuda()), b.cuda(), to_dev_nthwc(res)
+    hd = None if hist is None else to_dev_nthwc(hist)
+    base = wvd.causal_conv3d(xd, wp, Co, bias=bd, hist=hd, residual=rd)
+    try:
+        for cap in (8, 16):
+            log(f"conv tile walk {case} cap {cap}")
+            wvd.conv_max_workgroups(cap)
+            y = wvd.causal_conv3d(xd, wp, Co, bias=bd, hist=hd, residual=rd)
+            torch.cuda.synchronize()
+            assert torch.equal(y, base), cap
+    finally:
+        wvd.conv_max_workgroups(0)
+    ok, worst = bf16_elementwise_ok(from_dev_nthwc(base), ref)
+    assert ok, worst
+
+
+@pytest.mark.parametrize("C,T,H,W", [(96, 2, 21, 45), (192, 2, 18, 40), (384, 1, 11, 35)])
+def test_upsample_tile_walk_matches_one_tile_per_workgroup(C, T, H, W):
+    """The x2 phase convs (phases dealt as the fastest tile index) with 8 workgroups walking all
+    tiles give the same bits as the default launch."""
+    g = torch.Generator().manual_seed(5 * C + H)
+    x = wl.bf16_values(torch.randn((1, C, T, H, W), generator=g))
+    w = wl.bf16_values(wl.kaiming(g, (C, C, 3, 3)))
+    b = 0.1 * torch.randn((C,), generator=g)
+    xd, wp, bd = to_dev_nthwc(x), wvd.conv_pack(w.cuda(), wvd.WVD_PACK_PHASE2X), b.cuda()
+    base = wvd.upsample(xd, spatial=wp, spatial_bias=bd)
+    try:
+        wvd.conv_max_workgroups(8)
+        y = wvd.upsample(xd, spatial=wp, spatial_bias=bd)
+        torch.cuda.synchronize()
+    finally:
+        wvd.conv_max_workgroups(0)
+    assert torch.equal(y, base)
+    r = rel_max(from_dev_nthwc(base), oracle.spatial_upsample(x[0], w, b))
+    assert r <= 2e-2, r
+
+
 def test_bf16_conv_chunked_equals_one_shot_bitwise():
     """Carrying the history between chunks gives the very same bits as one conv over all frames."""
     Ci, Co, T, H, W = 96, 96, 5, 9, 14
