@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--frames-per-pass", type=int, default=4)
+    ap.add_argument("--early-frames-per-pass", type=int, default=0, metavar="N",
+                    help="latent frames per pass through the stages up to the last temporal upsample "
+                         "(per-level pass sizes; the later stages keep --frames-per-pass); 0: same")
     ap.add_argument("--latent-frames", type=int, default=31)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -160,13 +163,14 @@ def main():
     dec = wvd.Decoder(wvd.make_desc(), params)
     del params
     fpp = args.frames_per_pass
+    early = max(args.early_frames_per_pass, fpp)
     F = dec.video_frames(args.latent_frames, fpp)
     video = torch.empty((1, 3, F, wl.VIDEO_H, wl.VIDEO_W), dtype=torch.bfloat16, device="cuda")
-    dec.workspace(fpp)
+    dec.workspace(fpp, early)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        dec.decode(z, frames_per_pass=fpp, out=video)
+        dec.decode(z, frames_per_pass=fpp, out=video, early_frames_per_pass=early)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
 
@@ -175,7 +179,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        dec.decode(z, frames_per_pass=fpp, out=video)
+        dec.decode(z, frames_per_pass=fpp, out=video, early_frames_per_pass=early)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wvd.timing_enable(False)
@@ -210,9 +214,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "streaming 5 s decode: latents [1,48,31,44,78] -> video [1,3,121,704,1248], "
-                               f"{fpp} latent frames per pass, decoder 48->384, 2 mid resblocks, stages "
+                               f"{fpp} latent frames per pass"
+                               + (f" ({early} per pass through conv_in, the middle blocks and the two temporal "
+                                  f"stages)" if early > fpp else "")
+                               + ", decoder 48->384, 2 mid resblocks, stages "
                                "384/384/192/96 (2 resblocks each, time x2 on the first two), random Kaiming weights",
                    "latent_frames": args.latent_frames, "video_frames": F, "frames_per_pass": fpp,
+                   "early_frames_per_pass": early,
                    "global_batch": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),

@@ -99,6 +99,10 @@ def lib():
                                   _P, ctypes.c_size_t, _P], ctypes.c_int),
             "wvd_chunk_video_frames": ([ctypes.POINTER(DecoderDesc), ctypes.c_int64, ctypes.c_int, ctypes.c_int],
                                        ctypes.c_int64),
+            "wvd_decode_workspace_bytes_split": ([ctypes.POINTER(DecoderDesc), ctypes.c_int, ctypes.c_int],
+                                                 ctypes.c_size_t),
+            "wvd_decode_chunk_split": ([ctypes.POINTER(DecoderDesc), _P, _P, _T, ctypes.c_int, ctypes.c_int, _T,
+                                        ctypes.c_int64, ctypes.c_int, _P, ctypes.c_size_t, _P], ctypes.c_int),
             "wvd_timing_enable": ([ctypes.c_int], ctypes.c_int),
             "wvd_timing_reset": ([], ctypes.c_int),
             "wvd_timing_read": ([ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
@@ -126,6 +130,7 @@ def exported_symbols() -> Sequence[str]:
             "wvd_upsample_workspace_bytes", "wvd_upsample", "wvd_decoder_param_count", "wvd_decoder_param_info",
             "wvd_decoder_packed_bytes", "wvd_decoder_pack", "wvd_cache_bytes", "wvd_cache_init", "wvd_cache_reset",
             "wvd_cache_destroy", "wvd_cache_next_latent", "wvd_decode_workspace_bytes", "wvd_decode_chunk",
+            "wvd_decode_workspace_bytes_split", "wvd_decode_chunk_split",
             "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read",
             "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem", "wvd_conv_max_workgroups"]
 
@@ -318,7 +323,7 @@ class Decoder:
         _check(lib().wvd_cache_init(ctypes.byref(desc), _ptr(self.cache_storage), ctypes.byref(h)))
         self.cache = h
         self._ws = None
-        self._ws_frames = 0
+        self._ws_frames = None
 
     def __del__(self):
         try:
@@ -336,36 +341,52 @@ class Decoder:
             start += n
         return total
 
-    def workspace(self, frames_per_pass: int) -> torch.Tensor:
-        if self._ws is None or self._ws_frames < frames_per_pass:
-            nbytes = lib().wvd_decode_workspace_bytes(ctypes.byref(self.desc), frames_per_pass)
+    def workspace(self, frames_per_pass: int, early_frames_per_pass: Optional[int] = None) -> torch.Tensor:
+        early = max(early_frames_per_pass or frames_per_pass, frames_per_pass)
+        key = (early, frames_per_pass if early > frames_per_pass else 0)
+        if self._ws is None or self._ws_frames != key:
+            if key[1]:
+                nbytes = lib().wvd_decode_workspace_bytes_split(ctypes.byref(self.desc), key[0], key[1])
+            else:
+                nbytes = lib().wvd_decode_workspace_bytes(ctypes.byref(self.desc), key[0])
             self._ws = None
             self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-            self._ws_frames = frames_per_pass
+            self._ws_frames = key
         return self._ws
 
     def decode(self, z: torch.Tensor, frames_per_pass: int = 4, first_frame_rule: bool = True,
-               out: Optional[torch.Tensor] = None, z_layout: str = "NCTHW") -> torch.Tensor:
-        """z: bf16 latents [1, C, T, h, w] (NCTHW, default) or [1, T, h, w, C] (NTHWC)."""
+               out: Optional[torch.Tensor] = None, z_layout: str = "NCTHW",
+               early_frames_per_pass: Optional[int] = None) -> torch.Tensor:
+        """z: bf16 latents [1, C, T, h, w] (NCTHW, default) or [1, T, h, w, C] (NTHWC).
+        early_frames_per_pass > frames_per_pass: the stages up to the last temporal upsample take
+        that many latent frames per pass, the later ones (and the memory they need) still
+        frames_per_pass (wvd_decode_chunk_split); the video is the same bits."""
         if frames_per_pass < 1:
             raise ValueError("frames_per_pass must be at least 1")
+        early = max(early_frames_per_pass or frames_per_pass, frames_per_pass)
         T = z.shape[2] if z_layout == "NCTHW" else z.shape[1]
         F = self.video_frames(T, frames_per_pass, first_frame_rule)
         L = self.desc.n_stages
         vh, vw = self.desc.latent_h << L, self.desc.latent_w << L
         if out is None:
             out = torch.empty((1, self.desc.out_channels, F, vh, vw), dtype=torch.bfloat16, device=self.device)
-        ws = self.workspace(frames_per_pass)
+        ws = self.workspace(frames_per_pass, early)
         _check(lib().wvd_cache_reset(self.cache))
         start, offset = 0, 0
         while start < T:
-            n = min(frames_per_pass, T - start)
+            n = min(early, T - start)
             zc = z[:, :, start:start + n] if z_layout == "NCTHW" else z[:, start:start + n]
             zc = zc.contiguous()
             first = int(start == 0)
-            _check(lib().wvd_decode_chunk(ctypes.byref(self.desc), _ptr(self.packed), self.cache, _desc(zc, z_layout),
-                                          first, int(first_frame_rule), ctypes.byref(ncthw(out)), offset, _ptr(ws),
-                                          ws.numel(), _stream()))
+            if early > frames_per_pass:
+                _check(lib().wvd_decode_chunk_split(ctypes.byref(self.desc), _ptr(self.packed), self.cache,
+                                                    _desc(zc, z_layout), first, int(first_frame_rule),
+                                                    ctypes.byref(ncthw(out)), offset, frames_per_pass, _ptr(ws),
+                                                    ws.numel(), _stream()))
+            else:
+                _check(lib().wvd_decode_chunk(ctypes.byref(self.desc), _ptr(self.packed), self.cache,
+                                              _desc(zc, z_layout), first, int(first_frame_rule),
+                                              ctypes.byref(ncthw(out)), offset, _ptr(ws), ws.numel(), _stream()))
             offset += lib().wvd_chunk_video_frames(ctypes.byref(self.desc), n, first, int(first_frame_rule))
             start += n
         return out

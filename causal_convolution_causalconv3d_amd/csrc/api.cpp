@@ -882,20 +882,36 @@ constexpr int kHeadPlanes = 9;
 
 // Workspace buffers of the chunk driver (elements of bf16).
 struct WsLayout {
-  size_t zc, x0, x1, a, h, sc;  // byte offsets
+  size_t zc, x0, x1, a, h, sc, xm;  // byte offsets
   size_t total;
 };
 
-WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n) {
-  const ChunkFrames f = chunk_frames(d, n, false);  // the largest frame counts
-  int64_t stream = 0, act = 0, hbuf = 0, scbuf = 0;
+// The first stage after the last temporal upsample: from there on a pass's frames can be
+// processed in sub-passes (no stage changes the frame count). 0 when no stage is temporal.
+int split_stage(const wvd_decoder_desc* d) {
+  int s = 0;
+  for (int i = 0; i < d->n_stages; ++i)
+    if (d->stage_temporal[i]) s = i + 1;
+  return s;
+}
+
+// n latent frames per pass through conv_in, the middle blocks and the temporal stages; nh per
+// sub-pass through the later stages and the head when split (nh < n and a temporal stage
+// exists), with the split level's input for all n kept in its own buffer (xm).
+WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n, int64_t nh) {
+  const int L = d->n_stages;
+  const int split = (nh > 0 && nh < n && split_stage(d) > 0) ? split_stage(d) : L;
+  const ChunkFrames fl = chunk_frames(d, n, false);  // the largest frame counts
+  const ChunkFrames fh = split < L ? chunk_frames(d, nh, false) : fl;
+  int64_t stream = 0, act = 0, hbuf = 0, scbuf = 0, xm = 0;
   const int64_t hw0 = (int64_t)d->latent_h * d->latent_w;
   auto hw = [&](int level) { return hw0 << (2 * level); };
   int c = d->base_channels;
   stream = std::max(stream, n * hw(0) * c);
   act = std::max(act, n * hw(0) * std::max(c, d->z_channels));
   hbuf = std::max(hbuf, n * hw(0) * c);
-  for (int s = 0; s < d->n_stages; ++s) {
+  for (int s = 0; s < L; ++s) {
+    const ChunkFrames& f = s < split ? fl : fh;
     const int cs = d->stage_channels[s];
     const int64_t P = f.stage_in[s] * hw(s);
     stream = std::max(stream, P * std::max(c, cs));
@@ -908,10 +924,11 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n) {
     stream = std::max(stream, f.stage_out[s] * hw(s) * c);
     stream = std::max(stream, f.stage_out[s] * hw(s + 1) * c);
     act = std::max(act, f.stage_out[s] * hw(s + 1) * c);
+    if (s + 1 == split && split < L) xm = fl.stage_out[s] * hw(s + 1) * c;
   }
-  act = std::max(act, f.video * hw(d->n_stages) * c);
+  act = std::max(act, fh.video * hw(L) * c);
   // the head's fp32 tap planes Z (9 planes x 4 floats = 72 bf16 per position) live in a stream buffer
-  stream = std::max(stream, f.video * hw(d->n_stages) * kHeadPlanes * 8);
+  stream = std::max(stream, fh.video * hw(L) * kHeadPlanes * 8);
   WsLayout w;
   size_t off = 0;
   auto take = [&](int64_t elems) {
@@ -925,6 +942,7 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n) {
   w.a = take(act);
   w.h = take(hbuf);
   w.sc = take(scbuf);
+  w.xm = take(xm);
   w.total = off;
   return w;
 }
@@ -1043,7 +1061,13 @@ extern "C" int64_t wvd_cache_next_latent(wvd_cache c) { return c ? c->next_laten
 
 extern "C" size_t wvd_decode_workspace_bytes(const wvd_decoder_desc* d, int max_latent_frames) {
   if (check_desc(d) != WVD_OK || max_latent_frames <= 0) return 0;
-  return ws_layout(d, max_latent_frames).total;
+  return ws_layout(d, max_latent_frames, max_latent_frames).total;
+}
+
+extern "C" size_t wvd_decode_workspace_bytes_split(const wvd_decoder_desc* d, int max_latent_frames,
+                                                   int high_latent_frames) {
+  if (check_desc(d) != WVD_OK || max_latent_frames <= 0 || high_latent_frames < 0) return 0;
+  return ws_layout(d, max_latent_frames, high_latent_frames).total;
 }
 
 extern "C" int64_t wvd_chunk_video_frames(const wvd_decoder_desc* d, int64_t n, int first, int first_frame_rule) {
@@ -1051,9 +1075,15 @@ extern "C" int64_t wvd_chunk_video_frames(const wvd_decoder_desc* d, int64_t n, 
   return chunk_frames(d, n, first && first_frame_rule).video;
 }
 
-extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* packed, wvd_cache cache,
-                                       const wvd_tensor* z, int first, int first_frame_rule, wvd_tensor* video,
-                                       int64_t frame_offset, void* ws, size_t ws_bytes, wvd_stream stream) {
+namespace {
+
+// One chunk of n latent frames. With 0 < nh < n the stages after the last temporal upsample
+// and the head run in sub-passes of nh latent frames (the first one holding the chunk's first
+// latent frame), each with the caches the previous one left: the same operands in the same
+// order as one pass, so the same bits, while the early stages see all n frames at once.
+wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_cache cache, const wvd_tensor* z,
+                             int first, int first_frame_rule, wvd_tensor* video, int64_t frame_offset, int64_t nh,
+                             void* ws, size_t ws_bytes, wvd_stream stream) {
   WVD_TRY(check_desc(d));
   if (!packed || !aligned16(packed)) return fail(WVD_ERR_ALIGN, "packed weights null or not 16-byte aligned");
   if (!cache) return fail(WVD_ERR_ARG, "cache is null");
@@ -1070,6 +1100,7 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
   if (frame_offset != cache->next_frame)
     return fail(WVD_ERR_STATE, "frame_offset %lld, the previous chunk ended at %lld", (long long)frame_offset,
                 (long long)cache->next_frame);
+  if (nh < 0) return fail(WVD_ERR_ARG, "negative sub-pass size");
   const int64_t n = z->t;
   const bool rule = first && first_frame_rule;
   const ChunkFrames fr = chunk_frames(d, n, rule);
@@ -1081,7 +1112,8 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     return fail(WVD_ERR_SHAPE, "chunk frames %lld..%lld do not fit a video of %lld frames", (long long)frame_offset,
                 (long long)(frame_offset + fr.video), (long long)video->t);
   if (n > 4096) return fail(WVD_ERR_UNSUPPORTED, "chunk too long");
-  const WsLayout wl = ws_layout(d, n);
+  const int split = (nh > 0 && nh < n && split_stage(d) > 0) ? split_stage(d) : L;
+  const WsLayout wl = ws_layout(d, n, split < L ? nh : n);
   if (ws_bytes < wl.total) return fail(WVD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, wl.total);
   if (!ws || !aligned16(ws)) return fail(WVD_ERR_ALIGN, "workspace null or not 16-byte aligned");
 
@@ -1096,6 +1128,7 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
   bf16_t* ba = (bf16_t*)(wsb + wl.a);
   bf16_t* bh = (bf16_t*)(wsb + wl.h);
   bf16_t* bsc = (bf16_t*)(wsb + wl.sc);
+  bf16_t* bxm = (bf16_t*)(wsb + wl.xm);
   auto slot_ptr = [&](int slot) { return (bf16_t*)(cache->storage + p.slots[slot].offset); };
   auto slot_hist = [&](int slot) -> const bf16_t* {
     const int v = cache->valid[slot];
@@ -1131,10 +1164,11 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
                                    F_(p.conv_in_b), bx[cur], nullptr);
     WVD_TRY(cached_conv(cp, p.conv_in_slot, zin, (int)T, conv_flops(P, c, 27LL * d->z_channels)));
   }
-  auto resblock = [&](const ResPlan& r) -> wvd_status {
+  // a residual block reading x (the stream buffer, or the split level's input) and writing the
+  // stream buffer (in place when the residual is x itself)
+  auto resblock = [&](const ResPlan& r, const bf16_t* x) -> wvd_status {
     const int64_t P = T * H * Wd;
-    const bf16_t* x = bx[cur];
-    bf16_t* y = bx[cur];  // in place when the residual is x itself
+    bf16_t* y = bx[cur];
     const bf16_t* residual = x;
     if (r.cin != r.cout) {
       ConvProblem sc = plain_problem(x, nullptr, (int)T, H, Wd, r.cin, 0, W_(r.ws), r.cout, 1, 1, 1, F_(r.bs), bsc, nullptr);
@@ -1160,20 +1194,22 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     WVD_TRY(cached_conv(c2, r.slot2, a2, (int)T, conv_flops(P, r.cout, 27LL * r.cout)));
     return WVD_OK;
   };
-  for (const ResPlan& r : p.mid) WVD_TRY(resblock(r));
+  for (const ResPlan& r : p.mid) WVD_TRY(resblock(r, bx[cur]));
   // The last stage's spatial upsample also applies norm_out + SiLU in its epilogue when one
   // workgroup holds every channel (the L4 tensor is then written once, already activated).
   const bf16_t* act = nullptr;  // conv_out's input once norm_out has been applied
   bf16_t* zbuf = nullptr;       // a free buffer for the head's tap planes
-  for (int si = 0; si < L; ++si) {
+  // one stage: its residual blocks (the first reading x), its time conv and spatial upsample
+  // (into `up`, or the stream buffers)
+  auto run_stage = [&](int si, const bf16_t* x, bf16_t* up) -> wvd_status {
     const StagePlan& st = p.stages[si];
     for (const ResPlan& r : st.res) {
-      WVD_TRY(resblock(r));
+      WVD_TRY(resblock(r, x));
+      x = bx[cur];
       c = r.cout;
     }
     const bool fuse_out = si == L - 1 && conv_can_fuse_norm(c, F_(st.sb), F_(p.norm_out));
     const float* ng = fuse_out ? F_(p.norm_out) : nullptr;
-    const bf16_t* x = bx[cur];
     if (st.temporal) {
       const size_t fb = (size_t)H * Wd * c * 2;
       const int tf = rule ? 1 : 0;
@@ -1191,26 +1227,30 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
         WVD_TRY(cached_conv(cp, st.time_slot, src, Tc, conv_flops((int64_t)Tc * H * Wd, 2 * c, 3LL * c)));
       }
       T = To;
-      // spatial upsample from the time conv's output into the stream buffer
-      WVD_TRY(run_phase_conv(dst, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur], s, ng, d->eps));
+      // spatial upsample from the time conv's output into the stream buffer (or `up`)
+      bf16_t* out = up ? up : bx[cur];
+      WVD_TRY(run_phase_conv(dst, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), out, s, ng, d->eps));
       if (fuse_out) {
-        act = bx[cur];
+        act = out;
         zbuf = bx[cur ^ 1];
       }
     } else if (fuse_out) {
       WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), ba, s, ng, d->eps));
       act = ba;
       zbuf = bx[cur ^ 1];
+    } else if (up) {
+      WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), up, s));
     } else {
       WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur ^ 1], s));
       cur ^= 1;
     }
     H *= 2;
     Wd *= 2;
-  }
-  // norm_out + SiLU (unless fused above), then conv_out as temporal tap planes Z (fp32, in a free
-  // stream buffer) and the 9-tap stencil into the video (NCTHW) at frame_offset
-  {
+    return WVD_OK;
+  };
+  // norm_out + SiLU (unless fused above), then conv_out and the 9-tap stencil into the video
+  // (NCTHW) at frame `fo`
+  auto run_head = [&](int64_t fo) -> wvd_status {
     const int64_t P = T * H * Wd;
     if (!act) {
       WVD_TRY(run_norm(bx[cur], F_(p.norm_out), d->eps, 1, ba, P, c, s));
@@ -1227,14 +1267,11 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
       const double hb = (double)(T + std::min(Th, 2)) * H * Wd * c * 2.0 + (double)P * co * 2.0;
       WVD_TRY(run_mem(MEM_HEAD_FUSED, hb, s, "head launch", [&] {
         return launch_head_fused(act, hist, Th, (int)T, H, Wd, c, (int)round_up(c, 32), (const bf16_t*)W_(p.out_w),
-                                 F_(p.out_b), co, (bf16_t*)video->data, video->t, (int)frame_offset, s);
+                                 F_(p.out_b), co, (bf16_t*)video->data, video->t, (int)fo, s);
       }));
       int v = cache->valid[slot];
       WVD_TRY(update_slot((char*)slot_ptr(slot), v, act, (int)T, p.slots[slot].frame_bytes, s));
       cache->valid[slot] = v;
-      cache->next_latent += n;
-      cache->next_frame += fr.video;
-      if (first) cache->rule = first_frame_rule != 0;
       return WVD_OK;
     }
     float* Z = (float*)zbuf;
@@ -1250,15 +1287,58 @@ extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* pa
     WVD_TRY(cached_conv(cp, p.out_slot, act, (int)T, conv_flops(P, co, 27LL * c)));
     // reads the 9 tap planes (16 bytes per plane and position), writes co bf16 channels
     const double hb = (double)P * (kHeadPlanes * 16.0 + 2.0 * co);
-    WVD_TRY(run_mem(MEM_HEAD_STENCIL, hb, s, "head launch", [&] {
-      return launch_head_stencil(Z, co, F_(p.out_b), (bf16_t*)video->data, video->t, (int)frame_offset, (int)T, H, Wd,
-                                 s);
-    }));
+    return run_mem(MEM_HEAD_STENCIL, hb, s, "head launch", [&] {
+      return launch_head_stencil(Z, co, F_(p.out_b), (bf16_t*)video->data, video->t, (int)fo, (int)T, H, Wd, s);
+    });
+  };
+  if (split == L) {
+    for (int si = 0; si < L; ++si) WVD_TRY(run_stage(si, bx[cur], nullptr));
+    WVD_TRY(run_head(frame_offset));
+  } else {
+    // the early stages for all n latent frames, the last of them upsampling into xm
+    for (int si = 0; si < split; ++si) WVD_TRY(run_stage(si, bx[cur], si + 1 == split ? bxm : nullptr));
+    const int H0 = H, W0 = Wd, c0 = c;
+    int64_t t0 = 0, fo = frame_offset;
+    for (int64_t l0 = 0; l0 < n; l0 += nh) {
+      const int64_t m = std::min<int64_t>(nh, n - l0);
+      const ChunkFrames fs = chunk_frames(d, m, rule && l0 == 0);
+      T = fs.stage_in[split];
+      H = H0;
+      Wd = W0;
+      c = c0;
+      act = nullptr;
+      zbuf = nullptr;
+      const bf16_t* x = bxm + (size_t)t0 * H0 * W0 * c0;
+      for (int si = split; si < L; ++si) {
+        WVD_TRY(run_stage(si, x, nullptr));
+        x = bx[cur];
+      }
+      WVD_TRY(run_head(fo));
+      t0 += T;
+      fo += fs.video;
+    }
   }
   cache->next_latent += n;
   cache->next_frame += fr.video;
   if (first) cache->rule = first_frame_rule != 0;
   return WVD_OK;
+}
+
+}  // namespace
+
+extern "C" wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* packed, wvd_cache cache,
+                                       const wvd_tensor* z, int first, int first_frame_rule, wvd_tensor* video,
+                                       int64_t frame_offset, void* ws, size_t ws_bytes, wvd_stream stream) {
+  return decode_chunk_impl(d, packed, cache, z, first, first_frame_rule, video, frame_offset, 0, ws, ws_bytes,
+                           stream);
+}
+
+extern "C" wvd_status wvd_decode_chunk_split(const wvd_decoder_desc* d, const void* packed, wvd_cache cache,
+                                             const wvd_tensor* z, int first, int first_frame_rule, wvd_tensor* video,
+                                             int64_t frame_offset, int high_latent_frames, void* ws, size_t ws_bytes,
+                                             wvd_stream stream) {
+  return decode_chunk_impl(d, packed, cache, z, first, first_frame_rule, video, frame_offset, high_latent_frames, ws,
+                           ws_bytes, stream);
 }
 
 // ==============================================================================================

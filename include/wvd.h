@@ -219,6 +219,21 @@ wvd_status wvd_decode_chunk(const wvd_decoder_desc* d, const void* packed, wvd_c
 /* Video frames a chunk of n latent frames produces. */
 int64_t wvd_chunk_video_frames(const wvd_decoder_desc* d, int64_t n, int first, int first_frame_rule);
 
+/* Per-level pass sizes (the FastVideo compare page's suggestion to run many frames through the
+ * small early levels and few through the large late ones, section "Memory"): decode one chunk of
+ * n latent frames like wvd_decode_chunk, but with 0 < high_latent_frames < n the stages after
+ * the last temporal upsample and the head run in sub-passes of high_latent_frames latent frames
+ * (the last one shorter), each with the history the previous one left. The video is bit-for-bit
+ * the same as with wvd_decode_chunk; the early stages get n frames' worth of work per launch,
+ * while the memory of the late stages is bounded by high_latent_frames.
+ * high_latent_frames = 0 or >= n: one pass (wvd_decode_chunk). The workspace comes from
+ * wvd_decode_workspace_bytes_split(d, n, high_latent_frames); same errors as wvd_decode_chunk,
+ * and WVD_ERR_ARG for a negative high_latent_frames. */
+size_t wvd_decode_workspace_bytes_split(const wvd_decoder_desc* d, int max_latent_frames, int high_latent_frames);
+wvd_status wvd_decode_chunk_split(const wvd_decoder_desc* d, const void* packed, wvd_cache cache, const wvd_tensor* z,
+                                  int first, int first_frame_rule, wvd_tensor* video, int64_t frame_offset,
+                                  int high_latent_frames, void* ws, size_t ws_bytes, wvd_stream stream);
+
 /* ============================================================================================
  * Kernel timing (measurement support): when enabled, the library records a HIP event pair
  * around every launch of the matrix-core convolution kernel (and of the memory-bound kernels) on

@@ -8,7 +8,8 @@
     seeded positions (tests/golden/decoder_onepass_samples.npz, written by make_decoder_golden.py
     from the oracle alone), and bitwise pass-size invariance;
   * streaming 5 s decode [1,48,31,44,78] -> 121 frames: bitwise equal for 4 frames per pass, 3,
-    and all 31 in one pass (the one-shot form).
+    all 31 in one pass (the one-shot form), and per-level pass sizes (8 or 16 latent frames
+    through the early stages, sub-passes of 4 through the late ones).
 """
 import math
 import os
@@ -98,11 +99,11 @@ def test_streaming_decode_full_size_pass_size_invariant():
     torch.cuda.synchronize()
     assert tuple(v4.shape) == (1, 3, 121, 704, 1248)
     assert bool(torch.isfinite(v4.float()).all())
-    for fpp in (3, 31):
-        log(f"streaming decode fpp={fpp}")
-        v = dec.decode(z, frames_per_pass=fpp)
+    for fpp, early in ((3, None), (31, None), (4, 8), (4, 16)):
+        log(f"streaming decode fpp={fpp} early={early}")
+        v = dec.decode(z, frames_per_pass=fpp, early_frames_per_pass=early)
         torch.cuda.synchronize()
-        assert torch.equal(v, v4), fpp
+        assert torch.equal(v, v4), (fpp, early)
         del v
         dec._ws = None
         torch.cuda.empty_cache()

@@ -444,6 +444,23 @@ def test_small_decoder_matches_oracle_and_is_pass_size_invariant(rule):
     assert q >= 55.0
 
 
+@pytest.mark.parametrize("rule", [True, False])
+def test_small_decoder_per_level_pass_sizes_same_bits(rule):
+    """Early stages over many latent frames per pass, the late ones in sub-passes
+    (wvd_decode_chunk_split): the same bits as plain passes, for sub-passes that divide the chunk
+    or not, with and without the first-frame rule."""
+    hw = (5, 7)
+    z, params = wl.decoder_weights(SMALL_GPU, seed=51, latent_frames=7, latent_hw=hw)
+    dec = _gpu_decoder(SMALL_GPU, params, hw)
+    zd = z.to(torch.bfloat16).cuda()
+    base = dec.decode(zd, frames_per_pass=2, first_frame_rule=rule).clone()
+    for fpp, early in ((2, 4), (2, 7), (1, 3), (3, 5), (2, 2)):
+        log(f"split decode rule={rule} frames_per_pass={fpp} early={early}")
+        v = dec.decode(zd, frames_per_pass=fpp, first_frame_rule=rule, early_frames_per_pass=early)
+        torch.cuda.synchronize()
+        assert torch.equal(v, base), (fpp, early)
+
+
 WIDE_TAIL_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 32, 224))
 
 
