@@ -94,8 +94,15 @@ struct TimingRecord {
 };
 // The memory-bound kernels of the path, timed like the convs (algorithmic bytes: every input
 // element read once, every output element written once).
-enum MemKind { MEM_NORM_SILU = 0, MEM_HEAD_STENCIL = 1, MEM_CONVERT = 2, MEM_HEAD_FUSED = 3, MEM_KINDS = 4 };
-const char* const kMemKindNames[MEM_KINDS] = {"norm_silu", "head_stencil", "convert", "head_fused"};
+enum MemKind {
+  MEM_NORM_SILU = 0,
+  MEM_HEAD_STENCIL = 1,
+  MEM_CONVERT = 2,
+  MEM_HEAD_FUSED = 3,
+  MEM_HEAD_STREAM = 4,
+  MEM_KINDS = 5
+};
+const char* const kMemKindNames[MEM_KINDS] = {"norm_silu", "head_stencil", "convert", "head_fused", "head_stream"};
 struct LaunchRecord {
   int config;
   float ms;
@@ -1258,17 +1265,26 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       zbuf = bx[cur ^ 1];
     }
     const int co = d->out_channels;
-    if (head_fused_supported((int)round_up(c, 32))) {
+    const int cip = (int)round_up(c, 32);
+    if (head_stream_supported(cip, co) || head_fused_supported(cip)) {
       // tap conv + stencil in one kernel (no tap planes in memory); reads the activation (and
-      // its history) once, writes co bf16 channels
+      // its history) once, writes co bf16 channels; the input-stationary kernel up to 96
+      // channels and 3 colours
       const int slot = p.out_slot;
       const bf16_t* hist = slot_hist(slot);
       const int Th = cache->valid[slot];
       const double hb = (double)(T + std::min(Th, 2)) * H * Wd * c * 2.0 + (double)P * co * 2.0;
-      WVD_TRY(run_mem(MEM_HEAD_FUSED, hb, s, "head launch", [&] {
-        return launch_head_fused(act, hist, Th, (int)T, H, Wd, c, (int)round_up(c, 32), (const bf16_t*)W_(p.out_w),
-                                 F_(p.out_b), co, (bf16_t*)video->data, video->t, (int)fo, s);
-      }));
+      if (head_stream_supported(cip, co)) {
+        WVD_TRY(run_mem(MEM_HEAD_STREAM, hb, s, "head launch", [&] {
+          return launch_head_stream(act, hist, Th, (int)T, H, Wd, c, cip, (const bf16_t*)W_(p.out_w), F_(p.out_b), co,
+                                    (bf16_t*)video->data, video->t, (int)fo, s);
+        }));
+      } else {
+        WVD_TRY(run_mem(MEM_HEAD_FUSED, hb, s, "head launch", [&] {
+          return launch_head_fused(act, hist, Th, (int)T, H, Wd, c, cip, (const bf16_t*)W_(p.out_w), F_(p.out_b), co,
+                                   (bf16_t*)video->data, video->t, (int)fo, s);
+        }));
+      }
       int v = cache->valid[slot];
       WVD_TRY(update_slot((char*)slot_ptr(slot), v, act, (int)T, p.slots[slot].frame_bytes, s));
       cache->valid[slot] = v;

@@ -109,6 +109,12 @@ hipError_t launch_pack_head(const void* w, int w_bf16, int Co, int Ci, int Npad,
 // The head's tap conv and stencil fused (input channels padded to Cip <= 192): x [T][H][W][C]
 // bf16 with Th history frames, packed head weights [64][3][Cip], video NCTHW bf16.
 bool head_fused_supported(int Cip);
+// The input-stationary variant (each input frame read once per tile): Cip <= 96, Co <= 3; same
+// arguments and output.
+bool head_stream_supported(int Cip, int Co);
+hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
+                              const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
+                              hipStream_t s);
 hipError_t launch_head_fused(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
                              const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
                              hipStream_t s);

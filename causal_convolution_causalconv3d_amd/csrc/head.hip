@@ -220,6 +220,163 @@ __global__ __launch_bounds__(512, 1) void head_fused_kernel(const bf16_t* __rest
   }
 }
 
+// Input-stationary fused head (Cip <= 96, Co <= 3). A workgroup owns one 16 x 32 tile (14 x 30
+// outputs, one-pixel overlap as above) and walks the frames: each input frame f is loaded once
+// and feeds the three outputs it belongs to, Z_f (temporal tap 2), Z_{f+1} (tap 1) and Z_{f+2}
+// (tap 0), whose accumulators rotate after every frame; Z_f is then complete and goes through
+// LDS to the stencil. So the activations are read once per tile instead of once per temporal
+// tap, and only the 27 tap channels in use (9 taps x 3 colours, one 32-row matrix block) are
+// computed. The next frame's operands load into registers while the current one computes. The
+// sum order of a Z value is temporal tap outermost, then chunk, then K half.
+constexpr int HS_N = 27;  // tap rows kept: tap * 3 + colour
+constexpr int HS_ZS = 28; // LDS floats per position for Z (27 + pad, 16-byte aligned rows)
+
+template <int NCH>
+__global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ hist,
+                                                             int Th, int T, int H, int W, int C,
+                                                             const bf16_t* __restrict__ wpk, const float* __restrict__ bias,
+                                                             int Co, bf16_t* __restrict__ video, int64_t frames, int fbase) {
+  constexpr int Cip = NCH * 32;
+  __shared__ __attribute__((aligned(16))) bf16_t wl[32 * HF_WROW];
+  __shared__ __attribute__((aligned(16))) float zs[HF_ROWS * HF_COLS * HS_ZS];
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int numR = (H + HF_OROWS - 1) / HF_OROWS, numC = (W + HF_OCOLS - 1) / HF_OCOLS;
+  const int total = numR * numC;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int q8 = total >> 3, r8 = total & 7;
+  const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
+  if (lin >= total) return;
+  const int rt = lin / numC;
+  const int h0 = rt * HF_OROWS, w0 = (lin - rt * numC) * HF_OCOLS;
+
+  // weights into LDS: row n = tap * 3 + o of the 32-row block from packed row tap * 4 + o
+  constexpr int WK8 = 3 * Cip / 8;
+  for (int q = tid; q < 32 * WK8; q += 512) {
+    const int n = q / WK8, k8 = q - n * WK8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < HS_N) v = *(const u32x4*)(wpk + (int64_t)((n / 3) * 4 + n % 3) * (3 * Cip) + k8 * 8);
+    *(u32x4*)(&wl[n * HF_WROW + k8 * 8]) = v;
+  }
+
+  // this lane's positions: tile rows 2*wave + mb (image row h0 - 1 + that), column l32
+  const int64_t frame_elems = (int64_t)H * W * C;
+  const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
+  uint32_t poff[2];
+  bool pin[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int hh = h0 - 1 + 2 * wave + mb, ww = w0 - 1 + l32;
+    pin[mb] = (hh >= 0) & (hh < H) & (ww >= 0) & (ww < W);
+    poff[mb] = pin[mb] ? (uint32_t)(((int64_t)hh * W + ww) * C * 2) : 0u;
+  }
+  // the operands of frame f (negative: history), all chunks
+  auto load_frame = [&](u32x4 (&dst)[NCH][2][2], int f) {
+    const bf16_t* fb = (f >= 0) ? x + (int64_t)f * frame_elems : hist + (int64_t)(f + Th) * frame_elems;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)fb, (short)0, (int)frame_bytes, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int ch = c * 32 + half * 16 + q * 8;
+          const int vo = (pin[mb] & (ch < C)) ? (int)(poff[mb] + ch * 2) : (int)frame_bytes;
+          dst[c][mb][q] = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0);
+        }
+  };
+
+  floatx16 za[2], zb[2], zc[2];  // Z_f, Z_{f+1}, Z_{f+2} while frame f is consumed
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) za[mb][r] = zb[mb][r] = zc[mb][r] = 0.0f;
+  // frame f's contributions: tap 0 to Z_{f+2}, tap 1 to Z_{f+1}, tap 2 to Z_f
+  auto consume = [&](const u32x4 (&bf)[NCH][2][2]) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32x4 a0 = *(const u32x4*)(&wl[l32 * HF_WROW + 0 * Cip + c * 32 + half * 16 + q * 8]);
+        const u32x4 a1 = *(const u32x4*)(&wl[l32 * HF_WROW + 1 * Cip + c * 32 + half * 16 + q * 8]);
+        const u32x4 a2 = *(const u32x4*)(&wl[l32 * HF_WROW + 2 * Cip + c * 32 + half * 16 + q * 8]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, bf[c][mb][q]);
+          zc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), bv, zc[mb], 0, 0, 0);
+          zb[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), bv, zb[mb], 0, 0, 0);
+          za[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a2), bv, za[mb], 0, 0, 0);
+        }
+      }
+  };
+  float bo[3];
+#pragma unroll
+  for (int o = 0; o < 3; ++o) bo[o] = (bias && o < Co) ? bias[o] : 0.0f;
+  // Z_t (in za) through LDS to the stencil, then the rotation
+  auto finish = [&](int t) {
+    if (t >= 0) {
+      __syncthreads();  // the previous frame's stencil is done with zs
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        float* zp = zs + ((2 * wave + mb) * HF_COLS + l32) * HS_ZS;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = g * 8 + half * 4;
+          if (n < HS_N)
+            *(float4*)(zp + n) = make_float4(za[mb][g * 4], za[mb][g * 4 + 1], za[mb][g * 4 + 2], za[mb][g * 4 + 3]);
+        }
+      }
+      __syncthreads();
+      if (tid < HF_OROWS * HF_OCOLS) {
+        const int orow = tid / HF_OCOLS, ocol = tid - orow * HF_OCOLS;
+        const int h = h0 + orow, w = w0 + ocol;
+        if (h < H && w < W) {
+          float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+              const float* z = zs + ((orow + j) * HF_COLS + ocol + k) * HS_ZS + (j * 3 + k) * 3;
+              a0 += z[0];
+              a1 += z[1];
+              a2 += z[2];
+            }
+          const int64_t HW = (int64_t)H * W;
+          const int64_t pix = (int64_t)(fbase + t) * HW + (int64_t)h * W + w;
+          const float av[3] = {a0, a1, a2};
+#pragma unroll
+          for (int o = 0; o < 3; ++o)
+            if (o < Co) video[(int64_t)o * frames * HW + pix] = (bf16_t)f32_to_bf16(av[o] + bo[o]);
+        }
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      za[mb] = zb[mb];
+      zb[mb] = zc[mb];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) zc[mb][r] = 0.0f;
+    }
+  };
+
+  // frames before the history are zero: start at the oldest frame held
+  const int f0 = -(Th < 2 ? Th : 2);
+  u32x4 breg[2][NCH][2][2];
+  load_frame(breg[0], f0);
+  __syncthreads();  // weights in place
+  for (int f = f0; f < T; f += 2) {
+    if (f + 1 < T) load_frame(breg[1], f + 1);
+    consume(breg[0]);
+    finish(f);
+    if (f + 1 >= T) break;
+    if (f + 2 < T) load_frame(breg[0], f + 2);
+    consume(breg[1]);
+    finish(f + 1);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pack_head(const void* w, int w_bf16, int Co, int Ci, int Npad, int Cip, bf16_t* out, hipStream_t s) {
@@ -230,6 +387,34 @@ hipError_t launch_pack_head(const void* w, int w_bf16, int Co, int Ci, int Npad,
 }
 
 bool head_fused_supported(int Cip) { return Cip % 32 == 0 && Cip <= HF_MAXCIP; }
+
+bool head_stream_supported(int Cip, int Co) { return Cip % 32 == 0 && Cip <= 96 && Co <= 3; }
+
+hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
+                              const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
+                              hipStream_t s) {
+  if (T == 0 || H == 0 || W == 0) return hipSuccess;
+  if (!head_stream_supported(Cip, Co) || C > Cip || (int64_t)H * W * C * 2 >= ((int64_t)1 << 31) || Th < 0 ||
+      (Th > 0 && !hist))
+    return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)((H + HF_OROWS - 1) / HF_OROWS) * ((W + HF_OCOLS - 1) / HF_OCOLS);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  switch (Cip / 32) {
+    case 1:
+      hipLaunchKernelGGL(head_stream_kernel<1>, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, wpk,
+                         bias, Co, video, frames, fbase);
+      break;
+    case 2:
+      hipLaunchKernelGGL(head_stream_kernel<2>, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, wpk,
+                         bias, Co, video, frames, fbase);
+      break;
+    default:
+      hipLaunchKernelGGL(head_stream_kernel<3>, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, wpk,
+                         bias, Co, video, frames, fbase);
+      break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_head_fused(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
                              const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,

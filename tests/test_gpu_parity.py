@@ -464,13 +464,18 @@ def test_small_decoder_per_level_pass_sizes_same_bits(rule):
 WIDE_TAIL_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 32, 224))
 
 
-def test_wide_last_stage_decoder_matches_oracle():
-    """A last stage wider than one fused-epilogue tile (224 channels): norm_out runs as its own
-    pass and the head as the tap-plane conv + stencil kernels (the fused paths' fallbacks)."""
+MID_TAIL_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 32, 160))
+
+
+@pytest.mark.parametrize("spec", [WIDE_TAIL_GPU, MID_TAIL_GPU], ids=["tail224", "tail160"])
+def test_wide_last_stage_decoder_matches_oracle(spec):
+    """Last stages wider than the input-stationary head takes (96 channels): 160 channels run
+    the frame-tiled fused head; 224 channels, wider than one fused-epilogue tile, run norm_out as
+    its own pass and the head as the tap-plane conv + stencil kernels (the fused paths' fallbacks)."""
     hw = (2, 3)
-    z, params = wl.decoder_weights(WIDE_TAIL_GPU, seed=54, latent_frames=3, latent_hw=hw)
-    ref = oracle.decode(z[0], oracle.as_numpy_params(params), WIDE_TAIL_GPU, frames_per_pass=3)
-    dec = _gpu_decoder(WIDE_TAIL_GPU, params, hw)
+    z, params = wl.decoder_weights(spec, seed=54, latent_frames=3, latent_hw=hw)
+    ref = oracle.decode(z[0], oracle.as_numpy_params(params), spec, frames_per_pass=3)
+    dec = _gpu_decoder(spec, params, hw)
     zd = z.to(torch.bfloat16).cuda()
     v3 = dec.decode(zd, frames_per_pass=3)
     v1 = dec.decode(zd, frames_per_pass=1)
@@ -479,7 +484,7 @@ def test_wide_last_stage_decoder_matches_oracle():
     got = v3[0].float().cpu().numpy()
     assert got.shape == ref.shape
     q = psnr(got, ref)
-    log(f"wide-tail decoder psnr {q:.2f} dB")
+    log(f"wide-tail decoder {spec.stage_channels} psnr {q:.2f} dB")
     assert q >= 55.0
 
 
