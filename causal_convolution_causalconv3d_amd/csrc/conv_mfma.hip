@@ -1016,6 +1016,7 @@ enum ConfigId {
   PHASE_DMA_N3_W8,  // PHASE_N3_W8 with LDS-DMA staging
   PHASE_DMA_N3_W4,  // x2 upsampling phases: 96 x (8 rows x 32 columns), two workgroups per CU
   PHASE_DMA_N3_M1_W8,  // the same tile, one row per wave: two 8-wave workgroups per CU
+  HALO_DMA_N2_W8,  // 64 x (16 rows x 32 columns): small grids
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -1024,7 +1025,7 @@ const ConfigEntry kConfigs[] = {
     WVD_HALO_CONFIG(6, 1, 8),       WVD_HALO_CONFIG(3, 2, 8),       WVD_HALO_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_CONFIG(3, 2, 8),
     WVD_HALO_DMA_CONFIG(6, 1, 8),    WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
-    WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8),
+    WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -1056,7 +1057,14 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   const int64_t T = p.T, H = p.H, W = p.W;
   const int Npad = p.Npad, phases = p.phases;
   if (Npad <= 32) return LIN_N1_M4_W4;
-  if (phases == 1 && p.kh == 3 && p.kw == 3) return (one_n_tile && Npad > 96) ? HALO_DMA_N6_W8 : HALO_DMA_N3_W8;
+  if (phases == 1 && p.kh == 3 && p.kw == 3) {
+    if (one_n_tile) return Npad > 96 ? HALO_DMA_N6_W8 : HALO_DMA_N3_W8;
+    // a grid of 96-wide tiles that leaves CUs idle (the 4-frame 44x78 level: 144 tiles) takes
+    // 64-wide ones if they still run in one round: two thirds of the tile time
+    const int64_t b3 = blocks_for(kConfigs[HALO_DMA_N3_W8], T, H, W, Npad);
+    const int64_t b2 = blocks_for(kConfigs[HALO_DMA_N2_W8], T, H, W, Npad);
+    return (Npad % 64 == 0 && b3 < cus && b2 <= cus) ? HALO_DMA_N2_W8 : HALO_DMA_N3_W8;
+  }
   // The phase convs (K = 4 taps x C) have short reductions and heavy epilogues, so they run 8-row
   // DMA halo tiles with 80 KB of LDS, two workgroups per CU, whose epilogues overlap other waves'
   // matrix work: one row per wave (four waves per SIMD) measured fastest at 96 and 192 channels
