@@ -45,7 +45,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
   constexpr int NT = WAVES * 64;
   constexpr int WPIECES = BN * 4;  // 16-byte pieces of one weight K step
   constexpr int WLOADS = (WPIECES + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[4][BN * LDS_ROW];  // weight stages
+  // weight stages; after the K loop, the per-wave areas of the staged epilogue (one-block waves)
+  constexpr int NBPL = (NB % 3 == 0) ? 3 : ((NB % 2 == 0) ? 2 : 1);
+  constexpr int SBL = StagedShape<NBPL>::BYTES;
+  constexpr int LDS_ELEMS = (MB == 1 && WAVES * SBL / 2 > 4 * BN * LDS_ROW) ? WAVES * SBL / 2 : 4 * BN * LDS_ROW;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_all[LDS_ELEMS];
+  bf16_t(*lds)[BN * LDS_ROW] = reinterpret_cast<bf16_t(*)[BN * LDS_ROW]>(lds_all);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -272,6 +277,23 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
     step(std::integral_constant<int, 5>{}, k + 5);
   }
 
+  if constexpr (MB == 1 && !NORM) {
+    if (p.staged) {
+      // The launcher sets staged only for the plain output mapping, where a wave's 32 positions
+      // (consecutive in the frame) are consecutive in the output: the frame is staged as one
+      // row of H*W columns. Every wave is past the loop's last barrier, so the weight stages
+      // are free.
+      ConvProblem q = p;
+      q.H = 1;
+      q.W = HW;
+      q.Ho = 1;
+      q.Wo = HW;
+      const int row0[1] = {0};
+      conv_epilogue_staged<NB, 1, false, NBPL>(q, acc, row0, mbase, tf, n0, 0, 0, lane,
+                                               (char*)lds_all + wave * SBL);
+      return;
+    }
+  }
   conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
 }
 
@@ -1127,8 +1149,12 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   if (config_id) *config_id = id;
   ConvProblem q = p;
   q.time_tiles = c.time_tiles;
-  q.staged = c.staged && !p.y_f32 && p.N % 8 == 0 && p.nsplit % 8 == 0 && ((uintptr_t)p.y & 15) == 0 &&
-             ((uintptr_t)p.res & 15) == 0;
+  // the staged epilogue: the DMA kernels, and the linear kernel's one-block waves on the plain
+  // output mapping (consecutive positions of a frame consecutive in the output)
+  const bool plain_map = p.phases == 1 && p.hmul == 1 && p.wmul == 1 && p.Ho == p.H && p.Wo == p.W;
+  const bool lin_staged = c.halo == 0 && c.mb == 1 && plain_map && !p.norm_gamma;
+  q.staged = (c.staged || lin_staged) && !p.y_f32 && p.N % 8 == 0 && p.nsplit % 8 == 0 &&
+             ((uintptr_t)p.y & 15) == 0 && ((uintptr_t)p.res & 15) == 0;
   int64_t gx = c.phase_in_x ? blocks * p.phases : blocks;
   if (c.wgs_per_cu) {
     // DMA kernels: a multiple of 8 workgroups (XCD ranges); with persistent tiles no more than
