@@ -296,19 +296,35 @@ int history_frames_after(int T, int Th) {
   return Th;
 }
 
-// In-place update of a cache slot holding `valid` frames right-aligned in [2][frame].
-wvd_status update_slot(char* slot, int& valid, const void* x, int T, size_t frame_bytes, hipStream_t s) {
+// Cache slots are double-buffered: two halves of [2][frame], `half` naming the one that holds
+// the current history (`valid` frames, right-aligned). The update writes the next history (the
+// page's cached_conv rule: the last two input frames, or the old last frame and a one-frame
+// input) into the other half, so it can run as side work of the very launch that still reads
+// the current one (`job`, zero bytes when there is nothing to copy); `half` and `valid` become
+// the slot's state once that launch is enqueued.
+void slot_update_job(char* slot, int& half, int& valid, const void* x, int T, size_t frame_bytes, CopyJob& job) {
+  memset(&job, 0, sizeof(job));
+  const char* cur = slot + (size_t)half * 2 * frame_bytes;
+  char* nxt = slot + (size_t)(half ^ 1) * 2 * frame_bytes;
   if (T >= 2) {
-    WVD_HIP(hipMemcpyAsync(slot, (const char*)x + (size_t)(T - 2) * frame_bytes, 2 * frame_bytes,
-                           hipMemcpyDeviceToDevice, s),
-            "cache update");
+    job.src[0] = (const char*)x + (size_t)(T - 2) * frame_bytes;
+    job.dst[0] = nxt;
+    job.bytes[0] = (int64_t)(2 * frame_bytes);
     valid = 2;
   } else if (T == 1) {
-    if (valid >= 1) WVD_HIP(hipMemcpyAsync(slot, slot + frame_bytes, frame_bytes, hipMemcpyDeviceToDevice, s), "cache update");
-    WVD_HIP(hipMemcpyAsync(slot + frame_bytes, x, frame_bytes, hipMemcpyDeviceToDevice, s), "cache update");
+    if (valid >= 1) {
+      job.src[0] = cur + frame_bytes;
+      job.dst[0] = nxt;
+      job.bytes[0] = (int64_t)frame_bytes;
+    }
+    job.src[1] = x;
+    job.dst[1] = nxt + frame_bytes;
+    job.bytes[1] = (int64_t)frame_bytes;
     valid = valid >= 1 ? 2 : 1;
+  } else {
+    return;
   }
-  return WVD_OK;
+  half ^= 1;
 }
 
 }  // namespace
@@ -823,7 +839,7 @@ Plan make_plan(const wvd_decoder_desc* d) {
   off = 0;
   for (auto& s : p.slots) {
     s.offset = off;
-    off += (size_t)round_up((int64_t)(2 * s.frame_bytes), 256);
+    off += (size_t)round_up((int64_t)(4 * s.frame_bytes), 256);  // two halves of two frames
   }
   p.cache_bytes = off;
   return p;
@@ -960,6 +976,7 @@ struct wvd_cache_s {
   uint64_t hash;
   char* storage;
   std::vector<int> valid;  // frames held per slot (right-aligned)
+  std::vector<int> half;   // the slot half holding them
   int64_t next_latent;
   int64_t next_frame;
   int rule;  // first_frame_rule of the decode in progress (-1 before the first chunk)
@@ -1047,6 +1064,7 @@ extern "C" wvd_status wvd_cache_init(const wvd_decoder_desc* d, void* storage, w
   c->hash = desc_hash(d);
   c->storage = (char*)storage;
   c->valid.assign(p.slots.size(), 0);
+  c->half.assign(p.slots.size(), 0);
   c->next_latent = 0;
   c->next_frame = 0;
   c->rule = -1;
@@ -1057,6 +1075,7 @@ extern "C" wvd_status wvd_cache_init(const wvd_decoder_desc* d, void* storage, w
 extern "C" wvd_status wvd_cache_reset(wvd_cache c) {
   if (!c) return fail(WVD_ERR_ARG, "cache is null");
   std::fill(c->valid.begin(), c->valid.end(), 0);
+  std::fill(c->half.begin(), c->half.end(), 0);
   c->next_latent = 0;
   c->next_frame = 0;
   c->rule = -1;
@@ -1139,16 +1158,18 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
   auto slot_ptr = [&](int slot) { return (bf16_t*)(cache->storage + p.slots[slot].offset); };
   auto slot_hist = [&](int slot) -> const bf16_t* {
     const int v = cache->valid[slot];
-    return v ? (const bf16_t*)((char*)slot_ptr(slot) + (2 - v) * p.slots[slot].frame_bytes) : nullptr;
+    const size_t fb = p.slots[slot].frame_bytes;
+    return v ? (const bf16_t*)((char*)slot_ptr(slot) + (size_t)cache->half[slot] * 2 * fb + (2 - v) * fb) : nullptr;
   };
-  // conv with the slot's history, then the slot update from the conv's input
+  // conv with the slot's history; the slot update from the conv's input is its side work
   auto cached_conv = [&](ConvProblem cp, int slot, const bf16_t* input, int T, double flops) -> wvd_status {
     cp.hist = slot_hist(slot);
     cp.Th = cache->valid[slot];
+    int v = cache->valid[slot], h = cache->half[slot];
+    slot_update_job((char*)slot_ptr(slot), h, v, input, T, p.slots[slot].frame_bytes, cp.copy);
     WVD_TRY(run_conv(cp, s, flops));
-    int v = cache->valid[slot];
-    WVD_TRY(update_slot((char*)slot_ptr(slot), v, input, T, p.slots[slot].frame_bytes, s));
     cache->valid[slot] = v;
+    cache->half[slot] = h;
     return WVD_OK;
   };
 
@@ -1274,20 +1295,23 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       const bf16_t* hist = slot_hist(slot);
       const int Th = cache->valid[slot];
       const double hb = (double)(T + std::min(Th, 2)) * H * Wd * c * 2.0 + (double)P * co * 2.0;
+      // the slot update from the activation is the head launch's side work
+      int v = cache->valid[slot], h = cache->half[slot];
+      CopyJob job;
+      slot_update_job((char*)slot_ptr(slot), h, v, act, (int)T, p.slots[slot].frame_bytes, job);
       if (head_stream_supported(cip, co)) {
         WVD_TRY(run_mem(MEM_HEAD_STREAM, hb, s, "head launch", [&] {
           return launch_head_stream(act, hist, Th, (int)T, H, Wd, c, cip, (const bf16_t*)W_(p.out_w), F_(p.out_b), co,
-                                    (bf16_t*)video->data, video->t, (int)fo, s);
+                                    (bf16_t*)video->data, video->t, (int)fo, s, &job);
         }));
       } else {
         WVD_TRY(run_mem(MEM_HEAD_FUSED, hb, s, "head launch", [&] {
           return launch_head_fused(act, hist, Th, (int)T, H, Wd, c, cip, (const bf16_t*)W_(p.out_w), F_(p.out_b), co,
-                                   (bf16_t*)video->data, video->t, (int)fo, s);
+                                   (bf16_t*)video->data, video->t, (int)fo, s, &job);
         }));
       }
-      int v = cache->valid[slot];
-      WVD_TRY(update_slot((char*)slot_ptr(slot), v, act, (int)T, p.slots[slot].frame_bytes, s));
       cache->valid[slot] = v;
+      cache->half[slot] = h;
       return WVD_OK;
     }
     float* Z = (float*)zbuf;

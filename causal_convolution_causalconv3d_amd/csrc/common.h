@@ -38,6 +38,46 @@ __device__ __forceinline__ float silu_f32(float v) {
 // Host-side launch helpers (defined in the .hip files, called by api.cpp).
 namespace wvd {
 
+// Side work of a kernel launch: up to two byte ranges copied (16-byte multiples, 16-byte
+// aligned) that the kernel itself neither reads nor writes otherwise (the next history of a
+// double-buffered cache slot). Each workgroup copies its share once its own work is done, so
+// the copy runs beside other workgroups' matrix work.
+struct CopyJob {
+  const void* src[2];
+  void* dst[2];
+  int64_t bytes[2];
+};
+
+// The share of workgroup wg of nwg (threads tid of nthreads) of a CopyJob: 16-byte vector loads
+// and stores, four in flight per thread.
+__device__ __forceinline__ void run_copy_job(const CopyJob& c, int64_t wg, int64_t nwg, int tid, int nthreads) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = c.bytes[j] >> 4;
+    if (n == 0) continue;
+    const uint4* src = (const uint4*)c.src[j];
+    uint4* dst = (uint4*)c.dst[j];
+    const int64_t stride = nwg * nthreads;
+    int64_t i = wg * nthreads + tid;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+      const uint4 a = src[i], b = src[i + stride], d = src[i + 2 * stride], e = src[i + 3 * stride];
+      dst[i] = a;
+      dst[i + stride] = b;
+      dst[i + 2 * stride] = d;
+      dst[i + 3 * stride] = e;
+    }
+    for (; i < n; i += stride) dst[i] = src[i];
+  }
+}
+
+// run_copy_job over the whole launch: this workgroup's share.
+__device__ __forceinline__ void run_copy_share(const CopyJob& c) {
+  const int64_t wg = blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+  const int64_t nwg = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+  const int tid = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
+  run_copy_job(c, wg, nwg, tid, blockDim.x * blockDim.y * blockDim.z);
+}
+
 // One convolution "problem" for the matrix-core implicit-GEMM kernel. The GEMM is
 //   D[n][m] = sum_k Wpk[phase][n][k] * A[k][m]
 // with m an output position of the input grid (t, h, w), n an output channel and k a (tap,
@@ -71,6 +111,7 @@ struct ConvProblem {
   int norm_silu;
   int time_tiles;  // set by the launcher: the halo kernel's tile order
   int staged;      // set by the launcher: store the output through LDS (see conv_epilogue_staged)
+  CopyJob copy;    // side work (zero bytes: none)
 };
 
 // force_config >= 0 runs that configuration (hipErrorNotSupported when it cannot run p);
@@ -114,10 +155,10 @@ bool head_fused_supported(int Cip);
 bool head_stream_supported(int Cip, int Co);
 hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
                               const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
-                              hipStream_t s);
+                              hipStream_t s, const CopyJob* copy = nullptr);
 hipError_t launch_head_fused(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
                              const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
-                             hipStream_t s);
+                             hipStream_t s, const CopyJob* copy = nullptr);
 hipError_t launch_head_stencil(const float* Z, int Co, const float* bias, bf16_t* video, int64_t frames, int fbase,
                                int T, int H, int W, hipStream_t s);
 

@@ -291,10 +291,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void conv_mfma_kernel(const ConvProb
       const int row0[1] = {0};
       conv_epilogue_staged<NB, 1, false, NBPL>(q, acc, row0, mbase, tf, n0, 0, 0, lane,
                                                (char*)lds_all + wave * SBL);
+      run_copy_share(p.copy);
       return;
     }
   }
   conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
+  run_copy_share(p.copy);
 }
 
 // Halo-tile variant for KS x KS spatial taps: KS = 3 (phases == 1, kh == kw == 3, any kt) or
@@ -559,6 +561,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_kernel(const 
   if (g < ng) stage(std::integral_constant<int, 0>{}, g);
 
   conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tf, n0, pa, pb, half);
+  run_copy_share(p.copy);
 }
 
 // LDS-DMA variant of the 3x3-tap halo kernel. Same tiles, K order, fragments and epilogue; the
@@ -671,7 +674,10 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, G8 = gridDim.x >> 3;
   const int q8 = total >> 3, r8 = total & 7;
   const int xs = xcd * q8 + (xcd < r8 ? xcd : r8), xl = q8 + (xcd < r8 ? 1 : 0);
-  if (local >= xl) return;  // no tile for this workgroup (uniform)
+  if (local >= xl) {  // no tile for this workgroup (uniform)
+    run_copy_share(p.copy);
+    return;
+  }
   struct Tile {
     int tf, h0, w0, n0, phase;
   };
@@ -928,6 +934,7 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
       }
       conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tc.tf, tc.n0, pa, pb, half);
     }
+    run_copy_share(p.copy);
     return;
   }
   int g = 0;  // stage within the tile
@@ -978,6 +985,7 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
   }
   // fetches past the end (into slots and buffers nobody reads) land before the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  run_copy_share(p.copy);
 }
 
 // DMA conv kernels without a fused norm run persistent workgroups (one per resident slot,

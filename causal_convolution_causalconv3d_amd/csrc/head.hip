@@ -89,7 +89,8 @@ constexpr int HF_LDS = (HF_N * HF_WROW * 2 > HF_ROWS * HF_COLS * HF_Z * 4) ? HF_
 __global__ __launch_bounds__(512, 1) void head_fused_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ hist,
                                                             int Th, int T, int H, int W, int C, int Cip,
                                                             const bf16_t* __restrict__ wpk, const float* __restrict__ bias,
-                                                            int Co, bf16_t* __restrict__ video, int64_t frames, int fbase) {
+                                                            int Co, bf16_t* __restrict__ video, int64_t frames, int fbase,
+                                                            const CopyJob copy) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[HF_LDS];
   bf16_t* wl = (bf16_t*)lds;   // [64][HF_WROW] during the K loop
   float* zl = (float*)lds;     // [16][32][36] afterwards
@@ -218,6 +219,7 @@ __global__ __launch_bounds__(512, 1) void head_fused_kernel(const bf16_t* __rest
         if (o < Co) video[(int64_t)o * frames * HW + pix] = (bf16_t)f32_to_bf16(av[o] + (bias ? bias[o] : 0.0f));
     }
   }
+  run_copy_share(copy);
 }
 
 // Input-stationary fused head (Cip <= 96, Co <= 3). A workgroup owns one 16 x 32 tile (14 x 30
@@ -235,7 +237,8 @@ template <int NCH>
 __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ hist,
                                                              int Th, int T, int H, int W, int C,
                                                              const bf16_t* __restrict__ wpk, const float* __restrict__ bias,
-                                                             int Co, bf16_t* __restrict__ video, int64_t frames, int fbase) {
+                                                             int Co, bf16_t* __restrict__ video, int64_t frames, int fbase,
+                                                             const CopyJob copy) {
   constexpr int Cip = NCH * 32;
   __shared__ __attribute__((aligned(16))) bf16_t wl[32 * HF_WROW];
   __shared__ __attribute__((aligned(16))) float zs[HF_ROWS * HF_COLS * HS_ZS];
@@ -248,7 +251,10 @@ __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __res
   const int xcd = b & 7, local = b >> 3;
   const int q8 = total >> 3, r8 = total & 7;
   const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
-  if (lin >= total) return;
+  if (lin >= total) {
+    run_copy_share(copy);
+    return;
+  }
   const int rt = lin / numC;
   const int h0 = rt * HF_OROWS, w0 = (lin - rt * numC) * HF_OCOLS;
 
@@ -375,6 +381,7 @@ __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __res
     consume(breg[1]);
     finish(f + 1);
   }
+  run_copy_share(copy);
 }
 
 }  // namespace
@@ -392,7 +399,8 @@ bool head_stream_supported(int Cip, int Co) { return Cip % 32 == 0 && Cip <= 96 
 
 hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
                               const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
-                              hipStream_t s) {
+                              hipStream_t s, const CopyJob* copy) {
+  const CopyJob job = copy ? *copy : CopyJob{};
   if (T == 0 || H == 0 || W == 0) return hipSuccess;
   if (!head_stream_supported(Cip, Co) || C > Cip || (int64_t)H * W * C * 2 >= ((int64_t)1 << 31) || Th < 0 ||
       (Th > 0 && !hist))
@@ -402,15 +410,15 @@ hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T
   switch (Cip / 32) {
     case 1:
       hipLaunchKernelGGL(head_stream_kernel<1>, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, wpk,
-                         bias, Co, video, frames, fbase);
+                         bias, Co, video, frames, fbase, job);
       break;
     case 2:
       hipLaunchKernelGGL(head_stream_kernel<2>, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, wpk,
-                         bias, Co, video, frames, fbase);
+                         bias, Co, video, frames, fbase, job);
       break;
     default:
       hipLaunchKernelGGL(head_stream_kernel<3>, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, wpk,
-                         bias, Co, video, frames, fbase);
+                         bias, Co, video, frames, fbase, job);
       break;
   }
   return hipGetLastError();
@@ -418,13 +426,14 @@ hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T
 
 hipError_t launch_head_fused(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
                              const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
-                             hipStream_t s) {
+                             hipStream_t s, const CopyJob* copy) {
+  const CopyJob job = copy ? *copy : CopyJob{};
   if (T == 0 || H == 0 || W == 0) return hipSuccess;
   if (!head_fused_supported(Cip) || C > Cip || (int64_t)H * W * C * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)T * ((H + HF_OROWS - 1) / HF_OROWS) * ((W + HF_OCOLS - 1) / HF_OCOLS);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(head_fused_kernel, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, Cip, wpk, bias,
-                     Co, video, frames, fbase);
+                     Co, video, frames, fbase, job);
   return hipGetLastError();
 }
 

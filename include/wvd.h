@@ -194,7 +194,10 @@ wvd_status wvd_decoder_param_info(const wvd_decoder_desc* d, int index, const ch
 size_t wvd_decoder_packed_bytes(const wvd_decoder_desc* d);
 wvd_status wvd_decoder_pack(const wvd_decoder_desc* d, const float* const* params, void* packed, wvd_stream stream);
 
-/* The cache: every causal conv's two-frame history, in caller-owned device storage. */
+/* The cache: every causal conv's two-frame history, in caller-owned device storage, twice (the
+ * current history and the next one: a chunk's decode writes each slot's next history on a
+ * second HIP stream of the device, created at the first decode, beside the conv that reads the
+ * current one, and orders it before every later work on the caller's stream with events). */
 typedef struct wvd_cache_s* wvd_cache;
 size_t wvd_cache_bytes(const wvd_decoder_desc* d);
 wvd_status wvd_cache_init(const wvd_decoder_desc* d, void* storage, wvd_cache* out); /* empty history */
