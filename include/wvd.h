@@ -195,9 +195,8 @@ size_t wvd_decoder_packed_bytes(const wvd_decoder_desc* d);
 wvd_status wvd_decoder_pack(const wvd_decoder_desc* d, const float* const* params, void* packed, wvd_stream stream);
 
 /* The cache: every causal conv's two-frame history, in caller-owned device storage, twice (the
- * current history and the next one: a chunk's decode writes each slot's next history on a
- * second HIP stream of the device, created at the first decode, beside the conv that reads the
- * current one, and orders it before every later work on the caller's stream with events). */
+ * current history and the next one: the launch of a chunk's conv that reads a slot's current
+ * history also copies the conv's input frames into the slot's other half). */
 typedef struct wvd_cache_s* wvd_cache;
 size_t wvd_cache_bytes(const wvd_decoder_desc* d);
 wvd_status wvd_cache_init(const wvd_decoder_desc* d, void* storage, wvd_cache* out); /* empty history */
