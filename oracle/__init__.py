@@ -18,7 +18,12 @@ Readings taken where the page is silent or the workload text differs (each liste
     not the page's x / max(||x||, 1e-12) * sqrt(C) form; they differ by <= eps / (2 mean x^2).
   * The synthetic decoder has no post_quant_conv, attention, DupUp3D shortcut, unpatchify or
     clamp: conv_in -> mid residual blocks -> up stages (residual blocks, time conv on the
-    temporal stages, spatial x2 conv) -> norm_out + SiLU -> conv_out.
+    temporal stages, spatial x2 conv) -> norm_out + SiLU -> conv_out. A spec with the real
+    topology's switches (workloads.REAL_DECODER and smaller ones) adds them in the page's order:
+    post_quant_conv before conv_in (a 1x1x1 conv: per pass is the same as over all frames);
+    attention after the first mid block; per stage an optional spatial step and DupUp3D of the
+    stage's input added after it; unpatchify, then clamp. With norm_l2 the RMS norm is the
+    page's x / max(||x||, 1e-12) * sqrt(C) * gamma (rms_norm_l2).
   * Each stage's first residual block changes channels (with a 1x1x1 shortcut when they differ).
   * The upsample-stage workload runs the spatial step first, then the time conv.
   * A conv whose input has zero frames is skipped and leaves its history unchanged.
@@ -41,6 +46,15 @@ index, or a transposed operand fails one of them:
   decoder       frame counts 4T-3 (tests/golden/frame_counts.txt, the page's numbers); chunked ==
                 one-shot bitwise for every pass size; video causality; decode independence;
                 and the composition against torch float64 library ops.
+  real parts    (tests/test_oracle_real.py) rms_norm_l2 hand values, zero vector, and equality
+                with rms_norm(eps=0); attention: vanishing queries give the frame's mean value,
+                scalar loops, torch float64 scaled_dot_product_attention, equivariance under
+                position permutations; dup_up: ratio 8 is nearest x2 in t, h, w, ratio 2 maps
+                channel pairs to row pairs (loops), torch repeat_interleave/permute for five
+                shapes; unpatchify: loops and an inverse space-to-depth; clamp; the real
+                topology's 110 parameters (the page's count); a small real-topology decoder:
+                frame counts, chunked == one-shot bitwise, causality, and its composition
+                against torch float64 library ops.
 No absolute value of the synthetic decoder is printed on the pages: the decoder's output values
 are pinned only through the identities above (parity of absolute values: pinned by op, the
 composition by invariants).
@@ -203,19 +217,19 @@ def norm_silu(x, gamma, eps) -> np.ndarray:
 
 
 def resblock(x, p: Dict[str, np.ndarray], prefix: str, cache: Dict[str, np.ndarray], eps: float,
-             given_hist: Optional[np.ndarray] = None) -> np.ndarray:
+             given_hist: Optional[np.ndarray] = None, l2: bool = False) -> np.ndarray:
     """Residual block: conv2(SiLU(norm2(conv1(SiLU(norm1(x)))))) + shortcut, the shortcut being x
     or a 1x1x1 conv of x when the channel count changes (the page's residual block part).
 
     `given_hist`, when set, is the activated history placed in front of both convs' inputs (the
     single-block workload's given cache); otherwise each conv uses its own entry of `cache`."""
     x = _f32(x)
-    a1 = norm_silu(x, p[f"{prefix}.norm1.gamma"], eps)
+    a1 = silu(_norm(x, p[f"{prefix}.norm1.gamma"], eps, l2))
     if given_hist is not None:
         h = causal_conv3d(a1, p[f"{prefix}.conv1.weight"], p.get(f"{prefix}.conv1.bias"), given_hist)
     else:
         h = cached_conv(a1, p[f"{prefix}.conv1.weight"], p.get(f"{prefix}.conv1.bias"), cache, f"{prefix}.conv1")
-    a2 = norm_silu(h, p[f"{prefix}.norm2.gamma"], eps)
+    a2 = silu(_norm(h, p[f"{prefix}.norm2.gamma"], eps, l2))
     if given_hist is not None:
         h2 = causal_conv3d(a2, p[f"{prefix}.conv2.weight"], p.get(f"{prefix}.conv2.bias"), given_hist)
     else:
@@ -270,6 +284,85 @@ def upsample_stage(x, p: Dict[str, np.ndarray], prefix: str = "", cache=None) ->
 
 
 # ----------------------------------------------------------------------------------------------
+# Parts of the real topology (the page's attention, dup_up, unpatchify and rms_norm functions and
+# its part list): mid-block attention, DupUp3D, unpatchify, clamp, the L2 form of the RMS norm
+# ----------------------------------------------------------------------------------------------
+def rms_norm_l2(x, gamma) -> np.ndarray:
+    """The page's WanRMS_norm: x / max(||x||_2 over channels, 1e-12) * sqrt(C) * gamma[c], in
+    double, rounded to fp32 once."""
+    x64 = _f32(x).astype(np.float64)
+    C = x64.shape[0]
+    nrm = np.sqrt((x64 * x64).sum(axis=0, keepdims=True))
+    g = _f32(gamma).astype(np.float64).reshape((C,) + (1,) * (x64.ndim - 1))
+    return (x64 / np.maximum(nrm, 1e-12) * np.sqrt(C) * g).astype(np.float32)
+
+
+def _norm(x, gamma, spec_or_eps, l2: bool = False) -> np.ndarray:
+    return rms_norm_l2(x, gamma) if l2 else rms_norm(x, gamma, spec_or_eps)
+
+
+def attention(x, p: Dict[str, np.ndarray], prefix: str, eps: float, l2: bool = False) -> np.ndarray:
+    """The page's attention part, per frame: n = RMS norm of x (no SiLU); q, k, v = channels
+    [0, C), [C, 2C), [2C, 3C) of a 1x1 conv C -> 3C of n; softmax(q k^T / sqrt(C)) v over the
+    frame's h*w positions (one head of dim C, no mask); a 1x1 conv C -> C; plus x. The products
+    and the softmax in double (numpy matmul as the library step), each conv through conv3d."""
+    x = _f32(x)
+    C, T, H, W = x.shape
+    n = _norm(x, p[f"{prefix}.norm.gamma"], eps, l2)
+    qkv = causal_conv3d(n, p[f"{prefix}.qkv.weight"], p.get(f"{prefix}.qkv.bias"))
+    o = np.empty((C, T, H, W), dtype=np.float32)
+    for t in range(T):
+        q = qkv[:C, t].reshape(C, H * W).T.astype(np.float64)          # [positions, C]
+        k = qkv[C:2 * C, t].reshape(C, H * W).T.astype(np.float64)
+        v = qkv[2 * C:, t].reshape(C, H * W).T.astype(np.float64)
+        s = (q @ k.T) / np.sqrt(C)                                      # [query, key]
+        s -= s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        a = e / e.sum(axis=1, keepdims=True)
+        o[:, t] = (a @ v).T.reshape(C, H, W).astype(np.float32)
+    y = causal_conv3d(o, p[f"{prefix}.proj.weight"], p.get(f"{prefix}.proj.bias"))
+    return add(y, x)
+
+
+def dup_up(x, out_channels: int, ft: int, first: bool) -> np.ndarray:
+    """DupUp3D (the page's part list): with r = out * ft * 4 / in,
+    dup[c, ft*t + a, 2y + i, 2x + j] = x[(4*ft*c + 4a + 2i + j) // r, t, y, x]; on the pass
+    holding latent frame 0 only the last of that frame's ft time copies is kept."""
+    x = _f32(x)
+    Cin, T, H, W = x.shape
+    if (out_channels * ft * 4) % Cin:
+        raise ValueError("DupUp3D needs out * ft * 4 to be a multiple of the input channels")
+    r = out_channels * ft * 4 // Cin
+    out = np.empty((out_channels, ft * T, 2 * H, 2 * W), dtype=np.float32)
+    c = np.arange(out_channels)
+    for a in range(ft):
+        for i in range(2):
+            for j in range(2):
+                out[:, a::ft, i::2, j::2] = x[(4 * ft * c + 4 * a + 2 * i + j) // r]
+    return np.ascontiguousarray(out[:, ft - 1:]) if first else out
+
+
+def unpatchify(x, patch: int) -> np.ndarray:
+    """[3 * p^2, F, h, w] -> [3, F, p*h, p*w]: channel (k*p + j)*p + i is colour k at row offset i,
+    column offset j (the page's unpatchify)."""
+    x = _f32(x)
+    Cp, Fr, h, w = x.shape
+    if patch == 1:
+        return x
+    k_n = Cp // (patch * patch)
+    out = np.empty((k_n, Fr, patch * h, patch * w), dtype=np.float32)
+    for k in range(k_n):
+        for j in range(patch):
+            for i in range(patch):
+                out[k, :, i::patch, j::patch] = x[(k * patch + j) * patch + i]
+    return out
+
+
+def clamp(x, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
+    return np.minimum(np.maximum(_f32(x), np.float32(lo)), np.float32(hi))
+
+
+# ----------------------------------------------------------------------------------------------
 # The decoder
 # ----------------------------------------------------------------------------------------------
 def decoder_pass(z, p: Dict[str, np.ndarray], spec, cache: Dict[str, np.ndarray], first: bool) -> np.ndarray:
@@ -277,21 +370,36 @@ def decoder_pass(z, p: Dict[str, np.ndarray], spec, cache: Dict[str, np.ndarray]
     minus the parts the synthetic decoder leaves out). `cache` carries every causal conv's history
     from the previous pass and is updated; `first` marks the pass holding latent frame 0."""
     eps = spec.eps
-    x = cached_conv(_f32(z), p["conv_in.weight"], p.get("conv_in.bias"), cache, "conv_in")
+    l2 = getattr(spec, "norm_l2", False)
+    z = _f32(z)
+    if getattr(spec, "post_quant", False):
+        z = causal_conv3d(z, p["post_quant.weight"], p.get("post_quant.bias"))
+    x = cached_conv(z, p["conv_in.weight"], p.get("conv_in.bias"), cache, "conv_in")
     for i in range(spec.mid_resblocks):
-        x = resblock(x, p, f"mid.{i}", cache, eps)
-    for s in range(len(spec.stage_channels)):
+        x = resblock(x, p, f"mid.{i}", cache, eps, l2=l2)
+        if i == 0 and getattr(spec, "mid_attention", False):
+            x = attention(x, p, "mid.attn", eps, l2)
+    n_st = len(spec.stage_channels)
+    spatial = getattr(spec, "spatial", (True,) * n_st)
+    dup = getattr(spec, "dup", (False,) * n_st)
+    for s in range(n_st):
+        block_input = x
         for j in range(spec.stage_resblocks):
-            x = resblock(x, p, f"up.{s}.res.{j}", cache, eps)
+            x = resblock(x, p, f"up.{s}.res.{j}", cache, eps, l2=l2)
         if spec.temporal[s]:
             tw, tb = p[f"up.{s}.time.weight"], p.get(f"up.{s}.time.bias")
             if first:
                 x = time_upsample_first(x, tw, tb, cache, f"up.{s}.time")
             else:
                 x = time_upsample(x, tw, tb, cache, f"up.{s}.time")
-        x = spatial_upsample(x, p[f"up.{s}.spatial.weight"], p.get(f"up.{s}.spatial.bias"))
-    x = norm_silu(x, p["norm_out.gamma"], eps)
-    return cached_conv(x, p["conv_out.weight"], p.get("conv_out.bias"), cache, "conv_out")
+        if spatial[s]:
+            x = spatial_upsample(x, p[f"up.{s}.spatial.weight"], p.get(f"up.{s}.spatial.bias"))
+        if dup[s]:
+            x = add(x, dup_up(block_input, spec.stage_channels[s], 2 if spec.temporal[s] else 1, first))
+    x = silu(_norm(x, p["norm_out.gamma"], eps, l2))
+    y = cached_conv(x, p["conv_out.weight"], p.get("conv_out.bias"), cache, "conv_out")
+    y = unpatchify(y, getattr(spec, "patch", 1))
+    return clamp(y) if getattr(spec, "clamp", False) else y
 
 
 def split_passes(latent_frames: int, frames_per_pass: int) -> List[int]:

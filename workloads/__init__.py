@@ -67,9 +67,26 @@ class DecoderSpec:
     stage_resblocks: int = 2
     out_channels: int = 3
     eps: float = 1e-6
+    # Parts of the real Wan2.2 TI2V-5B decoder that the synthetic one leaves out (all off there)
+    post_quant: bool = False        # a 1x1x1 conv z -> z in front of conv_in
+    mid_attention: bool = False     # single-head attention per frame after the first mid block
+    spatial: Tuple[bool, ...] = (True, True, True, True)  # the stage ends with nearest x2 + 3x3
+    dup: Tuple[bool, ...] = (False, False, False, False)  # + DupUp3D of the stage input
+    patch: int = 1                  # unpatchify: out_channels = 3 * patch^2 -> 3 colours
+    clamp: bool = False             # clamp the video to [-1, 1]
+    norm_l2: bool = False           # RMS norm as x / max(||x||, 1e-12) * sqrt(C) (else 1 / sqrt(mean + eps))
 
 
 FULL_DECODER = DecoderSpec()
+
+# The real topology (z_dim 48, decoder base 256, channel multipliers 1, 2, 4, 4, three residual
+# blocks per up block, mid-block attention, DupUp3D shortcuts, 12-channel head + unpatchify +
+# clamp). eps: the GPU kernels normalise by 1 / sqrt(mean x^2 + eps), which equals the page's
+# x / max(||x||, 1e-12) * sqrt(C) for every x with ||x|| above 1e-12 up to rounding.
+REAL_DECODER = DecoderSpec(base_channels=1024, stage_channels=(1024, 1024, 512, 256), stage_resblocks=3,
+                           out_channels=12, eps=1e-27, post_quant=True, mid_attention=True,
+                           spatial=(True, True, True, False), dup=(True, True, True, False), patch=2, clamp=True,
+                           norm_l2=True)
 
 
 def resblock_param_list(prefix: str, cin: int, cout: int) -> List[Tuple[str, tuple, str]]:
@@ -93,16 +110,24 @@ def decoder_param_list(spec: DecoderSpec) -> List[Tuple[str, tuple, str]]:
     """(name, shape, draw kind) of every decoder parameter, in execution (= draw) order."""
     p: List[Tuple[str, tuple, str]] = []
     c = spec.base_channels
-    p += [("conv_in.weight", (c, spec.z_channels, 3, 3, 3), "kaiming"), ("conv_in.bias", (c,), "zero")]
+    z = spec.z_channels
+    if spec.post_quant:
+        p += [("post_quant.weight", (z, z, 1, 1, 1), "kaiming"), ("post_quant.bias", (z,), "zero")]
+    p += [("conv_in.weight", (c, z, 3, 3, 3), "kaiming"), ("conv_in.bias", (c,), "zero")]
     for i in range(spec.mid_resblocks):
         p += resblock_param_list(f"mid.{i}", c, c)
+        if i == 0 and spec.mid_attention:
+            p += [("mid.attn.norm.gamma", (c,), "gain"),
+                  ("mid.attn.qkv.weight", (3 * c, c, 1, 1, 1), "kaiming"), ("mid.attn.qkv.bias", (3 * c,), "zero"),
+                  ("mid.attn.proj.weight", (c, c, 1, 1, 1), "kaiming"), ("mid.attn.proj.bias", (c,), "zero")]
     for s, cs in enumerate(spec.stage_channels):
         for j in range(spec.stage_resblocks):
             p += resblock_param_list(f"up.{s}.res.{j}", c if j == 0 else cs, cs)
         c = cs
         if spec.temporal[s]:
             p += [(f"up.{s}.time.weight", (2 * c, c, 3, 1, 1), "kaiming"), (f"up.{s}.time.bias", (2 * c,), "zero")]
-        p += [(f"up.{s}.spatial.weight", (c, c, 3, 3), "kaiming"), (f"up.{s}.spatial.bias", (c,), "zero")]
+        if spec.spatial[s]:
+            p += [(f"up.{s}.spatial.weight", (c, c, 3, 3), "kaiming"), (f"up.{s}.spatial.bias", (c,), "zero")]
     p += [("norm_out.gamma", (c,), "gain")]
     p += [("conv_out.weight", (spec.out_channels, c, 3, 3, 3), "kaiming"), ("conv_out.bias", (spec.out_channels,), "zero")]
     return p
