@@ -53,7 +53,10 @@ class DecoderDesc(ctypes.Structure):
     _fields_ = [("z_channels", ctypes.c_int), ("base_channels", ctypes.c_int), ("n_stages", ctypes.c_int),
                 ("stage_channels", ctypes.c_int * MAX_STAGES), ("stage_temporal", ctypes.c_int * MAX_STAGES),
                 ("mid_resblocks", ctypes.c_int), ("stage_resblocks", ctypes.c_int), ("out_channels", ctypes.c_int),
-                ("eps", ctypes.c_float), ("latent_h", ctypes.c_int), ("latent_w", ctypes.c_int)]
+                ("eps", ctypes.c_float), ("latent_h", ctypes.c_int), ("latent_w", ctypes.c_int),
+                ("post_quant", ctypes.c_int), ("mid_attention", ctypes.c_int),
+                ("stage_no_spatial", ctypes.c_int * MAX_STAGES), ("stage_dup", ctypes.c_int * MAX_STAGES),
+                ("patch", ctypes.c_int), ("clamp", ctypes.c_int)]
 
 
 _lib = None
@@ -276,15 +279,46 @@ def upsample(x, spatial=None, spatial_bias=None, temporal=None, temporal_bias=No
 # The decoder
 # ------------------------------------------------------------------------------------------------
 def make_desc(z_channels=48, base_channels=384, stage_channels=(384, 384, 192, 96), stage_temporal=(1, 1, 0, 0),
-              mid_resblocks=2, stage_resblocks=2, out_channels=3, eps=1e-6, latent_h=44, latent_w=78) -> DecoderDesc:
+              mid_resblocks=2, stage_resblocks=2, out_channels=3, eps=1e-6, latent_h=44, latent_w=78,
+              post_quant=False, mid_attention=False, stage_spatial=None, stage_dup=None, patch=1,
+              clamp=False) -> DecoderDesc:
+    """The decoder descriptor; the defaults are the synthetic decoder, the keyword arguments from
+    post_quant on switch on the real Wan2.2 decoder's parts (see desc_from_spec)."""
     d = DecoderDesc()
     d.z_channels, d.base_channels, d.n_stages = z_channels, base_channels, len(stage_channels)
+    n = len(stage_channels)
+    spatial = (1,) * n if stage_spatial is None else stage_spatial
+    dup = (0,) * n if stage_dup is None else stage_dup
     for i, (c, t) in enumerate(zip(stage_channels, stage_temporal)):
         d.stage_channels[i] = c
         d.stage_temporal[i] = int(bool(t))
+        d.stage_no_spatial[i] = int(not spatial[i])
+        d.stage_dup[i] = int(bool(dup[i]))
     d.mid_resblocks, d.stage_resblocks, d.out_channels = mid_resblocks, stage_resblocks, out_channels
     d.eps, d.latent_h, d.latent_w = eps, latent_h, latent_w
+    d.post_quant, d.mid_attention = int(bool(post_quant)), int(bool(mid_attention))
+    d.patch, d.clamp = int(patch), int(bool(clamp))
     return d
+
+
+def desc_from_spec(spec, latent_h=44, latent_w=78) -> DecoderDesc:
+    """The descriptor of a workloads.DecoderSpec-like object (attribute names as there)."""
+    n = len(spec.stage_channels)
+    return make_desc(z_channels=spec.z_channels, base_channels=spec.base_channels,
+                     stage_channels=tuple(spec.stage_channels), stage_temporal=tuple(spec.temporal),
+                     mid_resblocks=spec.mid_resblocks, stage_resblocks=spec.stage_resblocks,
+                     out_channels=spec.out_channels, eps=spec.eps, latent_h=latent_h, latent_w=latent_w,
+                     post_quant=getattr(spec, "post_quant", False), mid_attention=getattr(spec, "mid_attention", False),
+                     stage_spatial=tuple(getattr(spec, "spatial", (True,) * n)),
+                     stage_dup=tuple(getattr(spec, "dup", (False,) * n)), patch=getattr(spec, "patch", 1),
+                     clamp=getattr(spec, "clamp", False))
+
+
+def video_shape(desc: DecoderDesc, frames: int):
+    """[1, colours, frames, H, W] of a decode with this descriptor."""
+    levels = sum(1 for i in range(desc.n_stages) if not desc.stage_no_spatial[i])
+    p = desc.patch if desc.patch >= 2 else 1
+    return (1, desc.out_channels // (p * p), frames, (desc.latent_h << levels) * p, (desc.latent_w << levels) * p)
 
 
 def param_names(desc: DecoderDesc):
@@ -366,10 +400,8 @@ class Decoder:
         early = max(early_frames_per_pass or frames_per_pass, frames_per_pass)
         T = z.shape[2] if z_layout == "NCTHW" else z.shape[1]
         F = self.video_frames(T, frames_per_pass, first_frame_rule)
-        L = self.desc.n_stages
-        vh, vw = self.desc.latent_h << L, self.desc.latent_w << L
         if out is None:
-            out = torch.empty((1, self.desc.out_channels, F, vh, vw), dtype=torch.bfloat16, device=self.device)
+            out = torch.empty(video_shape(self.desc, F), dtype=torch.bfloat16, device=self.device)
         ws = self.workspace(frames_per_pass, early)
         _check(lib().wvd_cache_reset(self.cache))
         start, offset = 0, 0

@@ -100,9 +100,13 @@ enum MemKind {
   MEM_CONVERT = 2,
   MEM_HEAD_FUSED = 3,
   MEM_HEAD_STREAM = 4,
-  MEM_KINDS = 5
+  MEM_ATTN = 5,     // the attention's softmax and value transpose
+  MEM_DUP = 6,      // the DupUp3D add
+  MEM_UNPATCH = 7,  // unpatchify (+ clamp) into the video
+  MEM_KINDS = 8
 };
-const char* const kMemKindNames[MEM_KINDS] = {"norm_silu", "head_stencil", "convert", "head_fused", "head_stream"};
+const char* const kMemKindNames[MEM_KINDS] = {"norm_silu", "head_stencil", "convert", "head_fused", "head_stream",
+                                              "attn_softmax_transpose", "dup_add", "unpatchify"};
 struct LaunchRecord {
   int config;
   float ms;
@@ -714,10 +718,13 @@ struct ResPlan {
 
 struct StagePlan {
   std::vector<ResPlan> res;
-  int c;
+  int cin, c;    // input and output channels
+  int level;     // spatial x2 steps before the stage (its resolution)
   int temporal;
+  int spatial;   // ends with nearest x2 + 3x3
+  int dup;       // + DupUp3D of the stage's input
   int tw, tb, time_slot;  // time conv params and cache slot (-1 if none)
-  int sw, sb;
+  int sw, sb;             // spatial conv params (-1 if none)
 };
 
 struct Slot {
@@ -727,25 +734,55 @@ struct Slot {
 
 struct Plan {
   std::vector<Param> params;
+  int pq_w, pq_b;  // post_quant_conv (-1 if none)
   int conv_in_w, conv_in_b, conv_in_slot;
   std::vector<ResPlan> mid;
+  int attn_gamma, attn_qkv_w, attn_qkv_b, attn_proj_w, attn_proj_b;  // mid attention (-1 if none)
   std::vector<StagePlan> stages;
+  int levels;      // spatial x2 steps in all: the head's level
+  int head_plain;  // conv_out as a plain 3x3x3 conv, then unpatchify (+ clamp) into the video
   int norm_out, out_w, out_b, out_slot;
   std::vector<Slot> slots;
   size_t packed_bytes, cache_bytes;
 };
 
+// Video colours and patch: out_channels = colours * patch^2 with unpatchify (patch >= 2).
+int desc_patch(const wvd_decoder_desc* d) { return d->patch >= 2 ? d->patch : 1; }
+int desc_colours(const wvd_decoder_desc* d) { return d->out_channels / (desc_patch(d) * desc_patch(d)); }
+int desc_levels(const wvd_decoder_desc* d) {
+  int l = 0;
+  for (int s = 0; s < d->n_stages; ++s) l += d->stage_no_spatial[s] ? 0 : 1;
+  return l;
+}
+
 wvd_status check_desc(const wvd_decoder_desc* d) {
   if (!d) return fail(WVD_ERR_ARG, "decoder desc is null");
   if (d->n_stages < 0 || d->n_stages > WVD_MAX_STAGES) return fail(WVD_ERR_ARG, "n_stages out of range");
-  auto okc = [](int c) { return c > 0 && c % 8 == 0 && c <= 512; };
+  auto okc = [](int c) { return c > 0 && c % 8 == 0 && c <= 2048; };
   if (!okc(d->z_channels) || !okc(d->base_channels))
-    return fail(WVD_ERR_UNSUPPORTED, "z and base channels must be multiples of 8 up to 512");
+    return fail(WVD_ERR_UNSUPPORTED, "z and base channels must be multiples of 8 up to 2048");
   for (int s = 0; s < d->n_stages; ++s)
-    if (!okc(d->stage_channels[s])) return fail(WVD_ERR_UNSUPPORTED, "stage channels must be multiples of 8 up to 512");
+    if (!okc(d->stage_channels[s])) return fail(WVD_ERR_UNSUPPORTED, "stage channels must be multiples of 8 up to 2048");
   if (d->mid_resblocks < 0 || d->stage_resblocks < 0 || d->mid_resblocks > 16 || d->stage_resblocks > 16)
     return fail(WVD_ERR_ARG, "resblock counts out of range");
-  if (d->out_channels <= 0 || d->out_channels > 4) return fail(WVD_ERR_UNSUPPORTED, "out_channels must be 1..4");
+  if (d->patch < 0 || d->patch > 4) return fail(WVD_ERR_UNSUPPORTED, "patch must be 0..4");
+  if (d->patch >= 2 ? (d->out_channels % (d->patch * d->patch) != 0 || desc_colours(d) > 4)
+                    : (d->out_channels <= 0 || d->out_channels > 4))
+    return fail(WVD_ERR_UNSUPPORTED, "out_channels must be 1..4 colours times patch^2");
+  for (int s = 0; s < d->n_stages; ++s) {
+    const int cin = s ? d->stage_channels[s - 1] : d->base_channels, co = d->stage_channels[s];
+    const int ft = d->stage_temporal[s] ? 2 : 1;
+    if (d->stage_no_spatial[s] && (d->stage_temporal[s] || d->stage_dup[s]))
+      return fail(WVD_ERR_UNSUPPORTED, "a stage without the spatial step can have no time step or DupUp3D");
+    if (d->stage_dup[s] && (co * ft * 4) % cin != 0)
+      return fail(WVD_ERR_UNSUPPORTED, "DupUp3D needs out * ft * 4 to be a multiple of the stage's input channels");
+  }
+  if (d->mid_attention) {
+    const int64_t hw = (int64_t)d->latent_h * d->latent_w;
+    if (d->mid_resblocks < 1) return fail(WVD_ERR_UNSUPPORTED, "mid attention follows the first mid block");
+    if (d->base_channels % 32 != 0 || hw % 8 != 0 || hw > 65536)
+      return fail(WVD_ERR_UNSUPPORTED, "mid attention needs base channels % 32 == 0 and latent h*w % 8 == 0, <= 65536");
+  }
   if (d->latent_h <= 0 || d->latent_w <= 0 || d->latent_h > 4096 || d->latent_w > 4096)
     return fail(WVD_ERR_ARG, "latent size out of range");
   if (!(d->eps >= 0.0f)) return fail(WVD_ERR_ARG, "eps must be >= 0");
@@ -804,32 +841,60 @@ ResPlan add_res(Plan& p, const wvd_decoder_desc* d, const std::string& pre, int 
 Plan make_plan(const wvd_decoder_desc* d) {
   Plan p;
   int c = d->base_channels;
-  p.conv_in_w = add_param(p, "conv_in.weight", K_CONV3, c, d->z_channels);
+  const int z = d->z_channels;
+  p.pq_w = p.pq_b = -1;
+  if (d->post_quant) {
+    p.pq_w = add_param(p, "post_quant.weight", K_CONV1, z, z);
+    p.pq_b = add_param(p, "post_quant.bias", K_BIAS, z, 0);
+  }
+  p.conv_in_w = add_param(p, "conv_in.weight", K_CONV3, c, z);
   p.conv_in_b = add_param(p, "conv_in.bias", K_BIAS, c, 0);
-  p.conv_in_slot = add_slot(p, d, 0, d->z_channels);
-  for (int i = 0; i < d->mid_resblocks; ++i) p.mid.push_back(add_res(p, d, "mid." + std::to_string(i), c, c, 0));
+  p.conv_in_slot = add_slot(p, d, 0, z);
+  p.attn_gamma = p.attn_qkv_w = p.attn_qkv_b = p.attn_proj_w = p.attn_proj_b = -1;
+  for (int i = 0; i < d->mid_resblocks; ++i) {
+    p.mid.push_back(add_res(p, d, "mid." + std::to_string(i), c, c, 0));
+    if (i == 0 && d->mid_attention) {
+      p.attn_gamma = add_param(p, "mid.attn.norm.gamma", K_GAMMA, c, 0);
+      p.attn_qkv_w = add_param(p, "mid.attn.qkv.weight", K_CONV1, 3 * c, c);
+      p.attn_qkv_b = add_param(p, "mid.attn.qkv.bias", K_BIAS, 3 * c, 0);
+      p.attn_proj_w = add_param(p, "mid.attn.proj.weight", K_CONV1, c, c);
+      p.attn_proj_b = add_param(p, "mid.attn.proj.bias", K_BIAS, c, 0);
+    }
+  }
+  int level = 0;
   for (int s = 0; s < d->n_stages; ++s) {
     StagePlan st;
     const int cs = d->stage_channels[s];
+    st.cin = c;
+    st.level = level;
     for (int j = 0; j < d->stage_resblocks; ++j)
-      st.res.push_back(add_res(p, d, "up." + std::to_string(s) + ".res." + std::to_string(j), j == 0 ? c : cs, cs, s));
+      st.res.push_back(
+          add_res(p, d, "up." + std::to_string(s) + ".res." + std::to_string(j), j == 0 ? c : cs, cs, level));
     c = cs;
     st.c = c;
     st.temporal = d->stage_temporal[s] != 0;
+    st.spatial = d->stage_no_spatial[s] == 0;
+    st.dup = d->stage_dup[s] != 0;
     st.tw = st.tb = st.time_slot = -1;
     if (st.temporal) {
       st.tw = add_param(p, "up." + std::to_string(s) + ".time.weight", K_TIME, 2 * c, c);
       st.tb = add_param(p, "up." + std::to_string(s) + ".time.bias", K_BIAS, 2 * c, 0);
-      st.time_slot = add_slot(p, d, s, c);
+      st.time_slot = add_slot(p, d, level, c);
     }
-    st.sw = add_param(p, "up." + std::to_string(s) + ".spatial.weight", K_SPATIAL, c, c);
-    st.sb = add_param(p, "up." + std::to_string(s) + ".spatial.bias", K_BIAS, c, 0);
+    st.sw = st.sb = -1;
+    if (st.spatial) {
+      st.sw = add_param(p, "up." + std::to_string(s) + ".spatial.weight", K_SPATIAL, c, c);
+      st.sb = add_param(p, "up." + std::to_string(s) + ".spatial.bias", K_BIAS, c, 0);
+      ++level;
+    }
     p.stages.push_back(st);
   }
+  p.levels = level;
+  p.head_plain = d->patch >= 2 || d->clamp;
   p.norm_out = add_param(p, "norm_out.gamma", K_GAMMA, c, 0);
-  p.out_w = add_param(p, "conv_out.weight", K_HEAD, d->out_channels, c);
+  p.out_w = add_param(p, "conv_out.weight", p.head_plain ? K_CONV3 : K_HEAD, d->out_channels, c);
   p.out_b = add_param(p, "conv_out.bias", K_BIAS, d->out_channels, 0);
-  p.out_slot = add_slot(p, d, d->n_stages, c);
+  p.out_slot = add_slot(p, d, p.levels, c);
   size_t off = 0;
   for (auto& q : p.params) {
     q.offset = off;
@@ -873,7 +938,13 @@ uint64_t desc_hash(const wvd_decoder_desc* d) {
   for (int s = 0; s < d->n_stages; ++s) {
     mix((uint32_t)d->stage_channels[s]);
     mix((uint32_t)d->stage_temporal[s]);
+    mix((uint32_t)d->stage_no_spatial[s]);
+    mix((uint32_t)d->stage_dup[s]);
   }
+  mix((uint32_t)d->post_quant);
+  mix((uint32_t)d->mid_attention);
+  mix((uint32_t)d->patch);
+  mix((uint32_t)d->clamp);
   uint32_t e;
   memcpy(&e, &d->eps, 4);
   mix(e);
@@ -906,6 +977,7 @@ constexpr int kHeadPlanes = 9;
 // Workspace buffers of the chunk driver (elements of bf16).
 struct WsLayout {
   size_t zc, x0, x1, a, h, sc, xm;  // byte offsets
+  size_t zq, keep, qkv, sc32, prob, vt, ao, head;  // the real topology's parts (0 bytes otherwise)
   size_t total;
 };
 
@@ -926,32 +998,37 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n, int64_t nh) {
   const int split = (nh > 0 && nh < n && split_stage(d) > 0) ? split_stage(d) : L;
   const ChunkFrames fl = chunk_frames(d, n, false);  // the largest frame counts
   const ChunkFrames fh = split < L ? chunk_frames(d, nh, false) : fl;
-  int64_t stream = 0, act = 0, hbuf = 0, scbuf = 0, xm = 0;
+  int64_t stream = 0, act = 0, hbuf = 0, scbuf = 0, xm = 0, keep = 0;
   const int64_t hw0 = (int64_t)d->latent_h * d->latent_w;
   auto hw = [&](int level) { return hw0 << (2 * level); };
   int c = d->base_channels;
   stream = std::max(stream, n * hw(0) * c);
   act = std::max(act, n * hw(0) * std::max(c, d->z_channels));
   hbuf = std::max(hbuf, n * hw(0) * c);
+  int level = 0;
   for (int s = 0; s < L; ++s) {
     const ChunkFrames& f = s < split ? fl : fh;
     const int cs = d->stage_channels[s];
-    const int64_t P = f.stage_in[s] * hw(s);
+    const int sp = d->stage_no_spatial[s] ? 0 : 1;
+    const int64_t P = f.stage_in[s] * hw(level);
+    if (d->stage_dup[s]) keep = std::max(keep, P * c);
     stream = std::max(stream, P * std::max(c, cs));
     act = std::max(act, P * std::max(c, cs));
     hbuf = std::max(hbuf, P * cs);
     if (c != cs) scbuf = std::max(scbuf, P * cs);
     c = cs;
     // time conv output, then the spatial upsample output at the next level
-    act = std::max(act, f.stage_out[s] * hw(s) * c);
-    stream = std::max(stream, f.stage_out[s] * hw(s) * c);
-    stream = std::max(stream, f.stage_out[s] * hw(s + 1) * c);
-    act = std::max(act, f.stage_out[s] * hw(s + 1) * c);
-    if (s + 1 == split && split < L) xm = fl.stage_out[s] * hw(s + 1) * c;
+    act = std::max(act, f.stage_out[s] * hw(level) * c);
+    stream = std::max(stream, f.stage_out[s] * hw(level) * c);
+    stream = std::max(stream, f.stage_out[s] * hw(level + sp) * c);
+    act = std::max(act, f.stage_out[s] * hw(level + sp) * c);
+    if (s + 1 == split && split < L) xm = fl.stage_out[s] * hw(level + sp) * c;
+    level += sp;
   }
-  act = std::max(act, fh.video * hw(L) * c);
+  act = std::max(act, fh.video * hw(level) * c);
   // the head's fp32 tap planes Z (9 planes x 4 floats = 72 bf16 per position) live in a stream buffer
-  stream = std::max(stream, fh.video * hw(L) * kHeadPlanes * 8);
+  const bool head_plain = d->patch >= 2 || d->clamp;
+  if (!head_plain) stream = std::max(stream, fh.video * hw(level) * kHeadPlanes * 8);
   WsLayout w;
   size_t off = 0;
   auto take = [&](int64_t elems) {
@@ -966,6 +1043,16 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n, int64_t nh) {
   w.h = take(hbuf);
   w.sc = take(scbuf);
   w.xm = take(xm);
+  w.zq = take(d->post_quant ? n * hw0 * d->z_channels : 0);
+  w.keep = take(keep);
+  const int64_t c0 = d->base_channels;
+  const bool at = d->mid_attention != 0;
+  w.qkv = take(at ? 3 * n * hw0 * c0 + 32 * c0 : 0);  // (+ 32 rows: the key tile's padding reads)
+  w.sc32 = take(at ? 2 * hw0 * hw0 : 0);             // fp32 scores of one frame
+  w.prob = take(at ? hw0 * hw0 : 0);
+  w.vt = take(at ? c0 * round_up(hw0, 32) : 0);
+  w.ao = take(at ? n * hw0 * c0 : 0);
+  w.head = take(head_plain ? fh.video * hw(level) * d->out_channels : 0);
   w.total = off;
   return w;
 }
@@ -1131,9 +1218,11 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
   const bool rule = first && first_frame_rule;
   const ChunkFrames fr = chunk_frames(d, n, rule);
   const int L = d->n_stages;
-  const int64_t vh = (int64_t)d->latent_h << L, vw = (int64_t)d->latent_w << L;
-  if (video->c != d->out_channels || video->h != vh || video->w != vw)
-    return fail(WVD_ERR_SHAPE, "video must be [1, %d, F, %lld, %lld]", d->out_channels, (long long)vh, (long long)vw);
+  const int colours = desc_colours(d), patch = desc_patch(d);
+  const int64_t vh = ((int64_t)d->latent_h << desc_levels(d)) * patch;
+  const int64_t vw = ((int64_t)d->latent_w << desc_levels(d)) * patch;
+  if (video->c != colours || video->h != vh || video->w != vw)
+    return fail(WVD_ERR_SHAPE, "video must be [1, %d, F, %lld, %lld]", colours, (long long)vh, (long long)vw);
   if (frame_offset < 0 || frame_offset + fr.video > video->t)
     return fail(WVD_ERR_SHAPE, "chunk frames %lld..%lld do not fit a video of %lld frames", (long long)frame_offset,
                 (long long)(frame_offset + fr.video), (long long)video->t);
@@ -1155,6 +1244,14 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
   bf16_t* bh = (bf16_t*)(wsb + wl.h);
   bf16_t* bsc = (bf16_t*)(wsb + wl.sc);
   bf16_t* bxm = (bf16_t*)(wsb + wl.xm);
+  bf16_t* bzq = (bf16_t*)(wsb + wl.zq);
+  bf16_t* bkeep = (bf16_t*)(wsb + wl.keep);
+  bf16_t* bqkv = (bf16_t*)(wsb + wl.qkv);
+  float* bs32 = (float*)(wsb + wl.sc32);
+  bf16_t* bprob = (bf16_t*)(wsb + wl.prob);
+  bf16_t* bvt = (bf16_t*)(wsb + wl.vt);
+  bf16_t* bao = (bf16_t*)(wsb + wl.ao);
+  bf16_t* bhead = (bf16_t*)(wsb + wl.head);
   auto slot_ptr = [&](int slot) { return (bf16_t*)(cache->storage + p.slots[slot].offset); };
   auto slot_hist = [&](int slot) -> const bf16_t* {
     const int v = cache->valid[slot];
@@ -1181,6 +1278,13 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       return launch_convert(z->data, 1, 1, zc, 1, 0, d->z_channels, (int)n, d->latent_h, d->latent_w, s);
     }));
     zin = zc;
+  }
+  if (p.pq_w >= 0) {  // post_quant_conv: 1x1x1, no history
+    const int64_t P = n * d->latent_h * d->latent_w;
+    ConvProblem cp = plain_problem(zin, nullptr, (int)n, d->latent_h, d->latent_w, d->z_channels, 0, W_(p.pq_w),
+                                   d->z_channels, 1, 1, 1, F_(p.pq_b), bzq, nullptr);
+    WVD_TRY(run_conv(cp, s, conv_flops(P, d->z_channels, d->z_channels)));
+    zin = bzq;
   }
   int cur = 0;  // index of the stream buffer holding the activation
   int H = d->latent_h, Wd = d->latent_w;
@@ -1222,7 +1326,47 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
     WVD_TRY(cached_conv(c2, r.slot2, a2, (int)T, conv_flops(P, r.cout, 27LL * r.cout)));
     return WVD_OK;
   };
-  for (const ResPlan& r : p.mid) WVD_TRY(resblock(r, bx[cur]));
+  // The mid block's attention, in place on x (level 0, T frames): n = RMS norm of x; q | k | v
+  // from one 1x1 conv C -> 3C whose channel thirds go to frames t, T + t, 2T + t; per frame the
+  // scores q k^T as a 1x1 conv of q whose weight rows are the frame's keys (fp32 out), the row
+  // softmax of scores / sqrt(C), o = P v as a 1x1 conv of P whose weight rows are the frame's
+  // values transposed; then proj + bias + x.
+  auto run_attention = [&](bf16_t* x) -> wvd_status {
+    const int hw = H * Wd;
+    const int64_t P = T * hw;
+    const int ldk = (int)round_up(hw, 32);
+    WVD_TRY(run_norm(x, F_(p.attn_gamma), d->eps, 0, ba, P, c, s));
+    ConvProblem qp = plain_problem(ba, nullptr, (int)T, H, Wd, c, 0, W_(p.attn_qkv_w), 3 * c, 1, 1, 1,
+                                   F_(p.attn_qkv_b), bqkv, nullptr);
+    qp.nsplit = c;
+    qp.fstride = (int)T;
+    qp.To = 3 * (int)T;
+    WVD_TRY(run_conv(qp, s, conv_flops(P, 3 * c, c)));
+    for (int64_t t = 0; t < T; ++t) {
+      const bf16_t* q = bqkv + (size_t)t * hw * c;
+      const bf16_t* k = bqkv + (size_t)(T + t) * hw * c;
+      const bf16_t* v = bqkv + (size_t)(2 * T + t) * hw * c;
+      ConvProblem sp = plain_problem(q, nullptr, 1, H, Wd, c, 0, k, hw, 1, 1, 1, nullptr, nullptr, nullptr);
+      sp.y = bs32;
+      sp.y_f32 = 1;
+      WVD_TRY(run_conv(sp, s, conv_flops(hw, hw, c)));
+      WVD_TRY(run_mem(MEM_ATTN, (double)hw * hw * 14.0, s, "softmax launch", [&] {
+        return launch_softmax_rows(bs32, hw, hw, hw, 1.0f / std::sqrt((float)c), bprob, hw, s);
+      }));
+      WVD_TRY(run_mem(MEM_ATTN, (double)hw * c * 2.0 + (double)c * ldk * 2.0, s, "transpose launch",
+                      [&] { return launch_transpose_pad(v, hw, c, bvt, ldk, s); }));
+      ConvProblem op = plain_problem(bprob, nullptr, 1, H, Wd, hw, 0, bvt, c, 1, 1, 1, nullptr,
+                                     bao + (size_t)t * hw * c, nullptr);
+      WVD_TRY(run_conv(op, s, conv_flops(hw, c, hw)));
+    }
+    ConvProblem pp = plain_problem(bao, nullptr, (int)T, H, Wd, c, 0, W_(p.attn_proj_w), c, 1, 1, 1,
+                                   F_(p.attn_proj_b), x, x);
+    return run_conv(pp, s, conv_flops(P, c, c));
+  };
+  for (size_t i = 0; i < p.mid.size(); ++i) {
+    WVD_TRY(resblock(p.mid[i], bx[cur]));
+    if (i == 0 && p.attn_qkv_w >= 0) WVD_TRY(run_attention(bx[cur]));
+  }
   // The last stage's spatial upsample also applies norm_out + SiLU in its epilogue when one
   // workgroup holds every channel (the L4 tensor is then written once, already activated).
   const bf16_t* act = nullptr;  // conv_out's input once norm_out has been applied
@@ -1231,13 +1375,20 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
   // (into `up`, or the stream buffers)
   auto run_stage = [&](int si, const bf16_t* x, bf16_t* up) -> wvd_status {
     const StagePlan& st = p.stages[si];
+    const int64_t T_in = T;
+    const int H_in = H, W_in = Wd;
+    if (st.dup && T_in > 0)  // the stage's input, for its DupUp3D shortcut after the upsampling
+      WVD_HIP(hipMemcpyAsync(bkeep, x, (size_t)T_in * H_in * W_in * st.cin * 2, hipMemcpyDeviceToDevice, s),
+              "DupUp3D source copy");
     for (const ResPlan& r : st.res) {
       WVD_TRY(resblock(r, x));
       x = bx[cur];
       c = r.cout;
     }
-    const bool fuse_out = si == L - 1 && conv_can_fuse_norm(c, F_(st.sb), F_(p.norm_out));
+    if (!st.spatial) return WVD_OK;  // (no time step or DupUp3D either)
+    const bool fuse_out = si == L - 1 && !st.dup && conv_can_fuse_norm(c, F_(st.sb), F_(p.norm_out));
     const float* ng = fuse_out ? F_(p.norm_out) : nullptr;
+    bf16_t* yout = nullptr;  // the upsampling's output
     if (st.temporal) {
       const size_t fb = (size_t)H * Wd * c * 2;
       const int tf = rule ? 1 : 0;
@@ -1258,6 +1409,7 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       // spatial upsample from the time conv's output into the stream buffer (or `up`)
       bf16_t* out = up ? up : bx[cur];
       WVD_TRY(run_phase_conv(dst, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), out, s, ng, d->eps));
+      yout = out;
       if (fuse_out) {
         act = out;
         zbuf = bx[cur ^ 1];
@@ -1268,9 +1420,20 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       zbuf = bx[cur ^ 1];
     } else if (up) {
       WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), up, s));
+      yout = up;
     } else {
       WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur ^ 1], s));
       cur ^= 1;
+      yout = bx[cur];
+    }
+    if (st.dup) {
+      // + DupUp3D of the stage input; on the pass holding latent frame 0 that frame's first
+      // time copy is dropped, as the time step passed it through once
+      const int ft = st.temporal ? 2 : 1, fo = (st.temporal && rule) ? 1 : 0;
+      const double db = (double)T * 4 * H_in * W_in * c * 4.0 + (double)T_in * H_in * W_in * st.cin * 2.0;
+      WVD_TRY(run_mem(MEM_DUP, db, s, "DupUp3D launch", [&] {
+        return launch_dup_add(yout, bkeep, (int)T, (int)T_in, H_in, W_in, st.cin, c, ft, fo, s);
+      }));
     }
     H *= 2;
     Wd *= 2;
@@ -1284,6 +1447,18 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       WVD_TRY(run_norm(bx[cur], F_(p.norm_out), d->eps, 1, ba, P, c, s));
       act = ba;
       zbuf = bx[cur ^ 1];
+    }
+    if (p.head_plain) {
+      // conv_out as a plain causal 3x3x3 conv to colours * patch^2 channels, then unpatchify
+      // (+ clamp) into the video
+      const int co = d->out_channels;
+      ConvProblem cp = plain_problem(act, nullptr, (int)T, H, Wd, c, 0, W_(p.out_w), co, 3, 3, 3, F_(p.out_b), bhead,
+                                     nullptr);
+      WVD_TRY(cached_conv(cp, p.out_slot, act, (int)T, conv_flops(P, co, 27LL * c)));
+      return run_mem(MEM_UNPATCH, (double)P * co * 4.0, s, "unpatchify launch", [&] {
+        return launch_unpatchify(bhead, (int)T, H, Wd, colours, patch, d->clamp, (bf16_t*)video->data, video->t,
+                                 (int)fo, s);
+      });
     }
     const int co = d->out_channels;
     const int cip = (int)round_up(c, 32);

@@ -131,6 +131,18 @@ hipError_t launch_conv_fp32(const float* x, const float* hist, const float* w, c
 hipError_t launch_norm_silu(const bf16_t* x, const float* gamma, float eps, int silu, bf16_t* y, int64_t positions,
                             int C, hipStream_t s);
 
+// The real topology's extra parts (topology.hip): the attention's row softmax (P = softmax of
+// scale * S per row, bf16) and value transpose (vt [C][ldo] from v [R][C], zero columns R..ldo),
+// the DupUp3D add (y [To][2H][2W][Co] += dup of x [T][H][W][Ci], output frame f + fo = ft*t + a),
+// and unpatchify (+ clamp) of out [T][h][w][colours*patch^2] into the NCTHW video at fbase.
+hipError_t launch_softmax_rows(const float* S, int64_t ld_s, int rows, int cols, float scale, bf16_t* P, int64_t ld_p,
+                               hipStream_t s);
+hipError_t launch_transpose_pad(const bf16_t* v, int R, int C, bf16_t* vt, int ldo, hipStream_t s);
+hipError_t launch_dup_add(bf16_t* y, const bf16_t* x, int To, int T, int H, int W, int Ci, int Co, int ft, int fo,
+                          hipStream_t s);
+hipError_t launch_unpatchify(const bf16_t* out, int T, int h, int w, int colours, int patch, int clamp, bf16_t* video,
+                             int64_t frames, int fbase, hipStream_t s);
+
 hipError_t launch_convert(const void* x, int x_bf16, int x_ncthw, void* y, int y_bf16, int y_ncthw, int C, int T,
                           int H, int W, hipStream_t s);
 

@@ -15,52 +15,62 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 // normalises 64/G positions per step with a single 16-byte load and store per lane; the
 // sum of squares is reduced across the G lanes with xor shuffles. fp32 statistics, one rounding.
 // ---------------------------------------------------------------------------------------------
-template <int G>
+// Channels past 512 (64 lanes x 8) take KPL chunks of 8 per lane, chunk sub + k * G.
+template <int G, int KPL>
 __global__ __launch_bounds__(256) void norm_silu_kernel(const bf16_t* __restrict__ x, const float* __restrict__ gamma,
                                                         float eps, int silu, bf16_t* __restrict__ y,
                                                         int64_t positions, int C) {
   constexpr int PPW = 64 / G;  // positions per wave step
   const int lane = threadIdx.x & 63;
-  const int sub = lane % G;    // 8-channel chunk of the position
+  const int sub = lane % G;    // first 8-channel chunk of the position
   const int slot = lane / G;   // which position of the step
   const int cv = C >> 3;       // chunks per position
-  const bool active = sub < cv;
-  float g[8];
+  bool active[KPL];
+  float g[KPL][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) g[e] = active ? gamma[sub * 8 + e] : 0.0f;
+  for (int k = 0; k < KPL; ++k) {
+    active[k] = sub + k * G < cv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[k][e] = active[k] ? gamma[(sub + k * G) * 8 + e] : 0.0f;
+  }
   const float inv_c = 1.0f / (float)C;
   const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   for (int64_t p0 = wave_id * PPW; p0 < positions; p0 += nwaves * PPW) {
     const int64_t pos = p0 + slot;
-    const bool ok = active && pos < positions;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    const int64_t off = pos * C + sub * 8;
-    if (ok) v = *(const u32x4*)(x + off);
-    float f[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f[2 * q] = bf16_lo(v[q]);
-      f[2 * q + 1] = bf16_hi(v[q]);
-    }
+    float f[KPL][8];
     float ss = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+    for (int k = 0; k < KPL; ++k) {
+      const bool ok = active[k] && pos < positions;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *(const u32x4*)(x + pos * C + (sub + k * G) * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[k][2 * q] = bf16_lo(v[q]);
+        f[k][2 * q + 1] = bf16_hi(v[q]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(f[k][e], f[k][e], ss);
+    }
 #pragma unroll
     for (int m = G / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
     const float r = rsqrtf(ss * inv_c + eps);
-    u32x4 o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float a = f[2 * q] * r * g[2 * q];
-      float b = f[2 * q + 1] * r * g[2 * q + 1];
-      if (silu) {
-        a = silu_f32(a);
-        b = silu_f32(b);
+    for (int k = 0; k < KPL; ++k) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float a = f[k][2 * q] * r * g[k][2 * q];
+        float b = f[k][2 * q + 1] * r * g[k][2 * q + 1];
+        if (silu) {
+          a = silu_f32(a);
+          b = silu_f32(b);
+        }
+        o[q] = pack_bf16x2(a, b);
       }
-      o[q] = pack_bf16x2(a, b);
+      if (active[k] && pos < positions) *(u32x4*)(y + pos * C + (sub + k * G) * 8) = o;
     }
-    if (ok) *(u32x4*)(y + off) = o;
   }
 }
 
@@ -147,28 +157,30 @@ hipError_t launch_norm_silu(const bf16_t* x, const float* gamma, float eps, int 
                             int C, hipStream_t s) {
   if (positions == 0) return hipSuccess;
   const int cv = C / 8;
+  if (C % 8 != 0 || cv > 64 * 4) return hipErrorInvalidValue;
   int G = 1;
-  while (G < cv) G *= 2;
-  const int ppb = 4 * (64 / G);  // positions per block step
+  while (G < cv && G < 64) G *= 2;
+  const int kpl = (cv + G - 1) / G;  // chunks per lane: 1 up to 512 channels
+  const int ppb = 4 * (64 / G);      // positions per block step
   int64_t blocks = (positions + ppb - 1) / ppb;
   if (blocks > 8192) blocks = 8192;
-#define WVD_NORM_CASE(GG) \
-  case GG:                \
-    hipLaunchKernelGGL(norm_silu_kernel<GG>, dim3((unsigned)blocks), dim3(256), 0, s, x, gamma, eps, silu, y, positions, C); \
-    break;
-  switch (G) {
-    WVD_NORM_CASE(1)
-    WVD_NORM_CASE(2)
-    WVD_NORM_CASE(4)
-    WVD_NORM_CASE(8)
-    WVD_NORM_CASE(16)
-    WVD_NORM_CASE(32)
-    WVD_NORM_CASE(64)
-    default:
-      return hipErrorInvalidValue;
+#define WVD_NORM_CASE(GG, KK) \
+  if (G == GG && kpl == KK) { \
+    hipLaunchKernelGGL((norm_silu_kernel<GG, KK>), dim3((unsigned)blocks), dim3(256), 0, s, x, gamma, eps, silu, y, positions, C); \
+    return hipGetLastError(); \
   }
+  WVD_NORM_CASE(1, 1)
+  WVD_NORM_CASE(2, 1)
+  WVD_NORM_CASE(4, 1)
+  WVD_NORM_CASE(8, 1)
+  WVD_NORM_CASE(16, 1)
+  WVD_NORM_CASE(32, 1)
+  WVD_NORM_CASE(64, 1)
+  WVD_NORM_CASE(64, 2)
+  WVD_NORM_CASE(64, 3)
+  WVD_NORM_CASE(64, 4)
 #undef WVD_NORM_CASE
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_convert(const void* x, int x_bf16, int x_ncthw, void* y, int y_bf16, int y_ncthw, int C, int T, int H,

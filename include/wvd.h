@@ -65,7 +65,7 @@ typedef struct {
 const char* wvd_last_error(void);
 /* ABI version; bumped on every incompatible change of this header. */
 int wvd_abi_version(void);
-#define WVD_ABI_VERSION 1
+#define WVD_ABI_VERSION 2
 
 /* ============================================================================================
  * Layout conversion (boundary marshalling): NCTHW <-> NTHWC, fp32 <-> bf16 (round to nearest
@@ -183,6 +183,13 @@ typedef struct {
   int out_channels;                   /* video channels (3) */
   float eps;                          /* RMS norm epsilon (1e-6) */
   int latent_h, latent_w;             /* latent frame size (44, 78) */
+  /* The real Wan2.2 TI2V-5B decoder's parts (the page's part list; all 0 in the synthetic one): */
+  int post_quant;                     /* a 1x1x1 conv z -> z in front of conv_in */
+  int mid_attention;                  /* single-head attention over each frame after mid block 0 */
+  int stage_no_spatial[WVD_MAX_STAGES]; /* 1: the stage has no nearest x2 + 3x3 step */
+  int stage_dup[WVD_MAX_STAGES];      /* 1: + DupUp3D of the stage's input after its upsampling */
+  int patch;                          /* unpatchify patch p (0 or 1: none); out_channels = 3 p^2 */
+  int clamp;                          /* clamp the video to [-1, 1] */
 } wvd_decoder_desc;
 
 /* Parameters, in the canonical order (execution order). For index i: its name (e.g.

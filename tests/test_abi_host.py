@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert set(wvd.exported_symbols()) == set(declared)
-    assert lib.wvd_abi_version() == 1
+    assert lib.wvd_abi_version() == 2
 
 
 def test_param_table_matches_the_workload_names_and_shapes():
