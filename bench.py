@@ -35,6 +35,8 @@ def algorithmic_conv_flops(spec: wl.DecoderSpec, latent_frames: int, fpp: int, h
     (4 taps of C per phase at the low resolution), real (unpadded) channel counts."""
     total = 0.0
     start = 0
+    n_st = len(spec.stage_channels)
+    spatial = getattr(spec, "spatial", (True,) * n_st)
     while start < latent_frames:
         n = min(fpp, latent_frames - start)
         first = start == 0
@@ -42,9 +44,14 @@ def algorithmic_conv_flops(spec: wl.DecoderSpec, latent_frames: int, fpp: int, h
         H, W = hw
         c = spec.base_channels
         P = T * H * W
+        if getattr(spec, "post_quant", False):
+            total += 2.0 * P * spec.z_channels * spec.z_channels
         total += 2.0 * P * c * 27 * spec.z_channels
-        for _ in range(spec.mid_resblocks):
+        for i in range(spec.mid_resblocks):
             total += 2.0 * P * c * 27 * c * 2
+            if i == 0 and getattr(spec, "mid_attention", False):
+                hw_ = H * W  # qkv, scores, values, proj
+                total += 2.0 * P * 3 * c * c + T * (2.0 * hw_ * hw_ * c * 2) + 2.0 * P * c * c
         for s, cs in enumerate(spec.stage_channels):
             P = T * H * W
             for j in range(spec.stage_resblocks):
@@ -57,8 +64,9 @@ def algorithmic_conv_flops(spec: wl.DecoderSpec, latent_frames: int, fpp: int, h
                 Tc = T - 1 if first else T
                 total += 2.0 * Tc * H * W * (2 * c) * 3 * c
                 T = 2 * T - 1 if first else 2 * T
-            total += 2.0 * (4 * T * H * W) * c * (4 * c)
-            H, W = 2 * H, 2 * W
+            if spatial[s]:
+                total += 2.0 * (4 * T * H * W) * c * (4 * c)
+                H, W = 2 * H, 2 * W
         total += 2.0 * T * H * W * spec.out_channels * 27 * c
         start += n
     return total
@@ -141,6 +149,10 @@ def main():
                     help="latent frames per pass through the stages up to the last temporal upsample "
                          "(per-level pass sizes; the later stages keep --frames-per-pass); 0: same")
     ap.add_argument("--latent-frames", type=int, default=31)
+    ap.add_argument("--topology", choices=("synthetic", "real"), default="synthetic",
+                    help="synthetic: the configured 384/384/192/96 decoder (the headline); real: the Wan2.2 "
+                         "TI2V-5B topology (1024/1024/512/256, mid attention, DupUp3D, 12-channel head, "
+                         "unpatchify, clamp) with random weights, no CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy kernel over MIB MiB (calibrates the HBM byte counters) and exit")
@@ -157,15 +169,17 @@ def main():
         profiling.copy_calibration_run(args.copy_calibration)
         return
 
-    spec = wl.FULL_DECODER
+    real = args.topology == "real"
+    spec = wl.REAL_DECODER if real else wl.FULL_DECODER
     _, params = wl.decoder_weights(spec, seed=4, latent_frames=4)
     z = wl.streaming_latents(seed=5, latent_frames=args.latent_frames).to(torch.bfloat16).cuda()
-    dec = wvd.Decoder(wvd.make_desc(), params)
+    dec = wvd.Decoder(wvd.desc_from_spec(spec), params)
     del params
     fpp = args.frames_per_pass
     early = max(args.early_frames_per_pass, fpp)
     F = dec.video_frames(args.latent_frames, fpp)
-    video = torch.empty((1, 3, F, wl.VIDEO_H, wl.VIDEO_W), dtype=torch.bfloat16, device="cuda")
+    video = torch.empty(wvd.video_shape(dec.desc, F), dtype=torch.bfloat16, device="cuda")
+    assert video.shape[3:] == (wl.VIDEO_H, wl.VIDEO_W)
     dec.workspace(fpp, early)
     torch.cuda.synchronize()
 
@@ -213,12 +227,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "streaming 5 s decode: latents [1,48,31,44,78] -> video [1,3,121,704,1248], "
+        "config": {"workload": f"streaming decode: latents [1,48,{args.latent_frames},44,78] -> video "
+                               f"[1,3,{F},704,1248], "
                                f"{fpp} latent frames per pass"
                                + (f" ({early} per pass through conv_in, the middle blocks and the two temporal "
                                   f"stages)" if early > fpp else "")
-                               + ", decoder 48->384, 2 mid resblocks, stages "
-                               "384/384/192/96 (2 resblocks each, time x2 on the first two), random Kaiming weights",
+                               + (", the Wan2.2 TI2V-5B decoder topology: post_quant_conv, conv_in 48->1024, mid "
+                                  "resblock + single-head attention + resblock, up blocks 1024/1024/512/256 (3 "
+                                  "resblocks each; time x2 on the first two, spatial x2 and DupUp3D on the first "
+                                  "three), conv_out 256->12, unpatchify, clamp; random Kaiming weights" if real else
+                                  ", decoder 48->384, 2 mid resblocks, stages "
+                                  "384/384/192/96 (2 resblocks each, time x2 on the first two), random Kaiming weights"),
+                   "topology": args.topology,
                    "latent_frames": args.latent_frames, "video_frames": F, "frames_per_pass": fpp,
                    "early_frames_per_pass": early,
                    "global_batch": 1, "parallelism": "none (1 GPU)"},
@@ -245,7 +265,7 @@ def main():
         "peak_hbm_gib": round(peak_alloc, 3),
         "peak_hbm_reserved_gib": round(peak_reserved, 3),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not real:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
 

@@ -1047,6 +1047,7 @@ enum ConfigId {
   PHASE_DMA_N3_W4,  // x2 upsampling phases: 96 x (8 rows x 32 columns), two workgroups per CU
   PHASE_DMA_N3_M1_W8,  // the same tile, one row per wave: two 8-wave workgroups per CU
   HALO_DMA_N2_W8,  // 64 x (16 rows x 32 columns): small grids
+  HALO_DMA_N1_W8,  // 32 x (16 rows x 32 columns): a few output channels (a 12-channel head)
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -1055,7 +1056,7 @@ const ConfigEntry kConfigs[] = {
     WVD_HALO_CONFIG(6, 1, 8),       WVD_HALO_CONFIG(3, 2, 8),       WVD_HALO_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_CONFIG(3, 2, 8),
     WVD_HALO_DMA_CONFIG(6, 1, 8),    WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
-    WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),
+    WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),    WVD_HALO_DMA_CONFIG(1, 2, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -1086,6 +1087,7 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   const int64_t cus = 256;
   const int64_t T = p.T, H = p.H, W = p.W;
   const int Npad = p.Npad, phases = p.phases;
+  if (Npad <= 32 && phases == 1 && p.kh == 3 && p.kw == 3) return HALO_DMA_N1_W8;
   if (Npad <= 32) return LIN_N1_M4_W4;
   if (phases == 1 && p.kh == 3 && p.kw == 3) {
     if (one_n_tile) return Npad > 96 ? HALO_DMA_N6_W8 : HALO_DMA_N3_W8;

@@ -80,12 +80,30 @@ __global__ __launch_bounds__(256) void dup_add_kernel(bf16_t* __restrict__ y, co
   bf16_t* yp = y + i * 8;
   const u32x4 v = *(const u32x4*)yp;
   u32x4 o;
+  if (r == 4 * ft) {
+    // each output channel c reads input channel c (nearest copies): 8 contiguous channels
+    const u32x4 d = *(const u32x4*)(xs + g * 8);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c0 = g * 8 + 2 * q;
-    const float lo = bf16_lo(v[q]) + bf16_to_f32(xs[(4 * ft * c0 + sub) / r]);
-    const float hi = bf16_hi(v[q]) + bf16_to_f32(xs[(4 * ft * (c0 + 1) + sub) / r]);
-    o[q] = pack_bf16x2(lo, hi);
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(bf16_lo(v[q]) + bf16_lo(d[q]), bf16_hi(v[q]) + bf16_hi(d[q]));
+  } else if (ft == 1 && r == 2) {
+    // channel c reads 2c + i (i the row parity): every other channel of 16 contiguous ones
+    const u32x4 d0 = *(const u32x4*)(xs + g * 16), d1 = *(const u32x4*)(xs + g * 16 + 8);
+    const bool odd = (Y & 1) != 0;
+    const uint32_t w[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = odd ? bf16_hi(w[2 * q]) : bf16_lo(w[2 * q]);
+      const float b = odd ? bf16_hi(w[2 * q + 1]) : bf16_lo(w[2 * q + 1]);
+      o[q] = pack_bf16x2(bf16_lo(v[q]) + a, bf16_hi(v[q]) + b);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c0 = g * 8 + 2 * q;
+      const float lo = bf16_lo(v[q]) + bf16_to_f32(xs[(4 * ft * c0 + sub) / r]);
+      const float hi = bf16_hi(v[q]) + bf16_to_f32(xs[(4 * ft * (c0 + 1) + sub) / r]);
+      o[q] = pack_bf16x2(lo, hi);
+    }
   }
   *(u32x4*)yp = o;
 }

@@ -57,6 +57,22 @@ def test_small_real_decoder_matches_oracle_and_is_pass_size_invariant(rule):
     assert 0.0 < float((videos[0].abs() < 1).float().mean()) < 1.0
 
 
+def test_dup_up_of_every_ratio_matches_oracle():
+    """DupUp3D ratios 8 (nearest copies, time x2), 4 with time x2 (channel halving: the general
+    gather), 4 without (nearest copies) and 2 (channel pairs to row pairs)."""
+    spec = _spec(stage_channels=(64, 32, 32, 16), dup=(True, True, True, False), clamp=False)
+    hw = (4, 6)
+    z, params = wl.decoder_weights(spec, seed=63, latent_frames=3, latent_hw=hw)
+    for rule in (True, False):
+        ref = oracle.decode(z[0], oracle.as_numpy_params(params), spec, frames_per_pass=2, first_frame_rule=rule)
+        dec = _decoder(spec, params, hw)
+        got = dec.decode(z.to(torch.bfloat16).cuda(), frames_per_pass=2, first_frame_rule=rule)[0].float().cpu().numpy()
+        q = psnr(got, ref)
+        log(f"dup ratios rule={rule} psnr {q:.2f} dB")
+        assert got.shape == ref.shape
+        assert q >= 55.0
+
+
 @pytest.mark.parametrize("rule", [True, False])
 def test_small_real_decoder_per_level_pass_sizes_same_bits(rule):
     spec = _spec()
