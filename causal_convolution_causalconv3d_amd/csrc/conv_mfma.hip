@@ -1048,6 +1048,7 @@ enum ConfigId {
   PHASE_DMA_N3_M1_W8,  // the same tile, one row per wave: two 8-wave workgroups per CU
   HALO_DMA_N2_W8,  // 64 x (16 rows x 32 columns): small grids
   HALO_DMA_N1_W8,  // 32 x (16 rows x 32 columns): a few output channels (a 12-channel head)
+  LIN_N4_W8,       // 128 x 256, 2 waves/SIMD: channel counts that are multiples of 128, not of 96
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -1057,6 +1058,7 @@ const ConfigEntry kConfigs[] = {
     WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_CONFIG(3, 2, 8),
     WVD_HALO_DMA_CONFIG(6, 1, 8),    WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),    WVD_HALO_DMA_CONFIG(1, 2, 8),
+    WVD_CONV_CONFIG(4, 1, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -1110,6 +1112,8 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
     if (Npad <= 96) return fills(LIN_N3_W8) ? n96 : LIN_N3_W4;
     return fills(LIN_N6_W8) ? LIN_N6_W8 : LIN_N6_W4;
   }
+  // (256, 512, 1024 channels: 96- and 192-wide tiles would leave a third of a tile empty)
+  if (Npad % 192 != 0 && Npad % 128 == 0 && fills(LIN_N4_W8)) return LIN_N4_W8;
   if (Npad % 192 == 0) {
     if (fills(LIN_N6_W8)) return LIN_N6_W8;
     if (fills(LIN_N6_W4)) return LIN_N6_W4;
