@@ -107,3 +107,33 @@ def test_streaming_decode_full_size_pass_size_invariant():
         del v
         dec._ws = None
         torch.cuda.empty_cache()
+
+
+def test_real_topology_full_size_streaming_properties():
+    """The Wan2.2 TI2V-5B topology at 704x1248 (random weights): 9 latent frames give 33 frames
+    in [-1, 1] (the clamp), every pass size and the per-level pass sizes give the same bits, and
+    latent frames after the first pass leave the first pass's video frames untouched."""
+    spec = wl.REAL_DECODER
+    _, params = wl.decoder_weights(spec, seed=4, latent_frames=4)
+    z = wl.streaming_latents(seed=5, latent_frames=9).to(torch.bfloat16).cuda()
+    dec = wvd.Decoder(wvd.desc_from_spec(spec), params)
+    del params
+    log("real topology full size, 9 latent frames")
+    v4 = dec.decode(z, frames_per_pass=4).clone()
+    torch.cuda.synchronize()
+    assert tuple(v4.shape) == (1, 3, 33, 704, 1248)
+    assert bool(torch.isfinite(v4.float()).all()) and float(v4.float().abs().max()) <= 1.0
+    for fpp, early in ((3, None), (4, 9)):
+        log(f"real topology fpp={fpp} early={early}")
+        v = dec.decode(z, frames_per_pass=fpp, early_frames_per_pass=early)
+        torch.cuda.synchronize()
+        assert torch.equal(v, v4), (fpp, early)
+        del v
+        dec._ws = None
+        torch.cuda.empty_cache()
+    z2 = z.clone()
+    z2[:, :, 4:] = 0
+    v = dec.decode(z2, frames_per_pass=4)
+    torch.cuda.synchronize()
+    assert torch.equal(v[:, :, :13], v4[:, :, :13])  # latent frames 0..3 -> video frames 0..12
+    assert not torch.equal(v[:, :, 13:], v4[:, :, 13:])
