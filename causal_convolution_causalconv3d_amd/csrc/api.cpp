@@ -444,7 +444,7 @@ extern "C" wvd_status wvd_rmsnorm_silu(const wvd_tensor* x, const float* gamma, 
   WVD_TRY(check_tensor(y, "y", WVD_BF16, WVD_NTHWC, true));
   if (!gamma) return fail(WVD_ERR_ARG, "gamma is null");
   if (x->c != y->c || x->t != y->t || !same_grid(x, y)) return fail(WVD_ERR_SHAPE, "y must have x's shape");
-  if (x->c % 8 != 0 || x->c > 512) return fail(WVD_ERR_UNSUPPORTED, "channels must be a multiple of 8, at most 512");
+  if (x->c % 8 != 0 || x->c > 2048) return fail(WVD_ERR_UNSUPPORTED, "channels must be a multiple of 8, at most 2048");
   if (!(eps >= 0.0f)) return fail(WVD_ERR_ARG, "eps must be >= 0");
   return run_norm((const bf16_t*)x->data, gamma, eps, apply_silu, (bf16_t*)y->data, x->t * x->h * x->w, (int)x->c,
                   (hipStream_t)stream);

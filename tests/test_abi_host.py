@@ -99,7 +99,7 @@ def test_validation_errors_before_any_launch():
                              ctypes.byref(yn), None, None)
     assert st == 4
     # norm: channels beyond the supported width
-    xb = _fake_tensor(1024, 1, 2, 2)
+    xb = _fake_tensor(4096, 1, 2, 2)
     st = L.wvd_rmsnorm_silu(ctypes.byref(xb), ctypes.c_void_p(0x3000), 1e-6, 1, ctypes.byref(xb), None)
     assert st == 8
 
@@ -145,3 +145,22 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(wvd, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         wvd.lib()
+
+
+def test_real_topology_descriptor_validation():
+    """The real topology's switches are checked before anything runs."""
+    L = wvd.lib()
+    ok = wvd.desc_from_spec(wl.REAL_DECODER)
+    assert L.wvd_decoder_param_count(ctypes.byref(ok)) == 110
+    assert wvd.video_shape(ok, 121) == (1, 3, 121, 704, 1248)
+
+    def bad(**kw):
+        spec = wl.REAL_DECODER.__class__(**{**wl.REAL_DECODER.__dict__, **kw})
+        return L.wvd_decoder_param_count(ctypes.byref(wvd.desc_from_spec(spec)))
+
+    assert bad(spatial=(True, False, True, False)) == -1            # a time step without the spatial step
+    assert bad(dup=(True, True, True, True), spatial=(True, True, True, True), stage_channels=(1024, 1024, 512, 200)) == -1
+    assert bad(out_channels=13) == -1                                # not colours * patch^2
+    assert bad(base_channels=1000) == -1                             # attention needs a multiple of 32
+    d = wvd.desc_from_spec(wl.REAL_DECODER, 44, 77)                  # h*w not a multiple of 8
+    assert L.wvd_decoder_param_count(ctypes.byref(d)) == -1
