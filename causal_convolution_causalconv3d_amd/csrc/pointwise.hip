@@ -36,40 +36,52 @@ __global__ __launch_bounds__(256) void norm_silu_kernel(const bf16_t* __restrict
   const float inv_c = 1.0f / (float)C;
   const int64_t wave_id = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
-  for (int64_t p0 = wave_id * PPW; p0 < positions; p0 += nwaves * PPW) {
-    const int64_t pos = p0 + slot;
-    float f[KPL][8];
-    float ss = 0.0f;
+  // U position steps per iteration, their loads issued together (more bytes in flight per lane)
+  constexpr int U = (KPL == 1) ? 2 : 1;
+  for (int64_t p0 = wave_id * PPW; p0 < positions; p0 += U * nwaves * PPW) {
+    u32x4 v[U][KPL];
+    int64_t pos[U];
 #pragma unroll
-    for (int k = 0; k < KPL; ++k) {
-      const bool ok = active[k] && pos < positions;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *(const u32x4*)(x + pos * C + (sub + k * G) * 8);
+    for (int u = 0; u < U; ++u) {
+      pos[u] = p0 + u * nwaves * PPW + slot;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f[k][2 * q] = bf16_lo(v[q]);
-        f[k][2 * q + 1] = bf16_hi(v[q]);
+      for (int k = 0; k < KPL; ++k) {
+        v[u][k] = u32x4{0u, 0u, 0u, 0u};
+        if (active[k] && pos[u] < positions) v[u][k] = *(const u32x4*)(x + pos[u] * C + (sub + k * G) * 8);
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(f[k][e], f[k][e], ss);
     }
 #pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    const float r = rsqrtf(ss * inv_c + eps);
+    for (int u = 0; u < U; ++u) {
+      float f[KPL][8];
+      float ss = 0.0f;
 #pragma unroll
-    for (int k = 0; k < KPL; ++k) {
-      u32x4 o;
+      for (int k = 0; k < KPL; ++k) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float a = f[k][2 * q] * r * g[k][2 * q];
-        float b = f[k][2 * q + 1] * r * g[k][2 * q + 1];
-        if (silu) {
-          a = silu_f32(a);
-          b = silu_f32(b);
+        for (int q = 0; q < 4; ++q) {
+          f[k][2 * q] = bf16_lo(v[u][k][q]);
+          f[k][2 * q + 1] = bf16_hi(v[u][k][q]);
         }
-        o[q] = pack_bf16x2(a, b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(f[k][e], f[k][e], ss);
       }
-      if (active[k] && pos < positions) *(u32x4*)(y + pos * C + (sub + k * G) * 8) = o;
+#pragma unroll
+      for (int m = G / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+      const float r = rsqrtf(ss * inv_c + eps);
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float a = f[k][2 * q] * r * g[k][2 * q];
+          float b = f[k][2 * q + 1] * r * g[k][2 * q + 1];
+          if (silu) {
+            a = silu_f32(a);
+            b = silu_f32(b);
+          }
+          o[q] = pack_bf16x2(a, b);
+        }
+        if (active[k] && pos[u] < positions) *(u32x4*)(y + pos[u] * C + (sub + k * G) * 8) = o;
+      }
     }
   }
 }
@@ -161,7 +173,7 @@ hipError_t launch_norm_silu(const bf16_t* x, const float* gamma, float eps, int 
   int G = 1;
   while (G < cv && G < 64) G *= 2;
   const int kpl = (cv + G - 1) / G;  // chunks per lane: 1 up to 512 channels
-  const int ppb = 4 * (64 / G);      // positions per block step
+  const int ppb = 4 * (64 / G) * (kpl == 1 ? 2 : 1);  // positions per block iteration (U steps)
   int64_t blocks = (positions + ppb - 1) / ppb;
   if (blocks > 8192) blocks = 8192;
 #define WVD_NORM_CASE(GG, KK) \
