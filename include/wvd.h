@@ -168,8 +168,16 @@ wvd_status wvd_upsample(const wvd_tensor* x, const void* spatial, const float* s
 
 /* ============================================================================================
  * The whole decoder, streamed in chunks of latent frames with an explicit cache handle
- * (the page's decode and decode_chunk functions, minus the parts absent from the synthetic
- * topology; its "Causal caches" part for what the cache carries).
+ * (the page's decode and decode_chunk functions and its part list; its "Causal caches" part for
+ * what the cache carries). The descriptor describes the synthetic decoder (the real topology's
+ * switches all 0) or the real Wan2.2 TI2V-5B topology: post_quant_conv, mid-block attention
+ * (base channels a multiple of 32, latent h*w a multiple of 8), stages without the spatial step
+ * (and then without a time step or DupUp3D), DupUp3D (out * ft * 4 a multiple of the stage's
+ * input channels), a head of colours * patch^2 channels with unpatchify and clamp. The RMS norm
+ * is gamma * x / sqrt(mean_c x^2 + eps) throughout; a tiny eps (1e-27) gives the page's
+ * x / max(||x||, 1e-12) * sqrt(C) * gamma for every position with a norm above 1e-12. Channels
+ * up to 2048. wvd_decoder_param_count returns -1 and wvd_last_error() says why for a
+ * descriptor outside these bounds.
  * ========================================================================================== */
 #define WVD_MAX_STAGES 8
 typedef struct {
@@ -180,7 +188,7 @@ typedef struct {
   int stage_temporal[WVD_MAX_STAGES]; /* time x2 on the stage (1, 1, 0, 0) */
   int mid_resblocks;                  /* residual blocks after conv_in (2) */
   int stage_resblocks;                /* residual blocks per stage (2) */
-  int out_channels;                   /* video channels (3) */
+  int out_channels;                   /* conv_out channels: video colours (3), times patch^2 */
   float eps;                          /* RMS norm epsilon (1e-6) */
   int latent_h, latent_w;             /* latent frame size (44, 78) */
   /* The real Wan2.2 TI2V-5B decoder's parts (the page's part list; all 0 in the synthetic one): */
