@@ -14,6 +14,7 @@ Command line (prints markdown):
   python -m causal_convolution_causalconv3d_amd.profiling stats <rocprof kernel_stats.csv> [--command CMD]
   python -m causal_convolution_causalconv3d_amd.profiling traffic --config NAME --fetch DIR --write DIR
       --copy-fetch DIR --copy-write DIR --copy-mib N [--command CMD ...]
+  python -m causal_convolution_causalconv3d_amd.profiling mfma <rocprof counter_collection.csv> [--command CMD]
 """
 import argparse
 import csv
@@ -179,6 +180,33 @@ def stats_summary(path: str, command: str, top: int = 25) -> str:
     return "\n".join(out) + "\n"
 
 
+def mfma_summary(path: str, command: str, top: int = 12, simds: int = 1024, xcds: int = 8) -> str:
+    """MFMA-busy share per kernel from one `--pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES ...`
+    run: SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x SIMDs), the kernel cycles being
+    GRBM_GUI_ACTIVE (summed over the XCDs) / XCDs; also the clock those cycles imply over the
+    dispatches' durations."""
+    acc: Dict[str, Dict[str, float]] = {}
+    dur: Dict[str, float] = {}
+    seen = set()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = re.sub(r"\(wvd::ConvProblem\)$", "", r["Kernel_Name"]).replace("void wvd::(anonymous namespace)::", "")
+            name = name if len(name) <= 70 else name[:67] + "..."
+            c = acc.setdefault(name, {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if r["Dispatch_Id"] not in seen:
+                seen.add(r["Dispatch_Id"])
+                dur[name] = dur.get(name, 0.0) + (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    rows = sorted(acc.items(), key=lambda kv: -dur[kv[0]])[:top]
+    out = ["Command:", "", f"    {command}", "",
+           "| kernel | ms | clock GHz | MFMA busy |", "|---|---:|---:|---:|"]
+    for name, c in rows:
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(cyc * simds, 1.0)
+        out.append(f"| `{name}` | {1e3 * dur[name]:.2f} | {cyc / max(dur[name], 1e-12) / 1e9:.2f} | {100 * busy:.1f}% |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m causal_convolution_causalconv3d_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -191,9 +219,14 @@ def main(argv=None):
         tr.add_argument(f"--{k}", required=True)
     tr.add_argument("--copy-mib", type=int, required=True)
     tr.add_argument("--command", action="append", default=[])
+    mf = sub.add_parser("mfma")
+    mf.add_argument("csv")
+    mf.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_summary(a.csv, a.command))
+    elif a.cmd == "mfma":
+        sys.stdout.write(mfma_summary(a.csv, a.command))
     else:
         sys.stdout.write(traffic_summary(a.config, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.command))
 
