@@ -270,8 +270,9 @@ def test_bf16_conv_chunked_equals_one_shot_bitwise():
 # ---------------------------------------------------------------------------------------------
 # RMS norm + SiLU
 # ---------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("C", [48, 96, 192, 384])
+@pytest.mark.parametrize("C", [48, 96, 192, 384, 520, 1024, 1536, 2048])
 def test_norm_silu_matches_oracle(C):
+    """Up to 512 channels one 16-byte chunk per lane; beyond, two to four per lane."""
     log(f"norm C={C}")
     x = wl.bf16_values(_rand((1, C, 3, 7, 11), C) * 3.0)
     gamma = 1.0 + 0.1 * _rand((C,), C + 1)
