@@ -69,6 +69,9 @@ CONV_CASES = [
     (384, 192, 3, 9, 10, (1, 1, 1), 0),   # residual-block shortcut
     (192, 384, 4, 6, 9, (3, 1, 1), 2),    # time conv, plain layout
     (96, 96, 1, 3, 3, (1, 3, 3), 0),      # a per-frame 2-D conv, tiny
+    (1024, 1024, 2, 9, 13, (3, 3, 3), 2), # the real topology's width: 11 channel tiles, the last partial
+    (1024, 512, 2, 5, 7, (1, 1, 1), 0),   # its shortcut (128-wide linear tiles)
+    (256, 12, 2, 7, 9, (3, 3, 3), 2),     # its 12-channel head (32-wide halo tiles)
 ]
 
 
