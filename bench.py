@@ -131,13 +131,14 @@ def cpu_baseline(seconds_hint: float = 15.0):
 
 def conv_launch_bytes(sh) -> float:
     """Algorithmic HBM bytes of one conv launch: the input frames it reads (with up to kt - 1 history
-    frames) once, the packed weights once, the bf16 output once (a residual read is not counted),
-    and the cache frames it copies as side work (read and written once)."""
+    frames) once, the packed weights once, the bf16 output once, the residual once when it adds
+    one, and the cache frames it copies as side work (read and written once)."""
     kt = 3 if sh["taps"] in (27, 3) else 1
     frames_in = sh["T"] + min(sh["Th"], kt - 1)
     hw = sh["H"] * sh["W"]
+    out = sh["T"] * hw * sh["phases"] * sh["N"]
     return 2.0 * (frames_in * hw * sh["Ci"] + sh["phases"] * sh["N"] * sh["taps"] * sh["Ci"]
-                  + sh["T"] * hw * sh["phases"] * sh["N"] + 2 * sh.get("copied", 0) * hw * sh["Ci"])
+                  + out * (2 if sh.get("res", 0) else 1) + 2 * sh.get("copied", 0) * hw * sh["Ci"])
 
 
 def main():

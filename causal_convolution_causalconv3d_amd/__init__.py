@@ -508,8 +508,8 @@ def timing_launches():
         cfg = ctypes.c_int()
         ms = ctypes.c_double()
         fl = ctypes.c_double()
-        sh = (ctypes.c_int * 9)()
+        sh = (ctypes.c_int * 10)()
         L.wvd_timing_launch(i, ctypes.byref(cfg), ctypes.byref(ms), ctypes.byref(fl), sh)
         out.append((names.get(cfg.value, "?"), ms.value, fl.value,
-                    dict(zip(("T", "H", "W", "Ci", "N", "taps", "phases", "Th", "copied"), list(sh)))))
+                    dict(zip(("T", "H", "W", "Ci", "N", "taps", "phases", "Th", "copied", "res"), list(sh)))))
     return out

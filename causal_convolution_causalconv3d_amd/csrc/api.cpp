@@ -90,7 +90,7 @@ struct TimingRecord {
   int mem;     // MemKind of a memory-bound kernel, or -1
   hipEvent_t start, stop;
   double flops;  // conv: algorithmic FLOPs; memory-bound kernel: algorithmic bytes
-  int shape[9];  // T, H, W, Ci, N, taps, phases, Th, cache frames copied as side work
+  int shape[10];  // T, H, W, Ci, N, taps, phases, Th, cache frames copied as side work, residual read
 };
 // The memory-bound kernels of the path, timed like the convs (algorithmic bytes: every input
 // element read once, every output element written once).
@@ -111,7 +111,7 @@ struct LaunchRecord {
   int config;
   float ms;
   double flops;
-  int shape[9];
+  int shape[10];
 };
 struct TimingState {
   std::mutex mu;
@@ -159,7 +159,7 @@ wvd_status run_conv(const ConvProblem& p, hipStream_t s, double flops) {
     WVD_HIP(hipEventRecord(e1, s), "hipEventRecord");
     std::lock_guard<std::mutex> lk(g_timing.mu);
     const int copied = (int)((p.copy.bytes[0] + p.copy.bytes[1]) / std::max<int64_t>(1, (int64_t)p.H * p.W * p.Ci * 2));
-    TimingRecord r{cfg, -1, e0, e1, flops, {p.T, p.H, p.W, p.Ci, p.N, p.ntaps, p.phases, p.Th, copied}};
+    TimingRecord r{cfg, -1, e0, e1, flops, {p.T, p.H, p.W, p.Ci, p.N, p.ntaps, p.phases, p.Th, copied, p.res ? 1 : 0}};
     g_timing.pending.push_back(r);
   }
   return WVD_OK;
@@ -1611,7 +1611,7 @@ extern "C" int wvd_timing_read_mem(int i, const char** name, int64_t* launches, 
   return MEM_KINDS;
 }
 
-extern "C" int wvd_timing_launch(int i, int* config, double* ms, double* flops, int shape[9]) {
+extern "C" int wvd_timing_launch(int i, int* config, double* ms, double* flops, int shape[10]) {
   const char* nm = nullptr;
   wvd_timing_read(0, &nm, nullptr, nullptr, nullptr);  // drains the pending events
   std::lock_guard<std::mutex> lk(g_timing.mu);
@@ -1622,7 +1622,7 @@ extern "C" int wvd_timing_launch(int i, int* config, double* ms, double* flops, 
   if (ms) *ms = r.ms;
   if (flops) *flops = r.flops;
   if (shape)
-    for (int k = 0; k < 9; ++k) shape[k] = r.shape[k];
+    for (int k = 0; k < 10; ++k) shape[k] = r.shape[k];
   return n;
 }
 
@@ -1646,7 +1646,7 @@ extern "C" int wvd_timing_read(int i, const char** name, int64_t* launches, doub
       g_timing.ms[r.config] += t;
       g_timing.flops[r.config] += r.flops;
       LaunchRecord l{r.config, t, r.flops, {}};
-      for (int k = 0; k < 9; ++k) l.shape[k] = r.shape[k];
+      for (int k = 0; k < 10; ++k) l.shape[k] = r.shape[k];
       g_timing.log.push_back(l);
     }
     g_timing.pool.push_back(r.start);

@@ -266,9 +266,9 @@ wvd_status wvd_timing_reset(void);
 int wvd_timing_read(int i, const char** name, int64_t* launches, double* ms, double* flops);
 /* Launch i (0-based, in launch order) since the last reset: its configuration index, milliseconds,
  * algorithmic FLOPs and problem shape {T, H, W, Ci, N, taps, phases, history frames, input frames
- * copied into a cache slot as side work}. Returns the number of recorded launches (call with
- * i = -1 to count). */
-int wvd_timing_launch(int i, int* config, double* ms, double* flops, int shape[9]);
+ * copied into a cache slot as side work, 1 if it reads a residual}. Returns the number of
+ * recorded launches (call with i = -1 to count). */
+int wvd_timing_launch(int i, int* config, double* ms, double* flops, int shape[10]);
 /* The memory-bound kernels (channel RMS norm + SiLU, the head's tap stencil, the latent layout
  * conversion), timed the same way: for kind i (0..count-1) a name, the launch count, the summed
  * milliseconds and the summed algorithmic bytes (every input element read once, every output
