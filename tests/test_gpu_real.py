@@ -104,3 +104,51 @@ def test_attention_at_the_full_latent_frame_matches_oracle():
     q = psnr(got, ref)
     log(f"attention decoder psnr {q:.2f} dB rel {rel_max(got, ref):.3e}")
     assert q >= 55.0
+
+
+def _random_spec(rng):
+    """A small decoder with random switches, kept inside the descriptor's bounds."""
+    base = int(rng.choice([32, 64]))
+    n_st = int(rng.integers(1, 4))
+    chans, temporal, spatial, dup = [], [], [], []
+    c = base
+    for s in range(n_st):
+        co = int(rng.choice([c, max(16, c // 2)]))
+        sp = bool(rng.random() < 0.8) or s == 0
+        t = sp and bool(rng.random() < 0.5)
+        ft = 2 if t else 1
+        d = sp and (co * ft * 4) % c == 0 and bool(rng.random() < 0.6)
+        chans.append(co), temporal.append(t), spatial.append(sp), dup.append(d)
+        c = co
+    patch = int(rng.choice([1, 2]))
+    return wl.DecoderSpec(z_channels=int(rng.choice([8, 16])), base_channels=base, stage_channels=tuple(chans),
+                          temporal=tuple(temporal), mid_resblocks=int(rng.integers(1, 3)),
+                          stage_resblocks=int(rng.integers(1, 3)), out_channels=3 * patch * patch, eps=1e-27,
+                          post_quant=bool(rng.random() < 0.5), mid_attention=bool(rng.random() < 0.5),
+                          spatial=tuple(spatial), dup=tuple(dup), patch=patch, clamp=False, norm_l2=True)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_small_decoders_match_oracle(seed):
+    """Seeded random topologies (stage counts, channel changes, time and spatial steps, DupUp3D,
+    post_quant_conv, attention, patch 1 or 2) and random pass sizes: PSNR >= 55 dB against the
+    oracle and the same bits for every pass size."""
+    rng = np.random.default_rng(100 + seed)
+    spec = _random_spec(rng)
+    hw = (4, 6) if seed % 2 else (2, 4)
+    T = int(rng.integers(2, 5))
+    rule = bool(seed % 3)
+    log(f"random decoder seed={seed} {spec} T={T} rule={rule}")
+    z, params = wl.decoder_weights(spec, seed=200 + seed, latent_frames=T, latent_hw=hw)
+    ref = oracle.decode(z[0], oracle.as_numpy_params(params), spec, frames_per_pass=T, first_frame_rule=rule)
+    dec = _decoder(spec, params, hw)
+    zd = z.to(torch.bfloat16).cuda()
+    videos = [dec.decode(zd, frames_per_pass=f, first_frame_rule=rule) for f in (T, 1, 2)]
+    torch.cuda.synchronize()
+    for v in videos[1:]:
+        assert torch.equal(v, videos[0])
+    got = videos[0][0].float().cpu().numpy()
+    assert got.shape == ref.shape
+    q = psnr(got, ref)
+    log(f"random decoder seed={seed} psnr {q:.2f} dB")
+    assert q >= 55.0
