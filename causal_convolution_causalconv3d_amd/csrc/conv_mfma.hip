@@ -595,9 +595,12 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
   // weight fetch distance D (steps ahead), slots NWS (> D, and k mod NWS a compile-time
   // function of the stage parity and the tap), barrier wait window WW = D - 2 steps (must not
   // exceed SPS - 2 so that the patch fetched at step 0 is in place for step SPS - 1)
-  // (2x2 taps on 8-row tiles: D = 3 and 4 slots, so that two workgroups fit in one CU's LDS)
+  // (2x2 taps on 8-row tiles: D = 3 and 4 slots, and 3x3 taps on 4-wave 8-row tiles: D = 2 and 3
+  // slots, so that two workgroups fit in one CU's LDS)
   constexpr bool SMALL = (SPS == 4 && WAVES * MB == 8);
-  constexpr int D = (SPS == 9) ? 5 : (SMALL ? 3 : 4), NWS = (SPS == 9) ? 6 : (SMALL ? 4 : 8), WW = D - 2;
+  constexpr bool SMALL3 = (SPS == 9 && WAVES == 4);
+  constexpr int D = (SPS == 9) ? (SMALL3 ? 2 : 5) : (SMALL ? 3 : 4);
+  constexpr int NWS = (SPS == 9) ? (SMALL3 ? 3 : 6) : (SMALL ? 4 : 8), WW = D - 2;
   static_assert(WW <= SPS - 2 && D < NWS && (2 * SPS) % NWS == 0, "fetch distance, slots and wait window");
   constexpr int BN = NB * 32;
   constexpr int TR = WAVES * MB;
@@ -819,7 +822,7 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
   fetch_patch(I0{}, cur, true);
   fetch_w(I0{}, cur.col, rs_cur);
   fetch_w(I1{}, cur.col + p.Cip, rs_cur);
-  fetch_w(I2{}, cur.col + 2 * p.Cip, rs_cur);
+  if constexpr (D >= 3) fetch_w(I2{}, cur.col + 2 * p.Cip, rs_cur);
   if constexpr (D >= 4) fetch_w(I3{}, cur.col + 3 * p.Cip, rs_cur);
   if constexpr (D == 5) fetch_w(I4{}, cur.col + 4 * p.Cip, rs_cur);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1049,6 +1052,7 @@ enum ConfigId {
   HALO_DMA_N2_W8,  // 64 x (16 rows x 32 columns): small grids
   HALO_DMA_N1_W8,  // 32 x (16 rows x 32 columns): a few output channels (a 12-channel head)
   LIN_N4_W8,       // 128 x 256, 2 waves/SIMD: channel counts that are multiples of 128, not of 96
+  HALO_DMA_N3_W4,  // 96 x (8 rows x 32 columns) on 4 waves in 80 KB: two workgroups per CU
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -1058,7 +1062,7 @@ const ConfigEntry kConfigs[] = {
     WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_CONFIG(3, 2, 8),
     WVD_HALO_DMA_CONFIG(6, 1, 8),    WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),    WVD_HALO_DMA_CONFIG(1, 2, 8),
-    WVD_CONV_CONFIG(4, 1, 8),
+    WVD_CONV_CONFIG(4, 1, 8),           WVD_HALO_DMA_CONFIG(3, 2, 4),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -1097,7 +1101,11 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
     // 64-wide ones if they still run in one round: two thirds of the tile time
     const int64_t b3 = blocks_for(kConfigs[HALO_DMA_N3_W8], T, H, W, Npad);
     const int64_t b2 = blocks_for(kConfigs[HALO_DMA_N2_W8], T, H, W, Npad);
-    return (Npad % 64 == 0 && b3 < cus && b2 <= cus) ? HALO_DMA_N2_W8 : HALO_DMA_N3_W8;
+    if (Npad % 64 == 0 && b3 < cus && b2 <= cus) return HALO_DMA_N2_W8;
+    // frames whose height leaves a 16-row tile mostly empty (the 88-row level: 96 rows tiled)
+    // take the 8-row tiles, two workgroups per CU, about 5 % slower on whole tiles
+    const int64_t r16 = (H + 15) / 16 * 16, r8 = (H + 7) / 8 * 8;
+    return (r16 * 100 > r8 * 107) ? HALO_DMA_N3_W4 : HALO_DMA_N3_W8;
   }
   // The phase convs (K = 4 taps x C) have short reductions and heavy epilogues, so they run 8-row
   // DMA halo tiles with 80 KB of LDS, two workgroups per CU, whose epilogues overlap other waves'
