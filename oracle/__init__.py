@@ -13,7 +13,7 @@ caches", and the functions cached_conv, causal_conv, residual_block, time_upsamp
 spatial_upsample, rms_norm, decode_chunk). bf16 workloads hand the oracle bf16-rounded values;
 inside the oracle nothing is rounded to bf16.
 
-Readings taken where the page is silent or the workload text differs (each listed in the design doc):
+Readings taken where the page is silent or the workload text differs:
   * RMS norm is gamma * x / sqrt(mean_c x^2 + eps), eps = 1e-6 (the workload's explicit eps),
     not the page's x / max(||x||, 1e-12) * sqrt(C) form; they differ by <= eps / (2 mean x^2).
   * The synthetic decoder has no post_quant_conv, attention, DupUp3D shortcut, unpatchify or
