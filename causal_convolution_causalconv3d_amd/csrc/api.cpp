@@ -665,7 +665,13 @@ extern "C" wvd_status wvd_upsample(const wvd_tensor* x, const void* spatial, con
   const size_t need = wvd_upsample_workspace_bytes(C, T, (int)x->h, (int)x->w, spatial != nullptr, temporal != nullptr, order);
   if (ws_bytes < need) return fail(WVD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
   if (need > 0 && (!ws || !aligned16(ws))) return fail(WVD_ERR_ALIGN, "workspace null or not 16-byte aligned");
-  if (T == 0) return WVD_OK;
+  if (T == 0) {  // no frames: the time conv's history passes through unchanged
+    if (time_hist_out && Th > 0)
+      WVD_HIP(hipMemcpyAsync(time_hist_out->data, time_hist->data, (size_t)numel(time_hist) * 2, hipMemcpyDeviceToDevice,
+                             (hipStream_t)stream),
+              "history copy");
+    return WVD_OK;
+  }
   hipStream_t s = (hipStream_t)stream;
   const int H = (int)x->h, W = (int)x->w;
   const bf16_t* hist = time_hist ? (const bf16_t*)time_hist->data : nullptr;

@@ -416,6 +416,69 @@ def test_upsample_time_first_with_history(first):
         assert rel_max(got[:, :1], ref0) <= 2e-2
 
 
+def test_empty_inputs_pass_histories_through():
+    """Zero-frame inputs launch nothing, give empty outputs and leave every history as it was (a
+    conv over no frames keeps its cache); a chunk after an empty one gives the same bits as
+    without it. The history outputs start as NaN so that a missed copy shows."""
+    log("empty inputs")
+    C, H, W = 96, 9, 14
+    nan = float("nan")
+    x = to_dev_nthwc(_rand((1, C, 4, H, W), 81))
+    empty = torch.empty((1, 0, H, W, C), dtype=torch.bfloat16, device="cuda")
+    # conv
+    wp = wvd.conv_pack(wl.kaiming(torch.Generator().manual_seed(82), (C, C, 3, 3, 3)).cuda())
+    h1 = torch.empty((1, 2, H, W, C), dtype=torch.bfloat16, device="cuda")
+    a = wvd.causal_conv3d(x[:, :2].contiguous(), wp, C, hist_out=h1)
+    h2 = torch.full_like(h1, nan)
+    e = wvd.causal_conv3d(empty, wp, C, hist=h1, hist_out=h2)
+    b = wvd.causal_conv3d(x[:, 2:].contiguous(), wp, C, hist=h2)
+    torch.cuda.synchronize()
+    assert e.shape == (1, 0, H, W, C)
+    assert torch.equal(h2, h1)
+    assert torch.equal(torch.cat([a, b], 1), wvd.causal_conv3d(x, wp, C))
+    # norm
+    assert wvd.rmsnorm_silu(empty, torch.ones(C, device="cuda"), 1e-6).shape == (1, 0, H, W, C)
+    # residual block: both convs' histories
+    cfg = wl.resblock_bf16(seed=83, C=C, T=4, H=H, W=W)
+    wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+    xr = to_dev_nthwc(cfg["x"])
+
+    def res_chunks(parts):
+        ys, g1, g2, start = [], None, None, 0
+        for n in parts:
+            t = wvd.history_frames_after(n, 0 if g1 is None else g1.shape[1])
+            o1 = torch.full((1, t, H, W, C), nan, dtype=torch.bfloat16, device="cuda")
+            o2 = torch.full_like(o1, nan)
+            ys.append(wvd.resblock(xr[:, start:start + n].contiguous(), wts, 1e-6, hist1=g1, hist2=g2, hist1_out=o1,
+                                   hist2_out=o2))
+            g1, g2, start = o1, o2, start + n
+        torch.cuda.synchronize()
+        return torch.cat(ys, 1), g1, g2
+
+    y0, a1, a2 = res_chunks([2, 2])
+    y1, b1, b2 = res_chunks([2, 0, 2])
+    assert torch.equal(y0, y1) and torch.equal(a1, b1) and torch.equal(a2, b2)
+    # upsample with a time step (not the first chunk): the time conv's history
+    wt = wvd.conv_pack(wl.kaiming(torch.Generator().manual_seed(84), (2 * C, C, 3, 1, 1)).cuda())
+    wsp = wvd.conv_pack(wl.kaiming(torch.Generator().manual_seed(85), (C, C, 3, 3)).cuda(), wvd.WVD_PACK_PHASE2X)
+
+    def up_chunks(parts):
+        ys, g, start = [], None, 0
+        for n in parts:
+            o = torch.full((1, wvd.history_frames_after(n, 0 if g is None else g.shape[1]), H, W, C), nan,
+                           dtype=torch.bfloat16, device="cuda")
+            ys.append(wvd.upsample(x[:, start:start + n].contiguous(), spatial=wsp, temporal=wt,
+                                   order=wvd.WVD_TIME_FIRST, time_hist=g, time_hist_out=o))
+            g, start = o, start + n
+        torch.cuda.synchronize()
+        return torch.cat(ys, 1), g
+
+    u0, g0 = up_chunks([2, 2])
+    u1, g1 = up_chunks([2, 0, 2])
+    assert u1.shape == (1, 8, 2 * H, 2 * W, C)
+    assert torch.equal(u0, u1) and torch.equal(g0, g1)
+
+
 # ---------------------------------------------------------------------------------------------
 # Whole decodes at reduced size
 # ---------------------------------------------------------------------------------------------
