@@ -110,8 +110,9 @@ wvd_status wvd_conv_pack(const void* w_raw, int w_dtype, int co, int ci, int kt,
  * hist_out: nullable; when set, receives the history this conv leaves for the next chunk (the
  *   page's cached_conv rule: the last min(T, 2) input frames, or the old last history frame
  *   followed by x when x has one frame). It may not alias hist; its t must be that frame count.
- * x may have zero frames (every entry point below too): nothing is computed, y is empty, and
- *   the history passes through unchanged into hist_out.
+ * x may have zero frames (so may the inputs of wvd_rmsnorm_silu, wvd_resblock and wvd_upsample;
+ *   wvd_decode_chunk rejects an empty chunk): nothing is computed, y is empty, and the history
+ *   passes through unchanged into hist_out.
  * ========================================================================================== */
 wvd_status wvd_causal_conv3d(const wvd_tensor* x, const void* w, int co, int kt, int kh, int kw,
                              const float* bias, const wvd_tensor* hist, const wvd_tensor* residual, wvd_tensor* y,
