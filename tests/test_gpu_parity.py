@@ -231,6 +231,44 @@ def test_conv_tile_walk_matches_one_tile_per_workgroup_and_oracle(case):
     assert ok, worst
 
 
+def test_wide_channel_tiles_same_bits_as_96_wide():
+    """256 output channels (a multiple of 128, not of 96) on a grid where the 128-wide halo tiles'
+    rounds over the chip take no longer: the automatic choice takes them; the K order is that of
+    the 96-wide tiles (compared with the oracle above, as is the forced 128-wide configuration on
+    the ragged cases), so the bits are the same, also with 8 workgroups walking all tiles. The
+    128-wide configuration has no fused-norm form and refuses a norm."""
+    Ci, Co, T, H, W = 256, 256, 2, 160, 320
+    log(f"wide tiles {Ci}->{Co} {T}x{H}x{W}")
+    x = to_dev_nthwc(wl.bf16_values(_rand((1, Ci, T, H, W), 91)))
+    wp = wvd.conv_pack(wl.kaiming(torch.Generator().manual_seed(92), (Co, Ci, 3, 3, 3)).cuda())
+    b = (0.1 * _rand((Co,), 93)).cuda()
+    hd = to_dev_nthwc(wl.bf16_values(_rand((1, Ci, 2, H, W), 94)))
+    try:
+        wvd.timing_reset()
+        wvd.timing_enable(True)
+        y = wvd.causal_conv3d(x, wp, Co, bias=b, hist=hd)
+        torch.cuda.synchronize()
+        wvd.timing_enable(False)
+        assert list(wvd.timing_read()) == ["conv_halo_dma_n4_m2_w8"]
+        wvd.conv_force_config("conv_halo_dma_n3_m2_w8")
+        y3 = wvd.causal_conv3d(x, wp, Co, bias=b, hist=hd)
+        wvd.conv_force_config(None)
+        wvd.conv_max_workgroups(8)
+        yw = wvd.causal_conv3d(x, wp, Co, bias=b, hist=hd)
+        torch.cuda.synchronize()
+        wvd.conv_max_workgroups(0)
+        assert torch.equal(y, y3) and torch.equal(y, yw)
+        cfg = wl.resblock_bf16(seed=95, C=96, T=2, H=5, W=7)
+        wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+        wvd.conv_force_config("conv_halo_dma_n4_m2_w8")
+        with pytest.raises(wvd.WvdError):
+            wvd.resblock(to_dev_nthwc(cfg["x"]), wts, 1e-6)
+    finally:
+        wvd.timing_enable(False)
+        wvd.conv_force_config(None)
+        wvd.conv_max_workgroups(0)
+
+
 @pytest.mark.parametrize("C,T,H,W", [(96, 2, 21, 45), (192, 2, 18, 40), (384, 1, 11, 35)])
 def test_upsample_tile_walk_matches_one_tile_per_workgroup(C, T, H, W):
     """The x2 phase convs (phases dealt as the fastest tile index) with 8 workgroups walking all
