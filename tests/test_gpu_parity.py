@@ -1,5 +1,5 @@
 """GPU parity: the HIP path (through the C ABI) against the oracle, element by element, on the
-same seeded inputs. Sizes span several tiles and ragged tails; the BASELINE-size cases follow in
+same seeded inputs. Sizes span several tiles and ragged tails; the full-size workload cases follow in
 test_gpu_fullsize.py.
 
 Tolerances. fp32 path: max abs error <= 1e-4 (fp32 accumulation of <= 27*Ci products against the
@@ -235,29 +235,32 @@ def test_wide_channel_tiles_same_bits_as_96_wide():
     """256 output channels (a multiple of 128, not of 96) on a grid where the 128-wide halo tiles'
     rounds over the chip take no longer: the automatic choice takes them; the K order is that of
     the 96-wide tiles (compared with the oracle above, as is the forced 128-wide configuration on
-    the ragged cases), so the bits are the same, also with 8 workgroups walking all tiles. The
-    128-wide configuration has no fused-norm form and refuses a norm."""
+    the ragged cases), so the bits are the same, with and without a residual, also with 8
+    workgroups walking all tiles. The 128-wide configuration has no fused-norm form and refuses a
+    norm."""
     Ci, Co, T, H, W = 256, 256, 2, 160, 320
     log(f"wide tiles {Ci}->{Co} {T}x{H}x{W}")
     x = to_dev_nthwc(wl.bf16_values(_rand((1, Ci, T, H, W), 91)))
     wp = wvd.conv_pack(wl.kaiming(torch.Generator().manual_seed(92), (Co, Ci, 3, 3, 3)).cuda())
     b = (0.1 * _rand((Co,), 93)).cuda()
     hd = to_dev_nthwc(wl.bf16_values(_rand((1, Ci, 2, H, W), 94)))
+    rd = to_dev_nthwc(wl.bf16_values(_rand((1, Co, T, H, W), 96)))
     try:
-        wvd.timing_reset()
-        wvd.timing_enable(True)
-        y = wvd.causal_conv3d(x, wp, Co, bias=b, hist=hd)
-        torch.cuda.synchronize()
-        wvd.timing_enable(False)
-        assert list(wvd.timing_read()) == ["conv_halo_dma_n4_m2_w8"]
-        wvd.conv_force_config("conv_halo_dma_n3_m2_w8")
-        y3 = wvd.causal_conv3d(x, wp, Co, bias=b, hist=hd)
-        wvd.conv_force_config(None)
-        wvd.conv_max_workgroups(8)
-        yw = wvd.causal_conv3d(x, wp, Co, bias=b, hist=hd)
-        torch.cuda.synchronize()
-        wvd.conv_max_workgroups(0)
-        assert torch.equal(y, y3) and torch.equal(y, yw)
+        for res in (None, rd):
+            wvd.timing_reset()
+            wvd.timing_enable(True)
+            y = wvd.causal_conv3d(x, wp, Co, bias=b, hist=hd, residual=res)
+            torch.cuda.synchronize()
+            wvd.timing_enable(False)
+            assert list(wvd.timing_read()) == ["conv_halo_dma_n4_m2_w8"]
+            wvd.conv_force_config("conv_halo_dma_n3_m2_w8")
+            y3 = wvd.causal_conv3d(x, wp, Co, bias=b, hist=hd, residual=res)
+            wvd.conv_force_config(None)
+            wvd.conv_max_workgroups(8)
+            yw = wvd.causal_conv3d(x, wp, Co, bias=b, hist=hd, residual=res)
+            torch.cuda.synchronize()
+            wvd.conv_max_workgroups(0)
+            assert torch.equal(y, y3) and torch.equal(y, yw), res is None
         cfg = wl.resblock_bf16(seed=95, C=96, T=2, H=5, W=7)
         wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
         wvd.conv_force_config("conv_halo_dma_n4_m2_w8")
