@@ -6,16 +6,29 @@ residual blocks, 4 up stages of 384/384/192/96 channels, 2 of them temporal): la
 121 bf16 frames of 704x1248 out. Inputs (latents, packed weights, cache, workspace) are resident
 in HBM before the timed region starts; the timed region holds exactly `--steps` decodes.
 
-Prints one JSON line: frames/s (value), ms per decode, the matrix-core conv kernels' achieved
-TFLOP/s against the bf16 dense peak (measured with HIP events around every conv launch in the
-timed region), peak HBM, and the CPU oracle timed on a bounded sample of the same decode.
+Prints one JSON line:
+  * value / ms_per_step: frames/s and ms per decode from a timed loop with no instrumentation;
+  * roofline, conv, epilogues: from a second, instrumented loop of the same `--steps` decodes
+    (HIP events around every conv and memory-bound launch, on the stream it runs on): the
+    dominant conv configuration's achieved TFLOP/s against the bf16 dense peak, all convs'
+    TFLOP/s, the memory-bound kernels' GB/s against the HBM peak;
+  * peak HBM of the decode;
+  * configs: the other workloads measured on their own (the fp32 single conv, the residual
+    block, the upsample stage, the one-pass decode), each with its conv TFLOP/s, memory-bound
+    GB/s, and the oracle's time on the host cores for the same workload or a bounded sample;
+  * cpu_baseline: the oracle on a bounded sample of the streaming decode, timed here, beside
+    the recorded wall time of the oracle's whole 121-frame decode (the stored samples' run).
 """
 import argparse
 import json
+import math
 import os
+import platform
+import subprocess
 import sys
 import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -26,6 +39,7 @@ import workloads as wl  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0
+GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 from causal_convolution_causalconv3d_amd import profiling  # noqa: E402
 
@@ -108,25 +122,225 @@ def achievable_peaks():
             "what": "torch.matmul bf16 8192^3 (hipBLASLt) and a 2 GiB device copy, 20 reps each, after the timed region"}
 
 
-def cpu_baseline(seconds_hint: float = 15.0):
-    """The oracle (as it stands) on a bounded sample of the same decode: a 20x28 latent crop,
-    one pass of 2 latent frames (8 video frames of 320x448), scaled to full-frame frames/s by the
-    crop's share of the 44x78 latent frame (about 10 s on 16 host cores)."""
+def host_info():
+    """The host the CPU baseline runs on: logical CPUs, CPU model, OMP_NUM_THREADS."""
+    model = platform.processor() or "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, check=True).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model, "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def _oracle():
     import oracle  # CPU baseline leg only
 
-    crop = (20, 28)
-    z, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=2, latent_hw=crop)
-    p = oracle.as_numpy_params(params)
-    zz = oracle._f32(z[0])
+    return oracle
+
+
+def _timed(fn):
     t0 = time.perf_counter()
-    video = oracle.decode(zz, p, wl.FULL_DECODER, frames_per_pass=2, first_frame_rule=False)
-    dt = time.perf_counter() - t0
+    out = fn()
+    return out, time.perf_counter() - t0
+
+
+def cpu_stream_sample():
+    """The oracle on a bounded sample of the streaming decode: a 20x28 latent crop of the same
+    latents, their first 3 latent frames in one pass with the first-frame rule (9 video frames of
+    320x448), scaled to full-frame frames/s by the crop's share of the 44x78 latent frame."""
+    oracle = _oracle()
+    crop, nf = (20, 28), 3
+    _, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
+    z = wl.streaming_latents(seed=5, latent_frames=31)[0, :, :nf, :crop[0], :crop[1]]
+    p = oracle.as_numpy_params(params)
+    video, dt = _timed(lambda: oracle.decode(oracle._f32(z), p, wl.FULL_DECODER, frames_per_pass=nf,
+                                             first_frame_rule=True))
     share = (crop[0] * crop[1]) / float(wl.LATENT_H * wl.LATENT_W)
-    frames_equiv = video.shape[1] * share
-    return {"value": frames_equiv / dt, "unit": "frames/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"oracle decode of a {crop[0]}x{crop[1]} latent crop, 2 latent frames (one pass, {video.shape[1]} "
-                      f"frames of {crop[0] * 16}x{crop[1] * 16}) in {dt:.1f} s, scaled by the crop's share "
-                      f"{share:.4f} of the 44x78 latent frame"}
+    return {"value": video.shape[1] * share / dt, "unit": "frames/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"oracle decode of a {crop[0]}x{crop[1]} crop of the streaming latents, their first {nf} "
+                      f"latent frames in one pass with the first-frame rule ({video.shape[1]} frames of "
+                      f"{crop[0] * 16}x{crop[1] * 16}) in {dt:.1f} s, scaled by the crop's share {share:.4f} of "
+                      f"the 44x78 latent frame"}
+
+
+def recorded_stream_oracle():
+    """The wall time of the oracle's whole 121-frame streaming decode, from the stored samples'
+    run (tests/golden/make_stream_golden.py), with the host it ran on; None if not stored."""
+    path = os.path.join(GOLDEN, "stream_decode_samples.npz")
+    if not os.path.exists(path):
+        return None
+    g = np.load(path)
+    sec = float(g["oracle_seconds"])
+    return {"value": 121.0 / sec, "unit": "frames/s", "seconds": round(sec, 1), "cores": int(g["threads"]),
+            "cpu_model": str(g["cpu_model"]), "nproc": int(g["nproc"]),
+            "what": f"the oracle's full 121-frame decode (passes of {int(g['oracle_pass'])} latent frames, "
+                    f"bitwise the one-shot decode), timed once when the stored samples were written; "
+                    f"not on this host"}
+
+
+def timed_calls(fn, reps):
+    """Median ms of `reps` calls of fn (each bracketed by events on the current stream)."""
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def instrumented(fn, reps):
+    """Per-config conv and memory-bound kernel figures over `reps` instrumented calls of fn."""
+    wvd.timing_reset()
+    wvd.timing_enable(True)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    wvd.timing_enable(False)
+    per_cfg = wvd.timing_read()
+    per_mem = wvd.timing_read_mem()
+    launches = wvd.timing_launches()
+    conv_ms = sum(v[1] for v in per_cfg.values())
+    conv_flops = sum(v[2] for v in per_cfg.values())
+    conv_bytes = sum(conv_launch_bytes(sh) for (_, _, _, sh) in launches)
+    out = {}
+    if per_cfg:
+        tf = conv_flops / (conv_ms * 1e-3) / 1e12
+        out["conv"] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                       "gbs_algorithmic": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
+                       "ms_per_call": round(conv_ms / reps, 4),
+                       "per_config": {k: {"launches_per_call": v[0] // reps, "us_per_launch": round(1000 * v[1] / v[0], 1),
+                                          "tflops": round(v[2] / (v[1] * 1e-3) / 1e12, 1),
+                                          "frac_of_peak": round(v[2] / (v[1] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                                      for k, v in per_cfg.items()}}
+    if per_mem:
+        out["memory_bound"] = {k: {"launches_per_call": v[0] // reps, "us_per_launch": round(1000 * v[1] / v[0], 1),
+                                   "gbs": round(v[2] / (v[1] * 1e-3) / 1e9, 1),
+                                   "frac_of_hbm": round(v[2] / (v[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                               for k, v in per_mem.items()}
+    return out
+
+
+def bench_single_conv(reps, cpu):
+    """The fp32 single causal conv [1,16,5,16,16] (latency bound: no roofline claim)."""
+    cfg = wl.single_conv_fp32()
+    x = cfg["x"].cuda()
+    w = cfg["weight"].cuda()
+    b = cfg["bias"].cuda()
+    y = torch.empty_like(x)
+    call = lambda: wvd.causal_conv3d(x, w, 16, bias=b, out=y, layout="NCTHW")  # noqa: E731
+    call()
+    ms = timed_calls(call, reps)
+    r = {"workload": "single causal conv, fp32: x [1,16,5,16,16], weight [16,16,3,3,3], bias, 2 causal zero frames",
+         "ms_per_call": round(ms, 4), "gflop": 2 * 1280 * 16 * 432 / 1e9}
+    if cpu:
+        oracle = _oracle()
+        _, dt = _timed(lambda: oracle.causal_conv3d(cfg["x"][0], cfg["weight"], cfg["bias"]))
+        r["cpu_oracle_seconds"] = round(dt, 4)
+    return r
+
+
+def bench_resblock(reps, cpu):
+    """The residual block [1,384,4,44,78] with its given 2-frame history (bf16, fp32 accumulation)."""
+    cfg = wl.resblock_bf16()
+    wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+    x = cfg["x"].permute(0, 2, 3, 4, 1).contiguous().to(torch.bfloat16).cuda()
+    hd = cfg["hist"].permute(0, 2, 3, 4, 1).contiguous().to(torch.bfloat16).cuda()
+    y = torch.empty_like(x)
+    call = lambda: wvd.resblock(x, wts, 1e-6, hist1=hd, hist2=hd, out=y)  # noqa: E731
+    call()
+    ms = timed_calls(call, reps)
+    flops = 2 * (2.0 * 4 * 44 * 78 * 384 * 27 * 384)
+    r = {"workload": "residual block, bf16 / fp32 acc: x [1,384,4,44,78] + 2-frame history, norm1 + SiLU, conv "
+                     "384->384, norm2 + SiLU, conv 384->384, + x",
+         "ms_per_call": round(ms, 4), "tflops_whole_block": round(flops / (ms * 1e-3) / 1e12, 1),
+         "algorithmic_tflop": round(flops / 1e12, 4)}
+    r.update(instrumented(call, reps))
+    if cpu:
+        oracle = _oracle()
+        p = oracle.as_numpy_params(cfg["params"])
+        _, dt = _timed(lambda: oracle.resblock(cfg["x"][0], p, "res", {}, 1e-6, given_hist=oracle._f32(cfg["hist"][0])))
+        r["cpu_oracle_seconds"] = round(dt, 2)
+    return r
+
+
+def bench_upsample(reps, cpu):
+    """The upsample stage [1,192,4,176,312] -> [1,192,8,352,624], spatial x2 first, then the time conv."""
+    cfg = wl.upsample_stage_bf16()
+    x = cfg["x"].permute(0, 2, 3, 4, 1).contiguous().to(torch.bfloat16).cuda()
+    ws = wvd.conv_pack(cfg["spatial.weight"].cuda(), wvd.WVD_PACK_PHASE2X)
+    wt = wvd.conv_pack(cfg["time.weight"].cuda())
+    bs, bt = cfg["spatial.bias"].cuda(), cfg["time.bias"].cuda()
+    y = torch.empty((1, 8, 352, 624, 192), dtype=torch.bfloat16, device="cuda")
+    call = lambda: wvd.upsample(x, spatial=ws, spatial_bias=bs, temporal=wt, temporal_bias=bt,  # noqa: E731
+                                order=wvd.WVD_SPATIAL_FIRST, out=y)
+    call()
+    ms = timed_calls(call, reps)
+    flops = 2.0 * (4 * 4 * 176 * 312) * 192 * (4 * 192) + 2.0 * 4 * 352 * 624 * 384 * 3 * 192
+    r = {"workload": "upsample stage, bf16: x [1,192,4,176,312] -> nearest x2 + 3x3 conv 192->192 (four 2x2 phase "
+                     "convs) -> causal (3,1,1) conv 192->384 into 8 frames -> [1,192,8,352,624]",
+         "ms_per_call": round(ms, 4), "tflops_whole_stage": round(flops / (ms * 1e-3) / 1e12, 1),
+         "algorithmic_tflop": round(flops / 1e12, 4),
+         "gbs_output": round(y.numel() * 2 / (ms * 1e-3) / 1e9, 1)}
+    r.update(instrumented(call, reps))
+    if cpu:
+        oracle = _oracle()
+        p = {k: oracle._f32(v) for k, v in cfg.items() if k != "x"}
+        _, dt = _timed(lambda: oracle.upsample_stage(cfg["x"][0], p))
+        r["cpu_oracle_seconds"] = round(dt, 2)
+    return r
+
+
+def bench_one_pass(dec, reps, cpu):
+    """The one-pass decode [1,48,4,44,78] -> [1,3,16,704,1248] (the decoder's weights, seed 4, a
+    non-first pass with empty caches), with PSNR against the oracle's stored samples."""
+    z, _ = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
+    zd = z.to(torch.bfloat16).cuda()
+    video = torch.empty((1, 3, 16, 704, 1248), dtype=torch.bfloat16, device="cuda")
+    call = lambda: dec.decode(zd, frames_per_pass=4, first_frame_rule=False, out=video)  # noqa: E731
+    call()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    call()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() / 2 ** 30
+    ms = timed_calls(call, reps)
+    r = {"workload": "one-pass decode: latents [1,48,4,44,78] -> video [1,3,16,704,1248], empty caches, "
+                     "first-frame rule off",
+         "ms_per_call": round(ms, 3), "frames_per_s": round(16 / (ms * 1e-3), 1), "peak_hbm_gib": round(peak, 3),
+         "algorithmic_tflop": round(algorithmic_conv_flops(wl.FULL_DECODER, 4, 4) / 1e12, 3)}
+    gp = os.path.join(GOLDEN, "decoder_onepass_samples.npz")
+    if os.path.exists(gp):
+        g = np.load(gp)
+        got = video[0].float().cpu().reshape(-1).numpy()[g["index"]].astype(np.float64)
+        mse = float(((got - g["value"]) ** 2).mean())
+        rng = float(g["vmax"] - g["vmin"])
+        r["psnr_db_vs_oracle_samples"] = round(10 * math.log10(rng * rng / mse), 2) if mse > 0 else None
+    r.update(instrumented(call, reps))
+    del video
+    if cpu:
+        oracle = _oracle()
+        crop = (20, 28)
+        zc, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=2, latent_hw=crop)
+        p = oracle.as_numpy_params(params)
+        v, dt = _timed(lambda: oracle.decode(oracle._f32(zc[0]), p, wl.FULL_DECODER, frames_per_pass=2,
+                                             first_frame_rule=False))
+        share = (crop[0] * crop[1]) / float(wl.LATENT_H * wl.LATENT_W)
+        r["cpu_oracle"] = {"frames_per_s": v.shape[1] * share / dt, "seconds": round(dt, 2),
+                           "sample": f"a {crop[0]}x{crop[1]} latent crop, 2 latent frames in one pass "
+                                     f"({v.shape[1]} frames), scaled by the crop's share {share:.4f}"}
+        if os.path.exists(gp):
+            sec = float(np.load(gp)["oracle_seconds"])
+            r["cpu_oracle"]["recorded_full_seconds"] = round(sec, 1)
+            r["cpu_oracle"]["recorded_full_threads"] = int(np.load(gp)["threads"])
+    return r
 
 
 def conv_launch_bytes(sh) -> float:
@@ -156,6 +370,8 @@ def main():
                          "TI2V-5B topology (1024/1024/512/256, mid attention, DupUp3D, 12-channel head, "
                          "unpatchify, clamp) with random weights, no CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' measurements")
+    ap.add_argument("--config-reps", type=int, default=10, help="timed calls per other workload (median)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy kernel over MIB MiB (calibrates the HBM byte counters) and exit")
     args = ap.parse_args()
@@ -184,30 +400,41 @@ def main():
     assert video.shape[3:] == (wl.VIDEO_H, wl.VIDEO_W)
     dec.workspace(fpp, early)
     torch.cuda.synchronize()
+    step = lambda: dec.decode(z, frames_per_pass=fpp, out=video, early_frames_per_pass=early)  # noqa: E731
 
     for _ in range(args.warmup):
-        dec.decode(z, frames_per_pass=fpp, out=video, early_frames_per_pass=early)
+        step()
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
 
-    wvd.timing_reset()
-    wvd.timing_enable(True)
+    # the headline: no instrumentation inside the timed region
+    wvd.timing_enable(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        dec.decode(z, frames_per_pass=fpp, out=video, early_frames_per_pass=early)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    peak_alloc = torch.cuda.max_memory_allocated() / 2 ** 30
+    peak_reserved = torch.cuda.max_memory_reserved() / 2 ** 30
+    elapsed = t1 - t0
+    ms_per_step = 1000.0 * elapsed / args.steps
+    fps = F * args.steps / elapsed
+    print(f"headline: {ms_per_step:.2f} ms per decode, {fps:.1f} frames/s", file=sys.stderr, flush=True)
+
+    # the breakdown: the same steps again with HIP events around every launch
+    wvd.timing_reset()
+    wvd.timing_enable(True)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
     wvd.timing_enable(False)
     per_cfg = wvd.timing_read()
     per_mem = wvd.timing_read_mem()
     launches = wvd.timing_launches()
-    peak_alloc = torch.cuda.max_memory_allocated() / 2 ** 30
-    peak_reserved = torch.cuda.max_memory_reserved() / 2 ** 30
-
-    elapsed = t1 - t0
-    ms_per_step = 1000.0 * elapsed / args.steps
-    fps = F * args.steps / elapsed
     conv_ms = sum(v[1] for v in per_cfg.values())
     conv_flops = sum(v[2] for v in per_cfg.values())
     # the dominant kernel: the conv configuration with the most time
@@ -224,6 +451,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step_instrumented": round(1000.0 * (t3 - t2) / args.steps, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -263,12 +491,31 @@ def main():
                           "frac_of_hbm": round(v[2] / (v[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                           "ms_per_step": round(v[1] / args.steps, 3)}
                       for k, v in per_mem.items()},
-        "achievable": achievable_peaks(),
         "peak_hbm_gib": round(peak_alloc, 3),
         "peak_hbm_reserved_gib": round(peak_reserved, 3),
     }
-    if not args.no_cpu_baseline and not real:
-        line["cpu_baseline"] = cpu_baseline()
+    cpu = not args.no_cpu_baseline and not real
+    if not args.no_configs and not real:
+        del video
+        dec._ws = None
+        torch.cuda.empty_cache()
+        configs = {}
+        for key, fn in (("single_conv_fp32", lambda: bench_single_conv(args.config_reps, cpu)),
+                        ("resblock", lambda: bench_resblock(args.config_reps, cpu)),
+                        ("upsample_stage", lambda: bench_upsample(args.config_reps, cpu)),
+                        ("one_pass_decode", lambda: bench_one_pass(dec, args.config_reps, cpu))):
+            configs[key] = fn()
+            torch.cuda.empty_cache()
+            print(f"{key}: {configs[key]['ms_per_call']} ms", file=sys.stderr, flush=True)
+        line["configs"] = configs
+    line["achievable"] = achievable_peaks()
+    if cpu:
+        cb = cpu_stream_sample()
+        cb["host"] = host_info()
+        rec = recorded_stream_oracle()
+        if rec is not None:
+            cb["recorded_full_decode"] = rec
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 

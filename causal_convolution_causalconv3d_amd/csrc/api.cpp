@@ -82,6 +82,16 @@ wvd_status check_tensor(const wvd_tensor* t, const char* name, int dtype, int la
 
 bool same_grid(const wvd_tensor* a, const wvd_tensor* b) { return a->h == b->h && a->w == b->w; }
 
+// Whether the byte ranges of two tensors overlap (empty tensors overlap nothing).
+bool overlaps(const wvd_tensor* a, const wvd_tensor* b) {
+  if (!a || !b || numel(a) == 0 || numel(b) == 0) return false;
+  const char* a0 = (const char*)a->data;
+  const char* b0 = (const char*)b->data;
+  const char* a1 = a0 + numel(a) * elem_size(a->dtype);
+  const char* b1 = b0 + numel(b) * elem_size(b->dtype);
+  return a0 < b1 && b0 < a1;
+}
+
 // ------------------------------------------------------------------------------------------
 // Timing of the matrix-core conv launches.
 // ------------------------------------------------------------------------------------------
@@ -406,6 +416,12 @@ extern "C" wvd_status wvd_causal_conv3d(const wvd_tensor* x, const void* w, int 
     if (hist && hist_out->data == hist->data && want > 0) return fail(WVD_ERR_ARG, "hist_out may not alias hist");
     if (x->layout != WVD_NTHWC) return fail(WVD_ERR_LAYOUT, "hist_out needs NTHWC tensors");
   }
+  // Workgroups read the frames and halo rows of x and hist that other workgroups write in y:
+  // an in-place call would race, so y may share no byte with them (nor hist_out with any of them).
+  if (overlaps(y, x)) return fail(WVD_ERR_ARG, "y may not overlap x");
+  if (overlaps(y, hist)) return fail(WVD_ERR_ARG, "y may not overlap hist");
+  if (hist_out && (overlaps(hist_out, x) || overlaps(hist_out, hist) || overlaps(hist_out, y)))
+    return fail(WVD_ERR_ARG, "hist_out may not overlap x, hist or y");
   if (!aligned16(w)) return fail(WVD_ERR_ALIGN, "weights not 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   const int T = (int)x->t, H = (int)x->h, W = (int)x->w, Ci = (int)x->c;

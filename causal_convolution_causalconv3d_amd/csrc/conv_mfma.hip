@@ -582,6 +582,17 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void conv_halo_kernel(const 
 // expcnt 6:4, lgkmcnt 11:8; expcnt 7 and lgkmcnt 15 do not wait).
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
+// Workgroup barrier for the DMA kernels' LDS traffic. The builtin alone is an intrinsic that
+// touches no memory as far as the compiler is concerned, so LDS loads and stores could be moved
+// across it; the empty asm statements with a memory clobber on both sides pin every memory
+// access to its side of the barrier. They emit no instruction and, unlike a workgroup fence,
+// add no s_waitcnt (the fetches still in flight are covered by the hand-counted vmcnt waits).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Waves per SIMD a DMA kernel is compiled for: two, or four for the one-row phase tiles (their
 // light main loop leaves the SIMDs to the epilogue's vector work, which other waves then overlap).
 template <int MB, int KS>
@@ -827,7 +838,7 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
   if constexpr (D >= 4) fetch_w(I3{}, cur.col + 3 * p.Cip, rs_cur);
   if constexpr (D == 5) fetch_w(I4{}, cur.col + 4 * p.Cip, rs_cur);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   read_a(wf[0], I0{}, 0);
   read_b(bf[0], I0{}, 0, 0);
   zero_acc();
@@ -876,7 +887,7 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
     constexpr int N = WW * WIW + (S < WW ? PIW : 0);
     static_assert(N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
   };
   auto stage = [&](auto PP) __attribute__((always_inline)) {
     step(PP, I0{});
@@ -912,7 +923,7 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) ph[mb] = tc.h0 + wave * MB + mb;
     if (p.staged) {
-      __builtin_amdgcn_s_barrier();
+      lds_barrier();
       constexpr auto fits1 = [](int nbp) constexpr {
         const int sb = 32 * (nbp * 64 + 16);
         return 2 * (PBYTES / sb) + 2 * (WBYTES / sb) >= WAVES;
@@ -976,7 +987,7 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
     nxt = next_stage(cur);
     zero_acc();
     // every wave is done with the staging areas before the next tile's fetches reuse them
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     read_a(wf[0], std::integral_constant<int, ((L ^ 1) * SPS) % NWS>{}, 0);
     read_b(bf[0], std::integral_constant<int, L ^ 1>{}, 0, 0);
     return false;

@@ -109,7 +109,10 @@ wvd_status wvd_conv_pack(const void* w_raw, int w_dtype, int co, int ci, int kt,
  * hist: nullable, hist.t <= P, same c, h, w as x.
  * hist_out: nullable; when set, receives the history this conv leaves for the next chunk (the
  *   page's cached_conv rule: the last min(T, 2) input frames, or the old last history frame
- *   followed by x when x has one frame). It may not alias hist; its t must be that frame count.
+ *   followed by x when x has one frame). Its t must be that frame count.
+ * Aliasing: y may share no byte with x or hist, and hist_out none with x, hist or y (the
+ *   workgroups read neighbouring rows and frames that others write); an overlap returns
+ *   WVD_ERR_ARG before anything is launched.
  * x may have zero frames (so may the inputs of wvd_rmsnorm_silu, wvd_resblock and wvd_upsample;
  *   wvd_decode_chunk rejects an empty chunk): nothing is computed, y is empty, and the history
  *   passes through unchanged into hist_out.

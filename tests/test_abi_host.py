@@ -72,7 +72,7 @@ def _fake_tensor(c, t, h, w, dtype=wvd.WVD_BF16, layout=wvd.WVD_NTHWC, ptr=0x100
 def test_validation_errors_before_any_launch():
     L = wvd.lib()
     x = _fake_tensor(16, 4, 8, 8)
-    y = _fake_tensor(16, 4, 8, 8)
+    y = _fake_tensor(16, 4, 8, 8, ptr=0x100000)
     # odd kernel sizes only
     st = L.wvd_causal_conv3d(ctypes.byref(x), ctypes.c_void_p(0x2000), 16, 2, 3, 3, None, None, None, ctypes.byref(y),
                              None, None)
@@ -94,9 +94,32 @@ def test_validation_errors_before_any_launch():
     assert st == 2
     # bf16 path needs NTHWC
     xn = _fake_tensor(16, 4, 8, 8, layout=wvd.WVD_NCTHW)
-    yn = _fake_tensor(16, 4, 8, 8, layout=wvd.WVD_NCTHW)
+    yn = _fake_tensor(16, 4, 8, 8, layout=wvd.WVD_NCTHW, ptr=0x100000)
     st = L.wvd_causal_conv3d(ctypes.byref(xn), ctypes.c_void_p(0x2000), 16, 3, 3, 3, None, None, None,
                              ctypes.byref(yn), None, None)
+    assert st == 4
+    # in-place and partly overlapping outputs are refused (a range check, not only equal bases):
+    # x spans 16 * 4 * 8 * 8 * 2 = 8192 bytes from 0x1000
+    for y_ptr in (0x1000, 0x1000 + 4096, 0x1000 - 2048):
+        y_ov = _fake_tensor(16, 4, 8, 8, ptr=y_ptr)
+        st = L.wvd_causal_conv3d(ctypes.byref(x), ctypes.c_void_p(0x2000), 16, 3, 3, 3, None, None, None,
+                                 ctypes.byref(y_ov), None, None)
+        assert st == 1 and b"overlap" in L.wvd_last_error(), hex(y_ptr)
+    # y overlapping the history, and hist_out overlapping x, are refused too
+    h2 = _fake_tensor(16, 2, 8, 8, ptr=0x200000)
+    y_h = _fake_tensor(16, 4, 8, 8, ptr=0x200000 + 2048)
+    st = L.wvd_causal_conv3d(ctypes.byref(x), ctypes.c_void_p(0x2000), 16, 3, 3, 3, None, ctypes.byref(h2), None,
+                             ctypes.byref(y_h), None, None)
+    assert st == 1 and b"overlap" in L.wvd_last_error()
+    ho = _fake_tensor(16, 2, 8, 8, ptr=0x1000 + 4096)
+    st = L.wvd_causal_conv3d(ctypes.byref(x), ctypes.c_void_p(0x2000), 16, 3, 3, 3, None, None, None,
+                             ctypes.byref(y), ctypes.byref(ho), None)
+    assert st == 1 and b"overlap" in L.wvd_last_error()
+    # adjacent but disjoint ranges pass validation (checked with an fp32 tensor pair whose
+    # launch would need a GPU, so only the layout error of a bf16 NCTHW pair is provoked)
+    y_adj = _fake_tensor(16, 4, 8, 8, layout=wvd.WVD_NCTHW, ptr=0x1000 + 8192)
+    st = L.wvd_causal_conv3d(ctypes.byref(xn), ctypes.c_void_p(0x2000), 16, 3, 3, 3, None, None, None,
+                             ctypes.byref(y_adj), None, None)
     assert st == 4
     # norm: channels beyond the supported width
     xb = _fake_tensor(4096, 1, 2, 2)
