@@ -84,6 +84,9 @@ def lib():
             "wvd_resblock_workspace_bytes": ([ctypes.c_int] * 5, ctypes.c_size_t),
             "wvd_resblock": ([_T, ctypes.POINTER(ResblockWeights), ctypes.c_float, _T, _T, _T, _T, _T, _P, ctypes.c_size_t,
                               _P], ctypes.c_int),
+            "wvd_resblock_noalloc_max_bytes": ([], ctypes.c_size_t),
+            "wvd_resblock_noalloc": ([_T, ctypes.POINTER(ResblockWeights), ctypes.c_float, _T, _T, _T, _T, _T, _P],
+                                     ctypes.c_int),
             "wvd_upsample_workspace_bytes": ([ctypes.c_int] * 7, ctypes.c_size_t),
             "wvd_upsample": ([_T, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int, _T, _T, _T, _P, ctypes.c_size_t, _P],
                              ctypes.c_int),
@@ -130,6 +133,7 @@ def exported_symbols() -> Sequence[str]:
     lib()
     return ["wvd_last_error", "wvd_abi_version", "wvd_convert", "wvd_conv_packed_bytes", "wvd_conv_pack",
             "wvd_causal_conv3d", "wvd_rmsnorm_silu", "wvd_resblock_workspace_bytes", "wvd_resblock",
+            "wvd_resblock_noalloc_max_bytes", "wvd_resblock_noalloc",
             "wvd_upsample_workspace_bytes", "wvd_upsample", "wvd_decoder_param_count", "wvd_decoder_param_info",
             "wvd_decoder_packed_bytes", "wvd_decoder_pack", "wvd_cache_bytes", "wvd_cache_init", "wvd_cache_reset",
             "wvd_cache_destroy", "wvd_cache_next_latent", "wvd_decode_workspace_bytes", "wvd_decode_chunk",
@@ -256,6 +260,17 @@ def resblock(x, wts: dict, eps, hist1=None, hist2=None, out=None, hist1_out=None
     _check(lib().wvd_resblock(_desc(x, "NTHWC"), ctypes.byref(rw), eps, _desc(hist1, "NTHWC"), _desc(hist2, "NTHWC"),
                               _desc(out, "NTHWC"), _desc(hist1_out, "NTHWC"), _desc(hist2_out, "NTHWC"), _ptr(ws), nbytes,
                               _stream()))
+    return out
+
+
+def resblock_noalloc(x, wts: dict, eps, out, hist1=None, hist2=None, hist1_out=None, hist2_out=None):
+    """wvd_resblock_noalloc: wvd_resblock with the library's built-in scratch as its workspace
+    (no device allocation inside the call; `out` must be given)."""
+    rw = ResblockWeights(wts["cin"], wts["cout"], *[wts[k].data_ptr() if wts[k] is not None else None for k in (
+        "gamma1", "conv1", "bias1", "gamma2", "conv2", "bias2", "shortcut", "shortcut_bias")])
+    _check(lib().wvd_resblock_noalloc(_desc(x, "NTHWC"), ctypes.byref(rw), eps, _desc(hist1, "NTHWC"),
+                                      _desc(hist2, "NTHWC"), _desc(out, "NTHWC"), _desc(hist1_out, "NTHWC"),
+                                      _desc(hist2_out, "NTHWC"), _stream()))
     return out
 
 

@@ -626,6 +626,57 @@ extern "C" wvd_status wvd_resblock(const wvd_tensor* x, const wvd_resblock_weigh
 }
 
 // ==============================================================================================
+// Residual block without a caller workspace
+// ==============================================================================================
+namespace {
+
+// The residual block's workspace (activated input, conv1 output, shortcut output) for callers
+// that cannot allocate: a file-scope device array, one copy per GPU, held until the process ends.
+// In host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+wvd_status scratch_for_current_device(char** out) {
+  int dev = -1;
+  WVD_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(WVD_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    WVD_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned16(ptr)) return fail(WVD_ERR_HIP, "scratch symbol has no usable device address");
+    g_scratch_ptr[dev] = (char*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return WVD_OK;
+}
+
+}  // namespace
+
+extern "C" size_t wvd_resblock_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" wvd_status wvd_resblock_noalloc(const wvd_tensor* x, const wvd_resblock_weights* wts, float eps,
+                                           const wvd_tensor* hist1, const wvd_tensor* hist2, wvd_tensor* y,
+                                           wvd_tensor* hist1_out, wvd_tensor* hist2_out, wvd_stream stream) {
+  WVD_TRY(check_resblock_weights(wts));
+  WVD_TRY(check_tensor(x, "x", WVD_BF16, WVD_NTHWC, true));
+  const size_t need = resblock_ws(wts->cin, wts->cout, x->t * x->h * x->w);
+  if (need > kNoAllocScratchBytes)
+    return fail(WVD_ERR_WORKSPACE,
+                "resblock_noalloc: this input needs %zu bytes of workspace, the built-in scratch holds %zu "
+                "(use wvd_resblock with a caller workspace)",
+                need, kNoAllocScratchBytes);
+  char* ws = nullptr;
+  WVD_TRY(scratch_for_current_device(&ws));
+  return wvd_resblock(x, wts, eps, hist1, hist2, y, hist1_out, hist2_out, ws, kNoAllocScratchBytes, stream);
+}
+
+// ==============================================================================================
 // Upsampling
 // ==============================================================================================
 extern "C" size_t wvd_upsample_workspace_bytes(int c, int t, int h, int w, int spatial, int temporal, int order) {

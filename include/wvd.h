@@ -154,6 +154,23 @@ wvd_status wvd_resblock(const wvd_tensor* x, const wvd_resblock_weights* wts, fl
                         const wvd_tensor* hist2, wvd_tensor* y, wvd_tensor* hist1_out, wvd_tensor* hist2_out,
                         void* ws, size_t ws_bytes, wvd_stream stream);
 
+/* wvd_resblock_noalloc - wvd_resblock without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Same arguments, layouts, validation and results as wvd_resblock (it runs
+ * the same kernels); the workspace is a scratch array built into the library, one per GPU,
+ * wvd_resblock_noalloc_max_bytes() (32 MiB) long, kept until the process ends.
+ * It calls no hipMalloc / hipFree and no allocating library routine (leave the per-launch
+ * timing of wvd_timing_enable off: it creates HIP events).
+ * Limit: inputs whose workspace, wvd_resblock_workspace_bytes(cin, cout, t, h, w), exceeds that
+ * size return WVD_ERR_WORKSPACE before anything is launched (the [1,384,4,44,78] block needs
+ * 21.1 MB). Nothing in the scratch needs to start at zero: every byte a call reads it wrote
+ * first in the same call. All calls on one GPU share its scratch: calls that may overlap in
+ * time on that GPU (other streams, other threads) race; order them on one stream. */
+size_t wvd_resblock_noalloc_max_bytes(void);
+wvd_status wvd_resblock_noalloc(const wvd_tensor* x, const wvd_resblock_weights* wts, float eps,
+                                const wvd_tensor* hist1, const wvd_tensor* hist2, wvd_tensor* y,
+                                wvd_tensor* hist1_out, wvd_tensor* hist2_out, wvd_stream stream);
+
 /* ============================================================================================
  * wvd_upsample - 2x upsampling steps (the page's upsample3d / upsample2d parts).
  *  spatial: per frame, nearest x2 in h and w then a 3x3 conv2d C -> C (zero pad 1) + bias;

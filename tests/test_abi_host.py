@@ -187,3 +187,20 @@ def test_real_topology_descriptor_validation():
     assert bad(base_channels=1000) == -1                             # attention needs a multiple of 32
     d = wvd.desc_from_spec(wl.REAL_DECODER, 44, 77)                  # h*w not a multiple of 8
     assert L.wvd_decoder_param_count(ctypes.byref(d)) == -1
+
+
+def test_resblock_noalloc_refuses_inputs_beyond_its_scratch():
+    """The allocation-free residual block names its limit and refuses a larger input before any
+    launch (host-only: the refusal comes before the device is touched)."""
+    L = wvd.lib()
+    cap = L.wvd_resblock_noalloc_max_bytes()
+    assert cap == 32 << 20
+    # [1, 384, 4, 44, 78]: 2 * 13728 * 384 * 2 bytes of workspace fits
+    assert L.wvd_resblock_workspace_bytes(384, 384, 4, 44, 78) <= cap
+    # [1, 384, 8, 44, 78] does not
+    assert L.wvd_resblock_workspace_bytes(384, 384, 8, 44, 78) > cap
+    x = _fake_tensor(384, 8, 44, 78)
+    y = _fake_tensor(384, 8, 44, 78, ptr=0x40000000)
+    rw = wvd.ResblockWeights(384, 384, 0x10000, 0x20000, None, 0x30000, 0x40000, None, None, None)
+    st = L.wvd_resblock_noalloc(ctypes.byref(x), ctypes.byref(rw), 1e-6, None, None, ctypes.byref(y), None, None, None)
+    assert st == 7 and b"scratch" in L.wvd_last_error()
