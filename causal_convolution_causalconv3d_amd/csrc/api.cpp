@@ -1053,7 +1053,19 @@ struct WsLayout {
   size_t zc, x0, x1, a, h, sc, xm;  // byte offsets
   size_t zq, keep, qkv, sc32, prob, vt, ao, head;  // the real topology's parts (0 bytes otherwise)
   size_t total;
+  int64_t tail_frames;  // frames per sub-pass of the fused last upsample + head (see run_tail)
 };
+
+// Whether the last stage is a spatial upsample without a time step or DupUp3D whose epilogue
+// applies norm_out + SiLU (one workgroup holds every channel; the packed parameters are
+// 256-byte aligned): its output is then only the head's input. The decode runs that upsample
+// and the head together in frame sub-passes, so the largest tensor of the decode, the last
+// level's activation, never exists for a whole pass at once.
+bool fused_tail(const wvd_decoder_desc* d) {
+  const int L = d->n_stages;
+  return !d->stage_no_spatial[L - 1] && !d->stage_dup[L - 1] && !d->stage_temporal[L - 1] &&
+         conv_can_fuse_norm_width(d->stage_channels[L - 1]);
+}
 
 // The first stage after the last temporal upsample: from there on a pass's frames can be
 // processed in sub-passes (no stage changes the frame count). 0 when no stage is temporal.
@@ -1073,6 +1085,7 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n, int64_t nh) {
   const ChunkFrames fl = chunk_frames(d, n, false);  // the largest frame counts
   const ChunkFrames fh = split < L ? chunk_frames(d, nh, false) : fl;
   int64_t stream = 0, act = 0, hbuf = 0, scbuf = 0, xm = 0, keep = 0;
+  const bool tail = fused_tail(d);
   const int64_t hw0 = (int64_t)d->latent_h * d->latent_w;
   auto hw = [&](int level) { return hw0 << (2 * level); };
   int c = d->base_channels;
@@ -1091,18 +1104,33 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n, int64_t nh) {
     hbuf = std::max(hbuf, P * cs);
     if (c != cs) scbuf = std::max(scbuf, P * cs);
     c = cs;
-    // time conv output, then the spatial upsample output at the next level
+    // time conv output, then the spatial upsample output at the next level (for a fused tail:
+    // the activated buffer, one sub-pass of frames at a time, sized below)
     act = std::max(act, f.stage_out[s] * hw(level) * c);
     stream = std::max(stream, f.stage_out[s] * hw(level) * c);
-    stream = std::max(stream, f.stage_out[s] * hw(level + sp) * c);
-    act = std::max(act, f.stage_out[s] * hw(level + sp) * c);
+    if (!(tail && s == L - 1)) {
+      stream = std::max(stream, f.stage_out[s] * hw(level + sp) * c);
+      act = std::max(act, f.stage_out[s] * hw(level + sp) * c);
+    }
     if (s + 1 == split && split < L) xm = fl.stage_out[s] * hw(level + sp) * c;
     level += sp;
   }
-  act = std::max(act, fh.video * hw(level) * c);
-  // the head's fp32 tap planes Z (9 planes x 4 floats = 72 bf16 per position) live in a stream buffer
+  // the head's input: norm_out's output for the whole pass, or a fused tail's sub-pass, as many
+  // frames as fit in what the activated buffer holds anyway (at least one)
+  int64_t tail_frames = fh.video;
+  if (tail) {
+    const int64_t per_frame = hw(level) * c;
+    tail_frames = std::min<int64_t>(fh.video, std::max<int64_t>(1, act / per_frame));
+    act = std::max(act, tail_frames * per_frame);
+  } else {
+    act = std::max(act, fh.video * hw(level) * c);
+  }
+  // the head's fp32 tap planes Z (9 planes x 4 floats = 72 bf16 per position) live in a stream
+  // buffer when neither fused head kernel takes the channel count
   const bool head_plain = d->patch >= 2 || d->clamp;
-  if (!head_plain) stream = std::max(stream, fh.video * hw(level) * kHeadPlanes * 8);
+  const int cip_out = (int)round_up(c, 32);
+  if (!head_plain && !head_stream_supported(cip_out, d->out_channels) && !head_fused_supported(cip_out))
+    stream = std::max(stream, tail_frames * hw(level) * kHeadPlanes * 8);
   WsLayout w;
   size_t off = 0;
   auto take = [&](int64_t elems) {
@@ -1128,6 +1156,7 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n, int64_t nh) {
   w.ao = take(at ? n * hw0 * c0 : 0);
   w.head = take(head_plain ? fh.video * hw(level) * d->out_channels : 0);
   w.total = off;
+  w.tail_frames = tail_frames;
   return w;
 }
 
@@ -1445,6 +1474,11 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
   // workgroup holds every channel (the L4 tensor is then written once, already activated).
   const bf16_t* act = nullptr;  // conv_out's input once norm_out has been applied
   bf16_t* zbuf = nullptr;       // a free buffer for the head's tap planes
+  // A fused tail (fused_tail): the last upsample's input, its size and stage, recorded by
+  // run_stage and consumed by run_tail.
+  const bool tail = fused_tail(d);
+  const bf16_t* tail_x = nullptr;
+  int tail_h = 0, tail_w = 0, tail_stage = -1;
   // one stage: its residual blocks (the first reading x), its time conv and spatial upsample
   // (into `up`, or the stream buffers)
   auto run_stage = [&](int si, const bf16_t* x, bf16_t* up) -> wvd_status {
@@ -1461,6 +1495,7 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
     }
     if (!st.spatial) return WVD_OK;  // (no time step or DupUp3D either)
     const bool fuse_out = si == L - 1 && !st.dup && conv_can_fuse_norm(c, F_(st.sb), F_(p.norm_out));
+    if (tail && si == L - 1 && !fuse_out) return fail(WVD_ERR_ALIGN, "norm_out or the last upsample's bias unaligned");
     const float* ng = fuse_out ? F_(p.norm_out) : nullptr;
     bf16_t* yout = nullptr;  // the upsampling's output
     if (st.temporal) {
@@ -1488,6 +1523,12 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
         act = out;
         zbuf = bx[cur ^ 1];
       }
+    } else if (fuse_out && tail) {
+      // the fused tail: this upsample runs with the head, in frame sub-passes (run_tail)
+      tail_x = x;
+      tail_h = H;
+      tail_w = Wd;
+      tail_stage = si;
     } else if (fuse_out) {
       WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), ba, s, ng, d->eps));
       act = ba;
@@ -1580,9 +1621,30 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       return launch_head_stencil(Z, co, F_(p.out_b), (bf16_t*)video->data, video->t, (int)fo, (int)T, H, Wd, s);
     });
   };
+  // The fused tail: the last upsample (norm_out + SiLU in its epilogue) and the head in sub-passes
+  // of wl.tail_frames frames, each written into the activated buffer and consumed by the head
+  // (whose cache slot carries the two frames before each sub-pass); otherwise just the head.
+  auto run_tail = [&](int64_t fo) -> wvd_status {
+    if (!tail_x) return run_head(fo);
+    const StagePlan& st = p.stages[tail_stage];
+    const int64_t Tall = T;
+    const size_t in_frame = (size_t)tail_h * tail_w * c;
+    for (int64_t f0 = 0; f0 < Tall; f0 += wl.tail_frames) {
+      const int64_t m = std::min<int64_t>(wl.tail_frames, Tall - f0);
+      WVD_TRY(run_phase_conv(tail_x + (size_t)f0 * in_frame, (int)m, tail_h, tail_w, c, W_(st.sw), F_(st.sb), ba, s,
+                             F_(p.norm_out), d->eps));
+      act = ba;
+      zbuf = bx[cur ^ 1];
+      T = m;
+      WVD_TRY(run_head(fo + f0));
+    }
+    T = Tall;
+    tail_x = nullptr;
+    return WVD_OK;
+  };
   if (split == L) {
     for (int si = 0; si < L; ++si) WVD_TRY(run_stage(si, bx[cur], nullptr));
-    WVD_TRY(run_head(frame_offset));
+    WVD_TRY(run_tail(frame_offset));
   } else {
     // the early stages for all n latent frames, the last of them upsampling into xm
     for (int si = 0; si < split; ++si) WVD_TRY(run_stage(si, bx[cur], si + 1 == split ? bxm : nullptr));
@@ -1602,7 +1664,7 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
         WVD_TRY(run_stage(si, x, nullptr));
         x = bx[cur];
       }
-      WVD_TRY(run_head(fo));
+      WVD_TRY(run_tail(fo));
       t0 += T;
       fo += fs.video;
     }

@@ -121,6 +121,8 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
 // Whether a conv with N output channels can apply RMS norm (+ SiLU) with gamma in its epilogue:
 // one channel tile, N % 8 == 0, bias (may be null) and gamma 16-byte aligned.
 bool conv_can_fuse_norm(int N, const float* bias, const float* gamma);
+// The width condition alone (bias and gamma 16-byte aligned assumed).
+bool conv_can_fuse_norm_width(int N);
 const char* conv_config_name(int config_id);
 int conv_config_count();
 

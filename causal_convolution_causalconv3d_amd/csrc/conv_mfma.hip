@@ -1160,9 +1160,11 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
 
 }  // namespace
 
+bool conv_can_fuse_norm_width(int N) { return round_up_int(N, 32) <= kMaxFusedNormN && N % 8 == 0; }
+
 bool conv_can_fuse_norm(int N, const float* bias, const float* gamma) {
   const auto a16 = [](const void* q) { return ((uintptr_t)q & 15u) == 0; };
-  return round_up_int(N, 32) <= kMaxFusedNormN && N % 8 == 0 && a16(bias) && a16(gamma) && gamma;
+  return conv_can_fuse_norm_width(N) && a16(bias) && a16(gamma) && gamma;
 }
 
 const char* conv_config_name(int id) { return (id >= 0 && id < kNumConfigs) ? kConfigs[id].name : "?"; }
