@@ -372,6 +372,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' measurements")
     ap.add_argument("--config-reps", type=int, default=10, help="timed calls per other workload (median)")
+    ap.add_argument("--workload", default="stream",
+                    choices=("stream", "single_conv_fp32", "resblock", "upsample_stage", "one_pass_decode"),
+                    help="stream: the headline decode (default); otherwise only that workload's measurement "
+                         "(--config-reps calls after a warm-up one), printed as one JSON line (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy kernel over MIB MiB (calibrates the HBM byte counters) and exit")
     args = ap.parse_args()
@@ -385,6 +389,21 @@ def main():
 
     if args.copy_calibration:
         profiling.copy_calibration_run(args.copy_calibration)
+        return
+
+    if args.workload != "stream":
+        cpu = not args.no_cpu_baseline
+        if args.workload == "one_pass_decode":
+            _, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
+            dec = wvd.Decoder(wvd.desc_from_spec(wl.FULL_DECODER), params)
+            r = bench_one_pass(dec, args.config_reps, cpu)
+        else:
+            fn = {"single_conv_fp32": bench_single_conv, "resblock": bench_resblock,
+                  "upsample_stage": bench_upsample}[args.workload]
+            r = fn(args.config_reps, cpu)
+        if cpu:
+            r["host"] = host_info()
+        print(json.dumps({"workload_key": args.workload, **r}), flush=True)
         return
 
     real = args.topology == "real"

@@ -117,6 +117,7 @@ def lib():
                                    ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
             "wvd_conv_force_config": ([ctypes.c_int], ctypes.c_int),
             "wvd_conv_max_workgroups": ([ctypes.c_int], ctypes.c_int),
+            "wvd_calib_dma_copy": ([_P, _P, ctypes.c_size_t, _P], ctypes.c_int),
             "wvd_timing_read_mem": ([ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         }
@@ -139,7 +140,8 @@ def exported_symbols() -> Sequence[str]:
             "wvd_cache_destroy", "wvd_cache_next_latent", "wvd_decode_workspace_bytes", "wvd_decode_chunk",
             "wvd_decode_workspace_bytes_split", "wvd_decode_chunk_split",
             "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read",
-            "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem", "wvd_conv_max_workgroups"]
+            "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem", "wvd_conv_max_workgroups",
+            "wvd_calib_dma_copy"]
 
 
 def _check(status: int):
@@ -501,6 +503,15 @@ def conv_force_config(config):
     elif isinstance(config, str):
         config = conv_config_names().index(config)
     _check(lib().wvd_conv_force_config(int(config)))
+
+
+def calib_dma_copy(src: torch.Tensor, dst: torch.Tensor):
+    """wvd_calib_dma_copy: copy src into dst (same byte size) through the conv kernels' load path."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst sizes differ")
+    _check(lib().wvd_calib_dma_copy(_ptr(src), _ptr(dst), n, _stream()))
+    return dst
 
 
 def conv_max_workgroups(n):

@@ -1695,6 +1695,15 @@ extern "C" wvd_status wvd_decode_chunk_split(const wvd_decoder_desc* d, const vo
 // ==============================================================================================
 // Timing
 // ==============================================================================================
+extern "C" wvd_status wvd_calib_dma_copy(const void* src, void* dst, size_t bytes, wvd_stream stream) {
+  if (!src || !dst) return fail(WVD_ERR_ARG, "calib_dma_copy: null pointer");
+  if (!aligned16(src) || !aligned16(dst) || bytes % 16) return fail(WVD_ERR_ALIGN, "calib_dma_copy: 16-byte multiples");
+  const char* a = (const char*)src;
+  const char* b = (const char*)dst;
+  if (a < b + bytes && b < a + bytes) return fail(WVD_ERR_ARG, "calib_dma_copy: src and dst overlap");
+  return hip_status(launch_dma_copy(src, dst, (int64_t)bytes, (hipStream_t)stream), "dma copy launch");
+}
+
 extern "C" wvd_status wvd_conv_force_config(int config) {
   if (config < -1 || config >= conv_config_count()) return fail(WVD_ERR_ARG, "conv config index out of range");
   g_force_config.store(config);

@@ -167,6 +167,8 @@ bool head_fused_supported(int Cip);
 // The input-stationary variant (each input frame read once per tile): Cip <= 96, Co <= 3; same
 // arguments and output.
 bool head_stream_supported(int Cip, int Co);
+// A device copy through the conv kernels' 16-byte buffer-load-to-LDS path (counter calibration).
+hipError_t launch_dma_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
                               const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
                               hipStream_t s, const CopyJob* copy = nullptr);

@@ -15,6 +15,7 @@ Command line (prints markdown):
   python -m causal_convolution_causalconv3d_amd.profiling traffic --config NAME --fetch DIR --write DIR
       --copy-fetch DIR --copy-write DIR --copy-mib N [--command CMD ...]
   python -m causal_convolution_causalconv3d_amd.profiling mfma <rocprof counter_collection.csv> [--command CMD]
+  python -m causal_convolution_causalconv3d_amd.profiling calib --fetch DIR --write DIR --copy-mib N [--command CMD ...]
 """
 import argparse
 import csv
@@ -72,6 +73,17 @@ def copy_calibration_run(mib: int) -> None:
         torch.neg(x, out=y)
     torch.cuda.synchronize()
     print(f"copy calibration: 3 dispatches of y = -x over {mib} MiB ({n * 4} bytes read and written each)", flush=True)
+    # the same bytes through the conv kernels' 16-byte buffer-load-to-LDS path
+    import causal_convolution_causalconv3d_amd as wvd
+
+    wvd.calib_dma_copy(x, y)
+    torch.cuda.synchronize()
+    assert torch.equal(x, y), "DMA copy mismatch"
+    for _ in range(3):
+        wvd.calib_dma_copy(x, y)
+    torch.cuda.synchronize()
+    print(f"copy calibration: 3 dispatches of dma_copy_kernel over {mib} MiB ({n * 4} bytes read and written each)",
+          flush=True)
 
 
 def kernel_symbol(config: str) -> str:
@@ -109,11 +121,34 @@ def _per_dispatch(d: str, counter: str, match) -> List[float]:
     return list(acc.values())
 
 
+COPY_KERNELS = {"neg": "y = -x, fp32, a plain elementwise copy",
+                "dma_copy": "dma_copy_kernel: 16-byte buffer loads into LDS, the conv kernels' load path"}
+
+
+def calib_summary(fetch: str, write: str, copy_mib: int, commands: List[str]) -> str:
+    """The counter-to-bytes factors of the two calibration copies side by side."""
+    copy_bytes = copy_mib * (1 << 20)
+    lines = ["# Counter calibration: FETCH_SIZE / WRITE_SIZE of copies of known size", "",
+             f"Each copy reads and writes {copy_mib} MiB per dispatch; the factor turns the counter into bytes",
+             "(true bytes / counted bytes, mean of the last 3 dispatches of each copy).", "", "Commands:", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "| copy | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch factor | write factor |", "|---|---:|---:|---:|---:|"]
+    for key, what in COPY_KERNELS.items():
+        cf = _per_dispatch(fetch, "FETCH_SIZE", lambda n, k=key: k in n)
+        cw = _per_dispatch(write, "WRITE_SIZE", lambda n, k=key: k in n)
+        if not (cf and cw):
+            raise RuntimeError(f"no dispatches of {key} in the counter files")
+        f_kib, w_kib = sum(cf[-3:]) / len(cf[-3:]), sum(cw[-3:]) / len(cw[-3:])
+        lines.append(f"| {what} | {f_kib:.1f} | {w_kib:.1f} | {copy_bytes / (f_kib * 1024):.4f} | "
+                     f"{copy_bytes / (w_kib * 1024):.4f} |")
+    return "\n".join(lines) + "\n"
+
+
 def traffic_summary(config: str, fetch: str, write: str, copy_fetch: str, copy_write: str, copy_mib: int,
-                    commands: List[str]) -> str:
+                    commands: List[str], copy_kernel: str = "neg") -> str:
     sym = kernel_symbol(config)
     is_kernel = lambda name: sym in name  # noqa: E731
-    is_copy = lambda name: "neg" in name  # noqa: E731
+    is_copy = lambda name: copy_kernel in name  # noqa: E731
     kf = _per_dispatch(fetch, "FETCH_SIZE", is_kernel)
     kw = _per_dispatch(write, "WRITE_SIZE", is_kernel)
     cf = _per_dispatch(copy_fetch, "FETCH_SIZE", is_copy)
@@ -132,8 +167,8 @@ def traffic_summary(config: str, fetch: str, write: str, copy_fetch: str, copy_w
         f"# HBM traffic of {config} in the streaming decode (704x1248, 4 latent frames per pass)",
         "",
         "Counters: rocprofv3 `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE` (KiB per dispatch), one run each,",
-        "averaged over every dispatch of the kernel; scaled by the same counters on a plain copy kernel",
-        f"(y = -x, fp32, {copy_mib} MiB read and written per dispatch, mean of its last 3 dispatches).",
+        "averaged over every dispatch of the kernel; scaled by the same counters on a copy kernel",
+        f"({COPY_KERNELS[copy_kernel]}; {copy_mib} MiB read and written per dispatch, mean of its last 3 dispatches).",
         "",
         "Commands:",
         "",
@@ -218,7 +253,13 @@ def main(argv=None):
     for k in ("fetch", "write", "copy-fetch", "copy-write"):
         tr.add_argument(f"--{k}", required=True)
     tr.add_argument("--copy-mib", type=int, required=True)
+    tr.add_argument("--copy-kernel", choices=sorted(COPY_KERNELS), default="neg")
     tr.add_argument("--command", action="append", default=[])
+    ca = sub.add_parser("calib")
+    ca.add_argument("--fetch", required=True)
+    ca.add_argument("--write", required=True)
+    ca.add_argument("--copy-mib", type=int, required=True)
+    ca.add_argument("--command", action="append", default=[])
     mf = sub.add_parser("mfma")
     mf.add_argument("csv")
     mf.add_argument("--command", default="")
@@ -227,8 +268,11 @@ def main(argv=None):
         sys.stdout.write(stats_summary(a.csv, a.command))
     elif a.cmd == "mfma":
         sys.stdout.write(mfma_summary(a.csv, a.command))
+    elif a.cmd == "calib":
+        sys.stdout.write(calib_summary(a.fetch, a.write, a.copy_mib, a.command))
     else:
-        sys.stdout.write(traffic_summary(a.config, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.command))
+        sys.stdout.write(traffic_summary(a.config, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.command,
+                                         a.copy_kernel))
 
 
 if __name__ == "__main__":

@@ -310,6 +310,13 @@ wvd_status wvd_conv_force_config(int config);
  * the default (one workgroup per resident slot). Results are the same for any n. WVD_ERR_ARG for
  * n < 0. Process-wide; not for use while another thread launches. */
 wvd_status wvd_conv_max_workgroups(int n);
+/* Measurement support: copy `bytes` (a multiple of 16; src and dst 16-byte aligned, device
+ * memory, not overlapping) with the convolution kernels' own load path: buffer loads that write
+ * 16 bytes per lane straight into LDS, read back and stored with 16-byte global stores. The
+ * hardware byte counters of this copy, whose true traffic is known, give the factor that turns
+ * the counters of the convolution kernels into bytes. WVD_ERR_ALIGN / WVD_ERR_ARG on bad
+ * arguments, before any launch. */
+wvd_status wvd_calib_dma_copy(const void* src, void* dst, size_t bytes, wvd_stream stream);
 
 #ifdef __cplusplus
 }
