@@ -16,6 +16,7 @@ Command line (prints markdown):
       --copy-fetch DIR --copy-write DIR --copy-mib N [--command CMD ...]
   python -m causal_convolution_causalconv3d_amd.profiling mfma <rocprof counter_collection.csv> [--command CMD]
   python -m causal_convolution_causalconv3d_amd.profiling calib --fetch DIR --write DIR --copy-mib N [--command CMD ...]
+  python -m causal_convolution_causalconv3d_amd.profiling lds <rocprof counter_collection.csv> [--command CMD]
 """
 import argparse
 import csv
@@ -242,6 +243,31 @@ def mfma_summary(path: str, command: str, top: int = 12, simds: int = 1024, xcds
     return "\n".join(out) + "\n"
 
 
+def lds_summary(path: str, command: str, top: int = 12) -> str:
+    """LDS bank-conflict share per kernel from one `--pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE ...`
+    run: bank-conflict cycles / LDS-active (indexed) cycles, summed over the kernel's dispatches."""
+    acc: Dict[str, Dict[str, float]] = {}
+    dur: Dict[str, float] = {}
+    seen = set()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = re.sub(r"\(wvd::ConvProblem\)$", "", r["Kernel_Name"]).replace("void wvd::(anonymous namespace)::", "")
+            name = name if len(name) <= 70 else name[:67] + "..."
+            c = acc.setdefault(name, {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if r["Dispatch_Id"] not in seen:
+                seen.add(r["Dispatch_Id"])
+                dur[name] = dur.get(name, 0.0) + (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    rows = sorted(acc.items(), key=lambda kv: -dur[kv[0]])[:top]
+    out = ["Command:", "", f"    {command}", "",
+           "| kernel | ms | LDS bank-conflict cycles / LDS-active cycles |", "|---|---:|---:|"]
+    for name, c in rows:
+        act = c.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        out.append(f"| `{name}` | {1e3 * dur[name]:.2f} | "
+                   f"{(100 * c.get('SQ_LDS_BANK_CONFLICT', 0.0) / act) if act else 0.0:.1f}% |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m causal_convolution_causalconv3d_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -263,11 +289,16 @@ def main(argv=None):
     mf = sub.add_parser("mfma")
     mf.add_argument("csv")
     mf.add_argument("--command", default="")
+    ld = sub.add_parser("lds")
+    ld.add_argument("csv")
+    ld.add_argument("--command", default="")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_summary(a.csv, a.command))
     elif a.cmd == "mfma":
         sys.stdout.write(mfma_summary(a.csv, a.command))
+    elif a.cmd == "lds":
+        sys.stdout.write(lds_summary(a.csv, a.command))
     elif a.cmd == "calib":
         sys.stdout.write(calib_summary(a.fetch, a.write, a.copy_mib, a.command))
     else:
