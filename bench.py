@@ -343,6 +343,46 @@ def bench_one_pass(dec, reps, cpu):
     return r
 
 
+def bench_winograd(reps):
+    """Same-box A/B of one causal 3x3x3 conv, direct (the decoder's kernel) against the Winograd
+    F(2x2, 3x3) prototype, at the real topology's 512-channel 176x312 and 256-channel 352x624
+    levels (16 frames, a 2-frame history, bias): median ms of each, the algorithmic (direct) conv
+    TFLOP/s both reach, the Winograd time split into its products and transforms, and the largest
+    difference between the two outputs relative to the direct one's largest value."""
+    out = {}
+    for C, T, H, W in ((512, 16, 176, 312), (256, 16, 352, 624)):
+        g = torch.Generator().manual_seed(C)
+        x = torch.nn.functional.silu(torch.randn((1, T, H, W, C), generator=g)).to(torch.bfloat16).cuda()
+        h = torch.randn((1, 2, H, W, C), generator=g).to(torch.bfloat16).cuda()
+        w = wl.kaiming(g, (C, C, 3, 3, 3)).cuda()
+        b = (0.1 * torch.randn((C,), generator=g)).cuda()
+        wd, ww = wvd.conv_pack(w), wvd.winograd_pack(w)
+        yd, yw = torch.empty_like(x), torch.empty_like(x)
+        ws = torch.empty(wvd.lib().wvd_winograd_workspace_bytes(C, C, T, 2, H, W), dtype=torch.uint8, device="cuda")
+        direct = lambda: wvd.causal_conv3d(x, wd, C, bias=b, hist=h, out=yd)  # noqa: E731
+        wino = lambda: wvd.causal_conv3d_winograd(x, ww, C, bias=b, hist=h, out=yw, ws=ws)  # noqa: E731
+        direct()
+        wino()
+        torch.cuda.synchronize()
+        diff = float((yw.float() - yd.float()).abs().max() / yd.float().abs().max())
+        md, mw = timed_calls(direct, reps), timed_calls(wino, reps)
+        flops = 2.0 * T * H * W * C * 27 * C
+        inst = instrumented(wino, reps)
+        key = f"{C}ch_{T}x{H}x{W}"
+        out[key] = {"direct_ms": round(md, 3), "winograd_ms": round(mw, 3), "speedup": round(md / mw, 3),
+                    "direct_tflops": round(flops / (md * 1e-3) / 1e12, 1),
+                    "winograd_effective_tflops": round(flops / (mw * 1e-3) / 1e12, 1),
+                    "winograd_products_ms": inst.get("conv", {}).get("ms_per_call"),
+                    "winograd_products_tflops": inst.get("conv", {}).get("tflops"),
+                    "winograd_transforms": inst.get("memory_bound"),
+                    "workspace_gib": round(ws.numel() / 2 ** 30, 2),
+                    "max_rel_diff_vs_direct": round(diff, 5)}
+        del x, h, yd, yw, ws
+        torch.cuda.empty_cache()
+    return {"workload": "one causal 3x3x3 conv C->C, bias, 2-frame history: direct vs Winograd F(2x2,3x3)",
+            "ms_per_call": None, "levels": out}
+
+
 def conv_launch_bytes(sh) -> float:
     """Algorithmic HBM bytes of one conv launch: the input frames it reads (with up to kt - 1 history
     frames) once, the packed weights once, the bf16 output once, the residual once when it adds
@@ -373,7 +413,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' measurements")
     ap.add_argument("--config-reps", type=int, default=10, help="timed calls per other workload (median)")
     ap.add_argument("--workload", default="stream",
-                    choices=("stream", "single_conv_fp32", "resblock", "upsample_stage", "one_pass_decode"),
+                    choices=("stream", "single_conv_fp32", "resblock", "upsample_stage", "one_pass_decode",
+                             "winograd"),
                     help="stream: the headline decode (default); otherwise only that workload's measurement "
                          "(--config-reps calls after a warm-up one), printed as one JSON line (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -393,6 +434,10 @@ def main():
 
     if args.workload != "stream":
         cpu = not args.no_cpu_baseline
+        if args.workload == "winograd":
+            r = bench_winograd(args.config_reps)
+            print(json.dumps({"workload_key": args.workload, **r}), flush=True)
+            return
         if args.workload == "one_pass_decode":
             _, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
             dec = wvd.Decoder(wvd.desc_from_spec(wl.FULL_DECODER), params)

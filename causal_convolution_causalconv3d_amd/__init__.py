@@ -118,6 +118,10 @@ def lib():
             "wvd_conv_force_config": ([ctypes.c_int], ctypes.c_int),
             "wvd_conv_max_workgroups": ([ctypes.c_int], ctypes.c_int),
             "wvd_calib_dma_copy": ([_P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+            "wvd_winograd_packed_bytes": ([ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
+            "wvd_winograd_pack": ([_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P], ctypes.c_int),
+            "wvd_winograd_workspace_bytes": ([ctypes.c_int] * 6, ctypes.c_size_t),
+            "wvd_causal_conv3d_winograd": ([_T, _P, ctypes.c_int, _P, _T, _T, _T, _P, ctypes.c_size_t, _P], ctypes.c_int),
             "wvd_timing_read_mem": ([ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         }
@@ -141,7 +145,8 @@ def exported_symbols() -> Sequence[str]:
             "wvd_decode_workspace_bytes_split", "wvd_decode_chunk_split",
             "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read",
             "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem", "wvd_conv_max_workgroups",
-            "wvd_calib_dma_copy"]
+            "wvd_calib_dma_copy", "wvd_winograd_packed_bytes", "wvd_winograd_pack", "wvd_winograd_workspace_bytes",
+            "wvd_causal_conv3d_winograd"]
 
 
 def _check(status: int):
@@ -226,6 +231,33 @@ def causal_conv3d(x, w, co, kernel=(3, 3, 3), bias=None, hist=None, residual=Non
             out = torch.empty((x.shape[0], co) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
     _check(lib().wvd_causal_conv3d(_desc(x, layout), _ptr(w), co, kt, kh, kw, _ptr(bias), _desc(hist, layout),
                                    _desc(residual, layout), _desc(out, layout), _desc(hist_out, layout), _stream()))
+    return out
+
+
+def winograd_pack(w: torch.Tensor) -> torch.Tensor:
+    """wvd_winograd_pack: the raw 3x3x3 weight [co, ci, 3, 3, 3] (fp32 or bf16, device) -> its 16
+    transformed component weights, packed."""
+    co, ci = w.shape[:2]
+    if tuple(w.shape[2:]) != (3, 3, 3):
+        raise WvdError(2, "winograd_pack needs a 3x3x3 weight")
+    out = torch.empty(lib().wvd_winograd_packed_bytes(co, ci), dtype=torch.uint8, device=w.device)
+    dt = WVD_BF16 if w.dtype == torch.bfloat16 else WVD_F32
+    _check(lib().wvd_winograd_pack(_ptr(w.contiguous()), dt, co, ci, _ptr(out), _stream()))
+    return out
+
+
+def causal_conv3d_winograd(x, w_packed, co, bias=None, hist=None, residual=None, out=None, ws=None):
+    """wvd_causal_conv3d_winograd on a [1, T, H, W, ci] bf16 tensor (NTHWC)."""
+    _, T, H, W, ci = x.shape
+    th = 0 if hist is None else hist.shape[1]
+    if out is None:
+        out = torch.empty(x.shape[:4] + (co,), dtype=x.dtype, device=x.device)
+    nbytes = lib().wvd_winograd_workspace_bytes(ci, co, T, th, H, W)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().wvd_causal_conv3d_winograd(_desc(x, "NTHWC"), _ptr(w_packed), co, _ptr(bias), _desc(hist, "NTHWC"),
+                                            _desc(residual, "NTHWC"), _desc(out, "NTHWC"), _ptr(ws), ws.numel(),
+                                            _stream()))
     return out
 
 

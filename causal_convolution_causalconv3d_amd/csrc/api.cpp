@@ -113,10 +113,13 @@ enum MemKind {
   MEM_ATTN = 5,     // the attention's softmax and value transpose
   MEM_DUP = 6,      // the DupUp3D add
   MEM_UNPATCH = 7,  // unpatchify (+ clamp) into the video
-  MEM_KINDS = 8
+  MEM_WINO_IN = 8,  // the Winograd input transform
+  MEM_WINO_OUT = 9, // the Winograd output transform
+  MEM_KINDS = 10
 };
 const char* const kMemKindNames[MEM_KINDS] = {"norm_silu", "head_stencil", "convert", "head_fused", "head_stream",
-                                              "attn_softmax_transpose", "dup_add", "unpatchify"};
+                                              "attn_softmax_transpose", "dup_add", "unpatchify", "winograd_in",
+                                              "winograd_out"};
 struct LaunchRecord {
   int config;
   float ms;
@@ -452,6 +455,100 @@ extern "C" wvd_status wvd_causal_conv3d(const wvd_tensor* x, const void* w, int 
     WVD_TRY(copy_history_out(x->data, T, hist ? hist->data : nullptr, Th, hist_out->data,
                              (size_t)H * W * Ci * elem_size(x->dtype), s));
   return WVD_OK;
+}
+
+// ==============================================================================================
+// Winograd F(2x2, 3x3) form of the causal 3x3x3 convolution (winograd.hip)
+// ==============================================================================================
+namespace {
+
+struct WinoWs {
+  size_t u, m, total;  // byte offsets of U [16][Th+T][tH][tW][Ci] bf16 and M [16][T][tH][tW][Co] fp32
+};
+
+WinoWs wino_ws(int ci, int co, int64_t t, int64_t th, int64_t h, int64_t w) {
+  const int64_t tiles = ((h + 1) / 2) * ((w + 1) / 2);
+  WinoWs r;
+  r.u = 0;
+  r.m = (size_t)round_up(16 * (t + th) * tiles * ci * 2, 256);
+  r.total = r.m + (size_t)round_up(16 * t * tiles * co * 4, 256);
+  return r;
+}
+
+}  // namespace
+
+extern "C" size_t wvd_winograd_packed_bytes(int co, int ci) {
+  if (co <= 0 || ci <= 0) return 0;
+  return (size_t)packed_elems(co, ci, 3, 16) * 2;
+}
+
+extern "C" wvd_status wvd_winograd_pack(const void* w_raw, int w_dtype, int co, int ci, void* packed,
+                                        wvd_stream stream) {
+  if (!w_raw || !packed) return fail(WVD_ERR_ARG, "winograd_pack: null pointer");
+  if (w_dtype != WVD_F32 && w_dtype != WVD_BF16) return fail(WVD_ERR_DTYPE, "winograd_pack: weight dtype");
+  if (co <= 0 || ci <= 0) return fail(WVD_ERR_SHAPE, "winograd_pack: channels must be positive");
+  if (!aligned16(packed)) return fail(WVD_ERR_ALIGN, "winograd_pack: packed buffer not 16-byte aligned");
+  return hip_status(launch_wino_pack(w_raw, w_dtype == WVD_BF16, co, ci, (int)round_up(co, 32), (int)round_up(ci, 32),
+                                     (bf16_t*)packed, (hipStream_t)stream),
+                    "winograd pack launch");
+}
+
+extern "C" size_t wvd_winograd_workspace_bytes(int ci, int co, int t, int th, int h, int w) {
+  if (ci <= 0 || co <= 0 || t < 0 || th < 0 || h <= 0 || w <= 0) return 0;
+  return wino_ws(ci, co, t, th, h, w).total;
+}
+
+extern "C" wvd_status wvd_causal_conv3d_winograd(const wvd_tensor* x, const void* w_packed, int co, const float* bias,
+                                                 const wvd_tensor* hist, const wvd_tensor* residual, wvd_tensor* y,
+                                                 void* ws, size_t ws_bytes, wvd_stream stream) {
+  WVD_TRY(check_tensor(x, "x", WVD_BF16, WVD_NTHWC, true));
+  WVD_TRY(check_tensor(y, "y", WVD_BF16, WVD_NTHWC, true));
+  if (!w_packed || !aligned16(w_packed)) return fail(WVD_ERR_ALIGN, "winograd: packed weights null or unaligned");
+  if (bias && !aligned16(bias)) return fail(WVD_ERR_ALIGN, "winograd: bias not 16-byte aligned");
+  const int Ci = (int)x->c, T = (int)x->t, H = (int)x->h, W = (int)x->w;
+  if (Ci % 8 != 0 || co <= 0 || co % 4 != 0)
+    return fail(WVD_ERR_UNSUPPORTED, "winograd: input channels a multiple of 8, output channels of 4");
+  if (y->c != co || y->t != x->t || !same_grid(x, y)) return fail(WVD_ERR_SHAPE, "y must be [1, co, T, H, W] of x");
+  int Th = 0;
+  if (hist) {
+    WVD_TRY(check_tensor(hist, "hist", WVD_BF16, WVD_NTHWC, true));
+    if (hist->c != x->c || !same_grid(hist, x) || hist->t > 2) return fail(WVD_ERR_SHAPE, "hist must be [1, ci, <=2, H, W]");
+    Th = (int)hist->t;
+  }
+  if (residual) {
+    WVD_TRY(check_tensor(residual, "residual", WVD_BF16, WVD_NTHWC, true));
+    if (residual->c != co || residual->t != x->t || !same_grid(residual, x))
+      return fail(WVD_ERR_SHAPE, "residual must have y's shape");
+  }
+  if (overlaps(y, x) || overlaps(y, hist)) return fail(WVD_ERR_ARG, "y may not overlap x or hist");
+  const WinoWs wl = wino_ws(Ci, co, T, Th, H, W);
+  if (ws_bytes < wl.total) return fail(WVD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, wl.total);
+  if (T == 0) return WVD_OK;
+  if (!ws || !aligned16(ws)) return fail(WVD_ERR_ALIGN, "workspace null or not 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int tH = (H + 1) / 2, tW = (W + 1) / 2;
+  const int64_t tiles = (int64_t)tH * tW;
+  bf16_t* U = (bf16_t*)((char*)ws + wl.u);
+  float* M = (float*)((char*)ws + wl.m);
+  const double in_bytes = 2.0 * (T + Th) * H * W * Ci + 2.0 * 16 * (T + Th) * tiles * Ci;
+  WVD_TRY(run_mem(MEM_WINO_IN, in_bytes, s, "winograd input transform", [&] {
+    return launch_wino_in((const bf16_t*)x->data, hist ? (const bf16_t*)hist->data : nullptr, T, Th, H, W, Ci, U, s);
+  }));
+  const int64_t u_plane = (int64_t)(T + Th) * tiles * Ci, m_plane = (int64_t)T * tiles * co;
+  const int64_t w_plane = packed_elems(co, Ci, 3, 1);
+  for (int xi = 0; xi < 16; ++xi) {
+    const bf16_t* u = U + xi * u_plane;
+    ConvProblem cp = plain_problem(u + (int64_t)Th * tiles * Ci, Th ? u : nullptr, T, tH, tW, Ci, Th,
+                                   (const bf16_t*)w_packed + xi * w_plane, co, 3, 1, 1, nullptr, nullptr, nullptr);
+    cp.y = M + xi * m_plane;
+    cp.y_f32 = 1;
+    WVD_TRY(run_conv(cp, s, conv_flops((int64_t)T * tiles, co, 3LL * Ci)));
+  }
+  const double out_bytes = 4.0 * 16 * T * tiles * co + 2.0 * T * H * W * co * (residual ? 2 : 1);
+  return run_mem(MEM_WINO_OUT, out_bytes, s, "winograd output transform", [&] {
+    return launch_wino_out(M, T, H, W, co, bias, residual ? (const bf16_t*)residual->data : nullptr, (bf16_t*)y->data,
+                           s);
+  });
 }
 
 extern "C" wvd_status wvd_rmsnorm_silu(const wvd_tensor* x, const float* gamma, float eps, int apply_silu, wvd_tensor* y,

@@ -169,6 +169,13 @@ bool head_fused_supported(int Cip);
 bool head_stream_supported(int Cip, int Co);
 // A device copy through the conv kernels' 16-byte buffer-load-to-LDS path (counter calibration).
 hipError_t launch_dma_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+// Winograd F(2x2, 3x3) steps (winograd.hip): the weight transform into 16 packed (3,1,1) weights,
+// the input transform into U [16][Th+T][tH][tW][C] and the output transform of M [16][T][tH][tW][Co].
+hipError_t launch_wino_pack(const void* w, int w_bf16, int Co, int Ci, int Npad, int Cip, bf16_t* out, hipStream_t s);
+hipError_t launch_wino_in(const bf16_t* x, const bf16_t* hist, int T, int Th, int H, int W, int C, bf16_t* U,
+                          hipStream_t s);
+hipError_t launch_wino_out(const float* M, int T, int H, int W, int Co, const float* bias, const bf16_t* res,
+                           bf16_t* y, hipStream_t s);
 hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
                               const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
                               hipStream_t s, const CopyJob* copy = nullptr);

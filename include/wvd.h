@@ -121,6 +121,30 @@ wvd_status wvd_causal_conv3d(const wvd_tensor* x, const void* w, int co, int kt,
                              const float* bias, const wvd_tensor* hist, const wvd_tensor* residual, wvd_tensor* y,
                              wvd_tensor* hist_out, wvd_stream stream);
 
+/* ============================================================================================
+ * wvd_causal_conv3d_winograd - the causal 3x3x3 convolution of wvd_causal_conv3d (bf16 path,
+ * same y, bias, hist and residual rules) computed with Winograd F(2x2, 3x3) in space and the
+ * causal 3-tap time convolution kept as is, as the page's decoder runs its up blocks'
+ * convolutions ("How the decoder got here", "The design"; there F(4x4, 3x3)). Each 2x2 output
+ * tile takes the 4x4 input tile around it (zero outside the frame); its 16 transformed
+ * components U = B^T d B (rounded to bf16) are multiplied with the transformed weights
+ * V = G g G^T (bf16) on the matrix cores, summed over channels and time taps in fp32 (16 products
+ * stored as fp32), and A^T M A + bias (+ residual) is rounded once into y. A layer-level
+ * prototype (the decoder keeps the direct kernel): about 2.25x fewer products, three extra
+ * memory-bound passes.
+ * x, hist, residual, y: bf16 NTHWC; Ci % 8 == 0, co % 4 == 0; hist.t <= 2; y may share no byte
+ * with x or hist. bias: nullable fp32 [co], 16-byte aligned. w_packed: from wvd_winograd_pack
+ * (the raw weight [co][ci][3][3][3], fp32 or bf16), wvd_winograd_packed_bytes(co, ci) bytes,
+ * 16-byte aligned. ws: wvd_winograd_workspace_bytes(ci, co, T, hist.t, H, W) bytes of device
+ * memory (16 transformed input planes and 16 fp32 product planes), 16-byte aligned.
+ * ========================================================================================== */
+size_t wvd_winograd_packed_bytes(int co, int ci);
+wvd_status wvd_winograd_pack(const void* w_raw, int w_dtype, int co, int ci, void* packed, wvd_stream stream);
+size_t wvd_winograd_workspace_bytes(int ci, int co, int t, int th, int h, int w);
+wvd_status wvd_causal_conv3d_winograd(const wvd_tensor* x, const void* w_packed, int co, const float* bias,
+                                      const wvd_tensor* hist, const wvd_tensor* residual, wvd_tensor* y, void* ws,
+                                      size_t ws_bytes, wvd_stream stream);
+
 /* Channel RMS norm + SiLU (the page's RMS norm part, in the x * gamma / sqrt(mean_c x^2 + eps)
  * form; the SiLU of its residual block part): bf16 NTHWC in and out, fp32 statistics, one
  * rounding. gamma: fp32 [C] device memory. x and y may be the same tensor. */
