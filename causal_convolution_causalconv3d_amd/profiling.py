@@ -17,6 +17,8 @@ Command line (prints markdown):
   python -m causal_convolution_causalconv3d_amd.profiling mfma <rocprof counter_collection.csv> [--command CMD]
   python -m causal_convolution_causalconv3d_amd.profiling calib --fetch DIR --write DIR --copy-mib N [--command CMD ...]
   python -m causal_convolution_causalconv3d_amd.profiling lds <rocprof counter_collection.csv> [--command CMD]
+  python -m causal_convolution_causalconv3d_amd.profiling hbm [--topology real] [--frames-per-pass N]
+      [--early-frames-per-pass N]   (host only: the peak's items from the library's size queries)
 """
 import argparse
 import csv
@@ -268,6 +270,39 @@ def lds_summary(path: str, command: str, top: int = 12) -> str:
     return "\n".join(out) + "\n"
 
 
+def hbm_summary(topology: str, latent_frames: int, fpp: int, early: int) -> str:
+    """Device memory a streaming decode holds at its peak, item by item, from the library's own
+    size queries (host only): packed weights, the double-buffered cache, the workspace (split into
+    the buffers the layout sizes), the whole video and the latents."""
+    import ctypes
+
+    import causal_convolution_causalconv3d_amd as wvd
+    import workloads as wl
+
+    spec = wl.REAL_DECODER if topology == "real" else wl.FULL_DECODER
+    d = wvd.desc_from_spec(spec)
+    L = wvd.lib()
+    dec_frames = 0
+    start = 0
+    while start < latent_frames:
+        n = min(fpp, latent_frames - start)
+        dec_frames += L.wvd_chunk_video_frames(ctypes.byref(d), n, int(start == 0), 1)
+        start += n
+    early = max(early, fpp)
+    ws = (L.wvd_decode_workspace_bytes_split(ctypes.byref(d), early, fpp) if early > fpp
+          else L.wvd_decode_workspace_bytes(ctypes.byref(d), fpp))
+    items = [("packed weights (bf16, channel-padded)", L.wvd_decoder_packed_bytes(ctypes.byref(d))),
+             ("cache (one slot per causal conv, two halves of two frames)", L.wvd_cache_bytes(ctypes.byref(d))),
+             (f"workspace ({early} latent frames per pass through the early stages, {fpp} through the late ones)", ws),
+             (f"video [1,3,{dec_frames},704,1248] bf16", 3 * dec_frames * 704 * 1248 * 2),
+             (f"latents [1,48,{latent_frames},44,78] bf16", 48 * latent_frames * 44 * 78 * 2)]
+    total = sum(b for _, b in items)
+    out = ["| item | GiB |", "|---|---:|"]
+    out += [f"| {k} | {b / 2 ** 30:.3f} |" for k, b in items]
+    out.append(f"| sum | {total / 2 ** 30:.3f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m causal_convolution_causalconv3d_amd.profiling")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -289,6 +324,11 @@ def main(argv=None):
     mf = sub.add_parser("mfma")
     mf.add_argument("csv")
     mf.add_argument("--command", default="")
+    hb = sub.add_parser("hbm")
+    hb.add_argument("--topology", choices=("synthetic", "real"), default="synthetic")
+    hb.add_argument("--latent-frames", type=int, default=31)
+    hb.add_argument("--frames-per-pass", type=int, default=4)
+    hb.add_argument("--early-frames-per-pass", type=int, default=0)
     ld = sub.add_parser("lds")
     ld.add_argument("csv")
     ld.add_argument("--command", default="")
@@ -297,6 +337,8 @@ def main(argv=None):
         sys.stdout.write(stats_summary(a.csv, a.command))
     elif a.cmd == "mfma":
         sys.stdout.write(mfma_summary(a.csv, a.command))
+    elif a.cmd == "hbm":
+        sys.stdout.write(hbm_summary(a.topology, a.latent_frames, a.frames_per_pass, a.early_frames_per_pass))
     elif a.cmd == "lds":
         sys.stdout.write(lds_summary(a.csv, a.command))
     elif a.cmd == "calib":

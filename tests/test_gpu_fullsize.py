@@ -9,7 +9,13 @@
     from the oracle alone), and bitwise pass-size invariance;
   * streaming 5 s decode [1,48,31,44,78] -> 121 frames: bitwise equal for 4 frames per pass, 3,
     all 31 in one pass (the one-shot form), and per-level pass sizes (8 or 16 latent frames
-    through the early stages, sub-passes of 4 through the late ones).
+    through the early stages, sub-passes of 4 through the late ones);
+  * the same streaming decode (4 latent frames per pass) against the oracle's decode of the whole
+    clip (tests/golden/stream_decode_samples.npz, written by make_stream_golden.py from the oracle
+    alone, in passes of 5 latent frames, bitwise its one-shot decode): PSNR over the samples and
+    on each sampled frame (frame 0, both sides of the GPU's and the oracle's first pass
+    boundaries, a later boundary, frame 120), and each frame's mean and mean square over all of
+    its pixels.
 """
 import math
 import os
@@ -25,6 +31,7 @@ from gpu_util import from_dev_nthwc, log, psnr, rel_max, to_dev_nthwc
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "decoder_onepass_samples.npz")
+STREAM_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "stream_decode_samples.npz")
 
 
 def test_resblock_full_size():
@@ -107,6 +114,43 @@ def test_streaming_decode_full_size_pass_size_invariant():
         del v
         dec._ws = None
         torch.cuda.empty_cache()
+
+
+def test_streaming_decode_full_size_against_the_one_shot_oracle():
+    if not os.path.exists(STREAM_GOLDEN):
+        pytest.skip("stream golden samples not generated (tests/golden/make_stream_golden.py)")
+    g = np.load(STREAM_GOLDEN)
+    _, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
+    z = wl.streaming_latents(seed=5, latent_frames=31)
+    dec = _full_decoder(params)
+    v = dec.decode(z.to(torch.bfloat16).cuda(), frames_per_pass=4)
+    torch.cuda.synchronize()
+    assert tuple(v.shape) == (1, 3, 121, 704, 1248)
+    video = v[0].float()
+    flat = video.reshape(-1)
+    idx = torch.from_numpy(g["index"]).cuda()
+    got = flat[idx].cpu().numpy().astype(np.float64)
+    ref = g["value"].astype(np.float64)
+    rng = float(g["vmax"] - g["vmin"])
+    err = got - ref
+    q = 10 * math.log10(rng * rng / float((err ** 2).mean()))
+    log(f"streaming decode vs one-shot oracle: psnr {q:.2f} dB over {ref.size} samples, max abs {np.abs(err).max():.3e}, "
+        f"range {rng:.3f}")
+    assert q >= 55.0
+    frame = (g["index"] // (704 * 1248)) % 121
+    for f in (0, 12, 13, 14, 16, 17, 60, 61, 120):
+        e = err[frame == f]
+        qf = 10 * math.log10(rng * rng / float((e ** 2).mean()))
+        log(f"  frame {f}: psnr {qf:.2f} dB over {e.size} samples, max abs {np.abs(e).max():.3e}")
+        assert qf >= 55.0, f
+    # every frame's mean and mean square over all its pixels
+    per_frame = video.permute(1, 0, 2, 3).reshape(121, -1).double()
+    mean = per_frame.mean(dim=1).cpu().numpy()
+    meansq = (per_frame ** 2).mean(dim=1).cpu().numpy()
+    dm = np.abs(mean - g["frame_mean"]).max() / rng
+    dq = np.abs(meansq / g["frame_meansq"] - 1.0).max()
+    log(f"  per-frame mean: max |diff| {dm:.2e} of the range; mean square: max rel diff {dq:.2e}")
+    assert dm <= 1e-3 and dq <= 1e-2
 
 
 def test_real_topology_full_size_streaming_properties():
