@@ -268,9 +268,11 @@ wvd_status run_time_conv(const bf16_t* x, const bf16_t* hist, int T, int H, int 
 // Nearest x2 + 3x3 conv as four phase convs: x [T][H][W][C] -> y [T][2H][2W][C]; with norm_gamma,
 // y is SiLU(RMS norm) of the upsampled tensor (fused in the epilogue).
 wvd_status run_phase_conv(const bf16_t* x, int T, int H, int W, int C, const void* wpk, const float* bias, bf16_t* y,
-                          hipStream_t s, const float* norm_gamma = nullptr, float norm_eps = 0.0f) {
+                          hipStream_t s, const float* norm_gamma = nullptr, float norm_eps = 0.0f,
+                          bf16_t* y_pre = nullptr) {
   ConvProblem p = plain_problem(x, nullptr, T, H, W, C, 0, wpk, C, 1, 1, 1, bias, y, nullptr);
   p.norm_gamma = norm_gamma;
+  p.y_pre = y_pre;
   p.norm_eps = norm_eps;
   p.norm_silu = 1;
   p.ntaps = 4;
@@ -1153,6 +1155,15 @@ struct WsLayout {
   int64_t tail_frames;  // frames per sub-pass of the fused last upsample + head (see run_tail)
 };
 
+// Whether a conv with c output channels can apply the next residual block's norm1 + SiLU in its
+// epilogue and store its own (pre-norm) output too: the dual store, on one channel tile (the
+// 3x3x3 convs up to 192 channels; the x2 phase convs from 97 to 192, their 192-wide tile).
+std::atomic<int> g_fuse_norm1{1};  // wvd_decode_fuse_norm1
+
+bool dual_store_width(int c, bool phase) {
+  return g_fuse_norm1.load() && conv_can_fuse_norm_width(c) && (!phase || c > 96);
+}
+
 // Whether the last stage is a spatial upsample without a time step or DupUp3D whose epilogue
 // applies norm_out + SiLU (one workgroup holds every channel; the packed parameters are
 // 256-byte aligned): its output is then only the head's input. The decode runs that upsample
@@ -1497,8 +1508,10 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
     WVD_TRY(cached_conv(cp, p.conv_in_slot, zin, (int)T, conv_flops(P, c, 27LL * d->z_channels)));
   }
   // a residual block reading x (the stream buffer, or the split level's input) and writing the
-  // stream buffer (in place when the residual is x itself)
-  auto resblock = [&](const ResPlan& r, const bf16_t* x) -> wvd_status {
+  // stream buffer (in place when the residual is x itself). pre_act: SiLU(norm1(x)) is already in
+  // the activated buffer (the producer's dual store). next_gamma: the next block's norm1 gain, when
+  // conv2 also writes SiLU(norm1_next(y)) into the activated buffer (its dual store).
+  auto resblock = [&](const ResPlan& r, const bf16_t* x, bool pre_act, const float* next_gamma) -> wvd_status {
     const int64_t P = T * H * Wd;
     bf16_t* y = bx[cur];
     const bf16_t* residual = x;
@@ -1507,7 +1520,7 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       WVD_TRY(run_conv(sc, s, conv_flops(P, r.cout, r.cin)));
       residual = bsc;
     }
-    WVD_TRY(run_norm(x, F_(r.gamma1), d->eps, 1, ba, P, r.cin, s));
+    if (!pre_act) WVD_TRY(run_norm(x, F_(r.gamma1), d->eps, 1, ba, P, r.cin, s));
     ConvProblem c1 = plain_problem(ba, nullptr, (int)T, H, Wd, r.cin, 0, W_(r.w1), r.cout, 3, 3, 3, F_(r.b1), bh, nullptr);
     // norm2 + SiLU fused into conv1's epilogue when one workgroup holds all output channels
     const bool fuse = conv_can_fuse_norm(r.cout, F_(r.b1), F_(r.gamma2));
@@ -1523,9 +1536,23 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       a2 = ba;
     }
     ConvProblem c2 = plain_problem(a2, nullptr, (int)T, H, Wd, r.cout, 0, W_(r.w2), r.cout, 3, 3, 3, F_(r.b2), y, residual);
+    if (next_gamma) {
+      // y = conv2 + bias + residual into the stream buffer, SiLU(norm1_next(y)) into the
+      // activated buffer (free: conv2 reads a2 from the conv1 output, fused there at this width)
+      if (a2 == ba) return fail(WVD_ERR_STATE, "dual store needs conv1's fused norm");
+      c2.y_pre = y;
+      c2.y = ba;
+      c2.norm_gamma = next_gamma;
+      c2.norm_eps = d->eps;
+      c2.norm_silu = 1;
+    }
     WVD_TRY(cached_conv(c2, r.slot2, a2, (int)T, conv_flops(P, r.cout, 27LL * r.cout)));
     return WVD_OK;
   };
+  // the next stage's first residual block takes its SiLU(norm1(x)) from the activated buffer,
+  // written by this stage's x2 upsample (its dual store)
+  bool stage_pre_act = false;
+  bool mid_pre_act = false;
   // The mid block's attention, in place on x (level 0, T frames): n = RMS norm of x; q | k | v
   // from one 1x1 conv C -> 3C whose channel thirds go to frames t, T + t, 2T + t; per frame the
   // scores q k^T as a 1x1 conv of q whose weight rows are the frame's keys (fp32 out), the row
@@ -1564,7 +1591,11 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
     return run_conv(pp, s, conv_flops(P, c, c));
   };
   for (size_t i = 0; i < p.mid.size(); ++i) {
-    WVD_TRY(resblock(p.mid[i], bx[cur]));
+    // (the middle blocks run at the base width; the attention sits between the first two)
+    const bool dual = i + 1 < p.mid.size() && !(i == 0 && p.attn_qkv_w >= 0) &&
+                      p.mid[i + 1].cin == p.mid[i].cout && dual_store_width(p.mid[i].cout, false);
+    WVD_TRY(resblock(p.mid[i], bx[cur], i > 0 && mid_pre_act, dual ? F_(p.mid[i + 1].gamma1) : nullptr));
+    mid_pre_act = dual;
     if (i == 0 && p.attn_qkv_w >= 0) WVD_TRY(run_attention(bx[cur]));
   }
   // The last stage's spatial upsample also applies norm_out + SiLU in its epilogue when one
@@ -1585,8 +1616,13 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
     if (st.dup && T_in > 0)  // the stage's input, for its DupUp3D shortcut after the upsampling
       WVD_HIP(hipMemcpyAsync(bkeep, x, (size_t)T_in * H_in * W_in * st.cin * 2, hipMemcpyDeviceToDevice, s),
               "DupUp3D source copy");
-    for (const ResPlan& r : st.res) {
-      WVD_TRY(resblock(r, x));
+    bool pre_act = stage_pre_act;
+    stage_pre_act = false;
+    for (size_t k = 0; k < st.res.size(); ++k) {
+      const ResPlan& r = st.res[k];
+      const bool dual = k + 1 < st.res.size() && st.res[k + 1].cin == r.cout && dual_store_width(r.cout, false);
+      WVD_TRY(resblock(r, x, pre_act, dual ? F_(st.res[k + 1].gamma1) : nullptr));
+      pre_act = dual;
       x = bx[cur];
       c = r.cout;
     }
@@ -1634,7 +1670,17 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), up, s));
       yout = up;
     } else {
-      WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur ^ 1], s));
+      // the next stage's first block's norm1 + SiLU in the epilogue too (dual store), when nothing
+      // is added to the upsampled output first (DupUp3D) and the widths allow it
+      const bool dual = !st.dup && si + 1 < L && !p.stages[si + 1].res.empty() &&
+                        p.stages[si + 1].res[0].cin == c && dual_store_width(c, true);
+      if (dual) {
+        WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), ba, s, F_(p.stages[si + 1].res[0].gamma1),
+                               d->eps, bx[cur ^ 1]));
+        stage_pre_act = true;
+      } else {
+        WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), bx[cur ^ 1], s));
+      }
       cur ^= 1;
       yout = bx[cur];
     }
@@ -1756,6 +1802,7 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       c = c0;
       act = nullptr;
       zbuf = nullptr;
+      stage_pre_act = false;  // (the split level's input comes from xm, never pre-activated)
       const bf16_t* x = bxm + (size_t)t0 * H0 * W0 * c0;
       for (int si = split; si < L; ++si) {
         WVD_TRY(run_stage(si, x, nullptr));
@@ -1804,6 +1851,11 @@ extern "C" wvd_status wvd_calib_dma_copy(const void* src, void* dst, size_t byte
 extern "C" wvd_status wvd_conv_force_config(int config) {
   if (config < -1 || config >= conv_config_count()) return fail(WVD_ERR_ARG, "conv config index out of range");
   g_force_config.store(config);
+  return WVD_OK;
+}
+
+extern "C" wvd_status wvd_decode_fuse_norm1(int on) {
+  g_fuse_norm1.store(on ? 1 : 0);
   return WVD_OK;
 }
 

@@ -109,6 +109,9 @@ struct ConvProblem {
   const float* norm_gamma;  // [N] or null
   float norm_eps;
   int norm_silu;
+  // With a fused norm, optionally also the pre-norm value (bias and residual added, one bf16
+  // rounding) in y's layout: the residual stream beside the next block's activated input.
+  bf16_t* y_pre;
   int time_tiles;  // set by the launcher: the halo kernel's tile order
   int staged;      // set by the launcher: store the output through LDS (see conv_epilogue_staged)
   CopyJob copy;    // side work (zero bytes: none)

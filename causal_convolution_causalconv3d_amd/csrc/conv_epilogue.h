@@ -184,9 +184,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NB, int MB, bool NORM, int NBP>
+// DUAL (with NORM): the residual (p.res, optional) is added before the norm's statistics, and the
+// pre-norm value (bias and residual added) is stored to p.y_pre beside the activated value in p.y:
+// a residual block's output and the next block's SiLU(norm1(.)) input from one epilogue.
+template <int NB, int MB, bool NORM, int NBP, bool DUAL = false>
 __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, floatx16 (&acc)[NB][MB], const int (&ph)[MB],
                                                      int w0, int tf, int n0, int pa, int pb, int lane, char* stage) {
+  static_assert(!DUAL || NORM, "the dual store belongs to the fused norm");
   const float* bias = opaque(p.bias);
   const float* gamma = opaque(p.norm_gamma);
   asm volatile("" : "+v"(lane));  // (the chunk indices below are per call, not hoisted)
@@ -216,9 +220,60 @@ __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, float
           for (int e = 0; e < 4; ++e) {
             const float v = acc[nb][mb][g * 4 + e] + bv[e];
             acc[nb][mb][g * 4 + e] = v;
-            ssm[mb] = fmaf(v, v, ssm[mb]);
+            if constexpr (!DUAL) ssm[mb] = fmaf(v, v, ssm[mb]);
           }
       }
+    }
+    if constexpr (DUAL) {
+      // + residual, read per row and pass the coalesced way through this wave's staging area
+      // (the plain epilogue's order: (acc + bias) + residual), then the sum of squares
+      if (p.res) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          if (ph[mb] >= p.H) continue;  // wave-uniform
+          const int orow = p.hmul * ph[mb] + pa;
+#pragma unroll
+          for (int pg = 0; pg < NPG; ++pg) {
+            const int cb = pg * S::NBP * 32;
+            if (cb >= p.N) continue;
+            __builtin_amdgcn_sched_barrier(0);
+            uint4 r[S::CPL];
+#pragma unroll
+            for (int i = 0; i < S::CPL; ++i) {
+              const int j = i * 64 + lane, q = j / S::CHP, c = j - (j / S::CHP) * S::CHP;
+              const int n = cb + c * 8, w = w0 + q;
+              r[i] = (w < p.W && n < p.N) ? *(const uint4*)(p.res + out_index(p, tf, n, orow, p.wmul * w + pb))
+                                          : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int i = 0; i < S::CPL; ++i) {
+              const int j = i * 64 + lane, q = j / S::CHP, c = j - (j / S::CHP) * S::CHP;
+              *(uint4*)(stage + q * S::PS + c * 16) = r[i];
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int nl = 0; nl < S::NBP; ++nl) {
+              const int nb = pg * S::NBP + nl;
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                if (nb * 32 + g * 8 >= p.N) continue;
+                const uint2 rr = *(const uint2*)(stage + l32 * S::PS + (nl * 32 + g * 8 + half * 4) * 2);
+                acc[nb][mb][g * 4 + 0] += bf16_lo(rr.x);
+                acc[nb][mb][g * 4 + 1] += bf16_hi(rr.x);
+                acc[nb][mb][g * 4 + 2] += bf16_lo(rr.y);
+                acc[nb][mb][g * 4 + 3] += bf16_hi(rr.y);
+              }
+            }
+            wave_lds_sync();
+          }
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ssm[mb] = fmaf(acc[nb][mb][r], acc[nb][mb][r], ssm[mb]);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -235,6 +290,30 @@ __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, float
       const int cb = n0 + pg * S::NBP * 32;
       if (cb >= p.N) continue;
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (DUAL) {
+        // the pre-norm value (bias and residual already in the accumulators), one rounding
+#pragma unroll
+        for (int nl = 0; nl < S::NBP; ++nl) {
+          const int nb = pg * S::NBP + nl;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            if (nb * 32 + g * 8 >= p.N) continue;
+            uint2 o;
+            o.x = pack_bf16x2(acc[nb][mb][g * 4 + 0], acc[nb][mb][g * 4 + 1]);
+            o.y = pack_bf16x2(acc[nb][mb][g * 4 + 2], acc[nb][mb][g * 4 + 3]);
+            *(uint2*)(stage + l32 * S::PS + (nl * 32 + g * 8 + half * 4) * 2) = o;
+          }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < S::CPL; ++i) {
+          const int j = i * 64 + lane, q = j / S::CHP, c = j - (j / S::CHP) * S::CHP;
+          const int n = cb + c * 8, w = w0 + q;
+          const uint4 o = *(const uint4*)(stage + q * S::PS + c * 16);
+          if (w < p.W && n < p.N) *(uint4*)(p.y_pre + out_index(p, tf, n, orow, p.wmul * w + pb)) = o;
+        }
+        wave_lds_sync();
+      }
       if (!NORM && p.res) {
         uint4 r[S::CPL];
 #pragma unroll

@@ -595,11 +595,11 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Waves per SIMD a DMA kernel is compiled for: two, or four for the one-row phase tiles (their
 // light main loop leaves the SIMDs to the epilogue's vector work, which other waves then overlap).
-template <int MB, int KS>
-constexpr int dma_waves_per_simd() { return (KS == 2 && MB == 1) ? 4 : 2; }
+template <int NB, int MB, int KS>
+constexpr int dma_waves_per_simd() { return (KS == 2 && MB == 1 && NB <= 3) ? 4 : 2; }
 
-template <int NB, int MB, int WAVES, int KS, bool NORM>
-__global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAVES)) void conv_halo_dma_kernel(
+template <int NB, int MB, int WAVES, int KS, bool NORM, bool DUAL = false>
+__global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 / WAVES)) void conv_halo_dma_kernel(
     const ConvProblem p) {
   static_assert(KS == 2 || KS == 3, "3x3 taps, or 2x2 phase taps");
   constexpr int SPS = KS * KS;
@@ -938,8 +938,8 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<MB, KS>() * 4 / WAV
         const int r = wave - 2 * PCAP;
         st = ((r / WCAP == 0) ? (char*)wslot(I0{}) : (char*)wslot(I1{})) + (r % WCAP) * SB;
       }
-      conv_epilogue_staged<NB, MB, NORM, NBP1>(p, acc, ph, tc.w0, tc.tf, tc.n0, pa, pb, lane, st);
-    } else {
+      conv_epilogue_staged<NB, MB, NORM, NBP1, DUAL>(p, acc, ph, tc.w0, tc.tf, tc.n0, pa, pb, lane, st);
+    } else if constexpr (!DUAL) {  // (the launcher stages every dual-store launch)
       int pw[MB];
       bool pv[MB];
 #pragma unroll
@@ -1018,32 +1018,44 @@ struct ConfigEntry {
   int wgs_per_cu;  // workgroups resident per CU (a DMA kernel then walks several tiles each)
   void (*kernel)(const ConvProblem);       // plain epilogue (bias, residual, fp32 planes)
   void (*kernel_norm)(const ConvProblem);  // fused RMS norm (+ SiLU) epilogue
+  void (*kernel_dual)(const ConvProblem);  // fused norm + the pre-norm value stored too (or null)
 };
 
 #define WVD_CONV_CONFIG(NB, MB, W) \
   { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, 0, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
-    conv_mfma_kernel<NB, MB, W, true> }
+    conv_mfma_kernel<NB, MB, W, true>, nullptr }
 // 3x3-tap halo convs order tiles time-fastest (measured 2-8% faster than frame-major on every
 // 3x3x3 layer: fewer input re-reads past L2); the phase convs have no temporal taps.
 #define WVD_HALO_CONFIG(NB, MB, W) \
   { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 0, 0, conv_halo_kernel<NB, MB, W, 3, false>, \
-    conv_halo_kernel<NB, MB, W, 3, true> }
+    conv_halo_kernel<NB, MB, W, 3, true>, nullptr }
 #define WVD_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, dma_waves_per_simd<MB, 3>() * 4 / W, \
+  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, dma_waves_per_simd<NB, MB, 3>() * 4 / W, \
     conv_halo_dma_kernel<NB, MB, W, 3, false>, \
-    conv_halo_dma_kernel<NB, MB, W, 3, true> }
+    conv_halo_dma_kernel<NB, MB, W, 3, true>, nullptr }
+// (the one-tile widths a residual block's conv2 takes at 96 and 192 channels: also the dual store)
+#define WVD_HALO_DMA_DUAL_CONFIG(NB, MB, W) \
+  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, dma_waves_per_simd<NB, MB, 3>() * 4 / W, \
+    conv_halo_dma_kernel<NB, MB, W, 3, false>, \
+    conv_halo_dma_kernel<NB, MB, W, 3, true>, conv_halo_dma_kernel<NB, MB, W, 3, true, true> }
 // (no fused-norm instantiation: the norm needs every channel in one tile, and the 96- and 192-wide
 // tiles cover those widths)
 #define WVD_HALO_DMA_PLAIN_CONFIG(NB, MB, W) \
-  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, dma_waves_per_simd<MB, 3>() * 4 / W, \
-    conv_halo_dma_kernel<NB, MB, W, 3, false>, nullptr }
+  { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, dma_waves_per_simd<NB, MB, 3>() * 4 / W, \
+    conv_halo_dma_kernel<NB, MB, W, 3, false>, nullptr, nullptr }
 #define WVD_PHASE_HALO_DMA_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<MB, 2>() * 4 / W, \
+  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<NB, MB, 2>() * 4 / W, \
     conv_halo_dma_kernel<NB, MB, W, 2, false>, \
-    conv_halo_dma_kernel<NB, MB, W, 2, true> }
+    conv_halo_dma_kernel<NB, MB, W, 2, true>, nullptr }
+// (192 channels in one tile, for a fused norm of that width with the pre-norm value stored too:
+// the x2 upsample that feeds a 192-channel residual block)
+#define WVD_PHASE_HALO_DMA_DUAL_CONFIG(NB, MB, W) \
+  { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<NB, MB, 2>() * 4 / W, \
+    conv_halo_dma_kernel<NB, MB, W, 2, false>, \
+    conv_halo_dma_kernel<NB, MB, W, 2, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, true> }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
   { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
-    conv_halo_kernel<NB, MB, W, 2, true> }
+    conv_halo_kernel<NB, MB, W, 2, true>, nullptr }
 
 // Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
 // bigger per-wave tiles at one wave per SIMD: the second wave issues matrix work while the first
@@ -1071,16 +1083,18 @@ enum ConfigId {
   LIN_N4_W8,       // 128 x 256, 2 waves/SIMD: channel counts that are multiples of 128, not of 96
   HALO_DMA_N3_W4,  // 96 x (8 rows x 32 columns) on 4 waves in 80 KB: two workgroups per CU
   HALO_DMA_N4_W8,  // 128 x (16 rows x 32 columns): channel counts that are multiples of 128, not of 96
+  PHASE_DMA_N6_M1_W8,  // x2 upsampling phases: 192 x (8 rows x 32 columns), one row per wave, 112 KB
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
     WVD_CONV_CONFIG(6, 1, 8),       WVD_CONV_CONFIG(6, 1, 4),       WVD_CONV_CONFIG(3, 1, 8),
     WVD_CONV_CONFIG(3, 1, 4),       WVD_CONV_CONFIG(1, 4, 4),       WVD_CONV_CONFIG(3, 2, 8),
     WVD_HALO_CONFIG(6, 1, 8),       WVD_HALO_CONFIG(3, 2, 8),       WVD_HALO_CONFIG(3, 2, 4),
-    WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_CONFIG(3, 2, 8),
-    WVD_HALO_DMA_CONFIG(6, 1, 8),    WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
+    WVD_PHASE_HALO_CONFIG(6, 1, 8), WVD_PHASE_HALO_CONFIG(3, 2, 8), WVD_HALO_DMA_DUAL_CONFIG(3, 2, 8),
+    WVD_HALO_DMA_DUAL_CONFIG(6, 1, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),    WVD_HALO_DMA_CONFIG(1, 2, 8),
     WVD_CONV_CONFIG(4, 1, 8),           WVD_HALO_DMA_CONFIG(3, 2, 4),    WVD_HALO_DMA_PLAIN_CONFIG(4, 2, 8),
+    WVD_PHASE_HALO_DMA_DUAL_CONFIG(6, 1, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -1112,8 +1126,9 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   const int64_t cus = 256;
   const int64_t T = p.T, H = p.H, W = p.W;
   const int Npad = p.Npad, phases = p.phases;
-  if (Npad <= 32 && phases == 1 && p.kh == 3 && p.kw == 3) return HALO_DMA_N1_W8;
-  if (Npad <= 32) return LIN_N1_M4_W4;
+  // (a dual store of at most 32 channels takes the 96-wide tile below, which has that epilogue)
+  if (Npad <= 32 && phases == 1 && p.kh == 3 && p.kw == 3 && !p.y_pre) return HALO_DMA_N1_W8;
+  if (Npad <= 32 && !(phases == 1 && p.kh == 3 && p.kw == 3)) return LIN_N1_M4_W4;
   if (phases == 1 && p.kh == 3 && p.kw == 3) {
     if (one_n_tile) return Npad > 96 ? HALO_DMA_N6_W8 : HALO_DMA_N3_W8;
     // a grid of 96-wide tiles that leaves CUs idle (the 4-frame 44x78 level: 144 tiles) takes
@@ -1140,6 +1155,8 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   // (5-9 % over two rows per wave on 4 waves), two rows per wave at 384 (8 %).
   if (phases == 4 && p.kh == 2 && p.kw == 2 && (Npad <= 96 || (!one_n_tile && Npad <= 192)))
     return PHASE_DMA_N3_M1_W8;
+  // a fused norm over 97-192 channels: all of them in one 192-wide phase tile
+  if (phases == 4 && p.kh == 2 && p.kw == 2 && one_n_tile && Npad <= 192) return PHASE_DMA_N6_M1_W8;
   if (phases == 4 && p.kh == 2 && p.kw == 2 && !one_n_tile) return PHASE_DMA_N3_W4;
   const auto fills = [&](int id) { return blocks_for(kConfigs[id], T, H, W, Npad) * phases >= cus; };
   const int n96 = (p.ntaps >= 9 && fills(LIN_N3_M2_W8)) ? LIN_N3_M2_W8 : LIN_N3_W8;
@@ -1178,6 +1195,7 @@ bool conv_config_fits(const ConvProblem& p, int id) {
   if (c.halo == 3 && !(p.phases == 1 && p.kh == 3 && p.kw == 3)) return false;
   if (c.halo == 2 && !(p.phases == 4 && p.kh == 2 && p.kw == 2)) return false;
   if (p.norm_gamma && (c.nb * 32 < p.Npad || !c.kernel_norm)) return false;
+  if (p.y_pre && (!p.norm_gamma || !c.kernel_dual)) return false;
   return true;
 }
 
@@ -1187,7 +1205,9 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   if (p.T == 0 || HW == 0) return hipSuccess;
   // one frame is addressed with 32-bit byte offsets
   if (HW * p.Ci * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  if (p.norm_gamma && (!conv_can_fuse_norm(p.N, p.bias, p.norm_gamma) || p.res || p.y_f32 || p.nsplit != p.N))
+  // (a fused norm takes a residual only with the dual store, which adds it before the statistics)
+  if (p.norm_gamma && (!conv_can_fuse_norm(p.N, p.bias, p.norm_gamma) || (p.res && !p.y_pre) || p.y_f32 ||
+                       p.nsplit != p.N))
     return hipErrorInvalidValue;
   int id = choose_config(p, p.norm_gamma != nullptr);
   if (force_config >= 0) {
@@ -1196,6 +1216,7 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   }
   const ConfigEntry& c = kConfigs[id];
   if (p.norm_gamma && !c.kernel_norm) return hipErrorNotSupported;
+  if (p.y_pre && (!p.norm_gamma || !c.kernel_dual)) return hipErrorNotSupported;
   const int64_t blocks = blocks_for(c, p.T, p.H, p.W, p.Npad);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (config_id) *config_id = id;
@@ -1206,7 +1227,8 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   const bool plain_map = p.phases == 1 && p.hmul == 1 && p.wmul == 1 && p.Ho == p.H && p.Wo == p.W;
   const bool lin_staged = c.halo == 0 && c.mb == 1 && plain_map && !p.norm_gamma;
   q.staged = (c.staged || lin_staged) && !p.y_f32 && p.N % 8 == 0 && p.nsplit % 8 == 0 &&
-             ((uintptr_t)p.y & 15) == 0 && ((uintptr_t)p.res & 15) == 0;
+             ((uintptr_t)p.y & 15) == 0 && ((uintptr_t)p.res & 15) == 0 && ((uintptr_t)p.y_pre & 15) == 0;
+  if (p.y_pre && !q.staged) return hipErrorNotSupported;  // the dual store exists staged only
   int64_t gx = c.phase_in_x ? blocks * p.phases : blocks;
   if (c.wgs_per_cu) {
     // DMA kernels: a multiple of 8 workgroups (XCD ranges); with persistent tiles no more than
@@ -1218,7 +1240,8 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
     }
   }
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(p.norm_gamma ? c.kernel_norm : c.kernel, dim3((unsigned)gx, 1, c.phase_in_x ? 1 : p.phases),
+  hipLaunchKernelGGL(p.y_pre ? c.kernel_dual : (p.norm_gamma ? c.kernel_norm : c.kernel),
+                     dim3((unsigned)gx, 1, c.phase_in_x ? 1 : p.phases),
                      dim3(c.waves * 64), 0, s, q);
   return hipGetLastError();
 }

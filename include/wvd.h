@@ -334,6 +334,16 @@ wvd_status wvd_conv_force_config(int config);
  * the default (one workgroup per resident slot). Results are the same for any n. WVD_ERR_ARG for
  * n < 0. Process-wide; not for use while another thread launches. */
 wvd_status wvd_conv_max_workgroups(int n);
+/* Tuning: with on != 0 (the default), wvd_decode_chunk applies each residual block's norm1 +
+ * SiLU in the epilogue of the conv that produces its input, where one workgroup holds every
+ * channel (the previous block's conv2 up to 192 channels, an x2 upsample of 97-192 channels not
+ * followed by a DupUp3D add): that conv stores both its output and the next block's activated
+ * input, and the standalone norm pass goes (the page's merge of the next conv's norm into the
+ * producing epilogue, "The merges"). With on == 0 every norm1 is a separate pass. The two videos
+ * differ by rounding only (the fused norm reads the unrounded fp32 output); either way decodes
+ * are bitwise independent of the pass size. Process-wide; not for use while another thread
+ * decodes. */
+wvd_status wvd_decode_fuse_norm1(int on);
 /* Measurement support: copy `bytes` (a multiple of 16; src and dst 16-byte aligned, device
  * memory, not overlapping) with the convolution kernels' own load path: buffer loads that write
  * 16 bytes per lane straight into LDS, read back and stored with 16-byte global stores. The

@@ -569,6 +569,40 @@ def test_small_decoder_per_level_pass_sizes_same_bits(rule):
         assert torch.equal(v, base), (fpp, early)
 
 
+# widths that reach every place the norm1 fusion applies: conv2 of up to 96 and of 97-192
+# channels, and an x2 upsample of 128 channels (no time step) feeding a residual block
+FUSE_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 160, 128, 96))
+
+
+@pytest.mark.parametrize("rule", [True, False])
+def test_decoder_with_norm1_fused_matches_oracle_and_is_pass_size_invariant(rule):
+    """wvd_decode_fuse_norm1: each block's norm1 + SiLU in the producing conv's epilogue (the
+    previous conv2's, or the x2 upsample's, which then stores two outputs; the default) or a
+    separate pass. Both against the oracle, each with the same bits for every pass size and
+    per-level sub-passes, and within rounding of each other."""
+    hw = (5, 7)
+    z, params = wl.decoder_weights(FUSE_GPU, seed=52, latent_frames=3, latent_hw=hw)
+    ref = oracle.decode(z[0], oracle.as_numpy_params(params), FUSE_GPU, frames_per_pass=3, first_frame_rule=rule)
+    dec = _gpu_decoder(FUSE_GPU, params, hw)
+    zd = z.to(torch.bfloat16).cuda()
+    got = {}
+    try:
+        for fused in (False, True):
+            wvd.decode_fuse_norm1(fused)
+            videos = [dec.decode(zd, frames_per_pass=f, first_frame_rule=rule).clone() for f in (3, 1, 2)]
+            videos.append(dec.decode(zd, frames_per_pass=1, first_frame_rule=rule, early_frames_per_pass=3))
+            torch.cuda.synchronize()
+            for v in videos[1:]:
+                assert torch.equal(v, videos[0]), fused
+            got[fused] = videos[0][0].float().cpu().numpy()
+            log(f"norm1 {'fused' if fused else 'separate'} rule={rule}: psnr {psnr(got[fused], ref):.2f} dB vs oracle")
+            assert psnr(got[fused], ref) >= 55.0
+    finally:
+        wvd.decode_fuse_norm1(True)
+    assert not np.array_equal(got[True], got[False])  # the fused path did run
+    assert psnr(got[True], got[False]) >= 55.0
+
+
 WIDE_TAIL_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 32, 224))
 
 
