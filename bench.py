@@ -383,6 +383,22 @@ def bench_winograd(reps):
             "ms_per_call": None, "levels": out}
 
 
+def conv_by_shape(launches, steps):
+    """Conv launches grouped by configuration and problem shape: launches per step, average us,
+    TFLOP/s (the kernel time of each layer of the decode)."""
+    groups = {}
+    for name, ms, fl, sh in launches:
+        key = (f"{name} T{sh['T']} {sh['H']}x{sh['W']} {sh['Ci']}->{sh['N']} taps{sh['taps']} ph{sh['phases']}"
+               + (" +res" if sh.get("res") else ""))
+        g = groups.setdefault(key, [0, 0.0, 0.0])
+        g[0] += 1
+        g[1] += ms
+        g[2] += fl
+    return {k: {"per_step": v[0] // steps, "avg_us": round(1000.0 * v[1] / v[0], 1),
+                "tflops": round(v[2] / (v[1] * 1e-3) / 1e12, 1)}
+            for k, v in sorted(groups.items(), key=lambda kv: -kv[1][1])}
+
+
 def conv_launch_bytes(sh) -> float:
     """Algorithmic HBM bytes of one conv launch: the input frames it reads (with up to kt - 1 history
     frames) once, the packed weights once, the bf16 output once, the residual once when it adds
@@ -554,6 +570,7 @@ def main():
                  "timed_tflop_per_step": round(conv_flops / args.steps / 1e12, 3),
                  "per_config": {k: {"launches": v[0], "ms": round(v[1], 3), "tflops": round(v[2] / (v[1] * 1e-3) / 1e12, 2)}
                                 for k, v in per_cfg.items()}},
+        "conv_by_shape": conv_by_shape(launches, args.steps),
         "epilogues": {k: {"launches_per_step": v[0] // args.steps, "avg_launch_us": round(1000.0 * v[1] / v[0], 2),
                           "gbs": round(v[2] / (v[1] * 1e-3) / 1e9, 1),
                           "frac_of_hbm": round(v[2] / (v[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

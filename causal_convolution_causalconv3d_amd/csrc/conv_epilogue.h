@@ -178,6 +178,15 @@ struct StagedShape {
   static_assert((32 * CHP) % 64 == 0, "pass shape");
 };
 
+// A 16-byte store marked non-temporal: the conv outputs are streamed out (a layer's output is
+// read back by the next kernel, long after the L2 has turned over), so they should not displace
+// the input patches and weights the other tiles are still reading from L2. (Measured on the
+// decode: 1-2 % faster overall, 8 % on the 192-channel x2 phase conv with its two outputs.)
+__device__ __forceinline__ void store_stream16(bf16_t* dst, uint4 v) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, v), (u32x4v*)dst);
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -310,7 +319,7 @@ __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, float
           const int j = i * 64 + lane, q = j / S::CHP, c = j - (j / S::CHP) * S::CHP;
           const int n = cb + c * 8, w = w0 + q;
           const uint4 o = *(const uint4*)(stage + q * S::PS + c * 16);
-          if (w < p.W && n < p.N) *(uint4*)(p.y_pre + out_index(p, tf, n, orow, p.wmul * w + pb)) = o;
+          if (w < p.W && n < p.N) store_stream16(p.y_pre + out_index(p, tf, n, orow, p.wmul * w + pb), o);
         }
         wave_lds_sync();
       }
@@ -372,7 +381,7 @@ __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, float
         const int j = i * 64 + lane, q = j / S::CHP, c = j - (j / S::CHP) * S::CHP;
         const int n = cb + c * 8, w = w0 + q;
         const uint4 o = *(const uint4*)(stage + q * S::PS + c * 16);
-        if (w < p.W && n < p.N) *(uint4*)((bf16_t*)p.y + out_index(p, tf, n, orow, p.wmul * w + pb)) = o;
+        if (w < p.W && n < p.N) store_stream16((bf16_t*)p.y + out_index(p, tf, n, orow, p.wmul * w + pb), o);
       }
       wave_lds_sync();
     }
