@@ -426,6 +426,10 @@ def main():
                          "TI2V-5B topology (1024/1024/512/256, mid attention, DupUp3D, 12-channel head, "
                          "unpatchify, clamp) with random weights, no CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--head", choices=("fused", "separate"), default="separate",
+                    help="the last x2 upsample, norm_out + SiLU and the head as one kernel where the decoder allows "
+                         "it (less memory, slower) or through the activated tensor (the default; "
+                         "wvd_decode_fuse_head)")
     ap.add_argument("--norm1", choices=("fused", "separate"), default="fused",
                     help="each residual block's norm1 + SiLU in the producing conv's epilogue (the default) or as "
                          "a separate pass (wvd_decode_fuse_norm1)")
@@ -473,6 +477,7 @@ def main():
     real = args.topology == "real"
     spec = wl.REAL_DECODER if real else wl.FULL_DECODER
     wvd.decode_fuse_norm1(args.norm1 == "fused")
+    wvd.decode_fuse_head(args.head == "fused")
     _, params = wl.decoder_weights(spec, seed=4, latent_frames=4)
     z = wl.streaming_latents(seed=5, latent_frames=args.latent_frames).to(torch.bfloat16).cuda()
     dec = wvd.Decoder(wvd.desc_from_spec(spec), params)
@@ -554,7 +559,7 @@ def main():
                                   "384/384/192/96 (2 resblocks each, time x2 on the first two), random Kaiming weights"),
                    "topology": args.topology,
                    "latent_frames": args.latent_frames, "video_frames": F, "frames_per_pass": fpp,
-                   "early_frames_per_pass": early, "norm1": args.norm1,
+                   "early_frames_per_pass": early, "norm1": args.norm1, "head": args.head,
                    "global_batch": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),

@@ -119,6 +119,7 @@ def lib():
             "wvd_conv_max_workgroups": ([ctypes.c_int], ctypes.c_int),
             "wvd_calib_dma_copy": ([_P, _P, ctypes.c_size_t, _P], ctypes.c_int),
             "wvd_decode_fuse_norm1": ([ctypes.c_int], ctypes.c_int),
+            "wvd_decode_fuse_head": ([ctypes.c_int], ctypes.c_int),
             "wvd_winograd_packed_bytes": ([ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
             "wvd_winograd_pack": ([_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P], ctypes.c_int),
             "wvd_winograd_workspace_bytes": ([ctypes.c_int] * 6, ctypes.c_size_t),
@@ -147,7 +148,7 @@ def exported_symbols() -> Sequence[str]:
             "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read",
             "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem", "wvd_conv_max_workgroups",
             "wvd_calib_dma_copy", "wvd_winograd_packed_bytes", "wvd_winograd_pack", "wvd_winograd_workspace_bytes",
-            "wvd_causal_conv3d_winograd", "wvd_decode_fuse_norm1"]
+            "wvd_causal_conv3d_winograd", "wvd_decode_fuse_norm1", "wvd_decode_fuse_head"]
 
 
 def _check(status: int):
@@ -542,6 +543,13 @@ def decode_fuse_norm1(on: bool):
     """wvd_decode_fuse_norm1: apply each residual block's norm1 + SiLU in the producing conv's
     epilogue (two outputs; the default) or, with False, as a separate pass."""
     _check(lib().wvd_decode_fuse_norm1(int(on)))
+
+
+def decode_fuse_head(on: bool):
+    """wvd_decode_fuse_head: run the last x2 upsample, norm_out + SiLU and the head as one kernel
+    where the decoder allows it (less memory, slower) or, with False (the default), through the
+    activated tensor. Caches and workspaces follow the switch: make them after setting it."""
+    _check(lib().wvd_decode_fuse_head(int(on)))
 
 
 def calib_dma_copy(src: torch.Tensor, dst: torch.Tensor):

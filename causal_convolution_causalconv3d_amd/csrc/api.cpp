@@ -903,6 +903,7 @@ struct StagePlan {
 struct Slot {
   int level, c;
   size_t offset, frame_bytes;
+  size_t alloc;  // bytes in the cache: two halves of two frames, or (the fused tail's carry) two frames
 };
 
 struct Plan {
@@ -915,6 +916,7 @@ struct Plan {
   int levels;      // spatial x2 steps in all: the head's level
   int head_plain;  // conv_out as a plain 3x3x3 conv, then unpatchify (+ clamp) into the video
   int norm_out, out_w, out_b, out_slot;
+  int tail_kernel;  // the fused tail kernel runs the last upsample and the head (out_slot: its carry)
   std::vector<Slot> slots;
   size_t packed_bytes, cache_bytes;
 };
@@ -926,6 +928,20 @@ int desc_levels(const wvd_decoder_desc* d) {
   int l = 0;
   for (int s = 0; s < d->n_stages; ++s) l += d->stage_no_spatial[s] ? 0 : 1;
   return l;
+}
+
+std::atomic<int> g_fuse_head{0};  // wvd_decode_fuse_head (off: measured slower, see wvd.h)
+
+// Whether the decode runs the fused tail kernel: the last stage is a spatial x2 upsample whose
+// epilogue can apply norm_out + SiLU (no time step, no DupUp3D), at 65-96 channels, and the head
+// is conv_out to at most 3 colours (no unpatchify or clamp). Its output head then never reads an
+// activated tensor: the head's temporal taps are carried between passes as partial sums.
+bool tail_kernel_used(const wvd_decoder_desc* d) {
+  const int L = d->n_stages;
+  if (L < 1 || !g_fuse_head.load() || d->patch >= 2 || d->clamp) return false;
+  const int c = d->stage_channels[L - 1];
+  return !d->stage_no_spatial[L - 1] && !d->stage_dup[L - 1] && !d->stage_temporal[L - 1] &&
+         tail_kernel_supported(c, (int)round_up(c, 32), d->out_channels);
 }
 
 wvd_status check_desc(const wvd_decoder_desc* d) {
@@ -986,6 +1002,7 @@ int add_slot(Plan& p, const wvd_decoder_desc* d, int level, int c) {
   s.level = level;
   s.c = c;
   s.frame_bytes = (size_t)(d->latent_h << level) * (size_t)(d->latent_w << level) * c * 2;
+  s.alloc = 4 * s.frame_bytes;
   s.offset = 0;
   p.slots.push_back(s);
   return (int)p.slots.size() - 1;
@@ -1068,6 +1085,13 @@ Plan make_plan(const wvd_decoder_desc* d) {
   p.out_w = add_param(p, "conv_out.weight", p.head_plain ? K_CONV3 : K_HEAD, d->out_channels, c);
   p.out_b = add_param(p, "conv_out.bias", K_BIAS, d->out_channels, 0);
   p.out_slot = add_slot(p, d, p.levels, c);
+  p.tail_kernel = tail_kernel_used(d) ? 1 : 0;
+  if (p.tail_kernel) {
+    // the head's carry: the partial sums of the next two output frames, [2][3][H][W] fp32
+    Slot& s = p.slots[p.out_slot];
+    s.frame_bytes = (size_t)(d->latent_h << p.levels) * (size_t)(d->latent_w << p.levels) * 3 * 4;
+    s.alloc = 2 * s.frame_bytes;
+  }
   size_t off = 0;
   for (auto& q : p.params) {
     q.offset = off;
@@ -1077,7 +1101,7 @@ Plan make_plan(const wvd_decoder_desc* d) {
   off = 0;
   for (auto& s : p.slots) {
     s.offset = off;
-    off += (size_t)round_up((int64_t)(4 * s.frame_bytes), 256);  // two halves of two frames
+    off += (size_t)round_up((int64_t)s.alloc, 256);
   }
   p.cache_bytes = off;
   return p;
@@ -1226,7 +1250,9 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n, int64_t nh) {
   // the head's input: norm_out's output for the whole pass, or a fused tail's sub-pass, as many
   // frames as fit in what the activated buffer holds anyway (at least one)
   int64_t tail_frames = fh.video;
-  if (tail) {
+  if (tail && tail_kernel_used(d)) {
+    // the fused tail kernel: no activated tensor at all
+  } else if (tail) {
     const int64_t per_frame = hw(level) * c;
     tail_frames = std::min<int64_t>(fh.video, std::max<int64_t>(1, act / per_frame));
     act = std::max(act, tail_frames * per_frame);
@@ -1272,6 +1298,7 @@ WsLayout ws_layout(const wvd_decoder_desc* d, int64_t n, int64_t nh) {
 
 struct wvd_cache_s {
   uint64_t hash;
+  int tail_kernel;  // the plan's fused-tail mode when the cache was made (it sets the head slot's layout)
   char* storage;
   std::vector<int> valid;  // frames held per slot (right-aligned)
   std::vector<int> half;   // the slot half holding them
@@ -1360,6 +1387,7 @@ extern "C" wvd_status wvd_cache_init(const wvd_decoder_desc* d, void* storage, w
   wvd_cache c = new (std::nothrow) wvd_cache_s;
   if (!c) return fail(WVD_ERR_ARG, "out of host memory");
   c->hash = desc_hash(d);
+  c->tail_kernel = p.tail_kernel;
   c->storage = (char*)storage;
   c->valid.assign(p.slots.size(), 0);
   c->half.assign(p.slots.size(), 0);
@@ -1445,6 +1473,9 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
 
   hipStream_t s = (hipStream_t)stream;
   const Plan p = make_plan(d);
+  if (cache->tail_kernel != p.tail_kernel)
+    return fail(WVD_ERR_STATE, "the cache was made with the fused head %s (wvd_decode_fuse_head)",
+                cache->tail_kernel ? "on" : "off");
   const char* pk = (const char*)packed;
   auto W_ = [&](int idx) -> const void* { return pk + p.params[idx].offset; };
   auto F_ = [&](int idx) -> const float* { return (const float*)(pk + p.params[idx].offset); };
@@ -1771,6 +1802,38 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
     if (!tail_x) return run_head(fo);
     const StagePlan& st = p.stages[tail_stage];
     const int64_t Tall = T;
+    if (p.tail_kernel) {
+      // the fused tail kernel: the x2 upsample with norm_out + SiLU and the head in one launch
+      // over the pass; the head's temporal taps come in and go out as the partial sums of the
+      // two frames after each pass (the out slot)
+      const int slot = p.out_slot;
+      ConvProblem cp = plain_problem(tail_x, nullptr, (int)Tall, tail_h, tail_w, c, 0, W_(st.sw), c, 1, 1, 1, F_(st.sb),
+                                     nullptr, nullptr);
+      cp.norm_gamma = F_(p.norm_out);
+      cp.norm_eps = d->eps;
+      cp.norm_silu = 1;
+      cp.ntaps = 4;
+      cp.phases = 4;
+      cp.kh = 2;
+      cp.kw = 2;
+      cp.Ho = 2 * tail_h;
+      cp.Wo = 2 * tail_w;
+      cp.hmul = 2;
+      cp.wmul = 2;
+      cp.head_w = (const bf16_t*)W_(p.out_w);
+      cp.head_b = F_(p.out_b);
+      cp.head_co = d->out_channels;
+      cp.video = (bf16_t*)video->data;
+      cp.video_frames = video->t;
+      cp.video_fbase = (int)fo;
+      cp.carry = (float*)slot_ptr(slot);
+      cp.carry_valid = cache->valid[slot] > 0 ? 1 : 0;
+      const int64_t P_in = Tall * tail_h * tail_w;
+      WVD_TRY(run_conv(cp, s, conv_flops(P_in * 4, c, 4LL * c) + conv_flops(P_in * 4, d->out_channels, 27LL * c)));
+      cache->valid[slot] = (int)std::min<int64_t>(2, cache->valid[slot] + Tall);
+      tail_x = nullptr;
+      return WVD_OK;
+    }
     const size_t in_frame = (size_t)tail_h * tail_w * c;
     for (int64_t f0 = 0; f0 < Tall; f0 += wl.tail_frames) {
       const int64_t m = std::min<int64_t>(wl.tail_frames, Tall - f0);
@@ -1856,6 +1919,11 @@ extern "C" wvd_status wvd_conv_force_config(int config) {
 
 extern "C" wvd_status wvd_decode_fuse_norm1(int on) {
   g_fuse_norm1.store(on ? 1 : 0);
+  return WVD_OK;
+}
+
+extern "C" wvd_status wvd_decode_fuse_head(int on) {
+  g_fuse_head.store(on ? 1 : 0);
   return WVD_OK;
 }
 

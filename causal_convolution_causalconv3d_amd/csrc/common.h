@@ -115,6 +115,21 @@ struct ConvProblem {
   int time_tiles;  // set by the launcher: the halo kernel's tile order
   int staged;      // set by the launcher: store the output through LDS (see conv_epilogue_staged)
   CopyJob copy;    // side work (zero bytes: none)
+  // The fused tail (head_w set): this x2 phase conv with norm_out + SiLU in its epilogue feeds the
+  // output head (a causal 3x3x3 conv to head_co <= 3 colours) inside the same kernel, so the
+  // activated tensor never reaches memory. head_w: the head's packed weight [Npad][3][Cip] (row
+  // (j*3 + k)*4 + o, temporal tap, channel); head_b [head_co]; the video NCTHW bf16 with
+  // video_frames frames per colour plane, this pass starting at frame video_fbase; carry
+  // [2][3][2H][2W] fp32: the head's partial sums of the two frames after the pass (read when
+  // carry_valid, written at the end).
+  const bf16_t* head_w;
+  const float* head_b;
+  int head_co;
+  bf16_t* video;
+  int64_t video_frames;
+  int video_fbase;
+  float* carry;
+  int carry_valid;
 };
 
 // force_config >= 0 runs that configuration (hipErrorNotSupported when it cannot run p);
@@ -170,6 +185,9 @@ bool head_fused_supported(int Cip);
 // The input-stationary variant (each input frame read once per tile): Cip <= 96, Co <= 3; same
 // arguments and output.
 bool head_stream_supported(int Cip, int Co);
+// Whether the fused tail (ConvProblem::head_w) takes an upsample of N channels (padded Cip) with a
+// head of co colours: the 96-wide one-row phase tile, so 64 < N <= 96, N % 8 == 0, co <= 3.
+bool tail_kernel_supported(int N, int Cip, int co);
 // A device copy through the conv kernels' 16-byte buffer-load-to-LDS path (counter calibration).
 hipError_t launch_dma_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 // Winograd F(2x2, 3x3) steps (winograd.hip): the weight transform into 16 packed (3,1,1) weights,

@@ -593,15 +593,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Wait until this wave's LDS operations (the fused tail's accumulations, which return nothing, so
+// the compiler waits for none of them) are done: lgkmcnt 0 only.
+__device__ __forceinline__ void lds_ops_done() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Waves per SIMD a DMA kernel is compiled for: two, or four for the one-row phase tiles (their
 // light main loop leaves the SIMDs to the epilogue's vector work, which other waves then overlap).
 template <int NB, int MB, int KS>
 constexpr int dma_waves_per_simd() { return (KS == 2 && MB == 1 && NB <= 3) ? 4 : 2; }
 
-template <int NB, int MB, int WAVES, int KS, bool NORM, bool DUAL = false>
-__global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 / WAVES)) void conv_halo_dma_kernel(
+template <int NB, int MB, int WAVES, int KS, bool NORM, bool DUAL = false, bool TAIL = false>
+__global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, KS>() * 4 / WAVES)) void conv_halo_dma_kernel(
     const ConvProblem p) {
   static_assert(KS == 2 || KS == 3, "3x3 taps, or 2x2 phase taps");
+  static_assert(!TAIL || (KS == 2 && NB == 3 && MB == 1 && WAVES == 8 && NORM && !DUAL), "the fused tail's tile");
   constexpr int SPS = KS * KS;
   // weight fetch distance D (steps ahead), slots NWS (> D, and k mod NWS a compile-time
   // function of the stage parity and the tap), barrier wait window WW = D - 2 steps (must not
@@ -642,6 +647,14 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
   __shared__ __attribute__((aligned(16))) bf16_t lds_w5[WBYTES / 2];
   __shared__ __attribute__((aligned(16))) bf16_t lds_w6[NWS > 6 ? WBYTES / 2 : 8];
   __shared__ __attribute__((aligned(16))) bf16_t lds_w7[NWS > 6 ? WBYTES / 2 : 8];
+  // The fused tail (TAIL): the head's weights as the first operand of the Z product (row m a
+  // tap-colour of one temporal tap, the 96 channels in the activation operand's order, rows of
+  // 104 elements: 16-byte reads of 32 rows are conflict free) and the frame's output accumulator
+  // (the 18 x 66 output pixels around the block's 16 x 64 activated positions; per pixel and
+  // colour a 16-byte group of the three temporal taps' sums and a pad).
+  constexpr int TZR = 104, TCR = 2 * TR + 2, TCC = 66, TCP = 12;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_hz[TAIL ? 96 * TZR : 8];
+  __shared__ __attribute__((aligned(16))) float lds_tc[TAIL ? TCR * TCC * TCP : 4];
   auto wslot = [&](auto I) -> bf16_t* {
     constexpr int i = decltype(I)::value;
     static_assert(i >= 0 && i < NWS, "slot");
@@ -671,8 +684,10 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
   const int l32 = lane & 31;
 
   // Walking several tiles per workgroup keeps the tile loop's state live through the epilogue,
-  // which the fused-norm epilogue cannot afford without spilling; those kernels take one tile.
-  constexpr bool PERSIST = !NORM;
+  // which the fused-norm epilogue cannot afford without spilling at four waves per SIMD; those
+  // kernels take one tile. The fused tail (one workgroup per CU, two waves per SIMD) walks the
+  // frames and phases of its block.
+  constexpr bool PERSIST = !NORM || TAIL;
   // Tiles. The x2 phase convs deal their four phases as the fastest index: the four tiles of a
   // position run side by side, share its input patch in L2 and write neighbouring outputs close
   // in time. Each XCD owns a contiguous range of tiles (workgroup b runs on XCD b % 8); within
@@ -689,7 +704,24 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3, G8 = gridDim.x >> 3;
   const int q8 = total >> 3, r8 = total & 7;
   const int xs = xcd * q8 + (xcd < r8 ? xcd : r8), xl = q8 + (xcd < r8 ? 1 : 0);
-  if (local >= xl) {  // no tile for this workgroup (uniform)
+  // The fused tail: workgroup -> a block of TR input rows x 32 columns at input row
+  // -1 + k (TR - 1), column -1 + m 31 (neighbouring blocks share a row or column: the head's
+  // 3x3 stencil needs the activated positions around its output tile, the block's 2 TR x 64
+  // positions less a one-pixel border), blocks dealt in contiguous ranges per XCD; its tiles are
+  // (frame, phase) in order. Otherwise a strided walk over the XCD's tile range.
+  int tb_h0 = 0, tb_w0 = 0;
+  int it_first = local, it_step = G8, it_end = xl;
+  if constexpr (TAIL) {
+    const int nbr = (2 * p.H + 2 * TR - 2) / (2 * TR - 2), nbc = (2 * p.W + 62) / 62;
+    const int nblk = nbr * nbc, per = (nblk + 7) >> 3;
+    const int blk = xcd * per + local;
+    if (blk >= nblk) return;  // (uniform)
+    tb_h0 = -1 + (blk / nbc) * (TR - 1);
+    tb_w0 = -1 + (blk - (blk / nbc) * nbc) * 31;
+    it_first = 0;
+    it_step = 1;
+    it_end = 4 * p.T;
+  } else if (local >= xl) {  // no tile for this workgroup (uniform)
     run_copy_share(p.copy);
     return;
   }
@@ -697,6 +729,7 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
     int tf, h0, w0, n0, phase;
   };
   auto decode = [&](int it) -> Tile {
+    if constexpr (TAIL) return {it >> 2, tb_h0, tb_w0, 0, it & 3};
     const int lin_p = xs + it;
     const int phase = lin_p % NPH, lin = lin_p / NPH;
     const int mt = lin / numN, nt = lin - (lin / numN) * numN;
@@ -768,10 +801,10 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
     return (c.i + 1 == p.kt) ? stage_at(c.chunk + 1, 0, c.nt) : stage_at(c.chunk, c.i + 1, c.nt);
   };
 
-  int it = local;                    // the current tile (index in the XCD range)
-  bool more = PERSIST && it + G8 < xl;  // whether there is a next tile
+  int it = it_first;                            // the current tile
+  bool more = PERSIST && it + it_step < it_end;  // whether there is a next tile
   Tile tc = decode(it);
-  Tile tn = more ? decode(it + G8) : tc;
+  Tile tn = more ? decode(it + it_step) : tc;
   __amdgpu_buffer_rsrc_t rs_cur = weight_rsrc(tc), rs_nxt = weight_rsrc(tn);
 
   // fetch a stage's patch (of the current or the next tile) into buffer BUF (live == false: zeros)
@@ -826,6 +859,51 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[nb]),
                                                               __builtin_bit_cast(bf16x8, a[mb]), acc[nb][mb], 0, 0, 0);
   };
+
+  // The fused tail's output pixels of this thread: px = tid + 512 u of the block's
+  // (2 TR - 2) x 62 output tile (video row 2 tb_h0 + 1 + px / 62, column 2 tb_w0 + 1 + px % 62),
+  // with the partial sums of the next two output frames (their temporal tap 0 and 1 terms).
+  constexpr int TOR = 2 * TR - 2, TOC = 62;
+  float to0[2][3], to1[2][3];
+  auto tail_pixel = [&](int u, int& Yo, int& Xo) -> bool {
+    const int px = tid + WAVES * 64 * u;
+    const int orow = px / TOC, ocol = px - (px / TOC) * TOC;
+    Yo = 2 * tb_h0 + 1 + orow;
+    Xo = 2 * tb_w0 + 1 + ocol;
+    return (px < TOR * TOC) & (Yo >= 0) & (Yo < 2 * p.H) & (Xo >= 0) & (Xo < 2 * p.W);
+  };
+  if constexpr (TAIL) {
+    // Z product operand: row m = 32 bz + r holds temporal tap bz of tap-colour (jk, o) where,
+    // with ri = (r / 8) * 4 + r % 4 the accumulator register and hf = (r / 4) % 2 the lane half
+    // that hold row r, (jk, o) = (ri, hf) for ri < 9 and (2 (ri - 9) + hf, 2) for 9 <= ri < 14
+    // (every lane then adds whole registers per spatial tap); its 96 channels in the order the
+    // activation operand holds them: K16 chunk q, half h2, element i8 is channel
+    // (q / 2) * 32 + (2 (q % 2) + i8 / 4) * 8 + h2 * 4 + i8 % 4.
+    for (int idx = tid; idx < 96 * 96; idx += WAVES * 64) {
+      const int m = idx / 96, kk = idx - (idx / 96) * 96;
+      const int bz = m >> 5, r = m & 31;
+      const int ri = (r >> 3) * 4 + (r & 3), hf = (r >> 2) & 1;
+      const int jk = ri < 9 ? ri : 2 * (ri - 9) + hf, o = ri < 9 ? hf : 2;
+      const int q = kk >> 4, h2 = (kk >> 3) & 1, i8 = kk & 7;
+      const int c = (q >> 1) * 32 + (2 * (q & 1) + (i8 >> 2)) * 8 + h2 * 4 + (i8 & 3);
+      bf16_t v = 0;
+      if (ri < 14 && jk < 9 && o < p.head_co && c < p.N) v = p.head_w[((int64_t)(jk * 4 + o) * 3 + bz) * p.Cip + c];
+      lds_hz[m * TZR + kk] = v;
+    }
+    for (int idx = tid; idx < TCR * TCC * TCP; idx += WAVES * 64) lds_tc[idx] = 0.0f;
+    const int64_t plane = (int64_t)(2 * p.H) * (2 * p.W);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int Yo, Xo;
+      const bool own = tail_pixel(u, Yo, Xo) && p.carry_valid;
+      const int64_t at = (int64_t)Yo * (2 * p.W) + Xo;
+#pragma unroll
+      for (int o = 0; o < 3; ++o) {
+        to0[u][o] = own ? p.carry[o * plane + at] : 0.0f;
+        to1[u][o] = own ? p.carry[(3 + o) * plane + at] : 0.0f;
+      }
+    }
+  }
 
   // prologue: the first tile's first stage (patch and steps 0 .. D - 1, all in stage 0)
   patch_offsets(tc);
@@ -952,6 +1030,162 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
     run_copy_share(p.copy);
     return;
   }
+  // The fused tail's epilogue of one phase tile: norm_out + SiLU of the accumulators (the plain
+  // fused-norm arithmetic) into bf16 operands, positions outside the frame zero (the head's
+  // padding); Z = head weights x activations (81 tap-colour rows of the three temporal taps:
+  // three 32-row blocks, K = 96); then every Z value is added into the frame's output
+  // accumulator at the pixel its spatial tap (j, k) serves, (Y - j + 1, X - k + 1), by plain
+  // reads, adds and writes of 16-byte groups (colour o: the three temporal taps). No two of them
+  // meet in one batch of reads and writes: within a wave, spatial taps k = 0 and 2 of
+  // neighbouring lanes meet at one pixel and run in two batches, in order (a wave's LDS
+  // operations complete in order); rows j = 0 and 2 of neighbouring waves meet and are separated
+  // by a barrier (j = 1 meets neither); the phases of a frame are separated by the main loop's
+  // barriers. So every sum is taken in one fixed order.
+  auto tail_epilogue = [&](const Tile& t) __attribute__((always_inline)) {
+    const int pa = t.phase >> 1, pb = t.phase & 1;
+    const int hh = t.h0 + wave, ww = t.w0 + l32;
+    const bool inside = (hh >= 0) & (hh < p.H) & (ww >= 0) & (ww < p.W);
+    const float* bias = opaque(p.bias);
+    const float* gamma = opaque(p.norm_gamma);
+    float ss = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = nb * 32 + g * 8;
+        if (c >= p.N) continue;  // (wave-uniform)
+        const float4 b4 = bias ? *(const float4*)(bias + c + half * 4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[nb][0][g * 4 + e] + bv[e];
+          acc[nb][0][g * 4 + e] = v;
+          ss = fmaf(v, v, ss);
+        }
+      }
+    ss += __shfl_xor(ss, 32, 64);
+    const float inv_n = 1.0f / (float)p.N;
+    const float rs = rsqrtf(ss * inv_n + p.norm_eps);
+    u32x4 xo[6];
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const int nb = q >> 1;
+      float v[8];
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = (q & 1) * 2 + gg;
+        const int c = nb * 32 + g * 8;
+        float4 gm = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (c < p.N) gm = *(const float4*)(gamma + c + half * 4);
+        const float gv[4] = {gm.x, gm.y, gm.z, gm.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float a = acc[nb][0][g * 4 + e] * rs * gv[e];
+          if (p.norm_silu) a = silu_f32(a);
+          v[gg * 4 + e] = (inside && c < p.N) ? a : 0.0f;
+        }
+      }
+      xo[q][0] = pack_bf16x2(v[0], v[1]);
+      xo[q][1] = pack_bf16x2(v[2], v[3]);
+      xo[q][2] = pack_bf16x2(v[4], v[5]);
+      xo[q][3] = pack_bf16x2(v[6], v[7]);
+    }
+    floatx16 z[3];
+#pragma unroll
+    for (int bz = 0; bz < 3; ++bz)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[bz][r] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 6; ++q)
+#pragma unroll
+      for (int bz = 0; bz < 3; ++bz) {
+        const u32x4 a = *(const u32x4*)(&lds_hz[(bz * 32 + l32) * TZR + q * 16 + half * 8]);
+        z[bz] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, xo[q]),
+                                                        z[bz], 0, 0, 0);
+      }
+    // accumulator index of pixel (Y + 1, X + 1) of this lane's position (Y, X) = (2 hh + pa,
+    // 2 ww + pb), the block's pixel rows and columns counted from (2 h0 - 1, 2 w0 - 1); a lane adds
+    // colour `half` of every spatial tap, and colour 2 of the taps jk with jk % 2 == half
+    const int rb = 2 * wave + pa + 2, cb = 2 * l32 + pb + 2;
+    auto batch = [&](auto J0, auto NJ, auto K0, auto NK) __attribute__((always_inline)) {
+      constexpr int j0 = decltype(J0)::value, nj = decltype(NJ)::value;
+      constexpr int k0 = decltype(K0)::value, nk = decltype(NK)::value;
+      float4 r[nj][nk], r2[nj][nk];
+#pragma unroll
+      for (int a = 0; a < nj; ++a)
+#pragma unroll
+        for (int b = 0; b < nk; ++b) {
+          const int jk = (j0 + a) * 3 + k0 + b;
+          const float* t = lds_tc + ((rb - j0 - a) * TCC + (cb - k0 - b)) * TCP;
+          r[a][b] = *(const float4*)(t + half * 4);
+          if (half == (jk & 1)) r2[a][b] = *(const float4*)(t + 8);
+        }
+#pragma unroll
+      for (int a = 0; a < nj; ++a)
+#pragma unroll
+        for (int b = 0; b < nk; ++b) {
+          const int jk = (j0 + a) * 3 + k0 + b;
+          float* t = lds_tc + ((rb - j0 - a) * TCC + (cb - k0 - b)) * TCP;
+          r[a][b].x += z[0][jk];
+          r[a][b].y += z[1][jk];
+          r[a][b].z += z[2][jk];
+          *(float4*)(t + half * 4) = r[a][b];
+          if (half == (jk & 1)) {
+            r2[a][b].x += z[0][9 + (jk >> 1)];
+            r2[a][b].y += z[1][9 + (jk >> 1)];
+            r2[a][b].z += z[2][9 + (jk >> 1)];
+            *(float4*)(t + 8) = r2[a][b];
+          }
+        }
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    // (the empty asm statements keep the compiler from moving a batch's reads above the previous
+    // batch's writes: the address another lane wrote is one this thread never wrote)
+    batch(C0{}, C2{}, C0{}, C2{});  // rows j = 0, 1, columns k = 0, 1
+    asm volatile("" ::: "memory");
+    batch(C0{}, C2{}, C2{}, C1{});  // rows j = 0, 1, column k = 2
+    lds_ops_done();
+    lds_barrier();
+    batch(C2{}, C1{}, C0{}, C2{});  // row j = 2, columns k = 0, 1
+    asm volatile("" ::: "memory");
+    batch(C2{}, C1{}, C2{}, C1{});  // row j = 2, column k = 2
+  };
+  // After a frame's last phase: output frame tf is complete (its tap 2 term is this frame's),
+  // + bias, one bf16 rounding into the video; the partial sums move on by a frame
+  // (sum order of an output frame f: ((tap 0 of f - 2) + tap 1 of f - 1) + tap 2 of f); the
+  // accumulator is cleared for the next frame.
+  auto tail_finish = [&](int tf) __attribute__((always_inline)) {
+    lds_ops_done();
+    lds_barrier();  // every wave's sums of the frame are in
+    const float* hb = opaque(p.head_b);
+    const int64_t plane = (int64_t)(2 * p.H) * (2 * p.W);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int Yo, Xo;
+      const bool own = tail_pixel(u, Yo, Xo);
+      const int px = tid + WAVES * 64 * u;
+      if (px < TOR * TOC) {
+        const int orow = px / TOC, ocol = px - (px / TOC) * TOC;
+        const float* src = lds_tc + ((orow + 2) * TCC + ocol + 2) * TCP;
+#pragma unroll
+        for (int o = 0; o < 3; ++o) {
+          const float4 cv = *(const float4*)(src + 4 * o);  // temporal taps 0, 1, 2 of colour o
+          const float f = to0[u][o] + cv.z;
+          if (own && o < p.head_co)
+            p.video[((int64_t)o * p.video_frames + p.video_fbase + tf) * plane + (int64_t)Yo * (2 * p.W) + Xo] =
+                (bf16_t)f32_to_bf16(f + (hb ? hb[o] : 0.0f));
+          to0[u][o] = to1[u][o] + cv.y;
+          to1[u][o] = cv.x;
+        }
+      }
+    }
+    lds_barrier();  // every read of the frame's sums is done
+    for (int idx = tid; idx < TCR * TCC * TCP / 4; idx += WAVES * 64)
+      *(float4*)(lds_tc + 4 * idx) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    lds_ops_done();
+  };
   int g = 0;  // stage within the tile
   auto after_stage = [&](auto PL) __attribute__((always_inline)) -> bool {
     constexpr int L = decltype(PL)::value;
@@ -961,7 +1195,11 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
     int ph[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) ph[mb] = tc.h0 + wave * MB + mb;
-    if (p.staged) {
+    if constexpr (TAIL) {
+      (void)ph;
+      tail_epilogue(tc);
+      if (tc.phase == 3) tail_finish(tc.tf);
+    } else if (p.staged) {
       conv_epilogue_staged<NB, MB, NORM, NBP>(p, acc, ph, tc.w0, tc.tf, tc.n0, pa, pb, lane,
                                               (char*)pbuf(PL) + wave * SShape::BYTES);
     } else {
@@ -975,12 +1213,12 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
       conv_epilogue<NB, MB, NORM>(p, acc, ph, pw, pv, tc.tf, tc.n0, pa, pb, half);
     }
     if (!more) return true;
-    it += G8;
-    more = PERSIST && it + G8 < xl;
+    it += it_step;
+    more = PERSIST && it + it_step < it_end;
     tc = tn;
     rs_cur = rs_nxt;
     if (more) {
-      tn = decode(it + G8);
+      tn = decode(it + it_step);
       rs_nxt = weight_rsrc(tn);
     }
     cur.nt = 0;
@@ -1000,6 +1238,21 @@ __global__ __launch_bounds__(WAVES * 64, (dma_waves_per_simd<NB, MB, KS>() * 4 /
   }
   // fetches past the end (into slots and buffers nobody reads) land before the workgroup exits
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if constexpr (TAIL) {
+    // the partial sums of the two frames after the pass, for the next one
+    const int64_t plane = (int64_t)(2 * p.H) * (2 * p.W);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int Yo, Xo;
+      if (!tail_pixel(u, Yo, Xo)) continue;
+      const int64_t at = (int64_t)Yo * (2 * p.W) + Xo;
+#pragma unroll
+      for (int o = 0; o < 3; ++o) {
+        p.carry[o * plane + at] = to0[u][o];
+        p.carry[(3 + o) * plane + at] = to1[u][o];
+      }
+    }
+  }
   run_copy_share(p.copy);
 }
 
@@ -1053,6 +1306,12 @@ struct ConfigEntry {
   { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<NB, MB, 2>() * 4 / W, \
     conv_halo_dma_kernel<NB, MB, W, 2, false>, \
     conv_halo_dma_kernel<NB, MB, W, 2, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, true> }
+// The fused tail: the x2 phase conv with norm_out + SiLU and the output head in one kernel (only
+// for problems with head_w set, never chosen or forced for others).
+#define WVD_TAIL_CONFIG(NB, MB, W) \
+  { "conv_tail_phase_head_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, 0, \
+    conv_halo_dma_kernel<NB, MB, W, 2, true, false, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, false, true>, \
+    nullptr }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
   { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
     conv_halo_kernel<NB, MB, W, 2, true>, nullptr }
@@ -1084,6 +1343,7 @@ enum ConfigId {
   HALO_DMA_N3_W4,  // 96 x (8 rows x 32 columns) on 4 waves in 80 KB: two workgroups per CU
   HALO_DMA_N4_W8,  // 128 x (16 rows x 32 columns): channel counts that are multiples of 128, not of 96
   PHASE_DMA_N6_M1_W8,  // x2 upsampling phases: 192 x (8 rows x 32 columns), one row per wave, 112 KB
+  TAIL_N3_M1_W8,       // the fused tail: PHASE_DMA_N3_M1_W8's tiles, all phases and frames of a block
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -1094,7 +1354,7 @@ const ConfigEntry kConfigs[] = {
     WVD_HALO_DMA_DUAL_CONFIG(6, 1, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),    WVD_HALO_DMA_CONFIG(1, 2, 8),
     WVD_CONV_CONFIG(4, 1, 8),           WVD_HALO_DMA_CONFIG(3, 2, 4),    WVD_HALO_DMA_PLAIN_CONFIG(4, 2, 8),
-    WVD_PHASE_HALO_DMA_DUAL_CONFIG(6, 1, 8),
+    WVD_PHASE_HALO_DMA_DUAL_CONFIG(6, 1, 8), WVD_TAIL_CONFIG(3, 1, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -1191,6 +1451,7 @@ int conv_config_count() { return kNumConfigs; }
 // norm needs one channel tile.
 bool conv_config_fits(const ConvProblem& p, int id) {
   if (id < 0 || id >= kNumConfigs) return false;
+  if ((id == TAIL_N3_M1_W8) != (p.head_w != nullptr)) return false;
   const ConfigEntry& c = kConfigs[id];
   if (c.halo == 3 && !(p.phases == 1 && p.kh == 3 && p.kw == 3)) return false;
   if (c.halo == 2 && !(p.phases == 4 && p.kh == 2 && p.kw == 2)) return false;
@@ -1199,12 +1460,33 @@ bool conv_config_fits(const ConvProblem& p, int id) {
   return true;
 }
 
+bool tail_kernel_supported(int N, int Cip, int co) { return N > 64 && N <= 96 && N % 8 == 0 && Cip == 96 && co >= 1 && co <= 3; }
+
 hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id, int force_config,
                             int max_workgroups) {
   const int64_t HW = (int64_t)p.H * p.W;
   if (p.T == 0 || HW == 0) return hipSuccess;
   // one frame is addressed with 32-bit byte offsets
   if (HW * p.Ci * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (p.head_w) {
+    // the fused tail: an x2 phase conv of N -> N channels with norm_out + SiLU, no history,
+    // residual or second output, a head of at most 3 colours; one workgroup per block
+    if (force_config >= 0 && force_config != TAIL_N3_M1_W8) return hipErrorNotSupported;
+    if (!tail_kernel_supported(p.N, p.Cip, p.head_co) || p.Ci != p.N || p.Npad != 96 || p.phases != 4 ||
+        p.kh != 2 || p.kw != 2 || p.ntaps != 4 || !conv_can_fuse_norm(p.N, p.bias, p.norm_gamma) || p.res ||
+        p.y_pre || p.hist || p.Th != 0 || !p.video || !p.carry || p.video_fbase < 0 ||
+        p.video_fbase + (int64_t)p.T > p.video_frames)
+      return hipErrorInvalidValue;
+    const int64_t nbr = (2 * (int64_t)p.H + 14) / 14, nbc = (2 * (int64_t)p.W + 62) / 62;
+    const int64_t gx = (nbr * nbc + 7) / 8 * 8;
+    if (gx > 0x7fffffff || 4 * (int64_t)p.T > 0x7fffffff) return hipErrorInvalidValue;
+    if (config_id) *config_id = TAIL_N3_M1_W8;
+    ConvProblem q = p;
+    q.time_tiles = 0;
+    q.staged = 0;
+    hipLaunchKernelGGL(kConfigs[TAIL_N3_M1_W8].kernel_norm, dim3((unsigned)gx), dim3(512), 0, s, q);
+    return hipGetLastError();
+  }
   // (a fused norm takes a residual only with the dual store, which adds it before the statistics)
   if (p.norm_gamma && (!conv_can_fuse_norm(p.N, p.bias, p.norm_gamma) || (p.res && !p.y_pre) || p.y_f32 ||
                        p.nsplit != p.N))

@@ -344,6 +344,20 @@ wvd_status wvd_conv_max_workgroups(int n);
  * are bitwise independent of the pass size. Process-wide; not for use while another thread
  * decodes. */
 wvd_status wvd_decode_fuse_norm1(int on);
+/* Memory option: with on != 0, a decoder whose last stage is a spatial x2 upsample (no time
+ * step, no DupUp3D) of 65-96 channels and whose head is conv_out to at most 3 colours (no
+ * unpatchify or clamp) runs that upsample, norm_out + SiLU and the head as one kernel per pass:
+ * the activated last-level tensor (the largest of the decode) is never written, and the head's
+ * causal cache holds, instead of its last two input frames, the partial sums of the two output
+ * frames after the pass (fp32, 3 x H x W each): at 704x1248, 650 MB less cache and 0.6 GiB less
+ * peak memory, but about 3 % slower (the fused kernel runs one workgroup per CU). With on == 0
+ * (the default) the upsample writes the activated tensor and the head reads it (in frame
+ * sub-passes). The cache layout follows the
+ * switch: wvd_cache_bytes, wvd_cache_init and the workspace sizes read it, and a decode whose
+ * switch differs from the one its cache was made with fails with WVD_ERR_STATE. The two videos
+ * differ by rounding only; either way decodes are bitwise independent of the pass size.
+ * Process-wide; not for use while another thread decodes. */
+wvd_status wvd_decode_fuse_head(int on);
 /* Measurement support: copy `bytes` (a multiple of 16; src and dst 16-byte aligned, device
  * memory, not overlapping) with the convolution kernels' own load path: buffer loads that write
  * 16 bytes per lane straight into LDS, read back and stored with 16-byte global stores. The

@@ -47,13 +47,25 @@ def test_sizes():
     assert L.wvd_conv_packed_bytes(3, 96, 3, 3, 3, 0) == 32 * 27 * 96 * 2
     assert L.wvd_conv_packed_bytes(96, 96, 1, 3, 3, 1) == 4 * 96 * 4 * 96 * 2
     assert L.wvd_conv_packed_bytes(48, 48, 2, 3, 3, 0) == 0
-    # cache: two frames per causal conv input, twice (the current history and the next one);
-    # 2 x 1.1 GB for the full decoder
+    # cache: two frames per causal conv input, twice (the current history and the next one); with
+    # the fused tail the head's slot holds instead the partial sums of the two output frames after
+    # a pass (2 x 3 colours x 704 x 1248 fp32)
     cache = L.wvd_cache_bytes(ctypes.byref(desc))
-    assert 2.0e9 < cache < 2.6e9
     ws4 = L.wvd_decode_workspace_bytes(ctypes.byref(desc), 4)
     ws8 = L.wvd_decode_workspace_bytes(ctypes.byref(desc), 8)
     assert 0 < ws4 < ws8
+    try:
+        wvd.decode_fuse_head(True)
+        cache_on = L.wvd_cache_bytes(ctypes.byref(desc))
+        ws4_on = L.wvd_decode_workspace_bytes(ctypes.byref(desc), 4)
+    finally:
+        wvd.decode_fuse_head(False)
+    up = lambda n: (n + 255) // 256 * 256
+    px = 704 * 1248
+    assert cache - cache_on == up(4 * px * 96 * 2) - up(2 * 3 * px * 4)
+    assert 2.0e9 < cache < 2.6e9 and 1.4e9 < cache_on < 1.7e9
+    # no activated last-level tensor for the head: the workspace shrinks too, never grows
+    assert ws4_on <= ws4
 
 
 def test_chunk_frame_counts():
@@ -160,6 +172,15 @@ def test_cache_state_machine_rejects_out_of_order_chunks():
                             ctypes.c_void_p(0x30000), ws, None)
     assert st == 2
     assert L.wvd_cache_next_latent(h) == 0
+    # a cache made with the fused head off, decoded with it on (the head slot's layouts differ)
+    try:
+        wvd.decode_fuse_head(True)
+        ws_on = L.wvd_decode_workspace_bytes(ctypes.byref(desc), 4)
+        st = L.wvd_decode_chunk(ctypes.byref(desc), packed, h, ctypes.byref(z), 1, 1, ctypes.byref(video), 0,
+                                ctypes.c_void_p(0x30000), ws_on, None)
+        assert st == 6 and b"fused head" in L.wvd_last_error()
+    finally:
+        wvd.decode_fuse_head(False)
     L.wvd_cache_destroy(h)
 
 

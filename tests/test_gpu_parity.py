@@ -603,6 +603,50 @@ def test_decoder_with_norm1_fused_matches_oracle_and_is_pass_size_invariant(rule
     assert psnr(got[True], got[False]) >= 55.0
 
 
+# last stages the fused tail kernel takes (65-96 channels, at most 3 colours)
+TAIL_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 32, 96))
+TAIL72_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 32, 72), out_channels=2)
+
+
+@pytest.mark.parametrize("spec,rule,hw", [(TAIL_GPU, True, (5, 7)), (TAIL_GPU, False, (2, 9)),
+                                          (TAIL72_GPU, True, (3, 4))], ids=["c96_rule", "c96", "c72_2colours"])
+def test_fused_tail_matches_oracle_and_unfused_and_is_pass_size_invariant(spec, rule, hw):
+    """wvd_decode_fuse_head: the last x2 upsample, norm_out + SiLU and the head in one kernel
+    (the head's temporal taps carried between passes as partial sums) against the path through the
+    activated tensor. Frame sizes that leave partial blocks (14 x 62 output pixels each) on both
+    edges; each mode against the oracle, with the same bits for every pass size and per-level
+    sub-passes (the carry), the two modes within rounding of each other."""
+    z, params = wl.decoder_weights(spec, seed=55, latent_frames=4, latent_hw=hw)
+    ref = oracle.decode(z[0], oracle.as_numpy_params(params), spec, frames_per_pass=4, first_frame_rule=rule)
+    zd = z.to(torch.bfloat16).cuda()
+    got = {}
+    try:
+        for fused in (False, True):
+            wvd.decode_fuse_head(fused)
+            dec = _gpu_decoder(spec, params, hw)  # (its cache and workspace follow the switch)
+            wvd.timing_reset()
+            wvd.timing_enable(True)
+            videos = [dec.decode(zd, frames_per_pass=f, first_frame_rule=rule).clone() for f in (4, 1, 3)]
+            videos.append(dec.decode(zd, frames_per_pass=1, first_frame_rule=rule, early_frames_per_pass=4))
+            torch.cuda.synchronize()
+            wvd.timing_enable(False)
+            ran = "conv_tail_phase_head_n3_m1_w8" in wvd.timing_read()
+            assert ran == fused
+            for v in videos[1:]:
+                assert torch.equal(v, videos[0]), fused
+            got[fused] = videos[0][0].float().cpu().numpy()
+            assert got[fused].shape == ref.shape
+            q = psnr(got[fused], ref)
+            log(f"tail {'fused' if fused else 'through memory'} {spec.stage_channels[-1]} ch rule={rule} {hw}: "
+                f"psnr {q:.2f} dB vs oracle, rel {rel_max(got[fused], ref):.3e}")
+            assert q >= 55.0
+    finally:
+        wvd.decode_fuse_head(False)
+        wvd.timing_enable(False)
+    assert not np.array_equal(got[True], got[False])
+    assert psnr(got[True], got[False]) >= 55.0
+
+
 WIDE_TAIL_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 32, 224))
 
 
