@@ -922,6 +922,12 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
   zero_acc();
 
   constexpr int NM = MB * NB;
+  // The first stage of a tile that follows an epilogue in this workgroup (persistent tiles):
+  // every fetch issued before that epilogue has landed (it starts with a full wait), so that
+  // stage's first WW steps, whose waits would cover only such fetches, wait for nothing. (A
+  // count there would also have to count the epilogue's stores, which the counter may retire
+  // out of order with the fetches: LLVM's own waits treat mixed loads and stores that way.)
+  bool fresh = false;
   auto step = [&](auto PP, auto SS) __attribute__((always_inline)) {
     constexpr int P = decltype(PP)::value;  // stage parity: patch buffer
     constexpr int S = decltype(SS)::value;  // spatial tap
@@ -964,7 +970,11 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
     // own fetches of steps <= k - WW have landed: the ones issued in steps k - WW + 1 .. k may not
     constexpr int N = WW * WIW + (S < WW ? PIW : 0);
     static_assert(N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+    if constexpr (PERSIST && S < WW) {
+      if (!fresh) __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+    }
     lds_barrier();
   };
   auto stage = [&](auto PP) __attribute__((always_inline)) {
@@ -979,6 +989,7 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
       step(PP, std::integral_constant<int, 7>{});
       step(PP, std::integral_constant<int, 8>{});
     }
+    fresh = false;
     cur = nxt;
     if (!nxt.nt) nxt = next_stage(nxt);  // (past a tile's last stage nxt is set at the switch)
   };
@@ -1191,6 +1202,10 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
     constexpr int L = decltype(PL)::value;
     if (++g < ng) return false;
     g = 0;
+    // every fetch this wave issued (the next tile's first patch and weights among them) lands
+    // before the epilogue's loads and stores go out (see `fresh`); the epilogue's first bias read
+    // waited for them anyway
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     const int pa = (KS == 2) ? (tc.phase >> 1) : 0, pb = (KS == 2) ? (tc.phase & 1) : 0;
     int ph[MB];
 #pragma unroll
@@ -1223,6 +1238,7 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
     }
     cur.nt = 0;
     nxt = next_stage(cur);
+    fresh = true;
     zero_acc();
     // every wave is done with the staging areas before the next tile's fetches reuse them
     lds_barrier();
