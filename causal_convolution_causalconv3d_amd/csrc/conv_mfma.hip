@@ -993,7 +993,6 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
     cur = nxt;
     if (!nxt.nt) nxt = next_stage(nxt);  // (past a tile's last stage nxt is set at the switch)
   };
-  using SShape = StagedShape<NBP>;
   // After each stage: at a tile's end (its last stage of parity PL) the epilogue, then the
   // switch to the next tile, whose first stage (parity PL ^ 1) is already fetched. Returns
   // whether the workgroup is done.
@@ -1215,8 +1214,19 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
       tail_epilogue(tc);
       if (tc.phase == 3) tail_finish(tc.tf);
     } else if (p.staged) {
-      conv_epilogue_staged<NB, MB, NORM, NBP>(p, acc, ph, tc.w0, tc.tf, tc.n0, pa, pb, lane,
-                                              (char*)pbuf(PL) + wave * SShape::BYTES);
+      // Staging areas: the finished stage's patch buffer and, since nothing is in flight now, the
+      // weight slot of the next tile's step D (fetched only at that tile's first step, after the
+      // barrier that closes this epilogue): the widest pass whose per-wave areas fit in both.
+      constexpr auto fits_pw = [](int nbp) constexpr {
+        const int sb = 32 * (nbp * 64 + 16);
+        return PBYTES / sb + WBYTES / sb >= WAVES;
+      };
+      constexpr int NBQ = (NB % 3 == 0 && fits_pw(3)) ? 3 : ((NB % 2 == 0 && fits_pw(2)) ? 2 : 1);
+      constexpr int SBQ = StagedShape<NBQ>::BYTES, PCAPQ = PBYTES / SBQ;
+      constexpr int FREE = (((L ^ 1) * SPS) + D) % NWS;
+      char* st = wave < PCAPQ ? (char*)pbuf(PL) + wave * SBQ
+                              : (char*)wslot(std::integral_constant<int, FREE>{}) + (wave - PCAPQ) * SBQ;
+      conv_epilogue_staged<NB, MB, NORM, NBQ>(p, acc, ph, tc.w0, tc.tf, tc.n0, pa, pb, lane, st);
     } else {
       int pw[MB];
       bool pv[MB];
