@@ -255,8 +255,17 @@ __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __res
     run_copy_share(copy);
     return;
   }
-  const int rt = lin / numC;
-  const int h0 = rt * HF_OROWS, w0 = (lin - rt * numC) * HF_OCOLS;
+  // Tiles in bands of HS_BAND tile rows, each band walked column by column: the workgroups an XCD
+  // runs at once (a run of consecutive tiles) then cover a 2D block of the frame, so a tile's
+  // halo rows and columns, which its neighbours above, below and beside read too, are read
+  // from HBM about once while they sit in that XCD's L2 (in row order the neighbours below ran a
+  // round later, after the rows had left L2).
+  constexpr int HS_BAND = 4;
+  const int band = lin / (HS_BAND * numC);
+  const int r0 = band * HS_BAND, bh = (numR - r0 < HS_BAND) ? numR - r0 : HS_BAND;
+  const int bidx = lin - band * HS_BAND * numC;
+  const int rt = r0 + bidx % bh, ct = bidx / bh;
+  const int h0 = rt * HF_OROWS, w0 = ct * HF_OCOLS;
 
   // weights into LDS: row n = tap * 3 + o of the 32-row block from packed row tap * 4 + o
   constexpr int WK8 = 3 * Cip / 8;
