@@ -116,15 +116,10 @@ def test_streaming_decode_full_size_pass_size_invariant():
         torch.cuda.empty_cache()
 
 
-def test_streaming_decode_full_size_against_the_one_shot_oracle():
-    if not os.path.exists(STREAM_GOLDEN):
-        pytest.skip("stream golden samples not generated (tests/golden/make_stream_golden.py)")
-    g = np.load(STREAM_GOLDEN)
-    _, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
-    z = wl.streaming_latents(seed=5, latent_frames=31)
-    dec = _full_decoder(params)
-    v = dec.decode(z.to(torch.bfloat16).cuda(), frames_per_pass=4)
-    torch.cuda.synchronize()
+def _check_stream_golden(v, g, label):
+    """The 121-frame 704x1248 video against the one-shot oracle's stored samples: PSNR over the
+    samples and at the first frame, pass boundaries and the last frame, and every frame's mean
+    and mean square over all its pixels."""
     assert tuple(v.shape) == (1, 3, 121, 704, 1248)
     video = v[0].float()
     flat = video.reshape(-1)
@@ -134,7 +129,7 @@ def test_streaming_decode_full_size_against_the_one_shot_oracle():
     rng = float(g["vmax"] - g["vmin"])
     err = got - ref
     q = 10 * math.log10(rng * rng / float((err ** 2).mean()))
-    log(f"streaming decode vs one-shot oracle: psnr {q:.2f} dB over {ref.size} samples, max abs {np.abs(err).max():.3e}, "
+    log(f"{label} vs one-shot oracle: psnr {q:.2f} dB over {ref.size} samples, max abs {np.abs(err).max():.3e}, "
         f"range {rng:.3f}")
     assert q >= 55.0
     frame = (g["index"] // (704 * 1248)) % 121
@@ -151,6 +146,48 @@ def test_streaming_decode_full_size_against_the_one_shot_oracle():
     dq = np.abs(meansq / g["frame_meansq"] - 1.0).max()
     log(f"  per-frame mean: max |diff| {dm:.2e} of the range; mean square: max rel diff {dq:.2e}")
     assert dm <= 1e-3 and dq <= 1e-2
+
+
+def test_streaming_decode_full_size_against_the_one_shot_oracle():
+    if not os.path.exists(STREAM_GOLDEN):
+        pytest.skip("stream golden samples not generated (tests/golden/make_stream_golden.py)")
+    g = np.load(STREAM_GOLDEN)
+    _, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
+    z = wl.streaming_latents(seed=5, latent_frames=31)
+    dec = _full_decoder(params)
+    v = dec.decode(z.to(torch.bfloat16).cuda(), frames_per_pass=4)
+    torch.cuda.synchronize()
+    _check_stream_golden(v, g, "streaming decode")
+
+
+def test_fused_tail_streaming_decode_full_size_against_the_one_shot_oracle():
+    """The same decode with the last upsample, norm_out and the head as one kernel
+    (wvd_decode_fuse_head): against the one-shot oracle's samples, and bitwise the same for 4 and
+    3 latent frames per pass (the head's partial sums carried across every pass boundary)."""
+    if not os.path.exists(STREAM_GOLDEN):
+        pytest.skip("stream golden samples not generated (tests/golden/make_stream_golden.py)")
+    g = np.load(STREAM_GOLDEN)
+    _, params = wl.decoder_weights(wl.FULL_DECODER, seed=4, latent_frames=4)
+    z = wl.streaming_latents(seed=5, latent_frames=31).to(torch.bfloat16).cuda()
+    try:
+        wvd.decode_fuse_head(True)
+        dec = _full_decoder(params)
+        wvd.timing_reset()
+        wvd.timing_enable(True)
+        v4 = dec.decode(z, frames_per_pass=4).clone()
+        torch.cuda.synchronize()
+        wvd.timing_enable(False)
+        ran = wvd.timing_read()
+        log(f"fused tail launches: {ran.get('conv_tail_phase_head_n3_m1_w8')}")
+        assert "conv_tail_phase_head_n3_m1_w8" in ran and "conv_phase_halo_dma_n3_m1_w8" not in ran
+        _check_stream_golden(v4, g, "fused-tail streaming decode")
+        log("fused tail, 3 latent frames per pass")
+        v3 = dec.decode(z, frames_per_pass=3)
+        torch.cuda.synchronize()
+        assert torch.equal(v3, v4)
+    finally:
+        wvd.decode_fuse_head(False)
+        wvd.timing_enable(False)
 
 
 def test_real_topology_full_size_streaming_properties():
