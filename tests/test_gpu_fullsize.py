@@ -1,12 +1,16 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the bench times.
 
-  * residual block [1,384,4,44,78] with its 2-frame cache: every output against the oracle;
+  * residual block [1,384,4,44,78] with its 2-frame cache: every output against the oracle, and
+    the histories it hands on (the last two frames of conv1's and conv2's activated inputs); its
+    conv2 alone, in the block's tile configuration, on the oracle's bf16-rounded input, every
+    output within the bf16 elementwise bound;
   * upsample stage [1,192,4,176,312] -> [1,192,8,352,624]: windows (corners, edges, centre)
     against the oracle run on the matching input crop plus a one-pixel halo (a conv is
     translation-equivariant, so the crop's interior equals the full-size result);
   * one-pass decode [1,48,4,44,78] -> [1,3,16,704,1248]: against the oracle's values at 32768
     seeded positions (tests/golden/decoder_onepass_samples.npz, written by make_decoder_golden.py
-    from the oracle alone), and bitwise pass-size invariance;
+    from the oracle alone), bitwise pass-size invariance, and the same bits from channels-last
+    latents;
   * streaming 5 s decode [1,48,31,44,78] -> 121 frames: bitwise equal for 4 frames per pass, 3,
     all 31 in one pass (the one-shot form), and per-level pass sizes (8 or 16 latent frames
     through the early stages, sub-passes of 4 through the late ones);
@@ -27,7 +31,7 @@ import torch
 import causal_convolution_causalconv3d_amd as wvd
 import oracle
 import workloads as wl
-from gpu_util import from_dev_nthwc, log, psnr, rel_max, to_dev_nthwc
+from gpu_util import bf16_elementwise_ok, from_dev_nthwc, log, psnr, rel_max, to_dev_nthwc
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "decoder_onepass_samples.npz")
@@ -35,17 +39,69 @@ STREAM_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "stream_decode
 
 
 def test_resblock_full_size():
+    """The block's output, and each step inside it: the histories it hands on are the last two
+    frames of norm1's activation (conv1's input) and of norm2's activation of conv1's output
+    (conv2's input), so both intermediate tensors are checked at full size too."""
     cfg = wl.resblock_bf16()  # [1,384,4,44,78] + [1,384,2,44,78] cache, seed 2
     p = oracle.as_numpy_params(cfg["params"])
-    ref = oracle.resblock(cfg["x"][0], p, "res", {}, 1e-6, given_hist=oracle._f32(cfg["hist"][0]))
+    hist = oracle._f32(cfg["hist"][0])
+    x = oracle._f32(cfg["x"][0])
+    a1 = oracle.norm_silu(x, p["res.norm1.gamma"], 1e-6)
+    h = oracle.causal_conv3d(a1, p["res.conv1.weight"], p.get("res.conv1.bias"), hist)
+    a2 = oracle.norm_silu(h, p["res.norm2.gamma"], 1e-6)
+    ref = oracle.resblock(x, p, "res", {}, 1e-6, given_hist=hist)
     wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
     hd = to_dev_nthwc(cfg["hist"])
-    y = wvd.resblock(to_dev_nthwc(cfg["x"]), wts, 1e-6, hist1=hd, hist2=hd)
+    C, T, H, W = x.shape
+    h1o = torch.empty((1, 2, H, W, C), dtype=torch.bfloat16, device="cuda")
+    h2o = torch.empty_like(h1o)
+    y = wvd.resblock(to_dev_nthwc(cfg["x"]), wts, 1e-6, hist1=hd, hist2=hd, hist1_out=h1o, hist2_out=h2o)
     torch.cuda.synchronize()
+    for name, got, want in (("norm1 activation", from_dev_nthwc(h1o), a1[:, T - 2:]),
+                            ("conv1 + norm2 activation", from_dev_nthwc(h2o), a2[:, T - 2:])):
+        r = rel_max(got, want)
+        log(f"resblock full size, {name} (frames {T - 2}, {T - 1}): rel {r:.3e}, psnr {psnr(got, want):.2f} dB")
+        assert r <= 2e-2
     got = from_dev_nthwc(y)
     r = rel_max(got, ref)
     log(f"resblock full size: rel {r:.3e}, psnr {psnr(got, ref):.2f} dB")
     assert r <= 2e-2
+
+
+def test_resblock_conv2_full_size_alone():
+    """conv2 of the full-size block by itself, on the oracle's conv2 input rounded to bf16 (so the
+    kernel's error is not mixed with that of the steps before it), with the block's residual, in
+    the same tile configuration the block launches: every output against the oracle."""
+    cfg = wl.resblock_bf16()
+    p = oracle.as_numpy_params(cfg["params"])
+    hist = oracle._f32(cfg["hist"][0])
+    x = oracle._f32(cfg["x"][0])
+    a1 = oracle.norm_silu(x, p["res.norm1.gamma"], 1e-6)
+    h = oracle.causal_conv3d(a1, p["res.conv1.weight"], p.get("res.conv1.bias"), hist)
+    a2 = torch.from_numpy(oracle.norm_silu(h, p["res.norm2.gamma"], 1e-6)).to(torch.bfloat16)
+    ref = oracle.add(oracle.causal_conv3d(a2.float().numpy(), p["res.conv2.weight"], p.get("res.conv2.bias"), hist), x)
+    wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+    hd = to_dev_nthwc(cfg["hist"])
+    xd = to_dev_nthwc(cfg["x"])
+    wvd.timing_enable(True)
+    try:
+        wvd.timing_reset()
+        wvd.resblock(xd, wts, 1e-6, hist1=hd, hist2=hd)
+        torch.cuda.synchronize()
+        in_block = wvd.timing_read()
+        wvd.timing_reset()
+        y = wvd.causal_conv3d(to_dev_nthwc(a2[None]), wts["conv2"], wts["cout"], bias=wts["bias2"], hist=hd,
+                              residual=xd)
+        torch.cuda.synchronize()
+        alone = wvd.timing_read()
+    finally:
+        wvd.timing_enable(False)
+    log(f"block convs {sorted(in_block)}, conv2 alone {sorted(alone)}")
+    assert len(alone) == 1 and next(iter(alone.values()))[0] == 1 and set(alone) <= set(in_block)
+    got = from_dev_nthwc(y)
+    ok, worst = bf16_elementwise_ok(got, ref)
+    log(f"resblock conv2 alone, full size: rel {rel_max(got, ref):.3e}, worst bf16 bound ratio {worst:.3f}")
+    assert ok
 
 
 def test_upsample_stage_full_size_windows():
@@ -86,6 +142,8 @@ def test_one_pass_decode_full_size_against_oracle_samples():
     assert bool(torch.isfinite(v4.float()).all())
     for fpp in (1, 3):
         assert torch.equal(dec.decode(zd, frames_per_pass=fpp, first_frame_rule=False), v4), fpp
+    z_cl = zd.permute(0, 2, 3, 4, 1).contiguous()
+    assert torch.equal(dec.decode(z_cl, frames_per_pass=4, first_frame_rule=False, z_layout="NTHWC"), v4)
     if not os.path.exists(GOLDEN):
         pytest.skip("golden samples not generated (tests/golden/make_decoder_golden.py)")
     g = np.load(GOLDEN)

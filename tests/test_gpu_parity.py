@@ -543,6 +543,9 @@ def test_small_decoder_matches_oracle_and_is_pass_size_invariant(rule):
     dec = _gpu_decoder(SMALL_GPU, params, hw)
     zd = z.to(torch.bfloat16).cuda()
     videos = [dec.decode(zd, frames_per_pass=f, first_frame_rule=rule) for f in (3, 1, 2)]
+    # the same latents handed over channels-last ([1, T, h, w, C]): the same bits
+    z_cl = zd.permute(0, 2, 3, 4, 1).contiguous()
+    videos += [dec.decode(z_cl, frames_per_pass=f, first_frame_rule=rule, z_layout="NTHWC") for f in (3, 2)]
     torch.cuda.synchronize()
     for v in videos[1:]:
         assert torch.equal(v, videos[0])
