@@ -433,6 +433,9 @@ def main():
     ap.add_argument("--norm1", choices=("fused", "separate"), default="fused",
                     help="each residual block's norm1 + SiLU in the producing conv's epilogue (the default) or as "
                          "a separate pass (wvd_decode_fuse_norm1)")
+    ap.add_argument("--shortcut", choices=("fused", "separate"), default="fused",
+                    help="a 192 -> 96 block's 1x1 shortcut in the epilogue of the x2 upsample that produces its "
+                         "input (the default) or as a separate pass (wvd_decode_fuse_shortcut)")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' measurements")
     ap.add_argument("--config-reps", type=int, default=10, help="timed calls per other workload (median)")
     ap.add_argument("--workload", default="stream",
@@ -478,6 +481,7 @@ def main():
     spec = wl.REAL_DECODER if real else wl.FULL_DECODER
     wvd.decode_fuse_norm1(args.norm1 == "fused")
     wvd.decode_fuse_head(args.head == "fused")
+    wvd.decode_fuse_shortcut(args.shortcut == "fused")
     _, params = wl.decoder_weights(spec, seed=4, latent_frames=4)
     z = wl.streaming_latents(seed=5, latent_frames=args.latent_frames).to(torch.bfloat16).cuda()
     dec = wvd.Decoder(wvd.desc_from_spec(spec), params)
@@ -560,6 +564,7 @@ def main():
                    "topology": args.topology,
                    "latent_frames": args.latent_frames, "video_frames": F, "frames_per_pass": fpp,
                    "early_frames_per_pass": early, "norm1": args.norm1, "head": args.head,
+                   "shortcut": args.shortcut,
                    "global_batch": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": round(dom_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),

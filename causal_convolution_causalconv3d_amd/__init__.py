@@ -120,6 +120,7 @@ def lib():
             "wvd_calib_dma_copy": ([_P, _P, ctypes.c_size_t, _P], ctypes.c_int),
             "wvd_decode_fuse_norm1": ([ctypes.c_int], ctypes.c_int),
             "wvd_decode_fuse_head": ([ctypes.c_int], ctypes.c_int),
+            "wvd_decode_fuse_shortcut": ([ctypes.c_int], ctypes.c_int),
             "wvd_winograd_packed_bytes": ([ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
             "wvd_winograd_pack": ([_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P], ctypes.c_int),
             "wvd_winograd_workspace_bytes": ([ctypes.c_int] * 6, ctypes.c_size_t),
@@ -148,7 +149,8 @@ def exported_symbols() -> Sequence[str]:
             "wvd_chunk_video_frames", "wvd_timing_enable", "wvd_timing_reset", "wvd_timing_read",
             "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem", "wvd_conv_max_workgroups",
             "wvd_calib_dma_copy", "wvd_winograd_packed_bytes", "wvd_winograd_pack", "wvd_winograd_workspace_bytes",
-            "wvd_causal_conv3d_winograd", "wvd_decode_fuse_norm1", "wvd_decode_fuse_head"]
+            "wvd_causal_conv3d_winograd", "wvd_decode_fuse_norm1", "wvd_decode_fuse_head",
+            "wvd_decode_fuse_shortcut"]
 
 
 def _check(status: int):
@@ -543,6 +545,12 @@ def decode_fuse_norm1(on: bool):
     """wvd_decode_fuse_norm1: apply each residual block's norm1 + SiLU in the producing conv's
     epilogue (two outputs; the default) or, with False, as a separate pass."""
     _check(lib().wvd_decode_fuse_norm1(int(on)))
+
+
+def decode_fuse_shortcut(on: bool):
+    """wvd_decode_fuse_shortcut: apply a 192 -> 96 residual block's 1x1 shortcut in the epilogue
+    of the x2 upsample that produces its input (default on)."""
+    _check(lib().wvd_decode_fuse_shortcut(int(on)))
 
 
 def decode_fuse_head(on: bool):

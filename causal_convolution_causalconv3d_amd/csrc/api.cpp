@@ -267,12 +267,19 @@ wvd_status run_time_conv(const bf16_t* x, const bf16_t* hist, int T, int H, int 
 
 // Nearest x2 + 3x3 conv as four phase convs: x [T][H][W][C] -> y [T][2H][2W][C]; with norm_gamma,
 // y is SiLU(RMS norm) of the upsampled tensor (fused in the epilogue).
+// sc_w / sc_b / sc_co / y_sc: the dual store's shortcut product in place of y_pre (ConvProblem::y_sc).
 wvd_status run_phase_conv(const bf16_t* x, int T, int H, int W, int C, const void* wpk, const float* bias, bf16_t* y,
                           hipStream_t s, const float* norm_gamma = nullptr, float norm_eps = 0.0f,
-                          bf16_t* y_pre = nullptr) {
+                          bf16_t* y_pre = nullptr, const void* sc_w = nullptr, const float* sc_b = nullptr,
+                          int sc_co = 0, bf16_t* y_sc = nullptr) {
   ConvProblem p = plain_problem(x, nullptr, T, H, W, C, 0, wpk, C, 1, 1, 1, bias, y, nullptr);
   p.norm_gamma = norm_gamma;
   p.y_pre = y_pre;
+  p.sc_w = (const bf16_t*)sc_w;
+  p.sc_b = sc_b;
+  p.sc_co = sc_co;
+  p.sc_wrow = (int)round_up(C, 32);
+  p.y_sc = y_sc;
   p.norm_eps = norm_eps;
   p.norm_silu = 1;
   p.ntaps = 4;
@@ -284,7 +291,8 @@ wvd_status run_phase_conv(const bf16_t* x, int T, int H, int W, int C, const voi
   p.Wo = 2 * W;
   p.hmul = 2;
   p.wmul = 2;
-  return run_conv(p, s, conv_flops((int64_t)T * H * W * 4, C, 4LL * C));
+  const int64_t P = (int64_t)T * H * W * 4;
+  return run_conv(p, s, conv_flops(P, C, 4LL * C) + (y_sc ? conv_flops(P, sc_co, C) : 0.0));
 }
 
 // History a conv leaves (the page's cached_conv rule), copied into a separate tensor.
@@ -1188,6 +1196,15 @@ bool dual_store_width(int c, bool phase) {
   return g_fuse_norm1.load() && conv_can_fuse_norm_width(c) && (!phase || c > 96);
 }
 
+// Whether an x2 upsample of c channels with the dual store also applies the next block's 1x1
+// shortcut (c -> cout) in that epilogue, in place of storing its pre-norm output (which only the
+// shortcut reads): the 192-wide phase tile, 96 shortcut outputs, packed rows 16-byte aligned.
+std::atomic<int> g_fuse_shortcut{1};  // wvd_decode_fuse_shortcut
+
+bool shortcut_in_upsample(int c, int cout, const void* w, const float* b) {
+  return g_fuse_shortcut.load() && c == 192 && cout == 96 && ((uintptr_t)w & 15) == 0 && ((uintptr_t)b & 15) == 0;
+}
+
 // Whether the last stage is a spatial upsample without a time step or DupUp3D whose epilogue
 // applies norm_out + SiLU (one workgroup holds every channel; the packed parameters are
 // 256-byte aligned): its output is then only the head's input. The decode runs that upsample
@@ -1542,11 +1559,17 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
   // stream buffer (in place when the residual is x itself). pre_act: SiLU(norm1(x)) is already in
   // the activated buffer (the producer's dual store). next_gamma: the next block's norm1 gain, when
   // conv2 also writes SiLU(norm1_next(y)) into the activated buffer (its dual store).
-  auto resblock = [&](const ResPlan& r, const bf16_t* x, bool pre_act, const float* next_gamma) -> wvd_status {
+  // sc_ready: the shortcut's output is already in its buffer (the producer's epilogue), and x is
+  // read by nothing.
+  auto resblock = [&](const ResPlan& r, const bf16_t* x, bool pre_act, const float* next_gamma,
+                      bool sc_ready = false) -> wvd_status {
     const int64_t P = T * H * Wd;
     bf16_t* y = bx[cur];
     const bf16_t* residual = x;
-    if (r.cin != r.cout) {
+    if (sc_ready) {
+      if (r.cin == r.cout || !pre_act) return fail(WVD_ERR_STATE, "a fused shortcut needs the pre-activated input");
+      residual = bsc;
+    } else if (r.cin != r.cout) {
       ConvProblem sc = plain_problem(x, nullptr, (int)T, H, Wd, r.cin, 0, W_(r.ws), r.cout, 1, 1, 1, F_(r.bs), bsc, nullptr);
       WVD_TRY(run_conv(sc, s, conv_flops(P, r.cout, r.cin)));
       residual = bsc;
@@ -1583,6 +1606,7 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
   // the next stage's first residual block takes its SiLU(norm1(x)) from the activated buffer,
   // written by this stage's x2 upsample (its dual store)
   bool stage_pre_act = false;
+  bool stage_sc_ready = false;  // the next stage's first shortcut is in bsc (the upsample's epilogue)
   bool mid_pre_act = false;
   // The mid block's attention, in place on x (level 0, T frames): n = RMS norm of x; q | k | v
   // from one 1x1 conv C -> 3C whose channel thirds go to frames t, T + t, 2T + t; per frame the
@@ -1648,11 +1672,14 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       WVD_HIP(hipMemcpyAsync(bkeep, x, (size_t)T_in * H_in * W_in * st.cin * 2, hipMemcpyDeviceToDevice, s),
               "DupUp3D source copy");
     bool pre_act = stage_pre_act;
+    bool sc_ready = stage_sc_ready;
     stage_pre_act = false;
+    stage_sc_ready = false;
+    if (sc_ready && st.res.empty()) return fail(WVD_ERR_STATE, "a fused shortcut without its block");
     for (size_t k = 0; k < st.res.size(); ++k) {
       const ResPlan& r = st.res[k];
       const bool dual = k + 1 < st.res.size() && st.res[k + 1].cin == r.cout && dual_store_width(r.cout, false);
-      WVD_TRY(resblock(r, x, pre_act, dual ? F_(st.res[k + 1].gamma1) : nullptr));
+      WVD_TRY(resblock(r, x, pre_act, dual ? F_(st.res[k + 1].gamma1) : nullptr, k == 0 && sc_ready));
       pre_act = dual;
       x = bx[cur];
       c = r.cout;
@@ -1705,7 +1732,15 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       // is added to the upsampled output first (DupUp3D) and the widths allow it
       const bool dual = !st.dup && si + 1 < L && !p.stages[si + 1].res.empty() &&
                         p.stages[si + 1].res[0].cin == c && dual_store_width(c, true);
-      if (dual) {
+      const ResPlan* r0 = dual ? &p.stages[si + 1].res[0] : nullptr;
+      if (dual && r0->cout != c && r0->ws >= 0 && shortcut_in_upsample(c, r0->cout, W_(r0->ws), F_(r0->bs))) {
+        // the pre-norm output is read by the block's 1x1 shortcut alone: its product goes to the
+        // shortcut buffer instead, and the stream buffer is not written
+        WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), ba, s, F_(r0->gamma1), d->eps, nullptr,
+                               W_(r0->ws), F_(r0->bs), r0->cout, bsc));
+        stage_pre_act = true;
+        stage_sc_ready = true;
+      } else if (dual) {
         WVD_TRY(run_phase_conv(x, (int)T, H, Wd, c, W_(st.sw), F_(st.sb), ba, s, F_(p.stages[si + 1].res[0].gamma1),
                                d->eps, bx[cur ^ 1]));
         stage_pre_act = true;
@@ -1866,6 +1901,7 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       act = nullptr;
       zbuf = nullptr;
       stage_pre_act = false;  // (the split level's input comes from xm, never pre-activated)
+      stage_sc_ready = false;
       const bf16_t* x = bxm + (size_t)t0 * H0 * W0 * c0;
       for (int si = split; si < L; ++si) {
         WVD_TRY(run_stage(si, x, nullptr));
@@ -1919,6 +1955,11 @@ extern "C" wvd_status wvd_conv_force_config(int config) {
 
 extern "C" wvd_status wvd_decode_fuse_norm1(int on) {
   g_fuse_norm1.store(on ? 1 : 0);
+  return WVD_OK;
+}
+
+extern "C" wvd_status wvd_decode_fuse_shortcut(int on) {
+  g_fuse_shortcut.store(on ? 1 : 0);
   return WVD_OK;
 }
 

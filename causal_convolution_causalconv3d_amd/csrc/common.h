@@ -112,6 +112,14 @@ struct ConvProblem {
   // With a fused norm, optionally also the pre-norm value (bias and residual added, one bf16
   // rounding) in y's layout: the residual stream beside the next block's activated input.
   bf16_t* y_pre;
+  // With the dual store on the 192-channel x2 phase tile, the pre-norm value's 1x1 product in
+  // place of the value itself (the next residual block's shortcut, that value's only reader):
+  // y_sc = sc_w x bf16(pre-norm) + sc_b, fp32 sums, one rounding, in y's layout with sc_co
+  // channels; sc_w row o holds output channel o's 192 weights at sc_w + o * sc_wrow.
+  const bf16_t* sc_w;
+  const float* sc_b;  // [sc_co] or null
+  bf16_t* y_sc;
+  int sc_co, sc_wrow;
   int time_tiles;  // set by the launcher: the halo kernel's tile order
   int staged;      // set by the launcher: store the output through LDS (see conv_epilogue_staged)
   CopyJob copy;    // side work (zero bytes: none)

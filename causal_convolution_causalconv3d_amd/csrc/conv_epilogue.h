@@ -196,10 +196,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 // DUAL (with NORM): the residual (p.res, optional) is added before the norm's statistics, and the
 // pre-norm value (bias and residual added) is stored to p.y_pre beside the activated value in p.y:
 // a residual block's output and the next block's SiLU(norm1(.)) input from one epilogue.
-template <int NB, int MB, bool NORM, int NBP, bool DUAL = false>
+// SC (with DUAL, 192 channels in one tile): instead of the pre-norm value, its 1x1 product with
+// p.sc_w (96 outputs) plus p.sc_b goes to p.y_sc (see ConvProblem::y_sc); sc_lds holds p.sc_w's
+// rows 196 elements apart.
+template <int NB, int MB, bool NORM, int NBP, bool DUAL = false, bool SC = false>
 __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, floatx16 (&acc)[NB][MB], const int (&ph)[MB],
-                                                     int w0, int tf, int n0, int pa, int pb, int lane, char* stage) {
+                                                     int w0, int tf, int n0, int pa, int pb, int lane, char* stage,
+                                                     const bf16_t* sc_lds = nullptr) {
   static_assert(!DUAL || NORM, "the dual store belongs to the fused norm");
+  static_assert(!SC || (DUAL && NB == 6 && NBP == 3), "the shortcut product: 192 channels in, 96-channel passes");
   const float* bias = opaque(p.bias);
   const float* gamma = opaque(p.norm_gamma);
   asm volatile("" : "+v"(lane));  // (the chunk indices below are per call, not hoisted)
@@ -290,6 +295,71 @@ __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, float
       rs[mb] = rsqrtf(ss * inv_n + p.norm_eps);
     }
   }
+  if constexpr (SC) {
+    // The shortcut's 96 x 192 product on the matrix cores, per row of 32 positions: the
+    // accumulators, rounded to bf16 as the pre-norm store would round them, are the second
+    // operand as they lie (K16 step (nb, q): this lane's registers 8q .. 8q + 7 of block nb, i.e.
+    // channels nb * 32 + (2q + j / 4) * 8 + half * 4 + j % 4 for j = 0 .. 7), and the first
+    // operand reads each weight row (in LDS) in that channel order (two 8-byte pieces). Then
+    // + bias, one rounding, and 16-byte stores through the staging area (one 96-channel pass).
+    typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+    const float* bsc = opaque(p.sc_b);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (ph[mb] >= p.H) continue;  // wave-uniform
+      const int orow = p.hmul * ph[mb] + pa;
+      floatx16 sa[3];
+#pragma unroll
+      for (int ob = 0; ob < 3; ++ob)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sa[ob][r] = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          __builtin_amdgcn_sched_barrier(0);
+          u32x4 b;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) b[i] = pack_bf16x2(acc[nb][mb][q * 8 + 2 * i], acc[nb][mb][q * 8 + 2 * i + 1]);
+          u32x4 a[3];
+#pragma unroll
+          for (int ob = 0; ob < 3; ++ob) {
+            const bf16_t* wr = sc_lds + (ob * 32 + l32) * 196 + nb * 32 + q * 16 + half * 4;
+            const uint2 lo = *(const uint2*)wr, hi = *(const uint2*)(wr + 8);
+            a[ob][0] = lo.x;
+            a[ob][1] = lo.y;
+            a[ob][2] = hi.x;
+            a[ob][3] = hi.y;
+          }
+#pragma unroll
+          for (int ob = 0; ob < 3; ++ob)
+            sa[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ob]),
+                                                             __builtin_bit_cast(bf16x8, b), sa[ob], 0, 0, 0);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ob = 0; ob < 3; ++ob)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = ob * 32 + g * 8 + half * 4;
+          const float4 b4 = bsc ? *(const float4*)(bsc + n) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          uint2 o;
+          o.x = pack_bf16x2(sa[ob][g * 4 + 0] + b4.x, sa[ob][g * 4 + 1] + b4.y);
+          o.y = pack_bf16x2(sa[ob][g * 4 + 2] + b4.z, sa[ob][g * 4 + 3] + b4.w);
+          *(uint2*)(stage + l32 * S::PS + n * 2) = o;
+        }
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < S::CPL; ++i) {
+        const int j = i * 64 + lane, q = j / S::CHP, c = j - (j / S::CHP) * S::CHP;
+        const int w = w0 + q;
+        const uint4 o = *(const uint4*)(stage + q * S::PS + c * 16);
+        const int64_t at = (((int64_t)(p.fbase + p.fmul * tf) * p.Ho + orow) * p.Wo + p.wmul * w + pb) * p.sc_co + c * 8;
+        if (w < p.W) store_stream16(p.y_sc + at, o);
+      }
+      wave_lds_sync();
+    }
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     if (ph[mb] >= p.H) continue;  // the whole row is outside the frame (wave-uniform)
@@ -299,7 +369,7 @@ __device__ __forceinline__ void conv_epilogue_staged(const ConvProblem& p, float
       const int cb = n0 + pg * S::NBP * 32;
       if (cb >= p.N) continue;
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (DUAL) {
+      if constexpr (DUAL && !SC) {
         // the pre-norm value (bias and residual already in the accumulators), one rounding
 #pragma unroll
         for (int nl = 0; nl < S::NBP; ++nl) {

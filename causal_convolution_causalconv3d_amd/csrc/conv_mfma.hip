@@ -602,11 +602,12 @@ __device__ __forceinline__ void lds_ops_done() { __builtin_amdgcn_s_waitcnt(0xC0
 template <int NB, int MB, int KS>
 constexpr int dma_waves_per_simd() { return (KS == 2 && MB == 1 && NB <= 3) ? 4 : 2; }
 
-template <int NB, int MB, int WAVES, int KS, bool NORM, bool DUAL = false, bool TAIL = false>
+template <int NB, int MB, int WAVES, int KS, bool NORM, bool DUAL = false, bool TAIL = false, bool SC = false>
 __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, KS>() * 4 / WAVES)) void conv_halo_dma_kernel(
     const ConvProblem p) {
   static_assert(KS == 2 || KS == 3, "3x3 taps, or 2x2 phase taps");
   static_assert(!TAIL || (KS == 2 && NB == 3 && MB == 1 && WAVES == 8 && NORM && !DUAL), "the fused tail's tile");
+  static_assert(!SC || (KS == 2 && NB == 6 && MB == 1 && WAVES == 8 && DUAL && !TAIL), "the shortcut product's tile");
   constexpr int SPS = KS * KS;
   // weight fetch distance D (steps ahead), slots NWS (> D, and k mod NWS a compile-time
   // function of the stage parity and the tap), barrier wait window WW = D - 2 steps (must not
@@ -654,6 +655,11 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
   // colour a 16-byte group of the three temporal taps' sums and a pad).
   constexpr int TZR = 104, TCR = 2 * TR + 2, TCC = 66, TCP = 12;
   __shared__ __attribute__((aligned(16))) bf16_t lds_hz[TAIL ? 96 * TZR : 8];
+  // The shortcut product's weight (SC): 96 rows of 192 channels, rows 196 elements apart (392
+  // bytes: the 8-byte operand reads of 32 rows fall on distinct banks), loaded once per
+  // workgroup; beside the 112 KB of the 192-wide phase tile it still fits the CU's LDS.
+  constexpr int SCR = 196;
+  __shared__ __attribute__((aligned(16))) bf16_t lds_sc[SC ? 96 * SCR : 4];
   __shared__ __attribute__((aligned(16))) float lds_tc[TAIL ? TCR * TCC * TCP : 4];
   auto wslot = [&](auto I) -> bf16_t* {
     constexpr int i = decltype(I)::value;
@@ -905,6 +911,18 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
     }
   }
 
+  // SC: this thread's 16-byte pieces of the shortcut weight (96 rows x 24 pieces), fetched
+  // before the prologue's fetches and written to LDS after its full wait
+  constexpr int SCN = SC ? (96 * 24 + WAVES * 64 - 1) / (WAVES * 64) : 1;
+  uint4 scv[SCN];
+  if constexpr (SC) {
+#pragma unroll
+    for (int i = 0; i < SCN; ++i) {
+      const int j = i * WAVES * 64 + tid;
+      scv[i] = j < 96 * 24 ? *(const uint4*)(p.sc_w + (int64_t)(j / 24) * p.sc_wrow + (j % 24) * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
   // prologue: the first tile's first stage (patch and steps 0 .. D - 1, all in stage 0)
   patch_offsets(tc);
   Stage cur = stage_at(0, 0, 0);
@@ -916,6 +934,17 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
   if constexpr (D >= 4) fetch_w(I3{}, cur.col + 3 * p.Cip, rs_cur);
   if constexpr (D == 5) fetch_w(I4{}, cur.col + 4 * p.Cip, rs_cur);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if constexpr (SC) {
+#pragma unroll
+    for (int i = 0; i < SCN; ++i) {
+      const int j = i * WAVES * 64 + tid;
+      if (j < 96 * 24) {
+        uint2* d = (uint2*)(lds_sc + (j / 24) * SCR + (j % 24) * 8);
+        d[0] = make_uint2(scv[i].x, scv[i].y);
+        d[1] = make_uint2(scv[i].z, scv[i].w);
+      }
+    }
+  }
   lds_barrier();
   read_a(wf[0], I0{}, 0);
   read_b(bf[0], I0{}, 0, 0);
@@ -1026,7 +1055,8 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
         const int r = wave - 2 * PCAP;
         st = ((r / WCAP == 0) ? (char*)wslot(I0{}) : (char*)wslot(I1{})) + (r % WCAP) * SB;
       }
-      conv_epilogue_staged<NB, MB, NORM, NBP1, DUAL>(p, acc, ph, tc.w0, tc.tf, tc.n0, pa, pb, lane, st);
+      conv_epilogue_staged<NB, MB, NORM, NBP1, DUAL, SC>(p, acc, ph, tc.w0, tc.tf, tc.n0, pa, pb, lane, st,
+                                                         lds_sc);
     } else if constexpr (!DUAL) {  // (the launcher stages every dual-store launch)
       int pw[MB];
       bool pv[MB];
@@ -1338,6 +1368,12 @@ struct ConfigEntry {
   { "conv_tail_phase_head_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, 0, \
     conv_halo_dma_kernel<NB, MB, W, 2, true, false, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, false, true>, \
     nullptr }
+// The 192-wide x2 phase tile with the dual store whose pre-norm value is replaced by its 1x1
+// product (ConvProblem::y_sc; only for problems with y_sc set, never chosen or forced for others).
+#define WVD_PHASE_SC_CONFIG(NB, MB, W) \
+  { "conv_phase_halo_dma_sc_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<NB, MB, 2>() * 4 / W, \
+    conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true>, \
+    conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true> }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
   { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
     conv_halo_kernel<NB, MB, W, 2, true>, nullptr }
@@ -1370,6 +1406,7 @@ enum ConfigId {
   HALO_DMA_N4_W8,  // 128 x (16 rows x 32 columns): channel counts that are multiples of 128, not of 96
   PHASE_DMA_N6_M1_W8,  // x2 upsampling phases: 192 x (8 rows x 32 columns), one row per wave, 112 KB
   TAIL_N3_M1_W8,       // the fused tail: PHASE_DMA_N3_M1_W8's tiles, all phases and frames of a block
+  PHASE_DMA_SC_N6_M1_W8,  // PHASE_DMA_N6_M1_W8's dual store with the shortcut product (y_sc)
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -1380,7 +1417,7 @@ const ConfigEntry kConfigs[] = {
     WVD_HALO_DMA_DUAL_CONFIG(6, 1, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 8), WVD_PHASE_HALO_DMA_CONFIG(3, 2, 4),
     WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),    WVD_HALO_DMA_CONFIG(1, 2, 8),
     WVD_CONV_CONFIG(4, 1, 8),           WVD_HALO_DMA_CONFIG(3, 2, 4),    WVD_HALO_DMA_PLAIN_CONFIG(4, 2, 8),
-    WVD_PHASE_HALO_DMA_DUAL_CONFIG(6, 1, 8), WVD_TAIL_CONFIG(3, 1, 8),
+    WVD_PHASE_HALO_DMA_DUAL_CONFIG(6, 1, 8), WVD_TAIL_CONFIG(3, 1, 8), WVD_PHASE_SC_CONFIG(6, 1, 8),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -1478,6 +1515,7 @@ int conv_config_count() { return kNumConfigs; }
 bool conv_config_fits(const ConvProblem& p, int id) {
   if (id < 0 || id >= kNumConfigs) return false;
   if ((id == TAIL_N3_M1_W8) != (p.head_w != nullptr)) return false;
+  if ((id == PHASE_DMA_SC_N6_M1_W8) != (p.y_sc != nullptr)) return false;
   const ConfigEntry& c = kConfigs[id];
   if (c.halo == 3 && !(p.phases == 1 && p.kh == 3 && p.kw == 3)) return false;
   if (c.halo == 2 && !(p.phases == 4 && p.kh == 2 && p.kw == 2)) return false;
@@ -1517,7 +1555,16 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   if (p.norm_gamma && (!conv_can_fuse_norm(p.N, p.bias, p.norm_gamma) || (p.res && !p.y_pre) || p.y_f32 ||
                        p.nsplit != p.N))
     return hipErrorInvalidValue;
-  int id = choose_config(p, p.norm_gamma != nullptr);
+  if (p.y_sc) {
+    // the shortcut product in the dual store's place: the 192-wide x2 phase tile with a fused
+    // norm, 96 shortcut outputs of all 192 channels, no pre-norm store or residual (the fused norm
+    // keeps all channels in one frame: nsplit == N, checked below)
+    if (!p.norm_gamma || p.y_pre || p.res || p.phases != 4 || p.kh != 2 || p.kw != 2 || p.N != 192 ||
+        p.Npad != 192 || p.sc_co != 96 || !p.sc_w || p.sc_wrow < 192 || p.sc_wrow % 8 ||
+        ((uintptr_t)p.sc_w & 15) || ((uintptr_t)p.sc_b & 15) || ((uintptr_t)p.y_sc & 15))
+      return hipErrorInvalidValue;
+  }
+  int id = p.y_sc ? PHASE_DMA_SC_N6_M1_W8 : choose_config(p, p.norm_gamma != nullptr);
   if (force_config >= 0) {
     if (!conv_config_fits(p, force_config)) return hipErrorNotSupported;
     id = force_config;
@@ -1536,7 +1583,7 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   const bool lin_staged = c.halo == 0 && c.mb == 1 && plain_map && !p.norm_gamma;
   q.staged = (c.staged || lin_staged) && !p.y_f32 && p.N % 8 == 0 && p.nsplit % 8 == 0 &&
              ((uintptr_t)p.y & 15) == 0 && ((uintptr_t)p.res & 15) == 0 && ((uintptr_t)p.y_pre & 15) == 0;
-  if (p.y_pre && !q.staged) return hipErrorNotSupported;  // the dual store exists staged only
+  if ((p.y_pre || p.y_sc) && !q.staged) return hipErrorNotSupported;  // the dual store exists staged only
   int64_t gx = c.phase_in_x ? blocks * p.phases : blocks;
   if (c.wgs_per_cu) {
     // DMA kernels: a multiple of 8 workgroups (XCD ranges); with persistent tiles no more than
@@ -1548,7 +1595,7 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
     }
   }
   if (gx > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(p.y_pre ? c.kernel_dual : (p.norm_gamma ? c.kernel_norm : c.kernel),
+  hipLaunchKernelGGL((p.y_pre || p.y_sc) ? c.kernel_dual : (p.norm_gamma ? c.kernel_norm : c.kernel),
                      dim3((unsigned)gx, 1, c.phase_in_x ? 1 : p.phases),
                      dim3(c.waves * 64), 0, s, q);
   return hipGetLastError();

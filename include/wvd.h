@@ -344,6 +344,16 @@ wvd_status wvd_conv_max_workgroups(int n);
  * are bitwise independent of the pass size. Process-wide; not for use while another thread
  * decodes. */
 wvd_status wvd_decode_fuse_norm1(int on);
+/* Tuning: with on != 0 (the default), when an x2 upsample of 192 channels stores both its output
+ * and the next block's activated input (wvd_decode_fuse_norm1) and that block starts with a 1x1
+ * shortcut to 96 channels (the page's residual block part: cin != cout), the upsample's epilogue
+ * applies the shortcut (plus its bias) to its own output, rounded to bf16 as the stored output
+ * would be, and stores that product instead of the output, which the shortcut alone would read;
+ * the shortcut pass goes. With on == 0 the output is stored and the shortcut runs as its own
+ * pass. The two videos differ by the summation order of the shortcut only; either way decodes
+ * are bitwise independent of the pass size. Process-wide; not for use while another thread
+ * decodes. */
+wvd_status wvd_decode_fuse_shortcut(int on);
 /* Memory option: with on != 0, a decoder whose last stage is a spatial x2 upsample (no time
  * step, no DupUp3D) of 65-96 channels and whose head is conv_out to at most 3 colours (no
  * unpatchify or clamp) runs that upsample, norm_out + SiLU and the head as one kernel per pass:

@@ -154,7 +154,10 @@ def test_spatial_upsample_every_config_matches_oracle(C, T, H, W):
             try:
                 y = wvd.upsample(xd, spatial=wp, spatial_bias=bd)
             except wvd.WvdError as e:
-                assert e.status == 8 and name.startswith(("conv_halo", "conv_tail")), (name, str(e))
+                # (3x3 halo tiles; the fused tail and the shortcut-product tile, which run only
+                # with the head or the shortcut attached)
+                assert e.status == 8 and name.startswith(("conv_halo", "conv_tail", "conv_phase_halo_dma_sc")), (
+                    name, str(e))
                 continue
             torch.cuda.synchronize()
             assert torch.equal(y, auto), name
@@ -604,6 +607,45 @@ def test_decoder_with_norm1_fused_matches_oracle_and_is_pass_size_invariant(rule
     finally:
         wvd.decode_fuse_norm1(True)
     assert not np.array_equal(got[True], got[False])  # the fused path did run
+    assert psnr(got[True], got[False]) >= 55.0
+
+
+# a 192 -> 96 stage change after a 192-channel x2 upsample with the dual store: the first block's
+# shortcut in that upsample's epilogue (the full decoder's 176x312 -> 352x624 step)
+SC_GPU = wl.DecoderSpec(z_channels=16, base_channels=64, stage_channels=(64, 64, 192, 96))
+
+
+@pytest.mark.parametrize("rule,hw", [(True, (5, 7)), (False, (3, 9))])
+def test_decoder_with_shortcut_in_upsample_matches_oracle_and_is_pass_size_invariant(rule, hw):
+    """wvd_decode_fuse_shortcut: the 192 -> 96 block's 1x1 shortcut applied in the epilogue of the
+    x2 upsample that produces its input (the default), or as its own pass. Both against the
+    oracle, each with the same bits for every pass size and per-level sub-passes, within rounding
+    of each other, and the fused launch seen in the timing records only when on."""
+    z, params = wl.decoder_weights(SC_GPU, seed=56, latent_frames=3, latent_hw=hw)
+    ref = oracle.decode(z[0], oracle.as_numpy_params(params), SC_GPU, frames_per_pass=3, first_frame_rule=rule)
+    dec = _gpu_decoder(SC_GPU, params, hw)
+    zd = z.to(torch.bfloat16).cuda()
+    got = {}
+    wvd.timing_enable(True)
+    try:
+        for fused in (False, True):
+            wvd.decode_fuse_shortcut(fused)
+            wvd.timing_reset()
+            videos = [dec.decode(zd, frames_per_pass=f, first_frame_rule=rule).clone() for f in (3, 1, 2)]
+            videos.append(dec.decode(zd, frames_per_pass=1, first_frame_rule=rule, early_frames_per_pass=3))
+            torch.cuda.synchronize()
+            ran = wvd.timing_read()
+            assert ("conv_phase_halo_dma_sc_n6_m1_w8" in ran) == fused, sorted(ran)
+            for v in videos[1:]:
+                assert torch.equal(v, videos[0]), fused
+            got[fused] = videos[0][0].float().cpu().numpy()
+            log(f"shortcut {'in the upsample' if fused else 'separate'} rule={rule} hw={hw}: "
+                f"psnr {psnr(got[fused], ref):.2f} dB vs oracle")
+            assert psnr(got[fused], ref) >= 55.0
+    finally:
+        wvd.decode_fuse_shortcut(True)
+        wvd.timing_enable(False)
+    assert not np.array_equal(got[True], got[False])
     assert psnr(got[True], got[False]) >= 55.0
 
 
