@@ -925,6 +925,7 @@ struct Plan {
   int head_plain;  // conv_out as a plain 3x3x3 conv, then unpatchify (+ clamp) into the video
   int norm_out, out_w, out_b, out_slot;
   int tail_kernel;  // the fused tail kernel runs the last upsample and the head (out_slot: its carry)
+  int head_carry;   // the input-stationary head (out_slot: its carried partial Z sums, two halves)
   std::vector<Slot> slots;
   size_t packed_bytes, cache_bytes;
 };
@@ -1099,6 +1100,15 @@ Plan make_plan(const wvd_decoder_desc* d) {
     Slot& s = p.slots[p.out_slot];
     s.frame_bytes = (size_t)(d->latent_h << p.levels) * (size_t)(d->latent_w << p.levels) * 3 * 4;
     s.alloc = 2 * s.frame_bytes;
+  }
+  p.head_carry = !p.tail_kernel && !p.head_plain && head_stream_supported((int)round_up(c, 32), d->out_channels);
+  if (p.head_carry) {
+    // the input-stationary head's carry: Z of the next two output frames as far as the frames
+    // before them contribute ([2][7][H][W] fp32 x 4 per half), double-buffered (every tile reads
+    // its neighbours' positions before they may have written theirs)
+    Slot& s = p.slots[p.out_slot];
+    s.frame_bytes = head_stream_carry_frame_bytes(d->latent_h << p.levels, d->latent_w << p.levels);
+    s.alloc = 4 * s.frame_bytes;
   }
   size_t off = 0;
   for (auto& q : p.params) {
@@ -1787,10 +1797,30 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
     const int co = d->out_channels;
     const int cip = (int)round_up(c, 32);
     if (head_stream_supported(cip, co) || head_fused_supported(cip)) {
-      // tap conv + stencil in one kernel (no tap planes in memory); reads the activation (and
-      // its history) once, writes co bf16 channels; the input-stationary kernel up to 96
-      // channels and 3 colours
+      // tap conv + stencil in one kernel (no tap planes in memory); reads the activation once,
+      // writes co bf16 channels; the input-stationary kernel up to 96 channels and 3 colours
+      // (with the frames before it as a carry), else the frame-tiled one (with the slot's
+      // history frames)
       const int slot = p.out_slot;
+      if (head_stream_supported(cip, co)) {
+        // the frames before this launch come in as the carried partial sums of the slot's
+        // current half; the launch leaves its own in the other half
+        if (!p.head_carry) return fail(WVD_ERR_STATE, "the head's cache slot holds no carry");
+        if (T == 0) return WVD_OK;
+        const size_t cfb = p.slots[slot].frame_bytes;
+        char* sp = (char*)slot_ptr(slot);
+        const float* cin = cache->valid[slot] ? (const float*)(sp + (size_t)cache->half[slot] * 2 * cfb) : nullptr;
+        float* cout = (float*)(sp + (size_t)(cache->half[slot] ^ 1) * 2 * cfb);
+        // reads the activation once and both carries, writes co bf16 channels
+        const double hb = (double)P * c * 2.0 + (double)P * co * 2.0 + (cin ? 2.0 : 0.0) * cfb + 2.0 * cfb;
+        WVD_TRY(run_mem(MEM_HEAD_STREAM, hb, s, "head launch", [&] {
+          return launch_head_stream(act, (int)T, H, Wd, c, cip, (const bf16_t*)W_(p.out_w), F_(p.out_b), co,
+                                    (bf16_t*)video->data, video->t, (int)fo, cin, cout, s);
+        }));
+        cache->half[slot] ^= 1;
+        cache->valid[slot] = (int)std::min<int64_t>(2, cache->valid[slot] + T);
+        return WVD_OK;
+      }
       const bf16_t* hist = slot_hist(slot);
       const int Th = cache->valid[slot];
       const double hb = (double)(T + std::min(Th, 2)) * H * Wd * c * 2.0 + (double)P * co * 2.0;
@@ -1798,17 +1828,10 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
       int v = cache->valid[slot], h = cache->half[slot];
       CopyJob job;
       slot_update_job((char*)slot_ptr(slot), h, v, act, (int)T, p.slots[slot].frame_bytes, job);
-      if (head_stream_supported(cip, co)) {
-        WVD_TRY(run_mem(MEM_HEAD_STREAM, hb, s, "head launch", [&] {
-          return launch_head_stream(act, hist, Th, (int)T, H, Wd, c, cip, (const bf16_t*)W_(p.out_w), F_(p.out_b), co,
-                                    (bf16_t*)video->data, video->t, (int)fo, s, &job);
-        }));
-      } else {
-        WVD_TRY(run_mem(MEM_HEAD_FUSED, hb, s, "head launch", [&] {
-          return launch_head_fused(act, hist, Th, (int)T, H, Wd, c, cip, (const bf16_t*)W_(p.out_w), F_(p.out_b), co,
-                                   (bf16_t*)video->data, video->t, (int)fo, s, &job);
-        }));
-      }
+      WVD_TRY(run_mem(MEM_HEAD_FUSED, hb, s, "head launch", [&] {
+        return launch_head_fused(act, hist, Th, (int)T, H, Wd, c, cip, (const bf16_t*)W_(p.out_w), F_(p.out_b), co,
+                                 (bf16_t*)video->data, video->t, (int)fo, s, &job);
+      }));
       cache->valid[slot] = v;
       cache->half[slot] = h;
       return WVD_OK;

@@ -205,9 +205,13 @@ hipError_t launch_wino_in(const bf16_t* x, const bf16_t* hist, int T, int Th, in
                           hipStream_t s);
 hipError_t launch_wino_out(const float* M, int T, int H, int W, int Co, const float* bias, const bf16_t* res,
                            bf16_t* y, hipStream_t s);
-hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
-                              const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
-                              hipStream_t s, const CopyJob* copy = nullptr);
+// The input-stationary head over T frames of x, its temporal taps from the frames before them
+// carried in (cin: the partial sums left by the previous launch, or null for none) and out (cout,
+// a different buffer of head_stream_carry_frame_bytes(H, W) * 2 bytes).
+size_t head_stream_carry_frame_bytes(int H, int W);
+hipError_t launch_head_stream(const bf16_t* x, int T, int H, int W, int C, int Cip, const bf16_t* wpk,
+                              const float* bias, int Co, bf16_t* video, int64_t frames, int fbase, const float* cin,
+                              float* cout, hipStream_t s);
 hipError_t launch_head_fused(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
                              const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
                              hipStream_t s, const CopyJob* copy = nullptr);

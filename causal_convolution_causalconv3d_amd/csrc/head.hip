@@ -230,19 +230,31 @@ __global__ __launch_bounds__(512, 1) void head_fused_kernel(const bf16_t* __rest
 // tap, and only the 27 tap channels in use (9 taps x 3 colours, one 32-row matrix block) are
 // computed. The next frame's operands load into registers while the current one computes. The
 // sum order of a Z value is temporal tap outermost, then chunk, then K half.
+//
+// The frames before the launch enter as a carry instead of as input frames: Z of the launch's
+// output frames 0 and 1 as far as those earlier frames contribute (taps 0 and 1 of frame 0, tap
+// 0 of frame 1), the two accumulators as they stood after the previous launch's last frame, in
+// fp32. The launch starts its accumulators from them and leaves its own in `cout`, so a decode in
+// several launches sums every Z value in the same order as one launch over all frames (same
+// bits), reads no history frames and copies none. Carry layout, per buffer: [2 frames][7 planes]
+// [H][W] float4, plane 2g + half holding rows 8g + 4 half + {0..3} of a position's Z column
+// (rows 0-27; rows 28-31 have no weights and are always 0). Each tile reads the carry of all its
+// 16 x 32 positions and writes that of its 14 x 30 interior (the tiles' interiors partition the
+// frame), so `cin` and `cout` must be different buffers.
 constexpr int HS_N = 27;  // tap rows kept: tap * 3 + colour
 constexpr int HS_ZS = 28; // LDS floats per position for Z (27 + pad, 16-byte aligned rows)
+constexpr int HS_CP = 7;  // carry planes (float4) per position and frame
 
 template <int NCH>
-__global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ hist,
-                                                             int Th, int T, int H, int W, int C,
+__global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __restrict__ x, int T, int H, int W, int C,
                                                              const bf16_t* __restrict__ wpk, const float* __restrict__ bias,
                                                              int Co, bf16_t* __restrict__ video, int64_t frames, int fbase,
-                                                             const CopyJob copy) {
+                                                             const float4* __restrict__ cin, float4* __restrict__ cout) {
   constexpr int Cip = NCH * 32;
   __shared__ __attribute__((aligned(16))) bf16_t wl[32 * HF_WROW];
   __shared__ __attribute__((aligned(16))) float zs[HF_ROWS * HF_COLS * HS_ZS];
   typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int numR = (H + HF_OROWS - 1) / HF_OROWS, numC = (W + HF_OCOLS - 1) / HF_OCOLS;
@@ -251,10 +263,7 @@ __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __res
   const int xcd = b & 7, local = b >> 3;
   const int q8 = total >> 3, r8 = total & 7;
   const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
-  if (lin >= total) {
-    run_copy_share(copy);
-    return;
-  }
+  if (lin >= total) return;
   // Tiles in bands of HS_BAND tile rows, each band walked column by column: the workgroups an XCD
   // runs at once (a run of consecutive tiles) then cover a 2D block of the frame, so a tile's
   // halo rows and columns, which its neighbours above, below and beside read too, are read
@@ -278,6 +287,7 @@ __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __res
 
   // this lane's positions: tile rows 2*wave + mb (image row h0 - 1 + that), column l32
   const int64_t frame_elems = (int64_t)H * W * C;
+  const int HW = H * W;  // (< 2^30: a frame of C >= 1 channels is under 2^31 bytes)
   const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
   uint32_t poff[2];
   bool pin[2];
@@ -285,11 +295,13 @@ __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __res
   for (int mb = 0; mb < 2; ++mb) {
     const int hh = h0 - 1 + 2 * wave + mb, ww = w0 - 1 + l32;
     pin[mb] = (hh >= 0) & (hh < H) & (ww >= 0) & (ww < W);
-    poff[mb] = pin[mb] ? (uint32_t)(((int64_t)hh * W + ww) * C * 2) : 0u;
+    poff[mb] = pin[mb] ? (uint32_t)((hh * W + ww) * C * 2) : 0u;
   }
-  // the operands of frame f (negative: history), all chunks
+  // carry index of this lane's position of tile row 2*wave + mb (frame 0, plane 0)
+  auto cpos = [&](int mb) { return (h0 - 1 + 2 * wave + mb) * W + (w0 - 1 + l32); };
+  // the operands of frame f, all chunks
   auto load_frame = [&](u32x4 (&dst)[NCH][2][2], int f) {
-    const bf16_t* fb = (f >= 0) ? x + (int64_t)f * frame_elems : hist + (int64_t)(f + Th) * frame_elems;
+    const bf16_t* fb = x + (int64_t)f * frame_elems;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)fb, (short)0, (int)frame_bytes, 0x00020000);
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
@@ -303,11 +315,32 @@ __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __res
         }
   };
 
-  floatx16 za[2], zb[2], zc[2];  // Z_f, Z_{f+1}, Z_{f+2} while frame f is consumed
+  u32x4 breg[2][NCH][2][2];
+  load_frame(breg[0], 0);
+
+  // Z_f, Z_{f+1}, Z_{f+2} while frame f is consumed; Z_0 and Z_1 start from the carry
+  floatx16 za[2], zb[2], zc[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) za[mb][r] = zb[mb][r] = zc[mb][r] = 0.0f;
+    for (int g = 0; g < 4; ++g) {
+      const int pl = 2 * g + half;
+      float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), c = a;
+      if (cin && pin[mb] && pl < HS_CP) {
+        a = cin[pl * HW + cpos(mb)];
+        c = cin[(HS_CP + pl) * HW + cpos(mb)];
+      }
+      za[mb][g * 4 + 0] = a.x;
+      za[mb][g * 4 + 1] = a.y;
+      za[mb][g * 4 + 2] = a.z;
+      za[mb][g * 4 + 3] = a.w;
+      zb[mb][g * 4 + 0] = c.x;
+      zb[mb][g * 4 + 1] = c.y;
+      zb[mb][g * 4 + 2] = c.z;
+      zb[mb][g * 4 + 3] = c.w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zc[mb][g * 4 + e] = 0.0f;
+    }
   // frame f's contributions: tap 0 to Z_{f+2}, tap 1 to Z_{f+1}, tap 2 to Z_f
   auto consume = [&](const u32x4 (&bf)[NCH][2][2]) {
 #pragma unroll
@@ -326,45 +359,61 @@ __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __res
         }
       }
   };
+  // the carry of the next launch (after the last frame): Z of its frames 0 and 1 so far, at this
+  // tile's interior positions (tile rows 1 .. 14, columns 1 .. 30); streamed out past the L2,
+  // since the next read comes after a whole upsample launch
+  auto store_carry = [&]() {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int trow = 2 * wave + mb;
+      if (!(pin[mb] & (trow >= 1) & (trow <= HF_OROWS) & (l32 >= 1) & (l32 <= HF_OCOLS))) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int pl = 2 * g + half;
+        if (pl >= HS_CP) continue;
+        const f32x4v a = {za[mb][g * 4 + 0], za[mb][g * 4 + 1], za[mb][g * 4 + 2], za[mb][g * 4 + 3]};
+        const f32x4v c = {zb[mb][g * 4 + 0], zb[mb][g * 4 + 1], zb[mb][g * 4 + 2], zb[mb][g * 4 + 3]};
+        __builtin_nontemporal_store(a, (f32x4v*)(cout + pl * HW + cpos(mb)));
+        __builtin_nontemporal_store(c, (f32x4v*)(cout + (HS_CP + pl) * HW + cpos(mb)));
+      }
+    }
+  };
   float bo[3];
 #pragma unroll
   for (int o = 0; o < 3; ++o) bo[o] = (bias && o < Co) ? bias[o] : 0.0f;
   // Z_t (in za) through LDS to the stencil, then the rotation
   auto finish = [&](int t) {
-    if (t >= 0) {
-      __syncthreads();  // the previous frame's stencil is done with zs
+    __syncthreads();  // the previous frame's stencil is done with zs
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        float* zp = zs + ((2 * wave + mb) * HF_COLS + l32) * HS_ZS;
+    for (int mb = 0; mb < 2; ++mb) {
+      float* zp = zs + ((2 * wave + mb) * HF_COLS + l32) * HS_ZS;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = g * 8 + half * 4;
-          if (n < HS_N)
-            *(float4*)(zp + n) = make_float4(za[mb][g * 4], za[mb][g * 4 + 1], za[mb][g * 4 + 2], za[mb][g * 4 + 3]);
-        }
+      for (int g = 0; g < 4; ++g) {
+        const int n = g * 8 + half * 4;
+        if (n < HS_N)
+          *(float4*)(zp + n) = make_float4(za[mb][g * 4], za[mb][g * 4 + 1], za[mb][g * 4 + 2], za[mb][g * 4 + 3]);
       }
-      __syncthreads();
-      if (tid < HF_OROWS * HF_OCOLS) {
-        const int orow = tid / HF_OCOLS, ocol = tid - orow * HF_OCOLS;
-        const int h = h0 + orow, w = w0 + ocol;
-        if (h < H && w < W) {
-          float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
+    }
+    __syncthreads();
+    if (tid < HF_OROWS * HF_OCOLS) {
+      const int orow = tid / HF_OCOLS, ocol = tid - orow * HF_OCOLS;
+      const int h = h0 + orow, w = w0 + ocol;
+      if (h < H && w < W) {
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
 #pragma unroll
-          for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < 3; ++j)
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-              const float* z = zs + ((orow + j) * HF_COLS + ocol + k) * HS_ZS + (j * 3 + k) * 3;
-              a0 += z[0];
-              a1 += z[1];
-              a2 += z[2];
-            }
-          const int64_t HW = (int64_t)H * W;
-          const int64_t pix = (int64_t)(fbase + t) * HW + (int64_t)h * W + w;
-          const float av[3] = {a0, a1, a2};
+          for (int k = 0; k < 3; ++k) {
+            const float* z = zs + ((orow + j) * HF_COLS + ocol + k) * HS_ZS + (j * 3 + k) * 3;
+            a0 += z[0];
+            a1 += z[1];
+            a2 += z[2];
+          }
+        const int64_t pix = (int64_t)(fbase + t) * HW + h * W + w;
+        const float av[3] = {a0, a1, a2};
 #pragma unroll
-          for (int o = 0; o < 3; ++o)
-            if (o < Co) video[(int64_t)o * frames * HW + pix] = (bf16_t)f32_to_bf16(av[o] + bo[o]);
-        }
+        for (int o = 0; o < 3; ++o)
+          if (o < Co) video[(int64_t)o * frames * HW + pix] = (bf16_t)f32_to_bf16(av[o] + bo[o]);
       }
     }
 #pragma unroll
@@ -376,21 +425,29 @@ __global__ __launch_bounds__(512, 1) void head_stream_kernel(const bf16_t* __res
     }
   };
 
-  // frames before the history are zero: start at the oldest frame held
-  const int f0 = -(Th < 2 ? Th : 2);
-  u32x4 breg[2][NCH][2][2];
-  load_frame(breg[0], f0);
   __syncthreads();  // weights in place
-  for (int f = f0; f < T; f += 2) {
-    if (f + 1 < T) load_frame(breg[1], f + 1);
+  // frames in pairs while a frame follows the pair, then the last one or two: the loop has one
+  // exit, so the accumulators leave it in fixed registers for the carry's stores
+  int f = 0;
+  for (; f + 2 < T; f += 2) {
+    load_frame(breg[1], f + 1);
     consume(breg[0]);
     finish(f);
-    if (f + 1 >= T) break;
-    if (f + 2 < T) load_frame(breg[0], f + 2);
+    load_frame(breg[0], f + 2);
     consume(breg[1]);
     finish(f + 1);
   }
-  run_copy_share(copy);
+  if (f + 1 < T) {
+    load_frame(breg[1], f + 1);
+    consume(breg[0]);
+    finish(f);
+    consume(breg[1]);
+    finish(f + 1);
+  } else {
+    consume(breg[0]);
+    finish(f);
+  }
+  store_carry();
 }
 
 }  // namespace
@@ -406,28 +463,31 @@ bool head_fused_supported(int Cip) { return Cip % 32 == 0 && Cip <= HF_MAXCIP; }
 
 bool head_stream_supported(int Cip, int Co) { return Cip % 32 == 0 && Cip <= 96 && Co <= 3; }
 
-hipError_t launch_head_stream(const bf16_t* x, const bf16_t* hist, int Th, int T, int H, int W, int C, int Cip,
-                              const bf16_t* wpk, const float* bias, int Co, bf16_t* video, int64_t frames, int fbase,
-                              hipStream_t s, const CopyJob* copy) {
-  const CopyJob job = copy ? *copy : CopyJob{};
+size_t head_stream_carry_frame_bytes(int H, int W) { return (size_t)H * W * HS_CP * 16; }
+
+hipError_t launch_head_stream(const bf16_t* x, int T, int H, int W, int C, int Cip, const bf16_t* wpk,
+                              const float* bias, int Co, bf16_t* video, int64_t frames, int fbase, const float* cin,
+                              float* cout, hipStream_t s) {
   if (T == 0 || H == 0 || W == 0) return hipSuccess;
-  if (!head_stream_supported(Cip, Co) || C > Cip || (int64_t)H * W * C * 2 >= ((int64_t)1 << 31) || Th < 0 ||
-      (Th > 0 && !hist))
+  if (!head_stream_supported(Cip, Co) || C > Cip || (int64_t)H * W * C * 2 >= ((int64_t)1 << 31) || !cout ||
+      cout == cin || ((uintptr_t)cin & 15u) || ((uintptr_t)cout & 15u))
     return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)((H + HF_OROWS - 1) / HF_OROWS) * ((W + HF_OCOLS - 1) / HF_OCOLS);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const float4* ci = (const float4*)cin;
+  float4* co = (float4*)cout;
   switch (Cip / 32) {
     case 1:
-      hipLaunchKernelGGL(head_stream_kernel<1>, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, wpk,
-                         bias, Co, video, frames, fbase, job);
+      hipLaunchKernelGGL(head_stream_kernel<1>, dim3((unsigned)blocks), dim3(512), 0, s, x, T, H, W, C, wpk, bias, Co,
+                         video, frames, fbase, ci, co);
       break;
     case 2:
-      hipLaunchKernelGGL(head_stream_kernel<2>, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, wpk,
-                         bias, Co, video, frames, fbase, job);
+      hipLaunchKernelGGL(head_stream_kernel<2>, dim3((unsigned)blocks), dim3(512), 0, s, x, T, H, W, C, wpk, bias, Co,
+                         video, frames, fbase, ci, co);
       break;
     default:
-      hipLaunchKernelGGL(head_stream_kernel<3>, dim3((unsigned)blocks), dim3(512), 0, s, x, hist, Th, T, H, W, C, wpk,
-                         bias, Co, video, frames, fbase, job);
+      hipLaunchKernelGGL(head_stream_kernel<3>, dim3((unsigned)blocks), dim3(512), 0, s, x, T, H, W, C, wpk, bias, Co,
+                         video, frames, fbase, ci, co);
       break;
   }
   return hipGetLastError();

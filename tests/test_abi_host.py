@@ -47,9 +47,10 @@ def test_sizes():
     assert L.wvd_conv_packed_bytes(3, 96, 3, 3, 3, 0) == 32 * 27 * 96 * 2
     assert L.wvd_conv_packed_bytes(96, 96, 1, 3, 3, 1) == 4 * 96 * 4 * 96 * 2
     assert L.wvd_conv_packed_bytes(48, 48, 2, 3, 3, 0) == 0
-    # cache: two frames per causal conv input, twice (the current history and the next one); with
-    # the fused tail the head's slot holds instead the partial sums of the two output frames after
-    # a pass (2 x 3 colours x 704 x 1248 fp32)
+    # cache: two frames per causal conv input, twice (the current history and the next one); the
+    # input-stationary head's slot holds instead its carried partial tap sums (two frames of 28
+    # fp32 per position, twice), and with the fused tail the partial sums of the two output frames
+    # after a pass (2 x 3 colours x 704 x 1248 fp32)
     cache = L.wvd_cache_bytes(ctypes.byref(desc))
     ws4 = L.wvd_decode_workspace_bytes(ctypes.byref(desc), 4)
     ws8 = L.wvd_decode_workspace_bytes(ctypes.byref(desc), 8)
@@ -62,8 +63,8 @@ def test_sizes():
         wvd.decode_fuse_head(False)
     up = lambda n: (n + 255) // 256 * 256
     px = 704 * 1248
-    assert cache - cache_on == up(4 * px * 96 * 2) - up(2 * 3 * px * 4)
-    assert 2.0e9 < cache < 2.6e9 and 1.4e9 < cache_on < 1.7e9
+    assert cache - cache_on == up(4 * px * 7 * 16) - up(2 * 3 * px * 4)
+    assert 1.7e9 < cache < 2.3e9 and 1.4e9 < cache_on < 1.7e9
     # no activated last-level tensor for the head: the workspace shrinks too, never grows
     assert ws4_on <= ws4
 
