@@ -121,6 +121,7 @@ def lib():
             "wvd_decode_fuse_norm1": ([ctypes.c_int], ctypes.c_int),
             "wvd_decode_fuse_head": ([ctypes.c_int], ctypes.c_int),
             "wvd_decode_fuse_shortcut": ([ctypes.c_int], ctypes.c_int),
+            "wvd_fuse_norm_shortcut": ([ctypes.c_int], ctypes.c_int),
             "wvd_winograd_packed_bytes": ([ctypes.c_int, ctypes.c_int], ctypes.c_size_t),
             "wvd_winograd_pack": ([_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P], ctypes.c_int),
             "wvd_winograd_workspace_bytes": ([ctypes.c_int] * 6, ctypes.c_size_t),
@@ -150,7 +151,7 @@ def exported_symbols() -> Sequence[str]:
             "wvd_timing_launch", "wvd_conv_force_config", "wvd_timing_read_mem", "wvd_conv_max_workgroups",
             "wvd_calib_dma_copy", "wvd_winograd_packed_bytes", "wvd_winograd_pack", "wvd_winograd_workspace_bytes",
             "wvd_causal_conv3d_winograd", "wvd_decode_fuse_norm1", "wvd_decode_fuse_head",
-            "wvd_decode_fuse_shortcut"]
+            "wvd_decode_fuse_shortcut", "wvd_fuse_norm_shortcut"]
 
 
 def _check(status: int):
@@ -551,6 +552,12 @@ def decode_fuse_shortcut(on: bool):
     """wvd_decode_fuse_shortcut: apply a 192 -> 96 residual block's 1x1 shortcut in the epilogue
     of the x2 upsample that produces its input (default on)."""
     _check(lib().wvd_decode_fuse_shortcut(int(on)))
+
+
+def fuse_norm_shortcut(on: bool):
+    """wvd_fuse_norm_shortcut: run a 384 -> (up to) 192 residual block's norm1 + SiLU and its 1x1
+    shortcut as one pass over its input (default on; the same bits either way)."""
+    _check(lib().wvd_fuse_norm_shortcut(int(on)))
 
 
 def decode_fuse_head(on: bool):

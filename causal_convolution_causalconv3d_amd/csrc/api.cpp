@@ -115,11 +115,12 @@ enum MemKind {
   MEM_UNPATCH = 7,  // unpatchify (+ clamp) into the video
   MEM_WINO_IN = 8,  // the Winograd input transform
   MEM_WINO_OUT = 9, // the Winograd output transform
-  MEM_KINDS = 10
+  MEM_NORM_SC = 10, // a residual block's norm1 + SiLU and 1x1 shortcut from one read of its input
+  MEM_KINDS = 11
 };
 const char* const kMemKindNames[MEM_KINDS] = {"norm_silu", "head_stencil", "convert", "head_fused", "head_stream",
                                               "attn_softmax_transpose", "dup_add", "unpatchify", "winograd_in",
-                                              "winograd_out"};
+                                              "winograd_out", "norm_shortcut"};
 struct LaunchRecord {
   int config;
   float ms;
@@ -205,6 +206,24 @@ wvd_status run_norm(const bf16_t* x, const float* gamma, float eps, int silu, bf
                     hipStream_t s) {
   return run_mem(MEM_NORM_SILU, 4.0 * (double)P * C + 4.0 * C, s, "norm launch",
                  [&] { return launch_norm_silu(x, gamma, eps, silu, y, P, C, s); });
+}
+
+std::atomic<int> g_fuse_norm_sc{1};  // wvd_fuse_norm_shortcut
+
+// Whether a residual block's norm1 and shortcut of cin -> cout channels run as one pass.
+bool norm_sc_fused(int cin, int cout, const void* wsc, const float* bsc, const float* gamma) {
+  return g_fuse_norm_sc.load() && cin != cout && norm_shortcut_supported(cin, cout) && aligned16(wsc) &&
+         aligned16(bsc) && aligned16(gamma);
+}
+
+// norm1 + SiLU of x into a and the 1x1 shortcut of x into sc, one read of x: reads x, the packed
+// weight and gamma, writes both outputs.
+wvd_status run_norm_sc(const bf16_t* x, const float* gamma, float eps, bf16_t* a, const void* wsc, int cout,
+                       const float* bsc, bf16_t* sc, int64_t P, int C, hipStream_t s) {
+  const double bytes = 2.0 * P * C * 2.0 + 2.0 * (double)P * cout + 2.0 * (double)cout * C + 4.0 * C;
+  return run_mem(MEM_NORM_SC, bytes, s, "norm and shortcut launch", [&] {
+    return launch_norm_shortcut(x, P, C, gamma, eps, a, (const bf16_t*)wsc, cout, bsc, sc, s);
+  });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -601,13 +620,18 @@ wvd_status resblock_core(const ResblockArgs& r, hipStream_t s, F1 after_conv1, F
   const wvd_resblock_weights* w = r.w;
   const int64_t P = (int64_t)r.T * r.H * r.W;
   const bf16_t* residual = r.x;
-  if (w->cin != w->cout) {
-    ConvProblem sc = plain_problem(r.x, nullptr, r.T, r.H, r.W, w->cin, 0, w->shortcut, w->cout, 1, 1, 1,
-                                   w->shortcut_bias, r.sc, nullptr);
-    WVD_TRY(run_conv(sc, s, conv_flops(P, w->cout, w->cin)));
+  if (norm_sc_fused(w->cin, w->cout, w->shortcut, w->shortcut_bias, w->gamma1)) {
+    WVD_TRY(run_norm_sc(r.x, w->gamma1, r.eps, r.a, w->shortcut, w->cout, w->shortcut_bias, r.sc, P, w->cin, s));
     residual = r.sc;
+  } else {
+    if (w->cin != w->cout) {
+      ConvProblem sc = plain_problem(r.x, nullptr, r.T, r.H, r.W, w->cin, 0, w->shortcut, w->cout, 1, 1, 1,
+                                     w->shortcut_bias, r.sc, nullptr);
+      WVD_TRY(run_conv(sc, s, conv_flops(P, w->cout, w->cin)));
+      residual = r.sc;
+    }
+    WVD_TRY(run_norm(r.x, w->gamma1, r.eps, 1, r.a, P, w->cin, s));
   }
-  WVD_TRY(run_norm(r.x, w->gamma1, r.eps, 1, r.a, P, w->cin, s));
   ConvProblem c1 = plain_problem(r.a, r.hist1, r.T, r.H, r.W, w->cin, r.th1, w->conv1, w->cout, 3, 3, 3, w->bias1, r.h,
                                  nullptr);
   // conv2's input a2 = SiLU(norm2(h)): fused into conv1's epilogue when one workgroup holds every
@@ -1579,6 +1603,11 @@ wvd_status decode_chunk_impl(const wvd_decoder_desc* d, const void* packed, wvd_
     if (sc_ready) {
       if (r.cin == r.cout || !pre_act) return fail(WVD_ERR_STATE, "a fused shortcut needs the pre-activated input");
       residual = bsc;
+    } else if (!pre_act && norm_sc_fused(r.cin, r.cout, W_(r.ws), F_(r.bs), F_(r.gamma1))) {
+      // norm1 and the shortcut from one read of x
+      WVD_TRY(run_norm_sc(x, F_(r.gamma1), d->eps, ba, W_(r.ws), r.cout, F_(r.bs), bsc, P, r.cin, s));
+      residual = bsc;
+      pre_act = true;
     } else if (r.cin != r.cout) {
       ConvProblem sc = plain_problem(x, nullptr, (int)T, H, Wd, r.cin, 0, W_(r.ws), r.cout, 1, 1, 1, F_(r.bs), bsc, nullptr);
       WVD_TRY(run_conv(sc, s, conv_flops(P, r.cout, r.cin)));
@@ -1978,6 +2007,11 @@ extern "C" wvd_status wvd_conv_force_config(int config) {
 
 extern "C" wvd_status wvd_decode_fuse_norm1(int on) {
   g_fuse_norm1.store(on ? 1 : 0);
+  return WVD_OK;
+}
+
+extern "C" wvd_status wvd_fuse_norm_shortcut(int on) {
+  g_fuse_norm_sc.store(on ? 1 : 0);
   return WVD_OK;
 }
 

@@ -156,6 +156,12 @@ hipError_t launch_conv_fp32(const float* x, const float* hist, const float* w, c
                             int T, int H, int W, int Th, int Co, int kt, int kh, int kw, int layout_ncthw,
                             hipStream_t s);
 
+// A residual block's norm1 + SiLU (act, [P][C]) and 1x1 shortcut (sc = W x + bias, [P][N]) from
+// one read of x [P][C] (NTHWC bf16): C = 384, N a multiple of 32 up to 192, wpk the shortcut's
+// packed weight (rows of C channels); both outputs equal the separate norm and 1x1 conv bit for bit.
+bool norm_shortcut_supported(int C, int N);
+hipError_t launch_norm_shortcut(const bf16_t* x, int64_t positions, int C, const float* gamma, float eps, bf16_t* act,
+                                const bf16_t* wpk, int N, const float* bias, bf16_t* sc, hipStream_t s);
 hipError_t launch_norm_silu(const bf16_t* x, const float* gamma, float eps, int silu, bf16_t* y, int64_t positions,
                             int C, hipStream_t s);
 

@@ -354,6 +354,14 @@ wvd_status wvd_decode_fuse_norm1(int on);
  * are bitwise independent of the pass size. Process-wide; not for use while another thread
  * decodes. */
 wvd_status wvd_decode_fuse_shortcut(int on);
+/* Tuning: with on != 0 (the default), a residual block whose channel count changes from 384 to
+ * at most 192 (a multiple of 32) takes its norm1 + SiLU and its 1x1 shortcut (the page's residual
+ * block: the input feeds both the normalised branch and, when cin != cout, the shortcut) from
+ * one read of its input, in one kernel, instead of in two passes that each read it; both outputs
+ * are bitwise the same either way. Used by wvd_resblock, wvd_resblock_noalloc and the decode
+ * calls when the weights, bias and gamma are 16-byte aligned. Process-wide; not for use while
+ * another thread runs those calls. */
+wvd_status wvd_fuse_norm_shortcut(int on);
 /* Memory option: with on != 0, a decoder whose last stage is a spatial x2 upsample (no time
  * step, no DupUp3D) of 65-96 channels and whose head is conv_out to at most 3 colours (no
  * unpatchify or clamp) runs that upsample, norm_out + SiLU and the head as one kernel per pass:

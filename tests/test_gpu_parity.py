@@ -416,6 +416,47 @@ def test_resblock_shortcut_and_histories_match_oracle():
     assert rel_max(a1_last, a1[:, -2:]) <= 2e-2
 
 
+def test_norm_shortcut_pass_same_bits_as_separate_passes():
+    """wvd_fuse_norm_shortcut: a 384 -> 192 block's norm1 + SiLU and 1x1 shortcut from one read of
+    its input give the same bits as the separate norm and 1x1 conv passes (several 256-position
+    tiles and a ragged tail; the activated input checked through conv1's saved history)."""
+    cfg = wl.resblock_bf16(seed=15, C=384, T=3, H=19, W=45, Cout=192, hist_frames=0)
+    wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
+    xd = to_dev_nthwc(cfg["x"])
+    outs = {}
+    try:
+        for fused in (False, True):
+            wvd.fuse_norm_shortcut(fused)
+            o1 = torch.empty((1, 2, 19, 45, 384), dtype=torch.bfloat16, device="cuda")
+            y = wvd.resblock(xd, wts, 1e-6, hist1_out=o1)
+            torch.cuda.synchronize()
+            outs[fused] = (y.clone(), o1.clone())
+    finally:
+        wvd.fuse_norm_shortcut(True)
+    assert torch.equal(outs[True][1], outs[False][1])
+    assert torch.equal(outs[True][0], outs[False][0])
+    log("norm + shortcut pass: same bits as the separate passes")
+
+
+def test_full_channel_decoder_norm_shortcut_same_bits():
+    """The decoder's 384 -> 192 block with norm1 and the shortcut in one pass (default) against
+    the separate passes: the same video."""
+    spec = wl.FULL_DECODER
+    hw = (3, 5)
+    z, params = wl.decoder_weights(spec, seed=51, latent_frames=2, latent_hw=hw)
+    zd = z.to(torch.bfloat16).cuda()
+    vids = {}
+    try:
+        for fused in (False, True):
+            wvd.fuse_norm_shortcut(fused)
+            dec = _gpu_decoder(spec, params, hw)
+            vids[fused] = dec.decode(zd, frames_per_pass=1).clone()
+            torch.cuda.synchronize()
+    finally:
+        wvd.fuse_norm_shortcut(True)
+    assert torch.equal(vids[True], vids[False])
+
+
 # ---------------------------------------------------------------------------------------------
 # Upsampling
 # ---------------------------------------------------------------------------------------------
