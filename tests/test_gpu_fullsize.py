@@ -19,8 +19,14 @@
     alone, in passes of 5 latent frames, bitwise its one-shot decode): PSNR over the samples and
     on each sampled frame (frame 0, both sides of the GPU's and the oracle's first pass
     boundaries, a later boundary, frame 120), and each frame's mean and mean square over all of
-    its pixels.
+    its pixels;
+  * the Wan2.2 TI2V-5B topology at 704x1248 (random weights, 2 latent frames -> 5 frames, clamp
+    off): against the oracle's decode in two passes of one latent frame
+    (tests/golden/real_decode_samples.npz, written by make_real_golden.py from the oracle alone),
+    the GPU decoding both latent frames in one pass, so the oracle's pass boundary is not one of
+    the GPU's.
 """
+import dataclasses
 import math
 import os
 
@@ -36,6 +42,7 @@ from gpu_util import bf16_elementwise_ok, from_dev_nthwc, log, psnr, rel_max, to
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "decoder_onepass_samples.npz")
 STREAM_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "stream_decode_samples.npz")
+REAL_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "real_decode_samples.npz")
 
 
 def test_resblock_full_size():
@@ -276,3 +283,43 @@ def test_real_topology_full_size_streaming_properties():
     torch.cuda.synchronize()
     assert torch.equal(v[:, :, :13], v4[:, :, :13])  # latent frames 0..3 -> video frames 0..12
     assert not torch.equal(v[:, :, 13:], v4[:, :, 13:])
+
+
+def test_real_topology_full_size_against_oracle_samples():
+    """The real topology without the clamp (random weights put most values outside [-1, 1]; the
+    clamp is pinned as clamped == clip(unclamped) on small decoders): 2 latent frames -> 5 frames
+    at 704x1248, one GPU pass against the oracle's two, PSNR over the stored samples and on each
+    frame, and each frame's mean and mean square."""
+    if not os.path.exists(REAL_GOLDEN):
+        pytest.skip("real-topology golden samples not generated (tests/golden/make_real_golden.py)")
+    g = np.load(REAL_GOLDEN)
+    spec = dataclasses.replace(wl.REAL_DECODER, clamp=False)
+    z, params = wl.decoder_weights(spec, seed=4, latent_frames=2)
+    dec = wvd.Decoder(wvd.desc_from_spec(spec), params)
+    del params
+    v = dec.decode(z.to(torch.bfloat16).cuda(), frames_per_pass=2)
+    torch.cuda.synchronize()
+    assert tuple(v.shape) == (1, 3, 5, 704, 1248)
+    video = v[0].float()
+    flat = video.reshape(-1)
+    got = flat[torch.from_numpy(g["index"]).cuda()].cpu().numpy().astype(np.float64)
+    ref = g["value"].astype(np.float64)
+    rng = float(g["vmax"] - g["vmin"])
+    err = got - ref
+    q = 10 * math.log10(rng * rng / float((err ** 2).mean()))
+    log(f"real topology vs oracle: psnr {q:.2f} dB over {ref.size} samples, max abs {np.abs(err).max():.3e}, "
+        f"range {rng:.3f}")
+    assert q >= 55.0
+    frame = (g["index"] // (704 * 1248)) % 5
+    for f in range(5):
+        e = err[frame == f]
+        qf = 10 * math.log10(rng * rng / float((e ** 2).mean()))
+        log(f"  frame {f}: psnr {qf:.2f} dB over {e.size} samples, max abs {np.abs(e).max():.3e}")
+        assert qf >= 55.0, f
+    per_frame = video.permute(1, 0, 2, 3).reshape(5, -1).double()
+    mean = per_frame.mean(dim=1).cpu().numpy()
+    meansq = (per_frame ** 2).mean(dim=1).cpu().numpy()
+    dm = np.abs(mean - g["frame_mean"]).max() / rng
+    dq = np.abs(meansq / g["frame_meansq"] - 1.0).max()
+    log(f"  per-frame mean: max |diff| {dm:.2e} of the range; mean square: max rel diff {dq:.2e}")
+    assert dm <= 1e-3 and dq <= 1e-2
