@@ -416,11 +416,13 @@ def test_resblock_shortcut_and_histories_match_oracle():
     assert rel_max(a1_last, a1[:, -2:]) <= 2e-2
 
 
-def test_norm_shortcut_pass_same_bits_as_separate_passes():
-    """wvd_fuse_norm_shortcut: a 384 -> 192 block's norm1 + SiLU and 1x1 shortcut from one read of
+@pytest.mark.parametrize("cout", [192, 160, 96])
+def test_norm_shortcut_pass_same_bits_as_separate_passes(cout):
+    """wvd_fuse_norm_shortcut: a 384 -> cout block's norm1 + SiLU and 1x1 shortcut from one read of
     its input give the same bits as the separate norm and 1x1 conv passes (several 256-position
-    tiles and a ragged tail; the activated input checked through conv1's saved history)."""
-    cfg = wl.resblock_bf16(seed=15, C=384, T=3, H=19, W=45, Cout=192, hist_frames=0)
+    tiles and a ragged tail; product passes of 96 and 64 outputs; the activated input checked
+    through conv1's saved history)."""
+    cfg = wl.resblock_bf16(seed=15, C=384, T=3, H=19, W=45, Cout=cout, hist_frames=0)
     wts = wvd.pack_resblock(cfg["params"], "res", "cuda")
     xd = to_dev_nthwc(cfg["x"])
     outs = {}
@@ -435,7 +437,7 @@ def test_norm_shortcut_pass_same_bits_as_separate_passes():
         wvd.fuse_norm_shortcut(True)
     assert torch.equal(outs[True][1], outs[False][1])
     assert torch.equal(outs[True][0], outs[False][0])
-    log("norm + shortcut pass: same bits as the separate passes")
+    log(f"norm + shortcut pass 384 -> {cout}: same bits as the separate passes")
 
 
 def test_full_channel_decoder_norm_shortcut_same_bits():
