@@ -604,6 +604,11 @@ def main():
             print(f"{key}: {configs[key]['ms_per_call']} ms", file=sys.stderr, flush=True)
         line["configs"] = configs
     line["achievable"] = achievable_peaks()
+    # context for the roofline fraction: the dominant conv against what the chip's own library GEMM
+    # sustains here (the bf16 figure assumes a clock that matrix work with random operands does
+    # not hold under the power limit)
+    line["roofline"]["frac_of_library_gemm"] = round(line["roofline"]["achieved"] /
+                                                     line["achievable"]["bf16_gemm_tflops"], 4)
     if cpu:
         cb = cpu_stream_sample()
         cb["host"] = host_info()
