@@ -469,8 +469,10 @@ hipError_t launch_head_stream(const bf16_t* x, int T, int H, int W, int C, int C
                               const float* bias, int Co, bf16_t* video, int64_t frames, int fbase, const float* cin,
                               float* cout, hipStream_t s) {
   if (T == 0 || H == 0 || W == 0) return hipSuccess;
-  if (!head_stream_supported(Cip, Co) || C > Cip || (int64_t)H * W * C * 2 >= ((int64_t)1 << 31) || !cout ||
-      cout == cin || ((uintptr_t)cin & 15u) || ((uintptr_t)cout & 15u))
+  // (the kernel indexes a frame's bytes and the carry's float4 planes, 2 x 7 per position, in 32 bits)
+  if (!head_stream_supported(Cip, Co) || C > Cip || (int64_t)H * W * C * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)H * W * 2 * HS_CP >= ((int64_t)1 << 31) || !cout || cout == cin || ((uintptr_t)cin & 15u) ||
+      ((uintptr_t)cout & 15u))
     return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)((H + HF_OROWS - 1) / HF_OROWS) * ((W + HF_OCOLS - 1) / HF_OCOLS);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
