@@ -1312,6 +1312,239 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
   run_copy_share(p.copy);
 }
 
+// LDS-DMA GEMM for the convolutions without spatial taps (1x1x1 convs and the (3,1,1) time conv):
+// the K loop of the linear kernel (32-channel chunk outermost, temporal taps inside, the same
+// operand layout per lane, so the same sums bit for bit), with both operands staged through LDS
+// by buffer loads that write LDS. A workgroup of 4 waves owns 128 positions of one frame x BN =
+// 2 * NB * 32 channels; the waves form a 2 x 2 grid, each 64 positions x NB * 32 channels (two
+// position blocks and NB channel blocks: every fragment read from LDS feeds two or NB matrix
+// ops). A K step stages 128 activation rows and BN weight rows of 32 channels (64 bytes each) in
+// one of four LDS stages; a row's four 16-byte pieces are stored XOR-swizzled by bits 2-3 of the
+// row, so the fragment reads of 16 consecutive rows fall on distinct banks without a pad. Step k
+// fetches step k + 3 into the stage that step k - 1 finished; before the barrier that ends step
+// k each wave waits for its own fetches of step k + 2 (the fragments of its first half are read
+// during step k + 1). Two workgroups (80 KB of LDS each at BN = 192) share a CU, so one's
+// epilogue overlaps the other's matrix work. The epilogue is the staged one, a position row of
+// 32 at a time.
+template <int NB>
+__global__ __launch_bounds__(256, 2) void conv_gemm_dma_kernel(const ConvProblem p) {
+  constexpr int WAVES = 4, MB = 2;
+  constexpr int BM = 2 * MB * 32;          // positions per tile
+  constexpr int BN = 2 * NB * 32;          // channels per tile
+  constexpr int ALOADS = BM * 4 / 64;      // 1 KB loads of a step's activation rows
+  constexpr int BLOADS = BN * 4 / 64;      // and of its weight rows
+  static_assert(ALOADS % WAVES == 0 && BLOADS % WAVES == 0, "loads per wave");
+  constexpr int AIW = ALOADS / WAVES, BIW = BLOADS / WAVES, LPW = AIW + BIW;
+  constexpr int SBYTES = (ALOADS + BLOADS) * 1024;
+  static_assert(4 * SBYTES <= 81920, "two workgroups per CU");
+  __shared__ __attribute__((aligned(16))) bf16_t lds_s0[SBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_s1[SBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_s2[SBYTES / 2];
+  __shared__ __attribute__((aligned(16))) bf16_t lds_s3[SBYTES / 2];
+  auto sbuf = [&](auto I) -> bf16_t* {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return lds_s0;
+    else if constexpr (i == 1) return lds_s1;
+    else if constexpr (i == 2) return lds_s2;
+    else return lds_s3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // Tile: frame tf, positions m0 .. m0 + BM - 1 of it, channels n0 .. n0 + BN - 1. Each XCD
+  // takes a contiguous range of tiles, channel tiles fastest (they share the activation rows in
+  // L2), then the frames of one position range (the temporal taps of neighbouring frames meet
+  // in L2).
+  const int HW = p.H * p.W;
+  const int tpf = (HW + BM - 1) / BM;
+  const int numN = (p.Npad + BN - 1) / BN;
+  const int total = p.T * tpf * numN;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int q8 = total >> 3, r8 = total & 7;
+  const int lin = xcd * q8 + (xcd < r8 ? xcd : r8) + local;
+  const int mt = lin / numN, nt = lin - (lin / numN) * numN;
+  const int tf = mt % p.T, m0 = (mt / p.T) * BM, n0 = nt * BN;
+
+  const int dt0 = -2 * (p.kt >> 1);
+  const int nchunks = p.Cip >> 5;
+  const int nk = p.kt * nchunks;
+  const int64_t frame_elems = (int64_t)HW * p.Ci;
+  const uint32_t frame_bytes = (uint32_t)(frame_elems * 2);
+  const int64_t wrow = (int64_t)p.ntaps * p.Cip;
+  const bf16_t* wbase = p.wpk + (int64_t)n0 * wrow;
+  const __amdgpu_buffer_rsrc_t rs_w =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, (int)((int64_t)(p.Npad - n0) * wrow * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_dead = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, (short)0, 0, 0x00020000);
+
+  // This lane's pieces: load L (of its wave) covers rows 16 L .. 16 L + 15 of the stage, lane l
+  // the row's LDS piece l % 4, which holds its 8-channel group l % 4 ^ (l / 16) % 4.
+  const int part = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t aoff[AIW], boff[BIW];
+#pragma unroll
+  for (int i = 0; i < AIW; ++i) {
+    const int m = m0 + (i * WAVES + wave) * 16 + (lane >> 2);
+    aoff[i] = m < HW ? (uint32_t)((m * p.Ci + part * 8) * 2) : frame_bytes;
+  }
+#pragma unroll
+  for (int i = 0; i < BIW; ++i) {
+    const int row = (i * WAVES + wave) * 16 + (lane >> 2);
+    boff[i] = (uint32_t)((row * wrow + part * 8) * 2);
+  }
+  // Fragment reads: row base + l32 (base a multiple of 32), 16-byte group half * 2 + q.
+  uint32_t fo[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) fo[q] = (uint32_t)(l32 * 64 + (((half * 2 + q) ^ ((l32 >> 2) & 3)) * 16));
+
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  struct Cur {
+    int step, chunk, ti;
+  };
+  auto advance = [&](Cur& c) {
+    const bool wrap = c.ti + 1 == p.kt;
+    c.ti = wrap ? 0 : c.ti + 1;
+    c.chunk += wrap ? 1 : 0;
+    c.step += 1;
+  };
+  // fetch K step c into stage SS (steps past the last one read nothing and write zeros)
+  auto fetch = [&](auto SS, const Cur& c) __attribute__((always_inline)) {
+    char* base = (char*)sbuf(SS);
+    const bool live = c.step < nk;
+    const int sf = tf + dt0 + c.ti;
+    const bool fok = live & (sf >= -p.Th);
+    const bf16_t* fb = (sf >= 0) ? p.x + (int64_t)sf * frame_elems
+                                 : ((sf >= -p.Th) ? p.hist + (int64_t)(sf + p.Th) * frame_elems : p.x);
+    const __amdgpu_buffer_rsrc_t rs_a =
+        __builtin_amdgcn_make_buffer_rsrc((void*)fb, (short)0, fok ? (int)frame_bytes : 0, 0x00020000);
+    const bool cok = c.chunk * 32 + part * 8 < p.Ci;
+#pragma unroll
+    for (int i = 0; i < AIW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void*)(base + (i * WAVES + wave) * 1024), 16,
+                                               (int)(cok ? aoff[i] + c.chunk * 64 : frame_bytes), 0, 0, 0);
+    const int col = c.ti * p.Cip + c.chunk * 32;
+    const __amdgpu_buffer_rsrc_t rs_b = live ? rs_w : rs_dead;
+#pragma unroll
+    for (int i = 0; i < BIW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void*)(base + (ALOADS + i * WAVES + wave) * 1024), 16,
+                                               (int)(boff[i] + col * 2), 0, 0, 0);
+  };
+
+  u32x4 wf[2][NB];
+  u32x4 af[2][MB];
+  auto read_frags = [&](u32x4 (&w)[NB], u32x4 (&a)[MB], auto SS, int q) __attribute__((always_inline)) {
+    const char* base = (const char*)sbuf(SS);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      w[nb] = *(const u32x4*)(base + (BM + (wn * NB + nb) * 32) * 64 + fo[q]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) a[mb] = *(const u32x4*)(base + ((wm * MB + mb) * 32) * 64 + fo[q]);
+  };
+
+  floatx16 acc[NB][MB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
+  auto compute = [&](const u32x4 (&w)[NB], const u32x4 (&a)[MB]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[nb]),
+                                                              __builtin_bit_cast(bf16x8, a[mb]), acc[nb][mb], 0, 0, 0);
+  };
+
+  // prologue: steps 0, 1, 2 into stages 0, 1, 2; steps 0 and 1 landed before the first reads
+  Cur cf = {0, 0, 0};
+  fetch(I0{}, cf);
+  advance(cf);
+  fetch(I1{}, cf);
+  advance(cf);
+  fetch(I2{}, cf);
+  advance(cf);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+  lds_barrier();
+  read_frags(wf[0], af[0], I0{}, 0);
+
+  constexpr int NM = MB * NB;
+  auto step = [&](auto SS) __attribute__((always_inline)) {
+    constexpr int S = decltype(SS)::value;  // k % 4
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(std::integral_constant<int, (S + 3) & 3>{}, cf);  // step k + 3, into the stage of step k - 1
+    advance(cf);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(wf[1], af[1], SS, 1);
+    compute(wf[0], af[0]);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(wf[0], af[0], std::integral_constant<int, (S + 1) & 3>{}, 0);  // step k + 1's first half
+    compute(wf[1], af[1]);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x006, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // own fetches of step k + 2 have landed (only step k + 3's may still be in flight)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
+    lds_barrier();
+  };
+  int k = 0;
+  for (; k + 4 <= nk; k += 4) {
+    step(I0{});
+    step(I1{});
+    step(I2{});
+    step(I3{});
+  }
+  const int rem = nk - k;
+  if (rem > 0) step(I0{});
+  if (rem > 1) step(I1{});
+  if (rem > 2) step(I2{});
+
+  // the fetches past the last step land before the stages become staging areas
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  constexpr int NBP = (NB % 3 == 0) ? 3 : ((NB % 2 == 0) ? 2 : 1);
+  constexpr int SB = StagedShape<NBP>::BYTES;
+  static_assert(3 * SB <= SBYTES, "staging areas");
+  char* st = wave < 3 ? (char*)lds_s0 + wave * SB : (char*)lds_s1;
+  // the frame as one row of H*W positions: a wave's 32 positions are consecutive in the output
+  ConvProblem q = p;
+  q.H = 1;
+  q.W = HW;
+  q.Ho = 1;
+  q.Wo = HW;
+  const int row0[1] = {0};
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    floatx16 a1[NB][1];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) a1[nb][0] = acc[nb][mb];
+    conv_epilogue_staged<NB, 1, false, NBP>(q, a1, row0, m0 + (wm * MB + mb) * 32, tf, n0 + wn * NB * 32, 0, 0,
+                                            lane, st);
+  }
+  run_copy_share(p.copy);
+}
+
 // DMA conv kernels without a fused norm run persistent workgroups (one per resident slot,
 // several tiles each).
 constexpr bool kPersistentDmaTiles = true;
@@ -1325,57 +1558,60 @@ struct ConfigEntry {
   int phase_in_x;  // the x2 phases are part of the linear block index (grid z = 1)
   int staged;      // the kernel has the LDS-staged epilogue (used when ConvProblem allows it)
   int wgs_per_cu;  // workgroups resident per CU (a DMA kernel then walks several tiles each)
+  int gemm;        // conv_gemm_dma_kernel: 2 x 2 waves of mb x nb blocks, one tile per workgroup
   void (*kernel)(const ConvProblem);       // plain epilogue (bias, residual, fp32 planes)
   void (*kernel_norm)(const ConvProblem);  // fused RMS norm (+ SiLU) epilogue
   void (*kernel_dual)(const ConvProblem);  // fused norm + the pre-norm value stored too (or null)
 };
 
 #define WVD_CONV_CONFIG(NB, MB, W) \
-  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, 0, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
+  { "conv_mfma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 0, 0, 0, 0, 0, 0, conv_mfma_kernel<NB, MB, W, false>, \
     conv_mfma_kernel<NB, MB, W, true>, nullptr }
 // 3x3-tap halo convs order tiles time-fastest (measured 2-8% faster than frame-major on every
 // 3x3x3 layer: fewer input re-reads past L2); the phase convs have no temporal taps.
 #define WVD_HALO_CONFIG(NB, MB, W) \
-  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 0, 0, conv_halo_kernel<NB, MB, W, 3, false>, \
+  { "conv_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 0, 0, 0, conv_halo_kernel<NB, MB, W, 3, false>, \
     conv_halo_kernel<NB, MB, W, 3, true>, nullptr }
 #define WVD_HALO_DMA_CONFIG(NB, MB, W) \
   { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, dma_waves_per_simd<NB, MB, 3>() * 4 / W, \
-    conv_halo_dma_kernel<NB, MB, W, 3, false>, \
+    0, conv_halo_dma_kernel<NB, MB, W, 3, false>, \
     conv_halo_dma_kernel<NB, MB, W, 3, true>, nullptr }
 // (the one-tile widths a residual block's conv2 takes at 96 and 192 channels: also the dual store)
 #define WVD_HALO_DMA_DUAL_CONFIG(NB, MB, W) \
   { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, dma_waves_per_simd<NB, MB, 3>() * 4 / W, \
-    conv_halo_dma_kernel<NB, MB, W, 3, false>, \
+    0, conv_halo_dma_kernel<NB, MB, W, 3, false>, \
     conv_halo_dma_kernel<NB, MB, W, 3, true>, conv_halo_dma_kernel<NB, MB, W, 3, true, true> }
 // (no fused-norm instantiation: the norm needs every channel in one tile, and the 96- and 192-wide
 // tiles cover those widths)
 #define WVD_HALO_DMA_PLAIN_CONFIG(NB, MB, W) \
   { "conv_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 3, 1, 0, 1, dma_waves_per_simd<NB, MB, 3>() * 4 / W, \
-    conv_halo_dma_kernel<NB, MB, W, 3, false>, nullptr, nullptr }
+    0, conv_halo_dma_kernel<NB, MB, W, 3, false>, nullptr, nullptr }
 #define WVD_PHASE_HALO_DMA_CONFIG(NB, MB, W) \
   { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<NB, MB, 2>() * 4 / W, \
-    conv_halo_dma_kernel<NB, MB, W, 2, false>, \
+    0, conv_halo_dma_kernel<NB, MB, W, 2, false>, \
     conv_halo_dma_kernel<NB, MB, W, 2, true>, nullptr }
 // (192 channels in one tile, for a fused norm of that width with the pre-norm value stored too:
 // the x2 upsample that feeds a 192-channel residual block)
 #define WVD_PHASE_HALO_DMA_DUAL_CONFIG(NB, MB, W) \
   { "conv_phase_halo_dma_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<NB, MB, 2>() * 4 / W, \
-    conv_halo_dma_kernel<NB, MB, W, 2, false>, \
+    0, conv_halo_dma_kernel<NB, MB, W, 2, false>, \
     conv_halo_dma_kernel<NB, MB, W, 2, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, true> }
 // The fused tail: the x2 phase conv with norm_out + SiLU and the output head in one kernel (only
 // for problems with head_w set, never chosen or forced for others).
 #define WVD_TAIL_CONFIG(NB, MB, W) \
   { "conv_tail_phase_head_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, 0, \
-    conv_halo_dma_kernel<NB, MB, W, 2, true, false, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, false, true>, \
+    0, conv_halo_dma_kernel<NB, MB, W, 2, true, false, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, false, true>, \
     nullptr }
 // The 192-wide x2 phase tile with the dual store whose pre-norm value is replaced by its 1x1
 // product (ConvProblem::y_sc; only for problems with y_sc set, never chosen or forced for others).
 #define WVD_PHASE_SC_CONFIG(NB, MB, W) \
   { "conv_phase_halo_dma_sc_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<NB, MB, 2>() * 4 / W, \
-    conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true>, \
+    0, conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true>, \
     conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true> }
+#define WVD_GEMM_DMA_CONFIG(NB) \
+  { "conv_gemm_dma_n" #NB "_m2_w4", NB, 2, 4, 0, 0, 0, 1, 0, 1, conv_gemm_dma_kernel<NB>, nullptr, nullptr }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
-  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
+  { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, 0, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
     conv_halo_kernel<NB, MB, W, 2, true>, nullptr }
 
 // Two waves per SIMD (8-wave workgroups, or two 4-wave workgroups per CU) measured faster than
@@ -1407,6 +1643,8 @@ enum ConfigId {
   PHASE_DMA_N6_M1_W8,  // x2 upsampling phases: 192 x (8 rows x 32 columns), one row per wave, 112 KB
   TAIL_N3_M1_W8,       // the fused tail: PHASE_DMA_N3_M1_W8's tiles, all phases and frames of a block
   PHASE_DMA_SC_N6_M1_W8,  // PHASE_DMA_N6_M1_W8's dual store with the shortcut product (y_sc)
+  GEMM_N3_W4,      // 1x1 and (3,1,1) convs: 192 x 128 GEMM tiles, both operands LDS-DMA staged
+  GEMM_N2_W4,      // the same, 128 x 128: channel counts that are multiples of 128, not of 192
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -1418,6 +1656,7 @@ const ConfigEntry kConfigs[] = {
     WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),    WVD_HALO_DMA_CONFIG(1, 2, 8),
     WVD_CONV_CONFIG(4, 1, 8),           WVD_HALO_DMA_CONFIG(3, 2, 4),    WVD_HALO_DMA_PLAIN_CONFIG(4, 2, 8),
     WVD_PHASE_HALO_DMA_DUAL_CONFIG(6, 1, 8), WVD_TAIL_CONFIG(3, 1, 8), WVD_PHASE_SC_CONFIG(6, 1, 8),
+    WVD_GEMM_DMA_CONFIG(3),             WVD_GEMM_DMA_CONFIG(2),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -1427,6 +1666,10 @@ constexpr int round_up_int(int v, int m) { return (v + m - 1) / m * m; }
 // Workgroups of a problem: per frame ceil(H*W / BM) position tiles (halo kernels: ceil(H / rows)
 // x ceil(W / 32)), times the channel tiles.
 int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t H, int64_t W, int Npad) {
+  if (c.gemm) {
+    const int64_t bn = (int64_t)c.nb * 64, bm = (int64_t)c.mb * 64;
+    return T * ((H * W + bm - 1) / bm) * ((Npad + bn - 1) / bn);
+  }
   const int64_t bn = (int64_t)c.nb * 32;
   const int64_t nt = (Npad + bn - 1) / bn;
   if (c.halo) {
@@ -1435,6 +1678,16 @@ int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t H, int64_t W, int Np
   }
   const int64_t bm = (int64_t)c.waves * c.mb * 32;
   return T * ((H * W + bm - 1) / bm) * nt;
+}
+
+// The GEMM kernel's problems: no spatial taps or phases, the plain output mapping (time-interleaved
+// frames allowed), no fused norm, second output or fused tail, and the staged epilogue's
+// conditions (bf16 output, N and nsplit multiples of 8, y and the residual 16-byte aligned).
+bool gemm_fits(const ConvProblem& p) {
+  const bool plain_map = p.phases == 1 && p.hmul == 1 && p.wmul == 1 && p.Ho == p.H && p.Wo == p.W;
+  return plain_map && p.kh == 1 && p.kw == 1 && p.ntaps == p.kt && !p.norm_gamma && !p.y_pre && !p.y_sc &&
+         !p.head_w && !p.y_f32 && p.Ci % 8 == 0 && p.N % 8 == 0 && p.nsplit % 8 == 0 &&
+         ((uintptr_t)p.y & 15) == 0 && ((uintptr_t)p.res & 15) == 0;
 }
 
 // Convolutions with 3x3 spatial taps take the LDS-DMA halo kernel with 96 x (16 x 32) tiles
@@ -1481,6 +1734,10 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   // a fused norm over 97-192 channels: all of them in one 192-wide phase tile
   if (phases == 4 && p.kh == 2 && p.kw == 2 && one_n_tile && Npad <= 192) return PHASE_DMA_N6_M1_W8;
   if (phases == 4 && p.kh == 2 && p.kw == 2 && !one_n_tile) return PHASE_DMA_N3_W4;
+  // Convolutions without spatial taps (1x1x1, the (3,1,1) time conv) of at least 128 output
+  // channels: the GEMM tiles, 192 wide unless 128-wide ones pad less
+  if (Npad >= 128 && gemm_fits(p))
+    return ((Npad + 191) / 192 * 192 <= (Npad + 127) / 128 * 128) ? GEMM_N3_W4 : GEMM_N2_W4;
   const auto fills = [&](int id) { return blocks_for(kConfigs[id], T, H, W, Npad) * phases >= cus; };
   const int n96 = (p.ntaps >= 9 && fills(LIN_N3_M2_W8)) ? LIN_N3_M2_W8 : LIN_N3_W8;
   if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup
@@ -1519,6 +1776,7 @@ bool conv_config_fits(const ConvProblem& p, int id) {
   const ConfigEntry& c = kConfigs[id];
   if (c.halo == 3 && !(p.phases == 1 && p.kh == 3 && p.kw == 3)) return false;
   if (c.halo == 2 && !(p.phases == 4 && p.kh == 2 && p.kw == 2)) return false;
+  if (c.gemm && !gemm_fits(p)) return false;
   if (p.norm_gamma && (c.nb * 32 < p.Npad || !c.kernel_norm)) return false;
   if (p.y_pre && (!p.norm_gamma || !c.kernel_dual)) return false;
   return true;
@@ -1584,6 +1842,7 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   q.staged = (c.staged || lin_staged) && !p.y_f32 && p.N % 8 == 0 && p.nsplit % 8 == 0 &&
              ((uintptr_t)p.y & 15) == 0 && ((uintptr_t)p.res & 15) == 0 && ((uintptr_t)p.y_pre & 15) == 0;
   if ((p.y_pre || p.y_sc) && !q.staged) return hipErrorNotSupported;  // the dual store exists staged only
+  if (c.gemm && !q.staged) return hipErrorNotSupported;                // (gemm_fits implies staged)
   int64_t gx = c.phase_in_x ? blocks * p.phases : blocks;
   if (c.wgs_per_cu) {
     // DMA kernels: a multiple of 8 workgroups (XCD ranges); with persistent tiles no more than

@@ -119,8 +119,10 @@ def test_bf16_conv_every_config_matches_oracle(case):
             try:
                 y = wvd.causal_conv3d(xd, wp, Co, kernel=k, bias=bd, hist=hd)
             except wvd.WvdError as e:
-                # (phase tiles, and the fused tail, which runs only with the head attached)
-                assert e.status == 8 and name.startswith(("conv_phase_halo", "conv_tail")), (name, str(e))
+                # (phase tiles, the fused tail, which runs only with the head attached, and the GEMM
+                # tiles, which take convs without spatial taps only)
+                assert e.status == 8 and name.startswith(("conv_phase_halo", "conv_tail", "conv_gemm")), (name, str(e))
+                assert not (name.startswith("conv_gemm") and k[1:] == (1, 1)), (name, str(e))
                 continue
             torch.cuda.synchronize()
             ok, worst = bf16_elementwise_ok(from_dev_nthwc(y), ref)
@@ -128,7 +130,55 @@ def test_bf16_conv_every_config_matches_oracle(case):
             ran += 1
     finally:
         wvd.conv_force_config(None)
-    assert ran == len([n for n in names if not n.startswith(("conv_phase_halo", "conv_tail"))])
+    tapless = k[1:] == (1, 1)
+    assert ran == len([n for n in names if not n.startswith(("conv_phase_halo", "conv_tail"))
+                       and (tapless or not n.startswith("conv_gemm"))])
+
+
+GEMM_CASES = [
+    # Ci, Co, T, H, W, kernel, Th, residual
+    (384, 768, 2, 44, 78, (3, 1, 1), 2, False),  # the first level's time conv (a ragged last tile per frame)
+    (192, 200, 3, 11, 13, (3, 1, 1), 1, True),   # a partial channel tile, one history frame, a residual
+    (48, 256, 2, 7, 9, (1, 1, 1), 0, False),     # a partial 32-channel chunk (Ci 48)
+    (1024, 512, 2, 5, 7, (1, 1, 1), 0, True),    # the real topology's shortcut width, a residual
+    (96, 384, 1, 16, 16, (3, 1, 1), 2, False),   # one frame, its first two taps in the history; 256 positions
+    (256, 128, 5, 3, 5, (3, 1, 1), 0, False),    # no history (the first frames' early taps read zeros), tiny frames
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: "x".join(map(str, c[:5])) + f"_k{''.join(map(str, c[5]))}_h{c[6]}"
+                         + ("_res" if c[7] else ""))
+def test_gemm_tiles_same_bits_as_linear_kernel(case):
+    """The LDS-DMA GEMM tiles of the convs without spatial taps keep the linear kernel's K order and
+    per-lane operand layout, so both of their widths give its bits; the automatic choice too; and
+    against the oracle (below a size the oracle finishes quickly) the single-op bar."""
+    Ci, Co, T, H, W, k, Th, with_res = case
+    log(f"gemm tiles {case}")
+    seed = Ci * 3 + Co * 5 + T * 7 + H * 11 + W * 13 + Th
+    x = wl.bf16_values(_rand((1, Ci, T, H, W), seed))
+    w = wl.bf16_values(wl.kaiming(torch.Generator().manual_seed(seed + 1), (Co, Ci) + k))
+    b = 0.1 * _rand((Co,), seed + 2)
+    hist = wl.bf16_values(_rand((1, Ci, Th, H, W), seed + 3)) if Th else None
+    res = wl.bf16_values(_rand((1, Co, T, H, W), seed + 4)) if with_res else None
+    xd, wp, bd = to_dev_nthwc(x), wvd.conv_pack(w.cuda()), b.cuda()
+    hd = None if hist is None else to_dev_nthwc(hist)
+    rd = None if res is None else to_dev_nthwc(res)
+    names = wvd.conv_config_names()
+    outs = {}
+    try:
+        for name in ("conv_mfma_n3_m1_w8", "conv_gemm_dma_n3_m2_w4", "conv_gemm_dma_n2_m2_w4", None):
+            wvd.conv_force_config(None if name is None else names.index(name))
+            outs[name] = wvd.causal_conv3d(xd, wp, Co, kernel=k, bias=bd, hist=hd, residual=rd)
+        torch.cuda.synchronize()
+    finally:
+        wvd.conv_force_config(None)
+    base = outs["conv_mfma_n3_m1_w8"]
+    for name, y in outs.items():
+        assert torch.equal(y, base), name
+    if not with_res and Ci * Co * k[0] * T * H * W < 1e9:
+        ref = oracle.causal_conv3d(x[0], w, b, None if hist is None else hist[0])
+        ok, worst = bf16_elementwise_ok(from_dev_nthwc(base), ref)
+        assert ok, worst
 
 
 @pytest.mark.parametrize("C,T,H,W", [(96, 2, 19, 37), (192, 1, 9, 40), (384, 2, 5, 7)])
@@ -155,9 +205,9 @@ def test_spatial_upsample_every_config_matches_oracle(C, T, H, W):
                 y = wvd.upsample(xd, spatial=wp, spatial_bias=bd)
             except wvd.WvdError as e:
                 # (3x3 halo tiles; the fused tail and the shortcut-product tile, which run only
-                # with the head or the shortcut attached)
-                assert e.status == 8 and name.startswith(("conv_halo", "conv_tail", "conv_phase_halo_dma_sc")), (
-                    name, str(e))
+                # with the head or the shortcut attached; the GEMM tiles of convs without spatial taps)
+                assert e.status == 8 and name.startswith(("conv_halo", "conv_tail", "conv_phase_halo_dma_sc",
+                                                          "conv_gemm")), (name, str(e))
                 continue
             torch.cuda.synchronize()
             assert torch.equal(y, auto), name
