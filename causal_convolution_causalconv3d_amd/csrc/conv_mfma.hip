@@ -1790,6 +1790,8 @@ hipError_t launch_conv_mfma(const ConvProblem& p, hipStream_t s, int* config_id,
   if (p.T == 0 || HW == 0) return hipSuccess;
   // one frame is addressed with 32-bit byte offsets
   if (HW * p.Ci * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  // and one phase's packed weight rows (the DMA and GEMM tiles' weight buffer ranges)
+  if ((int64_t)p.Npad * p.ntaps * p.Cip * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if (p.head_w) {
     // the fused tail: an x2 phase conv of N -> N channels with norm_out + SiLU, no history,
     // residual or second output, a head of at most 3 colours; one workgroup per block
