@@ -1315,28 +1315,30 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
 // LDS-DMA GEMM for the convolutions without spatial taps (1x1x1 convs and the (3,1,1) time conv):
 // the K loop of the linear kernel (32-channel chunk outermost, temporal taps inside, the same
 // operand layout per lane, so the same sums bit for bit), with both operands staged through LDS
-// by buffer loads that write LDS. A workgroup of 4 waves owns 128 positions of one frame x BN =
-// 2 * NB * 32 channels; the waves form a 2 x 2 grid, each 64 positions x NB * 32 channels (two
-// position blocks and NB channel blocks: every fragment read from LDS feeds two or NB matrix
-// ops). A K step stages 128 activation rows and BN weight rows of 32 channels (64 bytes each) in
-// one of four LDS stages; a row's four 16-byte pieces are stored XOR-swizzled by bits 2-3 of the
-// row, so the fragment reads of 16 consecutive rows fall on distinct banks without a pad. Step k
-// fetches step k + 3 into the stage that step k - 1 finished; before the barrier that ends step
-// k each wave waits for its own fetches of step k + 2 (the fragments of its first half are read
-// during step k + 1). Two workgroups (80 KB of LDS each at BN = 192) share a CU, so one's
-// epilogue overlaps the other's matrix work. The epilogue is the staged one, a position row of
-// 32 at a time.
-template <int NB>
-__global__ __launch_bounds__(256, 2) void conv_gemm_dma_kernel(const ConvProblem p) {
-  constexpr int WAVES = 4, MB = 2;
-  constexpr int BM = 2 * MB * 32;          // positions per tile
-  constexpr int BN = 2 * NB * 32;          // channels per tile
+// by buffer loads that write LDS. A workgroup owns BM = WM * 64 positions of one frame x BN =
+// WN * NB * 32 channels; its waves form a WM x WN grid, each 64 positions x NB * 32 channels
+// (two position blocks and NB channel blocks: every fragment read from LDS feeds two or NB
+// matrix ops). A K step stages BM activation rows and BN weight rows of 32 channels (64 bytes
+// each) in one of four LDS stages; a row's four 16-byte pieces are stored XOR-swizzled by bits
+// 2-3 of the row, so the fragment reads of 16 consecutive rows fall on distinct banks without a
+// pad. Step k fetches step k + 3 into the stage that step k - 1 finished; before the barrier
+// that ends step k each wave waits for its own fetches of step k + 2 (the fragments of its first
+// half are read during step k + 1). Two tile shapes: 4 waves (2 x 2, 128 x 192 or 128 x 128,
+// 80 or 64 KB of LDS), two workgroups per CU so that one's epilogue overlaps the other's matrix
+// work; and 8 waves (4 x 2, 256 x 256, 128 KB), one per CU, whose LDS traffic per matrix op is
+// a fifth lower (each staged row feeds more of them), for grids that fill the chip. The epilogue is the staged one, a position row of 32 at a time.
+template <int NB, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64, (WM * WN == 4) ? 2 : 1) void conv_gemm_dma_kernel(const ConvProblem p) {
+  constexpr int WAVES = WM * WN, MB = 2;
+  static_assert((WM == 2 && WN == 2) || (WM == 4 && WN == 2 && NB == 4), "the 4- and 8-wave tiles");
+  constexpr int BM = WM * MB * 32;          // positions per tile
+  constexpr int BN = WN * NB * 32;          // channels per tile
   constexpr int ALOADS = BM * 4 / 64;      // 1 KB loads of a step's activation rows
   constexpr int BLOADS = BN * 4 / 64;      // and of its weight rows
   static_assert(ALOADS % WAVES == 0 && BLOADS % WAVES == 0, "loads per wave");
   constexpr int AIW = ALOADS / WAVES, BIW = BLOADS / WAVES, LPW = AIW + BIW;
   constexpr int SBYTES = (ALOADS + BLOADS) * 1024;
-  static_assert(4 * SBYTES <= 81920, "two workgroups per CU");
+  static_assert(4 * SBYTES <= (WAVES == 4 ? 81920 : 163840), "LDS (4 waves: two workgroups per CU)");
   __shared__ __attribute__((aligned(16))) bf16_t lds_s0[SBYTES / 2];
   __shared__ __attribute__((aligned(16))) bf16_t lds_s1[SBYTES / 2];
   __shared__ __attribute__((aligned(16))) bf16_t lds_s2[SBYTES / 2];
@@ -1358,7 +1360,7 @@ __global__ __launch_bounds__(256, 2) void conv_gemm_dma_kernel(const ConvProblem
   const int wave = tid >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
 
   // Tile: frame tf, positions m0 .. m0 + BM - 1 of it, channels n0 .. n0 + BN - 1. Each XCD
   // takes a contiguous range of tiles, channel tiles fastest (they share the activation rows in
@@ -1525,8 +1527,9 @@ __global__ __launch_bounds__(256, 2) void conv_gemm_dma_kernel(const ConvProblem
   lds_barrier();
   constexpr int NBP = (NB % 3 == 0) ? 3 : ((NB % 2 == 0) ? 2 : 1);
   constexpr int SB = StagedShape<NBP>::BYTES;
-  static_assert(3 * SB <= SBYTES, "staging areas");
-  char* st = wave < 3 ? (char*)lds_s0 + wave * SB : (char*)lds_s1;
+  constexpr int CAP = SBYTES / SB;  // staging areas per stage
+  static_assert(2 * CAP >= WAVES, "staging areas");
+  char* st = wave < CAP ? (char*)lds_s0 + wave * SB : (char*)lds_s1 + (wave - CAP) * SB;
   // the frame as one row of H*W positions: a wave's 32 positions are consecutive in the output
   ConvProblem q = p;
   q.H = 1;
@@ -1558,7 +1561,8 @@ struct ConfigEntry {
   int phase_in_x;  // the x2 phases are part of the linear block index (grid z = 1)
   int staged;      // the kernel has the LDS-staged epilogue (used when ConvProblem allows it)
   int wgs_per_cu;  // workgroups resident per CU (a DMA kernel then walks several tiles each)
-  int gemm;        // conv_gemm_dma_kernel: 2 x 2 waves of mb x nb blocks, one tile per workgroup
+  int gemm;        // conv_gemm_dma_kernel's WM (waves along the positions; waves / WM along the
+                   // channels, each mb x nb blocks), one tile per workgroup; or 0
   void (*kernel)(const ConvProblem);       // plain epilogue (bias, residual, fp32 planes)
   void (*kernel_norm)(const ConvProblem);  // fused RMS norm (+ SiLU) epilogue
   void (*kernel_dual)(const ConvProblem);  // fused norm + the pre-norm value stored too (or null)
@@ -1608,8 +1612,9 @@ struct ConfigEntry {
   { "conv_phase_halo_dma_sc_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 1, 1, dma_waves_per_simd<NB, MB, 2>() * 4 / W, \
     0, conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true>, conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true>, \
     conv_halo_dma_kernel<NB, MB, W, 2, true, true, false, true> }
-#define WVD_GEMM_DMA_CONFIG(NB) \
-  { "conv_gemm_dma_n" #NB "_m2_w4", NB, 2, 4, 0, 0, 0, 1, 0, 1, conv_gemm_dma_kernel<NB>, nullptr, nullptr }
+#define WVD_GEMM_DMA_CONFIG(NB, WM, WN) \
+  { "conv_gemm_dma_n" #NB "_m2_w" #WM "x" #WN, NB, 2, WM * WN, 0, 0, 0, 1, 0, WM, conv_gemm_dma_kernel<NB, WM, WN>, \
+    nullptr, nullptr }
 #define WVD_PHASE_HALO_CONFIG(NB, MB, W) \
   { "conv_phase_halo_n" #NB "_m" #MB "_w" #W, NB, MB, W, 2, 0, 0, 0, 0, 0, conv_halo_kernel<NB, MB, W, 2, false>, \
     conv_halo_kernel<NB, MB, W, 2, true>, nullptr }
@@ -1645,6 +1650,7 @@ enum ConfigId {
   PHASE_DMA_SC_N6_M1_W8,  // PHASE_DMA_N6_M1_W8's dual store with the shortcut product (y_sc)
   GEMM_N3_W4,      // 1x1 and (3,1,1) convs: 192 x 128 GEMM tiles, both operands LDS-DMA staged
   GEMM_N2_W4,      // the same, 128 x 128: channel counts that are multiples of 128, not of 192
+  GEMM_N4_W8,      // 256 x 256 on 8 waves, one workgroup per CU: grids that fill the chip
   NUM_CONFIGS
 };
 const ConfigEntry kConfigs[] = {
@@ -1656,7 +1662,7 @@ const ConfigEntry kConfigs[] = {
     WVD_PHASE_HALO_DMA_CONFIG(3, 1, 8), WVD_HALO_DMA_CONFIG(2, 2, 8),    WVD_HALO_DMA_CONFIG(1, 2, 8),
     WVD_CONV_CONFIG(4, 1, 8),           WVD_HALO_DMA_CONFIG(3, 2, 4),    WVD_HALO_DMA_PLAIN_CONFIG(4, 2, 8),
     WVD_PHASE_HALO_DMA_DUAL_CONFIG(6, 1, 8), WVD_TAIL_CONFIG(3, 1, 8), WVD_PHASE_SC_CONFIG(6, 1, 8),
-    WVD_GEMM_DMA_CONFIG(3),             WVD_GEMM_DMA_CONFIG(2),
+    WVD_GEMM_DMA_CONFIG(3, 2, 2),       WVD_GEMM_DMA_CONFIG(2, 2, 2),    WVD_GEMM_DMA_CONFIG(4, 4, 2),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 static_assert(kNumConfigs == NUM_CONFIGS, "one table entry per ConfigId");
@@ -1667,7 +1673,7 @@ constexpr int round_up_int(int v, int m) { return (v + m - 1) / m * m; }
 // x ceil(W / 32)), times the channel tiles.
 int64_t blocks_for(const ConfigEntry& c, int64_t T, int64_t H, int64_t W, int Npad) {
   if (c.gemm) {
-    const int64_t bn = (int64_t)c.nb * 64, bm = (int64_t)c.mb * 64;
+    const int64_t bn = (int64_t)c.nb * 32 * (c.waves / c.gemm), bm = (int64_t)c.mb * 32 * c.gemm;
     return T * ((H * W + bm - 1) / bm) * ((Npad + bn - 1) / bn);
   }
   const int64_t bn = (int64_t)c.nb * 32;
@@ -1735,9 +1741,15 @@ int choose_config(const ConvProblem& p, bool one_n_tile) {
   if (phases == 4 && p.kh == 2 && p.kw == 2 && one_n_tile && Npad <= 192) return PHASE_DMA_N6_M1_W8;
   if (phases == 4 && p.kh == 2 && p.kw == 2 && !one_n_tile) return PHASE_DMA_N3_W4;
   // Convolutions without spatial taps (1x1x1, the (3,1,1) time conv) of at least 128 output
-  // channels: the GEMM tiles, 192 wide unless 128-wide ones pad less
-  if (Npad >= 128 && gemm_fits(p))
-    return ((Npad + 191) / 192 * 192 <= (Npad + 127) / 128 * 128) ? GEMM_N3_W4 : GEMM_N2_W4;
+  // channels: the GEMM tiles. The 8-wave 256 x 256 tiles where their grid gives every CU a
+  // workgroup and their width pads no more than the 4-wave ones (measured 15-36 % faster on the
+  // decodes' big time convs and shortcuts, as fast on the 88x156 level); else 4-wave tiles, 192
+  // wide unless 128-wide ones pad less
+  if (Npad >= 128 && gemm_fits(p)) {
+    const int p256 = (Npad + 255) / 256 * 256, p192 = (Npad + 191) / 192 * 192, p128 = (Npad + 127) / 128 * 128;
+    if (p256 <= std::min(p192, p128) && blocks_for(kConfigs[GEMM_N4_W8], T, H, W, Npad) >= cus) return GEMM_N4_W8;
+    return (p192 <= p128) ? GEMM_N3_W4 : GEMM_N2_W4;
+  }
   const auto fills = [&](int id) { return blocks_for(kConfigs[id], T, H, W, Npad) * phases >= cus; };
   const int n96 = (p.ntaps >= 9 && fills(LIN_N3_M2_W8)) ? LIN_N3_M2_W8 : LIN_N3_W8;
   if (one_n_tile) {  // a fused norm needs every channel of a position in one workgroup

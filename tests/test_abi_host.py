@@ -33,8 +33,8 @@ def test_conv_configuration_table():
     include the 3x3x3 halo tiles, the x2 phase tiles and both GEMM tiles of the tapless convs."""
     names = wvd.conv_config_names()
     assert len(names) == len(set(names))
-    assert {"conv_halo_dma_n3_m2_w8", "conv_phase_halo_dma_n3_m1_w8", "conv_gemm_dma_n3_m2_w4",
-            "conv_gemm_dma_n2_m2_w4", "conv_mfma_n6_m1_w8"} <= set(names)
+    assert {"conv_halo_dma_n3_m2_w8", "conv_phase_halo_dma_n3_m1_w8", "conv_gemm_dma_n3_m2_w2x2",
+            "conv_gemm_dma_n2_m2_w2x2", "conv_gemm_dma_n4_m2_w4x2", "conv_mfma_n6_m1_w8"} <= set(names)
 
 
 def test_param_table_matches_the_workload_names_and_shapes():

@@ -150,8 +150,9 @@ GEMM_CASES = [
                          + ("_res" if c[7] else ""))
 def test_gemm_tiles_same_bits_as_linear_kernel(case):
     """The LDS-DMA GEMM tiles of the convs without spatial taps keep the linear kernel's K order and
-    per-lane operand layout, so both of their widths give its bits; the automatic choice too; and
-    against the oracle (below a size the oracle finishes quickly) the single-op bar."""
+    per-lane operand layout, so all three tile shapes (4 and 8 waves, 128 to 256 channels) give its
+    bits; the automatic choice too; and against the oracle (below a size the oracle finishes
+    quickly) the single-op bar."""
     Ci, Co, T, H, W, k, Th, with_res = case
     log(f"gemm tiles {case}")
     seed = Ci * 3 + Co * 5 + T * 7 + H * 11 + W * 13 + Th
@@ -166,7 +167,8 @@ def test_gemm_tiles_same_bits_as_linear_kernel(case):
     names = wvd.conv_config_names()
     outs = {}
     try:
-        for name in ("conv_mfma_n3_m1_w8", "conv_gemm_dma_n3_m2_w4", "conv_gemm_dma_n2_m2_w4", None):
+        for name in ("conv_mfma_n3_m1_w8", "conv_gemm_dma_n3_m2_w2x2", "conv_gemm_dma_n2_m2_w2x2",
+                     "conv_gemm_dma_n4_m2_w4x2", None):
             wvd.conv_force_config(None if name is None else names.index(name))
             outs[name] = wvd.causal_conv3d(xd, wp, Co, kernel=k, bias=bd, hist=hd, residual=rd)
         torch.cuda.synchronize()
