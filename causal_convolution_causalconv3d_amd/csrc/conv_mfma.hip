@@ -1326,7 +1326,8 @@ __global__ __launch_bounds__(WAVES * 64, TAIL ? 1 : (dma_waves_per_simd<NB, MB, 
 // half are read during step k + 1). Two tile shapes: 4 waves (2 x 2, 128 x 192 or 128 x 128,
 // 80 or 64 KB of LDS), two workgroups per CU so that one's epilogue overlaps the other's matrix
 // work; and 8 waves (4 x 2, 256 x 256, 128 KB), one per CU, whose LDS traffic per matrix op is
-// a fifth lower (each staged row feeds more of them), for grids that fill the chip. The epilogue is the staged one, a position row of 32 at a time.
+// a fifth lower (each staged row feeds more of them), for grids that fill the chip. The epilogue
+// is the staged one, a position row of 32 at a time.
 template <int NB, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64, (WM * WN == 4) ? 2 : 1) void conv_gemm_dma_kernel(const ConvProblem p) {
   constexpr int WAVES = WM * WN, MB = 2;
