@@ -13,7 +13,8 @@
 Command line (prints markdown):
   python -m causal_convolution_causalconv3d_amd.profiling stats <rocprof kernel_stats.csv> [--command CMD]
   python -m causal_convolution_causalconv3d_amd.profiling traffic --config NAME --fetch DIR --write DIR
-      --copy-fetch DIR --copy-write DIR --copy-mib N [--command CMD ...]
+      --copy-fetch DIR --copy-write DIR --copy-mib N [--copy-kernel neg|dma_copy] [--workload TEXT]
+      [--command CMD ...]
   python -m causal_convolution_causalconv3d_amd.profiling mfma <rocprof counter_collection.csv> [--command CMD]
   python -m causal_convolution_causalconv3d_amd.profiling calib --fetch DIR --write DIR --copy-mib N [--command CMD ...]
   python -m causal_convolution_causalconv3d_amd.profiling lds <rocprof counter_collection.csv> [--command CMD]
@@ -147,8 +148,11 @@ def calib_summary(fetch: str, write: str, copy_mib: int, commands: List[str]) ->
     return "\n".join(lines) + "\n"
 
 
+STREAM_DECODE = "the streaming decode (704x1248, 4 latent frames per pass)"
+
+
 def traffic_summary(config: str, fetch: str, write: str, copy_fetch: str, copy_write: str, copy_mib: int,
-                    commands: List[str], copy_kernel: str = "neg") -> str:
+                    commands: List[str], copy_kernel: str = "neg", workload: str = STREAM_DECODE) -> str:
     sym = kernel_symbol(config)
     is_kernel = lambda name: sym in name  # noqa: E731
     is_copy = lambda name: copy_kernel in name  # noqa: E731
@@ -167,7 +171,7 @@ def traffic_summary(config: str, fetch: str, write: str, copy_fetch: str, copy_w
     fetch_b = kf_kib * 1024.0 * f_scale
     write_b = kw_kib * 1024.0 * w_scale
     lines = [
-        f"# HBM traffic of {config} in the streaming decode (704x1248, 4 latent frames per pass)",
+        f"# HBM traffic of {config} in {workload}",
         "",
         "Counters: rocprofv3 `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE` (KiB per dispatch), one run each,",
         "averaged over every dispatch of the kernel; scaled by the same counters on a copy kernel",
@@ -315,6 +319,7 @@ def main(argv=None):
         tr.add_argument(f"--{k}", required=True)
     tr.add_argument("--copy-mib", type=int, required=True)
     tr.add_argument("--copy-kernel", choices=sorted(COPY_KERNELS), default="neg")
+    tr.add_argument("--workload", default=STREAM_DECODE, help="what the counted run decoded (the title)")
     tr.add_argument("--command", action="append", default=[])
     ca = sub.add_parser("calib")
     ca.add_argument("--fetch", required=True)
@@ -345,7 +350,7 @@ def main(argv=None):
         sys.stdout.write(calib_summary(a.fetch, a.write, a.copy_mib, a.command))
     else:
         sys.stdout.write(traffic_summary(a.config, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.command,
-                                         a.copy_kernel))
+                                         a.copy_kernel, a.workload))
 
 
 if __name__ == "__main__":
