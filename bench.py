@@ -416,7 +416,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--frames-per-pass", type=int, default=4)
+    ap.add_argument("--frames-per-pass", type=int, default=None,
+                    help="latent frames per pass (default 4; with --topology real 2 through the late stages, "
+                         "4 through the early ones: the same speed at 16.9 instead of 22.9 GiB)")
     ap.add_argument("--early-frames-per-pass", type=int, default=0, metavar="N",
                     help="latent frames per pass through the stages up to the last temporal upsample "
                          "(per-level pass sizes; the later stages keep --frames-per-pass); 0: same")
@@ -487,6 +489,10 @@ def main():
     dec = wvd.Decoder(wvd.desc_from_spec(spec), params)
     del params
     fpp = args.frames_per_pass
+    if fpp is None:
+        fpp = 2 if real else 4
+        if real and args.early_frames_per_pass == 0:
+            args.early_frames_per_pass = 4
     early = max(args.early_frames_per_pass, fpp)
     F = dec.video_frames(args.latent_frames, fpp)
     video = torch.empty(wvd.video_shape(dec.desc, F), dtype=torch.bfloat16, device="cuda")
